@@ -1,0 +1,216 @@
+"""Benchmark of the all-mode matrix-free MTTKRP on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload c2] [--no-cpu]
+
+One step is one all-mode sweep (MTTKRP of every mode, in mode order, on one
+stream) over a tensor and factors already resident in HBM.  The default
+workload is the 256x256x256 fp64 tensor built from an exact rank-32 CP model
+plus Gaussian noise of standard deviation 1e-3, R = 32.  Other workloads (--workload) are for
+exploration; the JSON line names the one measured.
+
+Printed: one JSON line with the whole-job throughput (GFLOP/s, flops per mode
+2 * R * prod(I)), a roofline object for the MTTKRP launches (algorithmic
+bytes or flops per launch over their average duration, from HIP events on the
+library's stream inside the timed region), a cold-cache measurement (a 1 GiB
+buffer is written before each mode so the tensor cannot be served from the
+256 MB last-level cache), and the CPU oracle timed on a bounded sample of the
+same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PEAK_TFLOPS = {"f64": 78.6, "f32": 157.3}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c2",
+                    choices=["c1", "c2", "c3", "c4r8", "c4r64", "c4r512", "c5"])
+    ap.add_argument("--cold-reps", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the MTTKRP shards by slabs of the first mode; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from mttkrp_matrix_free_amd import api, inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t0 = time.time()
+    p = inputs.workload(args.workload)
+    log(f"[bench] workload {p.name} generated in {time.time() - t0:.1f} s")
+    dims = p.dims
+    d = len(dims)
+    R = p.rank
+    N = int(np.prod(dims))
+    s = p.X.dtype.itemsize
+    dt_name = "f64" if s == 8 else "f32"
+    X = torch.from_numpy(p.X).to(dev)
+    U = [torch.from_numpy(u).to(dev) for u in p.factors]
+    outs = [torch.empty((dims[m], R), dtype=X.dtype, device=dev) for m in range(d)]
+    ws_bytes = api.all_workspace_bytes(dims, R, X.dtype)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    flops_mode = 2.0 * R * N
+    bytes_mode = [s * (N + R * sum(dims[m] for m in range(d) if m != n) + R * dims[n])
+                  for n in range(d)]
+
+    def step(events=None):
+        for n in range(d):
+            if events is not None:
+                events[n][0].record(stream)
+            api.mttkrp(X, U, n, out=outs[n], ws=ws, stream=stream)
+            if events is not None:
+                events[n][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` all-mode sweeps, back to back ----
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+           for _ in range(d)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        step(ev[k])
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    wall = t_end - t_start
+    ms_per_step = wall * 1e3 / args.steps
+    mode_ms = [[ev[k][n][0].elapsed_time(ev[k][n][1]) for k in range(args.steps)]
+               for n in range(d)]
+    mode_avg = [float(np.mean(v)) for v in mode_ms]
+    value = d * flops_mode / (wall / args.steps) / 1e9
+
+    # ---- cold cache: a 1 GiB write before each mode, outside the event pair ----
+    cold = None
+    if args.cold_reps > 0:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        cms = [[] for _ in range(d)]
+        for _ in range(args.cold_reps):
+            for n in range(d):
+                flush.zero_()
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                api.mttkrp(X, U, n, out=outs[n], ws=ws, stream=stream)
+                b.record(stream)
+                torch.cuda.synchronize()
+                cms[n].append(a.elapsed_time(b))
+        del flush
+        cold_med = [float(np.median(v)) for v in cms]
+        cold = {
+            "ms_per_mode_median": [round(v, 5) for v in cold_med],
+            "gflops_all_mode": round(d * flops_mode / (sum(cold_med) / 1e3) / 1e9, 2),
+            "tensor_gbs_per_mode": [round(N * s / (v / 1e3) / 1e9, 1) for v in cold_med],
+            "reps": args.cold_reps,
+        }
+
+    # ---- roofline of the MTTKRP launches (per mode: tile kernel + split reduce) ----
+    ai = [flops_mode / b for b in bytes_mode]
+    peak_f = PEAK_TFLOPS[dt_name] * 1e12
+    ridge = peak_f / (HBM_PEAK_GBS * 1e9)
+    hbm_bound = float(np.mean(ai)) < ridge
+    tot_t = sum(mode_avg) / 1e3
+    if hbm_bound:
+        achieved = sum(bytes_mode) / tot_t / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = d * flops_mode / tot_t / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS[dt_name],
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS[dt_name], 4)}
+    roof["traffic"] = None
+    roof["per_launch_ms"] = [round(v, 5) for v in mode_avg]
+    roof["algorithmic_bytes_per_launch"] = bytes_mode
+    roof["flops_per_launch"] = flops_mode
+
+    # ---- CPU oracle on a bounded sample of the same workload ----
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        cores = len(os.sched_getaffinity(0))
+        nthreads = min(cores, 16)
+        done_flops = 0.0
+        t_cpu = 0.0
+        rows_done = [0] * d
+        budget = args.cpu_seconds
+        chunk = max(1, nthreads)
+        while t_cpu < budget:
+            progressed = False
+            for n in range(d):
+                if rows_done[n] >= dims[n] or t_cpu >= budget:
+                    continue
+                rr = list(range(rows_done[n], min(dims[n], rows_done[n] + chunk)))
+                a = time.perf_counter()
+                oracle.mttkrp(p.X, p.factors, n, rows=rr, nthreads=nthreads)
+                t_cpu += time.perf_counter() - a
+                done_flops += flops_mode * len(rr) / dims[n]
+                rows_done[n] += len(rr)
+                progressed = True
+            if not progressed:
+                break
+        cpu = {"value": round(done_flops / t_cpu / 1e9, 4), "unit": "GFLOP/s", "cores": nthreads,
+               "kind": "oracle",
+               "sample": f"output rows {rows_done} of modes 0..{d - 1} "
+                         f"({t_cpu:.1f} s; long-double oracle, OpenMP over rows)"}
+        log(f"[bench] cpu oracle {cpu}")
+
+    cfg = {"workload": p.name, "dims": list(dims), "rank": R, "modes": list(range(d)),
+           "step": "all-mode MTTKRP sweep", "cache": "warm (back-to-back sweeps)"}
+    line = {
+        "metric": "MTTKRP GFLOP/s (all-mode avg) and % of HBM/FP64 roofline, 1 MI355X",
+        "value": round(value, 2),
+        "unit": "GFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt_name,
+        "data": "synthetic",
+        "config": cfg,
+        "roofline": roof,
+        "cold_cache": cold,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,152 @@
+/*
+ * mttkrp.h -- C ABI of the matrix-free dense MTTKRP library for MI355X (gfx950).
+ *
+ * The operation ("A Performance Portable Matrix Free Dense MTTKRP in GenTen",
+ * abstract and TL;DR): the matricized tensor times Khatri-Rao product, the
+ * workhorse kernel of CP decompositions.  For mode n of a d-way dense tensor X
+ * with factor matrices U_m (I_m x R),
+ *
+ *     M(i_n, r) = sum over every i_m, m != n, of  X(i_0..i_{d-1}) * prod_{m != n} U_m(i_m, r),
+ *
+ * i.e. X_(n) times the Khatri-Rao product of the other factors, with the mode-n
+ * unfolding of "An HPC Approach to Accelerate Tensor Decompositions", Sec. 2.
+ * The Khatri-Rao matrix is never formed: extra device memory grows like
+ * R * sum(I_m), never like R * prod(I_m) (GenTen page, TL;DR).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  Pointers   X, factors[m], out, outs[m], lambda and ws point to DEVICE memory.
+ *             dims, the factors/outs pointer arrays, fit_hist, iters_done and
+ *             info point to HOST memory that is read or written during the call
+ *             only.  The library keeps no pointer after it returns.
+ *  Layout     X is row-major (C order) over dims: the last mode has unit stride.
+ *             U_m is I_m x R row-major.  out is I_n x R row-major.  A column-major
+ *             caller passes reversed dims, a reversed factor list and
+ *             mode' = order - 1 - mode.
+ *  Modes      0-based: mode in [0, order).  order in [3, 5].
+ *  Semantics  out is overwritten.  factors[mode] is not read (may be NULL).
+ *             out must not alias X, a factor or ws.
+ *  Ownership  The caller allocates and frees every buffer, including the
+ *             workspace ws, whose size the *_workspace_bytes queries return.
+ *             The library allocates no device memory.
+ *  Alignment  every device pointer must be 16-byte aligned (EALIGN otherwise).
+ *  Streams    `stream` is a hipStream_t (NULL: the default stream).  mttkrp*
+ *             calls only enqueue work and return; cp_als* synchronise the
+ *             stream once per sweep to read back the fit.
+ *  Errors     every argument is checked on the host before any HIP call; a bad
+ *             argument returns its code and touches nothing.  A launch failure
+ *             returns MTTKRP_EHIP.  A fault during execution surfaces at the
+ *             caller's next synchronisation.  Nothing is printed.
+ *  Threads    calls are reentrant; calls that share a ws buffer must not overlap.
+ */
+#ifndef MTTKRP_AMD_MTTKRP_H
+#define MTTKRP_AMD_MTTKRP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define MTTKRP_OK 0
+#define MTTKRP_EINVAL (-1)     /* null pointer, dims[m] < 1, rank < 1, mode out of range, iters < 0 */
+#define MTTKRP_EORDER (-2)     /* order not in [3, 5] */
+#define MTTKRP_ERANGE (-3)     /* a size overflows int64 or exceeds the library's index range */
+#define MTTKRP_EALIGN (-4)     /* a device pointer is not 16-byte aligned */
+#define MTTKRP_EWORKSPACE (-5) /* ws_bytes smaller than the size the query returns */
+#define MTTKRP_EHIP (-6)       /* a HIP runtime call or kernel launch failed */
+#define MTTKRP_ENOTSPD (-7)    /* CP-ALS: a Cholesky pivot of the R x R system was not positive */
+
+/* Text for a status code (static storage; never NULL). */
+const char *mttkrp_strerror(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int mttkrp_version(void);
+
+/* ---- workspace queries ----
+ * Write to *bytes the device workspace the matching call needs (0 is possible)
+ * for elem_bytes = 8 (fp64) or 4 (fp32).  It holds fp64 partial sums of the
+ * output from at most 1024 independent chunks (four workgroups per compute
+ * unit): at most 8 * 1024 * I_n * R + 256 bytes for one mode, so it grows
+ * with R * I_n and never with the Khatri-Rao size R * prod_{m != n} I_m. */
+int mttkrp_workspace_bytes(const int64_t *dims, int order, int64_t rank, int mode,
+                           int elem_bytes, size_t *bytes);
+int mttkrp_all_workspace_bytes(const int64_t *dims, int order, int64_t rank, int elem_bytes,
+                               size_t *bytes);
+int cp_als_workspace_bytes(const int64_t *dims, int order, int64_t rank, int elem_bytes,
+                           size_t *bytes);
+
+/* ---- MTTKRP of one mode ----
+ * out (I_mode x R) = X_(mode) times the Khatri-Rao product of every other factor.
+ * fp64: arithmetic in fp64.  fp32: fp32 products, accumulation of each
+ * contraction over at most one tensor fiber in fp32 and every longer sum in
+ * fp64; out is rounded to fp32 once. */
+int mttkrp_f64(const double *X, const int64_t *dims, int order, const double *const *factors,
+               int64_t rank, int mode, double *out, void *ws, size_t ws_bytes, void *stream);
+int mttkrp_f32(const float *X, const int64_t *dims, int order, const float *const *factors,
+               int64_t rank, int mode, float *out, void *ws, size_t ws_bytes, void *stream);
+
+/* ---- MTTKRP of every mode (the all-mode sweep of the GenTen page, Fig. 4) ----
+ * outs[m] (I_m x R) for m = 0..order-1, in mode order, on one stream.  X is
+ * read once per mode. */
+int mttkrp_all_f64(const double *X, const int64_t *dims, int order, const double *const *factors,
+                   int64_t rank, double *const *outs, void *ws, size_t ws_bytes, void *stream);
+int mttkrp_all_f32(const float *X, const int64_t *dims, int order, const float *const *factors,
+                   int64_t rank, float *const *outs, void *ws, size_t ws_bytes, void *stream);
+
+/* ---- CP-ALS driver (GenTen page, Fig. 5: MTTKRP plus inner product and
+ * Cholesky solve per step) ----
+ * Gauss-Seidel sweeps over the modes.  For mode n: V = Hadamard of the Grams
+ * U_m^T U_m (m != n); M = MTTKRP_n; V = L L^T (Cholesky, no pivoting);
+ * U_n <- M V^{-1}; lambda_r = ||U_n(:, r)||_2; columns with lambda_r > 0 are
+ * scaled to unit norm.  After the last mode the fit
+ *     1 - sqrt(max(0, ||X||^2 + ||model||^2 - 2 <X, model>)) / ||X||
+ * is read back to fit_hist[it] (HOST, length iters; NaN past the last sweep
+ * run).  factors: in = initial factors, out = final factors (DEVICE).
+ * lambda: DEVICE, length R.  tol > 0 stops after the first sweep whose fit
+ * changed by less than tol; tol <= 0 runs exactly iters sweeps.
+ * *iters_done (HOST) = sweeps run.  A non-positive Cholesky pivot stops the
+ * run with MTTKRP_ENOTSPD; the factors then hold the values of the failing
+ * step's start.  The R x R solve runs in fp64 for both element types. */
+int cp_als_f64(const double *X, const int64_t *dims, int order, int64_t rank,
+               double *const *factors, double *lambda, int iters, double tol, double *fit_hist,
+               int *iters_done, void *ws, size_t ws_bytes, void *stream);
+int cp_als_f32(const float *X, const int64_t *dims, int order, int64_t rank,
+               float *const *factors, float *lambda, int iters, double tol, double *fit_hist,
+               int *iters_done, void *ws, size_t ws_bytes, void *stream);
+
+/* ---- plan introspection (no device work) ----
+ * The decomposition mttkrp_* would launch for this problem: which modes are
+ * contracted on the matrix cores, which index the tile rows, the tile shape and
+ * the grid.  For tests and reports. */
+typedef struct {
+    int form;            /* 0: tile rows are the output mode (direct accumulation);
+                            1: the output index is fixed per tile and tile rows are
+                               reduced against their factor rows                      */
+    int layout;          /* 0: contraction index has unit stride; 1: row index has unit stride */
+    int k_modes[2];      /* contracted mode(s); k_modes[1] = -1 when one mode        */
+    int row_modes[2];    /* tile-row mode(s); row_modes[1] = -1 when one mode        */
+    int outer_modes[3];  /* modes iterated per tile (-1 = unused)                     */
+    int mb, nb;          /* wave tile: mb x 16 rows, nb x 16 rank columns            */
+    int b_in_lds;        /* 1: contraction-side factor rows staged in LDS             */
+    int vec;             /* 1: vectorised (4-element) tensor loads                    */
+    int64_t k_len;       /* contraction length                                        */
+    int64_t rows;        /* tile-row count per batch                                  */
+    int64_t batches;     /* outer tuples                                              */
+    int64_t splits;      /* independent chunks per output tile (1: no second pass)   */
+    int64_t rtiles;      /* rank tiles                                                */
+    int64_t grid;        /* workgroups of the main kernel                             */
+    size_t lds_bytes;    /* dynamic LDS of the main kernel                            */
+    size_t ws_bytes;     /* workspace of this mode                                    */
+} mttkrp_plan_info;
+
+int mttkrp_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_bytes,
+                mttkrp_plan_info *info);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MTTKRP_AMD_MTTKRP_H */

@@ -1,0 +1,173 @@
+"""Python entry points over the C ABI (include/mttkrp.h).
+
+Argument marshalling only: torch provides device memory and the current HIP
+stream, every step of the computation runs in the library's kernels.
+
+    mttkrp(X, factors, mode)        -> I_mode x R tensor
+    mttkrp_all(X, factors)          -> list of I_m x R tensors
+    cp_als(X, factors, iters)       -> (lambda, fit_hist, iters_done); factors updated in place
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import List, Optional, Sequence
+
+import torch
+
+from . import _lib
+from ._lib import MttkrpError, PlanInfo
+
+_DT = {torch.float64: ("f64", 8), torch.float32: ("f32", 4)}
+
+
+def _dims(shape) -> ctypes.Array:
+    return (ctypes.c_int64 * len(shape))(*[int(s) for s in shape])
+
+
+def _ptrs(tensors) -> ctypes.Array:
+    return (ctypes.c_void_p * len(tensors))(*[None if t is None else t.data_ptr() for t in tensors])
+
+
+def _stream_handle(stream) -> Optional[int]:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _check_tensor(X: torch.Tensor):
+    if not isinstance(X, torch.Tensor) or not X.is_cuda:
+        raise ValueError("X must be a CUDA (HIP) tensor")
+    if X.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {X.dtype}; float64 or float32")
+    if not X.is_contiguous():
+        raise ValueError("X must be contiguous (row-major)")
+
+
+def _check_factors(X: torch.Tensor, factors: Sequence[Optional[torch.Tensor]], skip: int = -1) -> int:
+    if len(factors) != X.dim():
+        raise ValueError(f"need {X.dim()} factors, got {len(factors)}")
+    R = None
+    for m, U in enumerate(factors):
+        if U is None:
+            if m == skip:
+                continue
+            raise ValueError(f"factor {m} is missing")
+        if U.dtype != X.dtype or U.device != X.device:
+            raise ValueError(f"factor {m} must match X in dtype and device")
+        if U.dim() != 2 or U.shape[0] != X.shape[m] or not U.is_contiguous():
+            raise ValueError(f"factor {m} must be a contiguous {X.shape[m]} x R matrix")
+        if R is None:
+            R = U.shape[1]
+        elif U.shape[1] != R:
+            raise ValueError("factors disagree on the rank")
+    if R is None:
+        raise ValueError("no factor given")
+    return int(R)
+
+
+def workspace_bytes(dims: Sequence[int], rank: int, mode: int, dtype=torch.float64) -> int:
+    n = ctypes.c_size_t(0)
+    st = _lib.lib().mttkrp_workspace_bytes(_dims(dims), len(dims), int(rank), int(mode),
+                                           _DT[dtype][1], ctypes.byref(n))
+    if st:
+        raise MttkrpError(st, "mttkrp_workspace_bytes")
+    return int(n.value)
+
+
+def all_workspace_bytes(dims: Sequence[int], rank: int, dtype=torch.float64) -> int:
+    n = ctypes.c_size_t(0)
+    st = _lib.lib().mttkrp_all_workspace_bytes(_dims(dims), len(dims), int(rank), _DT[dtype][1],
+                                               ctypes.byref(n))
+    if st:
+        raise MttkrpError(st, "mttkrp_all_workspace_bytes")
+    return int(n.value)
+
+
+def cp_als_workspace_bytes(dims: Sequence[int], rank: int, dtype=torch.float64) -> int:
+    n = ctypes.c_size_t(0)
+    st = _lib.lib().cp_als_workspace_bytes(_dims(dims), len(dims), int(rank), _DT[dtype][1],
+                                           ctypes.byref(n))
+    if st:
+        raise MttkrpError(st, "cp_als_workspace_bytes")
+    return int(n.value)
+
+
+def plan(dims: Sequence[int], rank: int, mode: int, dtype=torch.float64) -> dict:
+    info = PlanInfo()
+    st = _lib.lib().mttkrp_plan(_dims(dims), len(dims), int(rank), int(mode), _DT[dtype][1],
+                                ctypes.byref(info))
+    if st:
+        raise MttkrpError(st, "mttkrp_plan")
+    return info.as_dict()
+
+
+def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def mttkrp(X: torch.Tensor, factors: Sequence[Optional[torch.Tensor]], mode: int,
+           out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+           stream=None) -> torch.Tensor:
+    """M = X_(mode) times the Khatri-Rao product of the other factors."""
+    _check_tensor(X)
+    R = _check_factors(X, factors, skip=mode)
+    if not 0 <= mode < X.dim():
+        raise ValueError("mode out of range")
+    sfx, eb = _DT[X.dtype]
+    if out is None:
+        out = torch.empty((X.shape[mode], R), dtype=X.dtype, device=X.device)
+    need = workspace_bytes(X.shape, R, mode, X.dtype)
+    if ws is None:
+        ws = _workspace(need, X.device)
+    fn = getattr(_lib.lib(), f"mttkrp_{sfx}")
+    st = fn(X.data_ptr(), _dims(X.shape), X.dim(), _ptrs(factors), R, int(mode), out.data_ptr(),
+            None if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel(),
+            _stream_handle(stream))
+    if st:
+        raise MttkrpError(st, f"mttkrp_{sfx}")
+    return out
+
+
+def mttkrp_all(X: torch.Tensor, factors: Sequence[torch.Tensor],
+               outs: Optional[List[torch.Tensor]] = None, ws: Optional[torch.Tensor] = None,
+               stream=None) -> List[torch.Tensor]:
+    """MTTKRP of every mode, in mode order, on one stream."""
+    _check_tensor(X)
+    R = _check_factors(X, factors)
+    sfx, eb = _DT[X.dtype]
+    if outs is None:
+        outs = [torch.empty((X.shape[m], R), dtype=X.dtype, device=X.device) for m in range(X.dim())]
+    if ws is None:
+        ws = _workspace(all_workspace_bytes(X.shape, R, X.dtype), X.device)
+    fn = getattr(_lib.lib(), f"mttkrp_all_{sfx}")
+    st = fn(X.data_ptr(), _dims(X.shape), X.dim(), _ptrs(factors), R, _ptrs(outs),
+            None if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel(),
+            _stream_handle(stream))
+    if st:
+        raise MttkrpError(st, f"mttkrp_all_{sfx}")
+    return outs
+
+
+def cp_als(X: torch.Tensor, factors: List[torch.Tensor], iters: int, tol: float = 0.0,
+           ws: Optional[torch.Tensor] = None, stream=None):
+    """CP-ALS from the given factors (updated in place).
+
+    Returns (lambda, fit_hist, iters_done, status); status is 0 or ENOTSPD.
+    """
+    _check_tensor(X)
+    R = _check_factors(X, factors)
+    sfx, eb = _DT[X.dtype]
+    lam = torch.empty(R, dtype=X.dtype, device=X.device)
+    fit = (ctypes.c_double * max(1, iters))()
+    done = ctypes.c_int(0)
+    if ws is None:
+        ws = _workspace(cp_als_workspace_bytes(X.shape, R, X.dtype), X.device)
+    fn = getattr(_lib.lib(), f"cp_als_{sfx}")
+    st = fn(X.data_ptr(), _dims(X.shape), X.dim(), R, _ptrs(factors), lam.data_ptr(), int(iters),
+            float(tol), fit, ctypes.byref(done), ws.data_ptr(), ws.numel(), _stream_handle(stream))
+    if st not in (0, _lib.ENOTSPD):
+        raise MttkrpError(st, f"cp_als_{sfx}")
+    hist = [fit[i] for i in range(iters)]
+    return lam, hist, int(done.value), int(st)

@@ -1,0 +1,347 @@
+// CP-ALS kernels around the MTTKRP ("A Performance Portable Matrix Free Dense
+// MTTKRP in GenTen", Fig. 5: besides MTTKRP, each step needs inner products
+// and a Cholesky solve).  All R x R work is done in fp64 whatever the tensor
+// element type; every reduction runs in a fixed order (deterministic).
+//
+// Per mode n of a sweep:
+//   als_chol:      V = Hadamard_{m != n} G_m, then V = L L^T (no pivoting);
+//                  a non-positive pivot raises the failure flag.
+//   (MTTKRP of mode n into the fp64 buffer M)
+//   als_solve:     U_new(i, :) = M(i, :) V^{-1} by a forward and a back
+//                  substitution per row.
+//   als_normalize: lambda_r = ||U_new(:, r)||_2, U_n = U_new / lambda (columns
+//                  with lambda_r = 0 kept as they are).
+//   gram:          G_n = U_n^T U_n.
+// After the last mode, als_fit forms
+//   fit = 1 - sqrt(max(0, ||X||^2 + ||model||^2 - 2 <X, model>)) / ||X||
+// with <X, model> = sum_r lambda_r sum_i M(i, r) U_{d-1}(i, r) and
+// ||model||^2 = sum_{a,b} lambda_a lambda_b prod_m G_m(a, b).
+// Every kernel after a failed Cholesky returns without writing, so the
+// factors keep the values of the failing step's start.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mttkrp {
+
+constexpr int kRedThreads = 256;
+
+__device__ __forceinline__ double block_sum(double v, double *sh)
+{
+    // Fixed-order tree: wave butterfly, then wave results in index order.
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane == 0) sh[wave] = v;
+    __syncthreads();
+    double t = 0.0;
+    const int nw = (blockDim.x + 63) >> 6;
+    for (int w = 0; w < nw; ++w) t += sh[w];
+    return t;
+}
+
+// ||X||^2, first pass: one fp64 partial per workgroup (grid-stride, fixed order).
+template <typename T>
+__global__ __launch_bounds__(kRedThreads) void sumsq_partial_kernel(const T *__restrict__ X,
+                                                                    int64_t N,
+                                                                    double *__restrict__ partial)
+{
+    __shared__ double sh[kRedThreads / 64];
+    double s = 0.0;
+    for (int64_t i = (int64_t)blockIdx.x * kRedThreads + threadIdx.x; i < N;
+         i += (int64_t)gridDim.x * kRedThreads) {
+        const double x = (double)X[i];
+        s += x * x;
+    }
+    s = block_sum(s, sh);
+    if (threadIdx.x == 0) partial[blockIdx.x] = s;
+}
+
+__global__ __launch_bounds__(kRedThreads) void sum_final_kernel(const double *__restrict__ partial,
+                                                                int n, double *__restrict__ out)
+{
+    __shared__ double sh[kRedThreads / 64];
+    double s = 0.0;
+    for (int i = threadIdx.x; i < n; i += kRedThreads) s += partial[i];
+    s = block_sum(s, sh);
+    if (threadIdx.x == 0) *out = s;
+}
+
+// G = U^T U (R x R, fp64) of an I x R factor; one thread per entry.
+template <typename T>
+__global__ __launch_bounds__(256) void gram_kernel(const T *__restrict__ U, int64_t I, int64_t R,
+                                                   double *__restrict__ G,
+                                                   const int *__restrict__ flag)
+{
+    if (flag && *flag) return;
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= R * R) return;
+    const int64_t a = e / R, b = e - (e / R) * R;
+    double s = 0.0;
+    for (int64_t i = 0; i < I; ++i) s += (double)U[i * R + a] * (double)U[i * R + b];
+    G[e] = s;
+}
+
+// V = Hadamard_{m != n} G_m and its Cholesky factor L (lower, row-major, in
+// place in Lout).  One workgroup; V lives in LDS when it fits, else in Lout.
+__global__ __launch_bounds__(1024) void als_chol_kernel(const double *__restrict__ Gall,
+                                                        int order, int n, int64_t R,
+                                                        double *__restrict__ Lout,
+                                                        int *__restrict__ flag, int use_lds)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    if (*flag) return;
+    double *A = use_lds ? reinterpret_cast<double *>(smem) : Lout;
+    __shared__ int fail;
+    const int tid = threadIdx.x, nt = blockDim.x;
+    const int64_t RR = R * R;
+    for (int64_t e = tid; e < RR; e += nt) {
+        double v = 1.0;
+        for (int m = 0; m < order; ++m)
+            if (m != n) v *= Gall[(int64_t)m * RR + e];
+        A[e] = v;
+    }
+    if (tid == 0) fail = 0;
+    __syncthreads();
+    // Column by column (textbook order, as the reference solve):
+    //   L_jj = sqrt(V_jj - sum_{k<j} L_jk^2);  L_ij = (V_ij - sum_{k<j} L_ik L_jk) / L_jj.
+    for (int64_t j = 0; j < R; ++j) {
+        if (tid == 0) {
+            double d = A[j * R + j];
+            for (int64_t k = 0; k < j; ++k) d -= A[j * R + k] * A[j * R + k];
+            if (!(d > 0.0)) {
+                fail = 1;
+            } else {
+                A[j * R + j] = sqrt(d);
+            }
+        }
+        __syncthreads();
+        if (fail) break;
+        const double ljj = A[j * R + j];
+        for (int64_t i = j + 1 + tid; i < R; i += nt) {
+            double s = A[i * R + j];
+            for (int64_t k = 0; k < j; ++k) s -= A[i * R + k] * A[j * R + k];
+            A[i * R + j] = s / ljj;
+        }
+        __syncthreads();
+    }
+    if (fail) {
+        if (tid == 0) *flag = 1;
+        return;
+    }
+    // zero the strict upper triangle and copy out
+    for (int64_t e = tid; e < RR; e += nt) {
+        const int64_t i = e / R, c = e - (e / R) * R;
+        Lout[e] = c > i ? 0.0 : A[e];
+    }
+}
+
+// Row solves (L L^T) x = m for every row of M; one wave per row, R <= 64:
+// lane l holds component l.
+__global__ __launch_bounds__(256) void als_solve_wave_kernel(const double *__restrict__ M,
+                                                             const double *__restrict__ L,
+                                                             int64_t I, int64_t R,
+                                                             double *__restrict__ Unew,
+                                                             const int *__restrict__ flag)
+{
+    if (*flag) return;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= I) return;
+    double b = lane < R ? M[row * R + lane] : 0.0;
+    // forward: L y = b
+    for (int j = 0; j < (int)R; ++j) {
+        const double xj = __shfl(b, j) / L[(int64_t)j * R + j];
+        if (lane == j) b = xj;
+        if (lane > j && lane < R) b -= L[(int64_t)lane * R + j] * xj;
+    }
+    // back: L^T x = y
+    for (int j = (int)R - 1; j >= 0; --j) {
+        const double xj = __shfl(b, j) / L[(int64_t)j * R + j];
+        if (lane == j) b = xj;
+        if (lane < j) b -= L[(int64_t)j * R + lane] * xj;
+    }
+    if (lane < R) Unew[row * R + lane] = b;
+}
+
+// Row solves for any R: one workgroup per row, the row vector in LDS.
+__global__ __launch_bounds__(256) void als_solve_block_kernel(const double *__restrict__ M,
+                                                              const double *__restrict__ L,
+                                                              int64_t I, int64_t R,
+                                                              double *__restrict__ Unew,
+                                                              const int *__restrict__ flag)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    if (*flag) return;
+    double *x = reinterpret_cast<double *>(smem);
+    const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x;
+    for (int64_t i = tid; i < R; i += 256) x[i] = M[row * R + i];
+    __syncthreads();
+    for (int64_t j = 0; j < R; ++j) {
+        const double xj = x[j] / L[j * R + j];
+        __syncthreads();
+        if (tid == 0) x[j] = xj;
+        for (int64_t i = j + 1 + tid; i < R; i += 256) x[i] -= L[i * R + j] * xj;
+        __syncthreads();
+    }
+    for (int64_t j = R - 1; j >= 0; --j) {
+        const double xj = x[j] / L[j * R + j];
+        __syncthreads();
+        if (tid == 0) x[j] = xj;
+        for (int64_t i = tid; i < j; i += 256) x[i] -= L[j * R + i] * xj;
+        __syncthreads();
+    }
+    for (int64_t i = tid; i < R; i += 256) Unew[row * R + i] = x[i];
+}
+
+// lambda_r = ||U_new(:, r)||_2 and U_n = U_new / lambda_r; one thread per column.
+template <typename T>
+__global__ __launch_bounds__(256) void als_normalize_kernel(const double *__restrict__ Unew,
+                                                            int64_t I, int64_t R,
+                                                            T *__restrict__ Uout,
+                                                            double *__restrict__ lam64,
+                                                            T *__restrict__ lamT,
+                                                            const int *__restrict__ flag)
+{
+    if (*flag) return;
+    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (r >= R) return;
+    double s = 0.0;
+    for (int64_t i = 0; i < I; ++i) s += Unew[i * R + r] * Unew[i * R + r];
+    const double lam = sqrt(s);
+    for (int64_t i = 0; i < I; ++i) {
+        const double v = Unew[i * R + r];
+        Uout[i * R + r] = (T)(lam > 0.0 ? v / lam : v);
+    }
+    lam64[r] = lam;
+    if (lamT) lamT[r] = (T)lam;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void fill_kernel(T *__restrict__ p, int64_t n, T v)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+// Fit after the last mode of a sweep; one workgroup.  scal[0] = ||X||^2 in,
+// scal[1] = fit out.
+template <typename T>
+__global__ __launch_bounds__(kRedThreads) void als_fit_kernel(
+    const double *__restrict__ M, const T *__restrict__ Ulast, int64_t Ilast,
+    const double *__restrict__ lam64, const double *__restrict__ Gall, int order, int64_t R,
+    double *__restrict__ scal, const int *__restrict__ flag)
+{
+    __shared__ double sh[kRedThreads / 64];
+    if (*flag) return;
+    double inner = 0.0;
+    for (int64_t r = threadIdx.x; r < R; r += kRedThreads) {
+        double s = 0.0;
+        for (int64_t i = 0; i < Ilast; ++i) s += M[i * R + r] * (double)Ulast[i * R + r];
+        inner += lam64[r] * s;
+    }
+    inner = block_sum(inner, sh);
+    const int64_t RR = R * R;
+    double nrm2 = 0.0;
+    for (int64_t e = threadIdx.x; e < RR; e += kRedThreads) {
+        const int64_t a = e / R, b = e - (e / R) * R;
+        double v = lam64[a] * lam64[b];
+        for (int m = 0; m < order; ++m) v *= Gall[(int64_t)m * RR + e];
+        nrm2 += v;
+    }
+    nrm2 = block_sum(nrm2, sh);
+    if (threadIdx.x == 0) {
+        const double nx2 = scal[0];
+        double resid = nx2 + nrm2 - 2.0 * inner;
+        if (resid < 0.0) resid = 0.0;
+        scal[1] = nx2 > 0.0 ? 1.0 - sqrt(resid) / sqrt(nx2) : __builtin_nan("");
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers (used by the C-ABI driver)
+// ---------------------------------------------------------------------------
+
+template <typename T>
+hipError_t launch_sumsq(const T *X, int64_t N, double *partial, int nparts, double *out,
+                        hipStream_t s)
+{
+    hipLaunchKernelGGL(sumsq_partial_kernel<T>, dim3(nparts), dim3(kRedThreads), 0, s, X, N,
+                       partial);
+    hipLaunchKernelGGL(sum_final_kernel, dim3(1), dim3(kRedThreads), 0, s, (const double *)partial,
+                       nparts, out);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_gram(const T *U, int64_t I, int64_t R, double *G, const int *flag, hipStream_t s)
+{
+    const int64_t n = R * R;
+    hipLaunchKernelGGL(gram_kernel<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, U, I, R,
+                       G, flag);
+    return hipGetLastError();
+}
+
+hipError_t launch_chol(const double *Gall, int order, int n, int64_t R, double *L, int *flag,
+                       hipStream_t s)
+{
+    const size_t bytes = (size_t)R * R * sizeof(double);
+    const int use_lds = bytes <= 64 * 1024;
+    hipLaunchKernelGGL(als_chol_kernel, dim3(1), dim3(1024), use_lds ? bytes : 0, s, Gall, order,
+                       n, R, L, flag, use_lds);
+    return hipGetLastError();
+}
+
+hipError_t launch_solve(const double *M, const double *L, int64_t I, int64_t R, double *Unew,
+                        const int *flag, hipStream_t s)
+{
+    if (R <= 64) {
+        hipLaunchKernelGGL(als_solve_wave_kernel, dim3((unsigned)((I + 3) / 4)), dim3(256), 0, s, M,
+                           L, I, R, Unew, flag);
+    } else {
+        hipLaunchKernelGGL(als_solve_block_kernel, dim3((unsigned)I), dim3(256),
+                           (size_t)R * sizeof(double), s, M, L, I, R, Unew, flag);
+    }
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_normalize(const double *Unew, int64_t I, int64_t R, T *Uout, double *lam64,
+                            T *lamT, const int *flag, hipStream_t s)
+{
+    hipLaunchKernelGGL(als_normalize_kernel<T>, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, s,
+                       Unew, I, R, Uout, lam64, lamT, flag);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_fill(T *p, int64_t n, T v, hipStream_t s)
+{
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_kernel<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n, v);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_fit(const double *M, const T *Ulast, int64_t Ilast, const double *lam64,
+                      const double *Gall, int order, int64_t R, double *scal, const int *flag,
+                      hipStream_t s)
+{
+    hipLaunchKernelGGL(als_fit_kernel<T>, dim3(1), dim3(kRedThreads), 0, s, M, Ulast, Ilast, lam64,
+                       Gall, order, R, scal, flag);
+    return hipGetLastError();
+}
+
+template hipError_t launch_sumsq<double>(const double *, int64_t, double *, int, double *, hipStream_t);
+template hipError_t launch_sumsq<float>(const float *, int64_t, double *, int, double *, hipStream_t);
+template hipError_t launch_gram<double>(const double *, int64_t, int64_t, double *, const int *, hipStream_t);
+template hipError_t launch_gram<float>(const float *, int64_t, int64_t, double *, const int *, hipStream_t);
+template hipError_t launch_normalize<double>(const double *, int64_t, int64_t, double *, double *, double *, const int *, hipStream_t);
+template hipError_t launch_normalize<float>(const double *, int64_t, int64_t, float *, double *, float *, const int *, hipStream_t);
+template hipError_t launch_fill<double>(double *, int64_t, double, hipStream_t);
+template hipError_t launch_fill<float>(float *, int64_t, float, hipStream_t);
+template hipError_t launch_fill<int>(int *, int64_t, int, hipStream_t);
+template hipError_t launch_fit<double>(const double *, const double *, int64_t, const double *, const double *, int, int64_t, double *, const int *, hipStream_t);
+template hipError_t launch_fit<float>(const double *, const float *, int64_t, const double *, const double *, int, int64_t, double *, const int *, hipStream_t);
+
+}  // namespace mttkrp

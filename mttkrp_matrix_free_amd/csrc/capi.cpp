@@ -1,0 +1,397 @@
+// C ABI of the matrix-free MTTKRP library (declared in include/mttkrp.h).
+//
+// Every entry point validates its arguments on the host before any HIP call,
+// plans the decomposition (plan.cpp), fills the kernel parameter block and
+// enqueues the kernels on the caller's stream.  The library allocates no
+// device memory: partial sums and CP-ALS state live in the caller's
+// workspace.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <limits>
+
+#include "../../include/mttkrp.h"
+#include "plan.hpp"
+
+namespace mttkrp {
+
+template <typename T>
+hipError_t launch_mttkrp(const Plan &pl, hipStream_t stream);
+
+template <typename T>
+hipError_t launch_sumsq(const T *X, int64_t N, double *partial, int nparts, double *out,
+                        hipStream_t s);
+template <typename T>
+hipError_t launch_gram(const T *U, int64_t I, int64_t R, double *G, const int *flag, hipStream_t s);
+hipError_t launch_chol(const double *Gall, int order, int n, int64_t R, double *L, int *flag,
+                       hipStream_t s);
+hipError_t launch_solve(const double *M, const double *L, int64_t I, int64_t R, double *Unew,
+                        const int *flag, hipStream_t s);
+template <typename T>
+hipError_t launch_normalize(const double *Unew, int64_t I, int64_t R, T *Uout, double *lam64,
+                            T *lamT, const int *flag, hipStream_t s);
+template <typename T>
+hipError_t launch_fill(T *p, int64_t n, T v, hipStream_t s);
+template <typename T>
+hipError_t launch_fit(const double *M, const T *Ulast, int64_t Ilast, const double *lam64,
+                      const double *Gall, int order, int64_t R, double *scal, const int *flag,
+                      hipStream_t s);
+
+namespace {
+
+constexpr int kSumsqParts = 1024;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+// Checks shared by the MTTKRP entry points.  `factors` may hold NULL at `mode`
+// (mode < 0: every factor must be present).
+int check_common(const void *X, const int64_t *dims, int order, const void *const *factors,
+                 int64_t rank, int mode)
+{
+    if (!X || !dims || !factors) return MTTKRP_EINVAL;
+    if (order < 3 || order > kMaxOrder) return MTTKRP_EORDER;
+    if (rank < 1) return MTTKRP_EINVAL;
+    for (int m = 0; m < order; ++m) {
+        if (dims[m] < 1) return MTTKRP_EINVAL;
+        if (m != mode && !factors[m]) return MTTKRP_EINVAL;
+    }
+    if (!aligned16(X)) return MTTKRP_EALIGN;
+    for (int m = 0; m < order; ++m)
+        if (factors[m] && !aligned16(factors[m])) return MTTKRP_EALIGN;
+    return MTTKRP_OK;
+}
+
+// Factor pointers by role in the kernel parameter block.
+void bind_factors(KParams &k, const void *const *factors)
+{
+    k.Uk0 = factors[k.k_mode0];
+    k.Uk1 = k.k_mode1 >= 0 ? factors[k.k_mode1] : nullptr;
+    k.Ur0 = k.r_mode0 >= 0 ? factors[k.r_mode0] : nullptr;
+    k.Ur1 = k.r_mode1 >= 0 ? factors[k.r_mode1] : nullptr;
+    for (int j = 0; j < 3; ++j) k.Uo[j] = j < k.nouter ? factors[k.o_mode[j]] : nullptr;
+}
+
+template <typename T>
+int mttkrp_one(const T *X, const int64_t *dims, int order, const T *const *factors, int64_t rank,
+               int mode, void *out, int out64, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    Plan pl;
+    int st = make_plan(dims, order, rank, mode, (int)sizeof(T), pl);
+    if (st) return st;
+    if (pl.ws_bytes > ws_bytes) return MTTKRP_EWORKSPACE;
+    if (pl.ws_bytes > 0 && !ws) return MTTKRP_EINVAL;
+    pl.kp.X = X;
+    bind_factors(pl.kp, reinterpret_cast<const void *const *>(factors));
+    pl.kp.out = out;
+    pl.kp.out64 = out64;
+    pl.kp.partial = reinterpret_cast<double *>(ws);
+    return launch_mttkrp<T>(pl, stream) == hipSuccess ? MTTKRP_OK : MTTKRP_EHIP;
+}
+
+template <typename T>
+int mttkrp_entry(const T *X, const int64_t *dims, int order, const T *const *factors,
+                 int64_t rank, int mode, T *out, void *ws, size_t ws_bytes, void *stream)
+{
+    int st = check_common(X, dims, order, reinterpret_cast<const void *const *>(factors), rank,
+                          mode < 0 ? 0 : mode);
+    if (st) return st;
+    if (mode < 0 || mode >= order || !out) return MTTKRP_EINVAL;
+    if (!aligned16(out) || (ws && !aligned16(ws))) return MTTKRP_EALIGN;
+    return mttkrp_one<T>(X, dims, order, factors, rank, mode, out, 0, ws, ws_bytes,
+                         reinterpret_cast<hipStream_t>(stream));
+}
+
+int all_ws(const int64_t *dims, int order, int64_t rank, int elem, size_t *bytes)
+{
+    size_t mx = 0;
+    for (int m = 0; m < order; ++m) {
+        Plan pl;
+        const int st = make_plan(dims, order, rank, m, elem, pl);
+        if (st) return st;
+        mx = std::max(mx, pl.ws_bytes);
+    }
+    *bytes = mx;
+    return MTTKRP_OK;
+}
+
+template <typename T>
+int mttkrp_all_entry(const T *X, const int64_t *dims, int order, const T *const *factors,
+                     int64_t rank, T *const *outs, void *ws, size_t ws_bytes, void *stream)
+{
+    int st = check_common(X, dims, order, reinterpret_cast<const void *const *>(factors), rank, -1);
+    if (st) return st;
+    if (!outs) return MTTKRP_EINVAL;
+    for (int m = 0; m < order; ++m) {
+        if (!outs[m]) return MTTKRP_EINVAL;
+        if (!aligned16(outs[m])) return MTTKRP_EALIGN;
+    }
+    if (ws && !aligned16(ws)) return MTTKRP_EALIGN;
+    size_t need = 0;
+    st = all_ws(dims, order, rank, (int)sizeof(T), &need);
+    if (st) return st;
+    if (need > ws_bytes) return MTTKRP_EWORKSPACE;
+    if (need > 0 && !ws) return MTTKRP_EINVAL;
+    for (int m = 0; m < order; ++m) {
+        st = mttkrp_one<T>(X, dims, order, factors, rank, m, outs[m], 0, ws, ws_bytes,
+                           reinterpret_cast<hipStream_t>(stream));
+        if (st) return st;
+    }
+    return MTTKRP_OK;
+}
+
+// CP-ALS workspace layout (bytes, each piece 256-aligned):
+//   [mttkrp partials][M fp64 maxI x R][Unew fp64 maxI x R][G fp64 d x R x R]
+//   [L fp64 R x R][lambda fp64 R][sumsq partials][scalars: ||X||^2, fit][flag]
+struct AlsLayout {
+    size_t mt, M, Unew, G, L, lam, parts, scal, flag, total;
+};
+
+int als_layout(const int64_t *dims, int order, int64_t rank, int elem, AlsLayout &L)
+{
+    size_t mt = 0;
+    int st = all_ws(dims, order, rank, elem, &mt);
+    if (st) return st;
+    int64_t maxI = 0;
+    for (int m = 0; m < order; ++m) maxI = std::max<int64_t>(maxI, dims[m]);
+    const size_t R = (size_t)rank;
+    size_t off = 0;
+    L.mt = off;
+    off += round256(mt);
+    L.M = off;
+    off += round256(8 * (size_t)maxI * R);
+    L.Unew = off;
+    off += round256(8 * (size_t)maxI * R);
+    L.G = off;
+    off += round256(8 * (size_t)order * R * R);
+    L.L = off;
+    off += round256(8 * R * R);
+    L.lam = off;
+    off += round256(8 * R);
+    L.parts = off;
+    off += round256(8 * (size_t)kSumsqParts);
+    L.scal = off;
+    off += 256;
+    L.flag = off;
+    off += 256;
+    L.total = off;
+    return MTTKRP_OK;
+}
+
+template <typename T>
+int cp_als_entry(const T *X, const int64_t *dims, int order, int64_t rank, T *const *factors,
+                 T *lambda, int iters, double tol, double *fit_hist, int *iters_done, void *ws,
+                 size_t ws_bytes, void *stream_)
+{
+    if (!X || !dims || !factors || !lambda || !fit_hist || !iters_done) return MTTKRP_EINVAL;
+    if (order < 3 || order > kMaxOrder) return MTTKRP_EORDER;
+    if (rank < 1 || iters < 0) return MTTKRP_EINVAL;
+    for (int m = 0; m < order; ++m) {
+        if (dims[m] < 1 || !factors[m]) return MTTKRP_EINVAL;
+    }
+    if (!aligned16(X) || !aligned16(lambda) || (ws && !aligned16(ws))) return MTTKRP_EALIGN;
+    for (int m = 0; m < order; ++m)
+        if (!aligned16(factors[m])) return MTTKRP_EALIGN;
+    if (rank > 4096) return MTTKRP_ERANGE;  // single-workgroup Cholesky bound
+    AlsLayout L;
+    int st = als_layout(dims, order, rank, (int)sizeof(T), L);
+    if (st) return st;
+    if (L.total > ws_bytes) return MTTKRP_EWORKSPACE;
+    if (!ws) return MTTKRP_EINVAL;
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream_);
+    unsigned char *w = reinterpret_cast<unsigned char *>(ws);
+    double *M = reinterpret_cast<double *>(w + L.M);
+    double *Unew = reinterpret_cast<double *>(w + L.Unew);
+    double *G = reinterpret_cast<double *>(w + L.G);
+    double *Lc = reinterpret_cast<double *>(w + L.L);
+    double *lam64 = reinterpret_cast<double *>(w + L.lam);
+    double *parts = reinterpret_cast<double *>(w + L.parts);
+    double *scal = reinterpret_cast<double *>(w + L.scal);
+    int *flag = reinterpret_cast<int *>(w + L.flag);
+    const int64_t R = rank;
+
+    for (int it = 0; it < iters; ++it) fit_hist[it] = std::numeric_limits<double>::quiet_NaN();
+    *iters_done = 0;
+
+    int64_t N = 1;
+    for (int m = 0; m < order; ++m) N *= dims[m];
+    auto ok = [](hipError_t e) { return e == hipSuccess; };
+    if (!ok(launch_fill<int>(flag, 1, 0, s))) return MTTKRP_EHIP;
+    if (!ok(launch_fill<T>(lambda, R, T(1), s))) return MTTKRP_EHIP;
+    if (!ok(launch_sumsq<T>(X, N, parts, kSumsqParts, scal, s))) return MTTKRP_EHIP;
+    for (int m = 0; m < order; ++m)
+        if (!ok(launch_gram<T>(factors[m], dims[m], R, G + (size_t)m * R * R, flag, s)))
+            return MTTKRP_EHIP;
+
+    const T *cf[kMaxOrder];
+    for (int m = 0; m < order; ++m) cf[m] = factors[m];
+    double prev = std::numeric_limits<double>::quiet_NaN();
+    for (int it = 0; it < iters; ++it) {
+        for (int n = 0; n < order; ++n) {
+            if (!ok(launch_chol(G, order, n, R, Lc, flag, s))) return MTTKRP_EHIP;
+            st = mttkrp_one<T>(X, dims, order, cf, R, n, M, 1, w + L.mt, L.M - L.mt, s);
+            if (st) return st;
+            if (!ok(launch_solve(M, Lc, dims[n], R, Unew, flag, s))) return MTTKRP_EHIP;
+            if (!ok(launch_normalize<T>(Unew, dims[n], R, factors[n], lam64, lambda, flag, s)))
+                return MTTKRP_EHIP;
+            if (!ok(launch_gram<T>(factors[n], dims[n], R, G + (size_t)n * R * R, flag, s)))
+                return MTTKRP_EHIP;
+        }
+        if (!ok(launch_fit<T>(M, factors[order - 1], dims[order - 1], lam64, G, order, R, scal,
+                              flag, s)))
+            return MTTKRP_EHIP;
+        struct {
+            double fit;
+            int flag;
+        } host;
+        if (!ok(hipMemcpyAsync(&host.fit, scal + 1, sizeof(double), hipMemcpyDeviceToHost, s)))
+            return MTTKRP_EHIP;
+        if (!ok(hipMemcpyAsync(&host.flag, flag, sizeof(int), hipMemcpyDeviceToHost, s)))
+            return MTTKRP_EHIP;
+        if (!ok(hipStreamSynchronize(s))) return MTTKRP_EHIP;
+        if (host.flag) {
+            *iters_done = it;
+            return MTTKRP_ENOTSPD;
+        }
+        fit_hist[it] = host.fit;
+        *iters_done = it + 1;
+        if (tol > 0.0 && it > 0 && std::fabs(host.fit - prev) < tol) break;
+        prev = host.fit;
+    }
+    return MTTKRP_OK;
+}
+
+}  // namespace
+}  // namespace mttkrp
+
+using namespace mttkrp;
+
+extern "C" {
+
+const char *mttkrp_strerror(int status)
+{
+    switch (status) {
+    case MTTKRP_OK: return "success";
+    case MTTKRP_EINVAL: return "invalid argument (null pointer, non-positive size, mode out of range)";
+    case MTTKRP_EORDER: return "tensor order must be 3, 4 or 5";
+    case MTTKRP_ERANGE: return "problem size exceeds the supported index range";
+    case MTTKRP_EALIGN: return "device pointer not 16-byte aligned";
+    case MTTKRP_EWORKSPACE: return "workspace smaller than the size the query returns";
+    case MTTKRP_EHIP: return "HIP runtime call or kernel launch failed";
+    case MTTKRP_ENOTSPD: return "CP-ALS: Cholesky pivot of the R x R system not positive";
+    default: return "unknown status";
+    }
+}
+
+int mttkrp_version(void) { return 100; }
+
+int mttkrp_workspace_bytes(const int64_t *dims, int order, int64_t rank, int mode, int elem_bytes,
+                           size_t *bytes)
+{
+    if (!bytes) return MTTKRP_EINVAL;
+    Plan pl;
+    const int st = make_plan(dims, order, rank, mode, elem_bytes, pl);
+    if (st) return st;
+    *bytes = pl.ws_bytes;
+    return MTTKRP_OK;
+}
+
+int mttkrp_all_workspace_bytes(const int64_t *dims, int order, int64_t rank, int elem_bytes,
+                               size_t *bytes)
+{
+    if (!bytes || !dims) return MTTKRP_EINVAL;
+    if (order < 3 || order > kMaxOrder) return MTTKRP_EORDER;
+    if (elem_bytes != 4 && elem_bytes != 8) return MTTKRP_EINVAL;
+    return all_ws(dims, order, rank, elem_bytes, bytes);
+}
+
+int cp_als_workspace_bytes(const int64_t *dims, int order, int64_t rank, int elem_bytes,
+                           size_t *bytes)
+{
+    if (!bytes || !dims) return MTTKRP_EINVAL;
+    if (order < 3 || order > kMaxOrder) return MTTKRP_EORDER;
+    if (elem_bytes != 4 && elem_bytes != 8) return MTTKRP_EINVAL;
+    if (rank > 4096) return MTTKRP_ERANGE;
+    AlsLayout L;
+    const int st = als_layout(dims, order, rank, elem_bytes, L);
+    if (st) return st;
+    *bytes = L.total;
+    return MTTKRP_OK;
+}
+
+int mttkrp_f64(const double *X, const int64_t *dims, int order, const double *const *factors,
+               int64_t rank, int mode, double *out, void *ws, size_t ws_bytes, void *stream)
+{
+    return mttkrp_entry<double>(X, dims, order, factors, rank, mode, out, ws, ws_bytes, stream);
+}
+
+int mttkrp_f32(const float *X, const int64_t *dims, int order, const float *const *factors,
+               int64_t rank, int mode, float *out, void *ws, size_t ws_bytes, void *stream)
+{
+    return mttkrp_entry<float>(X, dims, order, factors, rank, mode, out, ws, ws_bytes, stream);
+}
+
+int mttkrp_all_f64(const double *X, const int64_t *dims, int order, const double *const *factors,
+                   int64_t rank, double *const *outs, void *ws, size_t ws_bytes, void *stream)
+{
+    return mttkrp_all_entry<double>(X, dims, order, factors, rank, outs, ws, ws_bytes, stream);
+}
+
+int mttkrp_all_f32(const float *X, const int64_t *dims, int order, const float *const *factors,
+                   int64_t rank, float *const *outs, void *ws, size_t ws_bytes, void *stream)
+{
+    return mttkrp_all_entry<float>(X, dims, order, factors, rank, outs, ws, ws_bytes, stream);
+}
+
+int cp_als_f64(const double *X, const int64_t *dims, int order, int64_t rank,
+               double *const *factors, double *lambda, int iters, double tol, double *fit_hist,
+               int *iters_done, void *ws, size_t ws_bytes, void *stream)
+{
+    return cp_als_entry<double>(X, dims, order, rank, factors, lambda, iters, tol, fit_hist,
+                                iters_done, ws, ws_bytes, stream);
+}
+
+int cp_als_f32(const float *X, const int64_t *dims, int order, int64_t rank, float *const *factors,
+               float *lambda, int iters, double tol, double *fit_hist, int *iters_done, void *ws,
+               size_t ws_bytes, void *stream)
+{
+    return cp_als_entry<float>(X, dims, order, rank, factors, lambda, iters, tol, fit_hist,
+                               iters_done, ws, ws_bytes, stream);
+}
+
+int mttkrp_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_bytes,
+                mttkrp_plan_info *info)
+{
+    if (!info) return MTTKRP_EINVAL;
+    Plan pl;
+    const int st = make_plan(dims, order, rank, mode, elem_bytes, pl);
+    if (st) return st;
+    std::memset(info, 0, sizeof(*info));
+    info->form = pl.form;
+    info->layout = pl.layout;
+    info->k_modes[0] = pl.k_modes[0];
+    info->k_modes[1] = pl.k_modes[1];
+    info->row_modes[0] = pl.row_modes[0];
+    info->row_modes[1] = pl.row_modes[1];
+    for (int j = 0; j < 3; ++j) info->outer_modes[j] = pl.outer_modes[j];
+    info->mb = pl.mb;
+    info->nb = pl.nb;
+    info->b_in_lds = pl.b_in_lds ? 1 : 0;
+    info->vec = pl.vec ? 1 : 0;
+    info->k_len = pl.kp.K;
+    info->rows = pl.kp.nrows;
+    info->batches = pl.kp.nbatch;
+    info->splits = pl.kp.nsplit;
+    info->rtiles = pl.kp.nrtiles;
+    info->grid = pl.grid;
+    info->lds_bytes = pl.lds_bytes;
+    info->ws_bytes = pl.ws_bytes;
+    return MTTKRP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,270 @@
+// Host planner for the matrix-free MTTKRP (pure host code, no HIP calls).
+//
+// Chooses, for one mode, the contraction group run on the matrix cores, the
+// tile rows, the outer (Hadamard) modes, the wave tile, and the split of the
+// work over workgroups.  The split rule follows a plain cache/traffic model:
+// X is streamed once per rank tile; a split adds 2 * nsplit * I_n * R * 8
+// bytes of partial sums, kept under a tenth of the tensor traffic; the grid
+// aims at four workgroups per compute unit.  (The GenTen page names a tile-size
+// heuristic and cache models for this choice; their formulas are not given,
+// so this is a reading for gfx950: 160 KB LDS and 512 registers per lane per
+// SIMD.)
+#include "plan.hpp"
+
+#include <algorithm>
+#include <climits>
+
+#include "../../include/mttkrp.h"
+
+namespace mttkrp {
+
+namespace {
+
+bool mul_ok(int64_t a, int64_t b, int64_t &out)
+{
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > INT64_MAX / a) return false;
+    out = a * b;
+    return true;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_bytes, Plan &plan)
+{
+    if (!dims) return MTTKRP_EINVAL;
+    if (order < 3 || order > kMaxOrder) return MTTKRP_EORDER;
+    if (rank < 1 || mode < 0 || mode >= order) return MTTKRP_EINVAL;
+    if (elem_bytes != 4 && elem_bytes != 8) return MTTKRP_EINVAL;
+    for (int m = 0; m < order; ++m)
+        if (dims[m] < 1) return MTTKRP_EINVAL;
+
+    // Sizes: every element offset and every workspace byte count must fit in
+    // int64 with room for the kernels' index arithmetic.
+    int64_t N = 1;
+    for (int m = 0; m < order; ++m)
+        if (!mul_ok(N, dims[m], N)) return MTTKRP_ERANGE;
+    int64_t tmp;
+    if (!mul_ok(N, 8, tmp) || tmp > (INT64_C(1) << 50)) return MTTKRP_ERANGE;
+    for (int m = 0; m < order; ++m)
+        if (!mul_ok(dims[m], rank, tmp) || !mul_ok(tmp, 8 * 1024, tmp)) return MTTKRP_ERANGE;
+    if (rank > (INT64_C(1) << 24)) return MTTKRP_ERANGE;
+
+    const int d = order;
+    const int n = mode;
+    int64_t S[kMaxOrder];
+    {
+        int64_t s = 1;
+        for (int m = d - 1; m >= 0; --m) {
+            S[m] = s;
+            s *= dims[m];
+        }
+    }
+
+    Plan p;
+    p.elem_bytes = elem_bytes;
+    KParams &k = p.kp;
+    k.R = rank;
+    k.In = dims[n];
+    k.r_mode0 = k.r_mode1 = -1;
+    k.k_mode0 = k.k_mode1 = -1;
+    k.IkB = 1;
+    k.IrB = 1;
+
+    bool in_k[kMaxOrder] = {false, false, false, false, false};
+    bool in_rows[kMaxOrder] = {false, false, false, false, false};
+
+    // A contraction mode shorter than 32 is merged with its left neighbour
+    // (when that neighbour is free) so that the matrix-core K dimension is not
+    // mostly padding; the merged Khatri-Rao tile must fit in LDS at one
+    // 16-column rank block.
+    const int64_t kMergeMax = (int64_t)(kLdsBudget / ((16 + 8) * (size_t)elem_bytes));
+    auto choose_k = [&](int last) {
+        int first = last;
+        if (dims[last] < 32 && last - 1 >= 0 && last - 1 != n &&
+            dims[last - 1] * dims[last] <= kMergeMax)
+            first = last - 1;
+        if (first == last) {
+            k.k_mode0 = last;
+            k.K = dims[last];
+        } else {
+            k.k_mode0 = first;
+            k.k_mode1 = last;
+            k.IkB = dims[last];
+            k.K = dims[first] * dims[last];
+        }
+        k.k_stride = S[last];
+        for (int m = first; m <= last; ++m) in_k[m] = true;
+        return first;
+    };
+
+    if (n == d - 1) {
+        // Output mode has unit stride: tile rows are the output rows.
+        p.layout = 1;
+        p.form = 0;
+        choose_k(d - 2);
+        k.nrows = dims[n];
+        k.row_stride = 1;
+        in_rows[n] = true;
+    } else {
+        p.layout = 0;
+        const int kq = choose_k(d - 1);
+        int rlast = -1;
+        if (kq - 1 != n) {
+            rlast = kq - 1;
+        } else if (n >= 1) {
+            rlast = n - 1;
+        }
+        if (rlast >= 0) {
+            p.form = 1;
+            int rfirst = rlast;
+            if (dims[rlast] < 64 && rlast - 1 >= 0 && rlast - 1 != n) rfirst = rlast - 1;
+            k.r_mode0 = rfirst;
+            k.nrows = dims[rlast];
+            if (rfirst != rlast) {
+                k.r_mode1 = rlast;
+                k.IrB = dims[rlast];
+                k.nrows = dims[rfirst] * dims[rlast];
+            }
+            k.row_stride = S[rlast];
+            for (int m = rfirst; m <= rlast; ++m) in_rows[m] = true;
+        } else {
+            // n == 0 and every other mode is contracted: rows are the output.
+            p.form = 0;
+            k.nrows = dims[n];
+            k.row_stride = S[n];
+            in_rows[n] = true;
+        }
+    }
+
+    // Outer modes: everything else except the output mode.
+    k.nouter = 0;
+    k.nbatch = 1;
+    for (int m = 0; m < d; ++m) {
+        if (in_k[m] || in_rows[m] || m == n) continue;
+        k.o_mode[k.nouter] = m;
+        k.o_dim[k.nouter] = dims[m];
+        k.o_stride[k.nouter] = S[m];
+        k.nbatch *= dims[m];
+        ++k.nouter;
+    }
+    for (int j = k.nouter; j < 3; ++j) {
+        k.o_mode[j] = -1;
+        k.o_dim[j] = 1;
+        k.o_stride[j] = 0;
+    }
+    k.n_stride = S[n];
+
+    // Vectorised loads need every 4-element group inside the tensor and
+    // aligned with the row/fibre starts.
+    if (p.layout == 0)
+        p.vec = (k.K % 4 == 0) && (k.row_stride % 4 == 0);
+    else
+        p.vec = (k.nrows % 4 == 0) && (k.k_stride % 4 == 0);
+    if (p.layout == 0) {
+        for (int j = 0; j < k.nouter; ++j)
+            if (k.o_stride[j] % 4 != 0) p.vec = false;
+        if (p.form == 1 && k.n_stride % 4 != 0) p.vec = false;
+    } else {
+        for (int j = 0; j < k.nouter; ++j)
+            if (k.o_stride[j] % 4 != 0) p.vec = false;
+    }
+
+    // Wave tile: mb x 16 rows, nb x 16 rank columns.
+    const int64_t ncb = ceil_div(rank, 16);  // 16-wide rank blocks
+    int nb_pref = ncb >= 4 ? 4 : (ncb >= 2 ? 2 : 1);
+    if (elem_bytes == 4 && ncb >= 8 && p.layout == 0 && p.form == 1) nb_pref = 8;
+    if (p.layout == 1)
+        p.mb = 4;
+    else if (p.form == 1)
+        p.mb = (k.nrows >= 64 && nb_pref <= 2) ? 4 : 2;
+    else
+        p.mb = 2;
+
+    k.Kpad = ceil_div(k.K, 16) * 16;
+    auto bpitch_for = [&](int nb) { return 16 * nb + (elem_bytes == 8 ? 4 : 8); };
+    auto b_bytes = [&](int nb) { return (size_t)k.Kpad * bpitch_for(nb) * elem_bytes; };
+    p.nb = nb_pref;
+    p.b_in_lds = b_bytes(p.nb) <= kLdsBudget;
+    if (!p.b_in_lds) {
+        if (k.k_mode1 < 0) {
+            // Contraction factor read through L1/L2 instead of LDS; wide rank
+            // tile so X is re-read fewer times.
+            if (p.layout == 0) {
+                p.mb = 2;
+                p.nb = ncb >= 8 ? 8 : nb_pref;
+            } else {
+                p.nb = nb_pref;
+            }
+        } else {
+            while (p.nb > 1 && b_bytes(p.nb) > kLdsBudget) p.nb /= 2;
+            if (b_bytes(p.nb) > kLdsBudget) return MTTKRP_ERANGE;
+            p.b_in_lds = true;
+        }
+    }
+    k.bpitch = p.b_in_lds ? bpitch_for(p.nb) : 0;
+
+    // Work decomposition.
+    const int64_t rows_per_tile = 16 * p.mb;
+    k.nrtiles = ceil_div(rank, 16 * p.nb);
+    if (p.form == 1) {
+        k.nunits = k.In;
+        k.nrowtiles = ceil_div(k.nrows, rows_per_tile);
+        k.nitems = k.nbatch * k.nrowtiles;
+    } else {
+        k.nunits = ceil_div(k.In, rows_per_tile);
+        k.nrowtiles = 1;
+        k.nitems = k.nbatch;
+    }
+    const int64_t base = k.nunits * k.nrtiles;
+    const int64_t target = 4 * kNumCU;
+    int64_t want = std::max<int64_t>(1, ceil_div(target, base));
+    // Partial-sum traffic cap: 2 * nsplit * I_n * R * 8 <= N * elem / 10.
+    const int64_t out_bytes = k.In * rank * 8;
+    const int64_t cap_traffic = std::max<int64_t>(1, (N * elem_bytes / 10) / std::max<int64_t>(1, 2 * out_bytes));
+    want = std::min<int64_t>(want, std::min<int64_t>(cap_traffic, 1024));
+    int64_t chunk = ceil_div(k.nitems, want);
+    if (k.nitems >= kWaves) chunk = ceil_div(chunk, kWaves) * kWaves;
+    k.chunk = std::max<int64_t>(1, chunk);
+    k.nsplit = ceil_div(k.nitems, k.chunk);
+    k.grid_real = k.nunits * k.nsplit * k.nrtiles;
+    k.grid_per_xcd = ceil_div(k.grid_real, kNumXCD);
+    p.grid = k.grid_per_xcd * kNumXCD;
+    if (p.grid > INT_MAX) return MTTKRP_ERANGE;
+
+    size_t red = 0;
+    if (p.form == 1)
+        red = (size_t)kWaves * 16 * p.nb * 8;
+    else
+        red = (size_t)rows_per_tile * 16 * p.nb * 8;
+    p.lds_bytes = std::max(p.b_in_lds ? b_bytes(p.nb) : (size_t)0, red);
+    p.ws_bytes = k.nsplit > 1 ? (size_t)k.nsplit * (size_t)out_bytes : 0;
+    p.ws_bytes = (p.ws_bytes + 255) / 256 * 256;
+
+    p.k_modes[0] = k.k_mode0;
+    p.k_modes[1] = k.k_mode1;
+    if (p.form == 1) {
+        p.row_modes[0] = k.r_mode0;
+        p.row_modes[1] = k.r_mode1;
+    } else {
+        p.row_modes[0] = n;
+        p.row_modes[1] = -1;
+    }
+    for (int j = 0; j < 3; ++j) p.outer_modes[j] = k.o_mode[j];
+    plan = p;
+    return MTTKRP_OK;
+}
+
+size_t als_extra_bytes(const int64_t *dims, int order, int64_t rank)
+{
+    int64_t maxI = 0;
+    for (int m = 0; m < order; ++m) maxI = std::max<int64_t>(maxI, dims[m]);
+    const size_t R = (size_t)rank;
+    // M (fp64), Grams of every mode, V, L, lambda, scalars
+    size_t b = 8 * ((size_t)maxI * R + (size_t)order * R * R + 2 * R * R + R + 64);
+    return (b + 255) / 256 * 256;
+}
+
+}  // namespace mttkrp

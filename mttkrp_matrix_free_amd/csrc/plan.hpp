@@ -1,0 +1,103 @@
+// Host planner and kernel parameter block for the matrix-free MTTKRP.
+//
+// Decomposition (one mode n of a d-way row-major tensor):
+//   * A contraction group K of one or two consecutive modes is summed on the
+//     matrix cores against the factor rows of those modes: T(row, r) =
+//     sum_k X(.., row, .., k) * B(k, r), with B(k, r) = U_ka(k / I_kb, r) *
+//     U_kb(k % I_kb, r) (a Khatri-Rao tile of at most two factors, built in LDS
+//     on the fly).  This is the mode-k product of "An HPC Approach to
+//     Accelerate Tensor Decompositions", Eq. (1), with the factor as the
+//     matrix.
+//   * Tile rows index one or two consecutive modes (layout 0: the contraction
+//     index has unit stride, rows are fibres) or the output mode itself when
+//     it is the last mode (layout 1: rows have unit stride).
+//   * Every remaining mode is an "outer" mode, iterated per tile, whose factor
+//     row is a Hadamard multiplier (the tile Hadamard product of the GenTen
+//     page, Fig. 2).
+//   * form 0: tile rows are the output rows; the outer multiplier scales B and
+//     the matrix-core accumulators sum over every outer tuple directly.
+//     form 1: the output index is an outer index fixed per workgroup; after
+//     each tile the accumulators are reduced over the tile rows against the
+//     row factors and the outer multiplier.
+// Partial results of independent chunks go to a workspace and are summed in a
+// fixed order by a second kernel (deterministic), as the GenTen page's Fig. 2
+// allows several workgroups per slice.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mttkrp {
+
+constexpr int kMaxOrder = 5;
+constexpr int kWaves = 4;              // waves per workgroup
+constexpr int kThreads = 64 * kWaves;  // threads per workgroup
+constexpr int kNumCU = 256;            // MI355X compute units
+constexpr int kNumXCD = 8;             // accelerator complex dies (L2 domains)
+constexpr size_t kLdsBudget = 80 * 1024;  // dynamic LDS per workgroup (2 WGs / CU of 160 KB)
+
+struct KParams {
+    const void *X;
+    // factor rows by role (device): contraction group, tile rows, outer modes
+    const void *Uk0, *Uk1;     // Uk1 = null when the contraction group is one mode
+    const void *Ur0, *Ur1;     // form 1 only; Ur1 = null for one row mode
+    const void *Uo[3];         // null past nouter
+    void *out;                 // I_n x R, element type of the problem
+    double *partial;           // [nsplit][I_n][R] fp64 partial sums (nsplit > 1)
+    int64_t R;
+    int64_t In;                // output rows
+    // contraction group
+    int64_t K;                 // contraction length
+    int64_t Kpad;              // K rounded up to 16
+    int64_t k_stride;          // element stride of k in X
+    int k_mode0, k_mode1;      // k = i_{k_mode0} * IkB + i_{k_mode1}; k_mode1 = -1: single mode
+    int64_t IkB;
+    // tile rows
+    int64_t nrows;             // rows per batch
+    int64_t row_stride;        // element stride of the row index
+    int r_mode0, r_mode1;      // form 1 only; row = i_{r_mode0} * IrB + i_{r_mode1}
+    int64_t IrB;
+    // outer modes (decoded last-fastest from the batch index)
+    int nouter;
+    int o_mode[3];
+    int64_t o_dim[3];
+    int64_t o_stride[3];
+    int64_t nbatch;
+    int64_t n_stride;          // form 1: stride of the output mode
+    // decomposition
+    int64_t nunits;            // form 1: I_n; form 0: row tiles of the output
+    int64_t nrowtiles;         // form 1: row tiles per batch
+    int64_t nitems;            // work items per unit (form 1: batches x row tiles; form 0: batches)
+    int64_t chunk;             // items per workgroup
+    int64_t nsplit;            // chunks per unit
+    int64_t nrtiles;           // rank tiles
+    int64_t grid_real;         // nunits * nsplit * nrtiles
+    int64_t grid_per_xcd;      // ceil(grid_real / kNumXCD)
+    int bpitch;                // LDS row pitch of B (elements)
+    int out64;                 // 1: `out` is fp64 whatever the element type
+};
+
+struct Plan {
+    int elem_bytes = 8;
+    int form = 1;
+    int layout = 0;   // 0: contraction index contiguous; 1: rows contiguous
+    int mb = 4, nb = 2;
+    bool b_in_lds = true;
+    bool vec = true;
+    int k_modes[2] = {-1, -1};
+    int row_modes[2] = {-1, -1};
+    int outer_modes[3] = {-1, -1, -1};
+    KParams kp{};
+    int64_t grid = 0;        // launched grid (multiple of kNumXCD)
+    size_t lds_bytes = 0;
+    size_t ws_bytes = 0;
+};
+
+// Fills `plan` for mode `mode`.  Returns 0 or a MTTKRP_* status.  Pure host
+// code: no HIP call.  Pointers in plan.kp are left null.
+int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_bytes, Plan &plan);
+
+// Workspace of the CP-ALS driver beyond the MTTKRP workspace (bytes).
+size_t als_extra_bytes(const int64_t *dims, int order, int64_t rank);
+
+}  // namespace mttkrp

@@ -11,3 +11,21 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
     config.addinivalue_line("markers", "slow: takes more than a few seconds on the CPU")
+
+
+def pytest_collection_modifyitems(config, items):
+    """GPU tests need a visible GPU; without one they are skipped (the CPU suite
+    runs with -m "not gpu" anyway)."""
+    if not any("gpu" in item.keywords for item in items):
+        return
+    try:
+        import torch
+        have_gpu = torch.cuda.is_available()
+    except Exception:  # pragma: no cover
+        have_gpu = False
+    if have_gpu:
+        return
+    skip = pytest.mark.skip(reason="no GPU visible")
+    for item in items:
+        if "gpu" in item.keywords:
+            item.add_marker(skip)

@@ -1,0 +1,192 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, rejects bad arguments with the documented codes before any
+HIP call, and plans within the hardware limits and the matrix-free memory
+contract (workspace independent of the Khatri-Rao size; "A Performance
+Portable Matrix Free Dense MTTKRP in GenTen", TL;DR).
+
+Calls made here all fail validation or are pure queries; none launches work.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mttkrp_matrix_free_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mttkrp.h")
+
+P = ctypes.c_void_p
+FAKE = 0x7F0000001000          # aligned, never dereferenced (validation fails first)
+FAKE_MIS = 0x7F0000001008      # 8-byte aligned only
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while", "for", "sizeof")))
+
+
+def dims_arr(d):
+    return (ctypes.c_int64 * len(d))(*d)
+
+
+def ptrs(vals):
+    return (ctypes.c_void_p * len(vals))(*vals)
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = header_functions()
+    assert set(_lib.EXPORTS) == set(names), (sorted(set(names) ^ set(_lib.EXPORTS)))
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_strerror_and_version(L):
+    for code in range(0, -8, -1):
+        s = _lib.strerror(code)
+        assert s and s != "unknown status"
+    assert _lib.strerror(-99) == "unknown status"
+    assert L.mttkrp_version() >= 100
+
+
+def call_f64(L, X=FAKE, dims=(4, 5, 6), order=None, factors=None, rank=3, mode=0, out=FAKE,
+             ws=None, ws_bytes=0):
+    order = len(dims) if order is None else order
+    if factors is None:
+        factors = [FAKE] * max(len(dims) if dims is not None else order, 1)
+    return L.mttkrp_f64(X, dims_arr(dims) if dims is not None else None, order,
+                        ptrs(factors) if factors != "null" else None, rank, mode, out, ws,
+                        ws_bytes, None)
+
+
+def test_validation_codes(L):
+    # null pointers
+    assert call_f64(L, X=None) == _lib.EINVAL
+    assert call_f64(L, out=None) == _lib.EINVAL
+    assert call_f64(L, dims=None, order=3) == _lib.EINVAL
+    assert call_f64(L, factors="null") == _lib.EINVAL
+    assert call_f64(L, factors=[FAKE, None, FAKE]) == _lib.EINVAL
+    # order
+    assert call_f64(L, dims=(4, 5), order=2) == _lib.EORDER
+    assert call_f64(L, dims=(2, 2, 2, 2, 2, 2), order=6) == _lib.EORDER
+    # sizes, rank, mode
+    assert call_f64(L, dims=(4, 0, 6)) == _lib.EINVAL
+    assert call_f64(L, dims=(4, -1, 6)) == _lib.EINVAL
+    assert call_f64(L, rank=0) == _lib.EINVAL
+    assert call_f64(L, mode=3) == _lib.EINVAL
+    assert call_f64(L, mode=-1) == _lib.EINVAL
+    # alignment
+    assert call_f64(L, X=FAKE_MIS) == _lib.EALIGN
+    assert call_f64(L, out=FAKE_MIS) == _lib.EALIGN
+    assert call_f64(L, factors=[FAKE, FAKE_MIS, FAKE]) == _lib.EALIGN
+    # overflow of the element count / index range
+    assert call_f64(L, dims=(1 << 40, 1 << 40, 4)) == _lib.ERANGE
+    assert call_f64(L, dims=(1 << 20, 1 << 20, 1 << 12)) == _lib.ERANGE
+    # workspace too small (this plan needs partial sums)
+    need = ctypes.c_size_t()
+    assert L.mttkrp_workspace_bytes(dims_arr((256, 256, 256)), 3, 32, 2, 8, ctypes.byref(need)) == 0
+    assert need.value > 0
+    assert call_f64(L, dims=(256, 256, 256), rank=32, mode=2, ws=FAKE, ws_bytes=need.value - 256) \
+        == _lib.EWORKSPACE
+    assert call_f64(L, dims=(256, 256, 256), rank=32, mode=2, ws=None, ws_bytes=0) == _lib.EWORKSPACE
+
+
+def test_target_factor_may_be_null(L):
+    # factors[mode] == NULL is allowed; with the workspace missing the call stops
+    # at the workspace check, before any launch.
+    st = L.mttkrp_f64(FAKE, dims_arr((256, 256, 256)), 3, ptrs([FAKE, FAKE, None]), 32, 2, FAKE,
+                      None, 0, None)
+    assert st == _lib.EWORKSPACE
+
+
+def test_all_and_als_validation(L):
+    d = dims_arr((4, 5, 6))
+    outs = ptrs([FAKE, FAKE, FAKE])
+    assert L.mttkrp_all_f64(FAKE, d, 3, ptrs([FAKE, None, FAKE]), 3, outs, None, 0, None) == _lib.EINVAL
+    assert L.mttkrp_all_f64(FAKE, d, 3, ptrs([FAKE] * 3), 3, ptrs([FAKE, FAKE_MIS, FAKE]), None, 0,
+                            None) == _lib.EALIGN
+    assert L.mttkrp_all_f32(FAKE, d, 7, ptrs([FAKE] * 3), 3, outs, None, 0, None) == _lib.EORDER
+    fit = (ctypes.c_double * 4)()
+    done = ctypes.c_int()
+    args = dict(X=FAKE, dims=d, order=3, R=3, F=ptrs([FAKE] * 3), lam=FAKE, iters=4, tol=0.0,
+                fit=fit, done=ctypes.byref(done), ws=FAKE, wsb=1 << 20)
+
+    def als(**kw):
+        a = dict(args)
+        a.update(kw)
+        return L.cp_als_f64(a["X"], a["dims"], a["order"], a["R"], a["F"], a["lam"], a["iters"],
+                            a["tol"], a["fit"], a["done"], a["ws"], a["wsb"], None)
+    assert als(X=None) == _lib.EINVAL
+    assert als(lam=None) == _lib.EINVAL
+    assert als(fit=None) == _lib.EINVAL
+    assert als(iters=-1) == _lib.EINVAL
+    assert als(order=2) == _lib.EORDER
+    assert als(F=ptrs([FAKE, FAKE, None])) == _lib.EINVAL
+    assert als(lam=FAKE_MIS) == _lib.EALIGN
+    assert als(wsb=16) == _lib.EWORKSPACE
+    assert als(R=5000) == _lib.ERANGE
+
+
+WORKLOADS = [
+    ((64, 48, 32), 16, 8), ((256, 256, 256), 32, 8), ((512, 512, 512), 2000, 8),
+    ((128, 128, 128, 64), 8, 4), ((128, 128, 128, 64), 64, 4), ((128, 128, 128, 64), 512, 4),
+    ((50, 50, 50, 20, 10), 64, 8),
+    # ragged and degenerate shapes
+    ((1, 1, 1), 1, 8), ((33, 17, 19), 17, 8), ((7, 1, 5, 3), 5, 4), ((2, 3, 2, 3, 2), 3, 8),
+    ((5, 7, 1), 100, 8), ((1, 9, 4, 1, 6), 33, 4),
+]
+
+
+@pytest.mark.parametrize("dims,R,eb", WORKLOADS)
+def test_plans_within_limits_and_matrix_free_memory(L, dims, R, eb):
+    d = len(dims)
+    kr_bytes_max = 0
+    for n in range(d):
+        info = _lib.PlanInfo()
+        assert L.mttkrp_plan(dims_arr(dims), d, R, n, eb, ctypes.byref(info)) == 0
+        assert info.grid % 8 == 0 and info.grid >= 8
+        assert info.lds_bytes <= 80 * 1024
+        assert info.mb in (2, 4) and info.nb in (1, 2, 4, 8)
+        assert info.splits >= 1 and info.rtiles == -(-R // (16 * info.nb))
+        # the contraction modes and the tile-row modes are disjoint and exclude n
+        used = [m for m in list(info.k_modes) + list(info.row_modes) + list(info.outer_modes) if m >= 0]
+        if info.form == 0:
+            assert n in list(info.row_modes)
+        else:
+            assert n not in used
+        assert len(used) == len(set(used))
+        assert sorted(set(used) | {n}) == list(range(d))
+        # workspace: bounded by the output size times a hardware constant,
+        # never by the Khatri-Rao size prod_{m != n} I_m * R
+        ws = ctypes.c_size_t()
+        assert L.mttkrp_workspace_bytes(dims_arr(dims), d, R, n, eb, ctypes.byref(ws)) == 0
+        assert ws.value == info.ws_bytes
+        assert ws.value <= 8 * 1024 * dims[n] * R + 256
+        kr = 1
+        for m in range(d):
+            if m != n:
+                kr *= dims[m]
+        kr_bytes_max = max(kr_bytes_max, kr * R * eb)
+    allws = ctypes.c_size_t()
+    assert L.mttkrp_all_workspace_bytes(dims_arr(dims), d, R, eb, ctypes.byref(allws)) == 0
+    als = ctypes.c_size_t()
+    if R <= 4096:
+        assert L.cp_als_workspace_bytes(dims_arr(dims), d, R, eb, ctypes.byref(als)) == 0
+        assert als.value >= allws.value
+
+
+def test_workspace_far_below_khatri_rao_at_rank_2000(L):
+    """The 512^3, R = 2000 case: the explicit Khatri-Rao matrix of one mode is
+    512*512*2000*8 B = 4.19 GB; the matrix-free path needs no workspace."""
+    for n in range(3):
+        ws = ctypes.c_size_t()
+        assert L.mttkrp_workspace_bytes(dims_arr((512, 512, 512)), 3, 2000, n, 8, ctypes.byref(ws)) == 0
+        assert ws.value <= 0.01 * 512 * 512 * 2000 * 8

@@ -1,0 +1,118 @@
+"""GPU CP-ALS driver against the CPU oracle's CP-ALS ("A Performance Portable
+Matrix Free Dense MTTKRP in GenTen", Fig. 5: MTTKRP plus inner product and
+Cholesky solve per step).
+
+Bars: the fit of every sweep within 1e-9 of the oracle's; lambda and factors
+after the first sweep within 1e-10 (relative); after more sweeps the R x R
+solves may amplify rounding differences (an over-factored model), so only
+the fit is binding there and factors are checked loosely.
+"""
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+from mttkrp_matrix_free_amd import _lib, api, inputs  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+NT = min(16, len(os.sched_getaffinity(0)))
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+@pytest.mark.parametrize("dims,true_rank,R,iters", [
+    ((12, 10, 8), 3, 4, 1), ((12, 10, 8), 3, 4, 6), ((9, 8, 7, 6), 2, 5, 5),
+    ((6, 5, 7, 4, 3), 2, 3, 4), ((40, 35, 30), 5, 70, 3),
+])
+def test_als_small_vs_oracle(dims, true_rank, R, iters):
+    p = inputs.random_cp_problem(dims, true_rank, R, sigma=0.05, seed=31)
+    say(f"  cp_als {dims} R={R} iters={iters}")
+    F0, lam0, fit0, st0 = oracle.cp_als(p.X, p.factors, iters, nthreads=NT)
+    assert st0 == 0
+    X = dev(p.X)
+    U = [dev(u) for u in p.factors]
+    lam, fit, done, st = api.cp_als(X, U, iters)
+    assert st == 0 and done == iters
+    for it in range(iters):
+        assert abs(fit[it] - fit0[it]) <= 1e-9, (it, fit[it], fit0[it])
+    if iters == 1:
+        assert rel(lam.cpu().numpy(), lam0) <= 1e-10
+        for m in range(len(dims)):
+            assert rel(U[m].cpu().numpy(), F0[m]) <= 1e-10, m
+    else:
+        assert rel(lam.cpu().numpy(), lam0) <= 1e-6
+        for m in range(len(dims)):
+            assert rel(U[m].cpu().numpy(), F0[m]) <= 1e-6, m
+
+
+def test_fiveway_als_workload_vs_stored_oracle():
+    """50x50x50x20x10, rank-10 model + noise, R = 64, 10 sweeps.  The oracle's
+    run is stored by tests/golden/make_oracle_golden.py (oracle only)."""
+    g = json.load(open(os.path.join(GOLDEN, "fiveway_als_oracle.json")))
+    p = inputs.fiveway_als()
+    assert list(p.dims) == g["dims"] and p.rank == g["rank"]
+    X = dev(p.X)
+    U = [dev(u) for u in p.factors]
+    lam, fit, done, st = api.cp_als(X, U, g["iters"])
+    say("  fit gpu   ", fit)
+    say("  fit oracle", g["fit"])
+    assert st == 0 and done == g["iters"]
+    for it in range(g["iters"]):
+        assert abs(fit[it] - g["fit"][it]) <= 1e-9, (it, fit[it], g["fit"][it])
+    assert np.all(np.diff(fit) >= -1e-12)
+    assert rel(lam.cpu().numpy(), g["lambda"]) <= 1e-6
+
+
+def test_als_not_spd_leaves_factors():
+    p = inputs.random_cp_problem((10, 9, 8), 2, 3, sigma=0.0, seed=32)
+    Z = [u.copy() for u in p.factors]
+    for u in Z:
+        u[:, 1] = 0.0
+    X = dev(p.X)
+    U = [dev(u) for u in Z]
+    lam, fit, done, st = api.cp_als(X, U, 3)
+    assert st == _lib.ENOTSPD and done == 0
+    assert all(np.isnan(f) for f in fit)
+    for m in range(3):
+        assert np.array_equal(U[m].cpu().numpy(), Z[m])
+
+
+def test_als_tolerance_stops_early():
+    p = inputs.random_cp_problem((15, 14, 13), 2, 2, sigma=0.0, seed=33)
+    X = dev(p.X)
+    U = [dev(u) for u in p.factors]
+    lam, fit, done, st = api.cp_als(X, U, 50, tol=1e-10)
+    assert st == 0 and 1 < done < 50
+    assert all(np.isnan(f) for f in fit[done:])
+
+
+def test_als_float32():
+    p = inputs.random_cp_problem((20, 18, 16, 6), 3, 4, sigma=0.05, seed=34)
+    F0, lam0, fit0, st0 = oracle.cp_als(p.X, p.factors, 4, nthreads=NT)
+    X = dev(p.X.astype(np.float32))
+    U = [dev(u.astype(np.float32)) for u in p.factors]
+    lam, fit, done, st = api.cp_als(X, U, 4)
+    assert st == 0
+    # fp32 inputs differ from the fp64 ones by rounding: compare the fit loosely
+    for it in range(4):
+        assert abs(fit[it] - fit0[it]) <= 1e-4, (it, fit[it], fit0[it])

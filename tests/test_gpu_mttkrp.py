@@ -1,0 +1,217 @@
+"""GPU parity: the HIP MTTKRP against the CPU oracle on the same seeded inputs.
+
+Bar (relative Frobenius error per mode): 1e-12 for fp64, 1e-5 for fp32.
+Small and ragged shapes are compared in full; the large workloads on sampled
+output rows (which the oracle computes one by one) plus properties that hold
+at any size (closed form for exact CP tensors, cross-mode inner product).
+Every call goes through the C ABI (include/mttkrp.h) via the ctypes binding.
+"""
+import ctypes
+import os
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+from mttkrp_matrix_free_amd import _lib, api, inputs  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+NT = min(16, len(os.sched_getaffinity(0)))
+TOL = {np.dtype(np.float64): 1e-12, np.dtype(np.float32): 1e-5}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def rel_fro(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))
+
+
+def run_modes(p, modes=None, rows=None):
+    X = dev(p.X)
+    U = [dev(u) for u in p.factors]
+    d = p.X.ndim
+    errs = {}
+    for n in (range(d) if modes is None else modes):
+        say(f"  {p.name} mode {n} R={p.rank} dtype={p.X.dtype}")
+        M = api.mttkrp(X, U, n)
+        torch.cuda.synchronize()
+        Mg = M.cpu().numpy()
+        if rows is None:
+            Mo = oracle.mttkrp(p.X, p.factors, n, nthreads=NT)
+            errs[n] = rel_fro(Mg, Mo)
+        else:
+            rr = rows(p.dims[n])
+            Mo = oracle.mttkrp(p.X, p.factors, n, rows=rr, nthreads=NT)
+            errs[n] = rel_fro(Mg[rr], Mo)
+    del X, U
+    return errs
+
+
+SWEEP = [
+    ((33, 17, 19), 17, np.float64), ((33, 17, 19), 17, np.float32),
+    ((5, 7, 1), 100, np.float64), ((1, 1, 1), 1, np.float64), ((7, 1, 5, 3), 5, np.float64),
+    ((2, 3, 2, 3, 2), 3, np.float64), ((1, 9, 4, 1, 6), 33, np.float32),
+    ((40, 30, 20, 10), 64, np.float32), ((13, 11, 9, 7, 5), 24, np.float64),
+    ((100, 3, 70), 1, np.float64), ((130, 70, 50), 40, np.float64),
+    ((24, 20, 520), 40, np.float64),     # contraction too long for LDS: factor read from L2
+    ((36, 520, 20), 40, np.float64),     # same, output is the unit-stride mode
+    ((64, 64, 96), 130, np.float32),     # several rank tiles, 8-block tiles in fp32
+    ((17, 19, 23, 4), 19, np.float64),   # short last mode merged into the contraction
+    ((9, 10, 11, 12, 13), 7, np.float32),
+]
+
+
+@pytest.mark.parametrize("dims,R,dt", SWEEP, ids=[f"{'x'.join(map(str, d))}-R{r}-{np.dtype(t).name}"
+                                                  for d, r, t in SWEEP])
+def test_sweep_full_parity(dims, R, dt):
+    p = inputs.random_problem(dims, R, dtype=dt, seed=len(dims) * 1000 + R)
+    errs = run_modes(p)
+    for n, e in errs.items():
+        assert e <= TOL[np.dtype(dt)], (dims, R, n, e)
+
+
+def test_small_workload_64x48x32():
+    p = inputs.small_uniform_3way()
+    errs = run_modes(p)
+    say("  errors", errs)
+    assert all(e <= 1e-12 for e in errs.values()), errs
+
+
+def test_lowrank_cube_256_sampled_and_closed_form():
+    p = inputs.lowrank_cube_256(with_noise=True)
+    errs = run_modes(p, rows=lambda I: [0, 1, 77, 128, 200, I - 1])
+    say("  sampled-row errors", errs)
+    assert all(e <= 1e-12 for e in errs.values()), errs
+    # noise-free: the full output against the closed form U_n * Hadamard(U_m^T U_m)
+    q = inputs.lowrank_cube_256(with_noise=False)
+    X = dev(q.X)
+    U = [dev(u) for u in q.factors]
+    for n in range(3):
+        V = np.ones((32, 32))
+        for m in range(3):
+            if m != n:
+                V *= q.factors[m].T @ q.factors[m]
+        M = api.mttkrp(X, U, n).cpu().numpy()
+        e = rel_fro(M, q.factors[n] @ V)
+        say(f"  closed form mode {n}: {e:.3e}")
+        assert e <= 1e-12
+
+
+def test_highrank_cube_512_sampled_and_inner_products():
+    p = inputs.highrank_cube_512()
+    X = dev(p.X)
+    U = [dev(u) for u in p.factors]
+    inner = []
+    for n in range(3):
+        say(f"  512^3 R=2000 mode {n}")
+        M = api.mttkrp(X, U, n)
+        torch.cuda.synchronize()
+        inner.append(float(torch.sum(M * U[n]).item()))
+        rows = [0, 511] if n != 1 else [3, 300]
+        Mo = oracle.mttkrp(p.X, p.factors, n, rows=rows, nthreads=NT)
+        e = rel_fro(M[rows].cpu().numpy(), Mo)
+        say(f"    sampled rows {rows}: {e:.3e}")
+        assert e <= 1e-12
+        del M
+    # <X, [[U]]> computed through every mode agrees
+    ref = inner[0]
+    for v in inner[1:]:
+        assert abs(v - ref) <= 1e-12 * abs(ref) * 10, inner
+
+
+@pytest.mark.parametrize("R", [8, 64, 512])
+def test_fourway_f32_sampled(R):
+    p = inputs.fourway_f32(R)
+    errs = run_modes(p, rows=lambda I: [0, I // 3, I - 1])
+    say("  sampled-row errors", errs)
+    assert all(e <= 1e-5 for e in errs.values()), errs
+
+
+def test_fiveway_workload_full():
+    p = inputs.fiveway_als()
+    errs = run_modes(p)
+    say("  errors", errs)
+    assert all(e <= 1e-12 for e in errs.values()), errs
+
+
+def test_all_modes_entry_and_determinism():
+    p = inputs.random_problem((45, 38, 29, 6), 21, seed=5)
+    X = dev(p.X)
+    U = [dev(u) for u in p.factors]
+    outs = api.mttkrp_all(X, U)
+    outs2 = api.mttkrp_all(X, U)
+    for n in range(4):
+        single = api.mttkrp(X, U, n)
+        assert torch.equal(outs[n], single), n
+        assert torch.equal(outs[n], outs2[n]), n
+        assert rel_fro(outs[n].cpu().numpy(), oracle.mttkrp(p.X, p.factors, n, nthreads=NT)) <= 1e-12
+
+
+def test_target_factor_not_read():
+    p = inputs.random_problem((20, 30, 40), 9, seed=6)
+    X = dev(p.X)
+    U = [dev(u) for u in p.factors]
+    for n in range(3):
+        ref = api.mttkrp(X, U, n)
+        V = list(U)
+        V[n] = None
+        assert torch.equal(api.mttkrp(X, V, n), ref)
+        V[n] = torch.full_like(U[n], float("nan"))
+        assert torch.equal(api.mttkrp(X, V, n), ref)
+
+
+def test_nan_propagates_to_its_rows():
+    p = inputs.random_problem((12, 10, 8, 6), 5, seed=7)
+    Xn = p.X.copy()
+    Xn[3, 4, 5, 2] = np.nan
+    X = dev(Xn)
+    U = [dev(u) for u in p.factors]
+    star = (3, 4, 5, 2)
+    for n in range(4):
+        M = api.mttkrp(X, U, n).cpu().numpy()
+        bad = np.isnan(M).any(axis=1)
+        assert bad[star[n]] and bad.sum() == 1, (n, np.nonzero(bad))
+
+
+def test_workspace_and_alignment_errors_on_device():
+    p = inputs.random_problem((256, 64, 128), 32, seed=8)
+    X = dev(p.X)
+    U = [dev(u) for u in p.factors]
+    need = api.workspace_bytes(X.shape, 32, 2)
+    assert need > 0
+    small = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(_lib.MttkrpError) as ei:
+        api.mttkrp(X, U, 2, ws=small)
+    assert ei.value.status == _lib.EWORKSPACE
+    L = _lib.lib()
+    dims = (ctypes.c_int64 * 3)(256, 64, 128)
+    ptrs = (ctypes.c_void_p * 3)(*[u.data_ptr() for u in U])
+    out = torch.empty(256, 32, dtype=torch.float64, device="cuda")
+    st = L.mttkrp_f64(X.data_ptr() + 8, dims, 3, ptrs, 32, 0, out.data_ptr(), None, 0, None)
+    assert st == _lib.EALIGN
+
+
+def test_workspace_reuse_across_calls():
+    """One workspace buffer serves several calls in a row (partials are fully
+    rewritten each time)."""
+    p = inputs.random_problem((64, 96, 40), 24, seed=9)
+    X = dev(p.X)
+    U = [dev(u) for u in p.factors]
+    ws = torch.full((api.all_workspace_bytes(X.shape, 24),), 255, dtype=torch.uint8, device="cuda")
+    for n in (2, 0, 1, 2):
+        M = api.mttkrp(X, U, n, ws=ws).cpu().numpy()
+        assert rel_fro(M, oracle.mttkrp(p.X, p.factors, n, nthreads=NT)) <= 1e-12
