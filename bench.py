@@ -12,7 +12,7 @@ Printed: one JSON line with the whole-job throughput (GFLOP/s, flops per mode
 2 * R * prod(I)), a roofline object for the MTTKRP launches (algorithmic
 bytes or flops per launch over their average duration, from HIP events on the
 library's stream inside the timed region), a cold-cache measurement (a 1 GiB
-buffer is written before each mode so the tensor cannot be served from the
+buffer is read before each mode so the tensor cannot be served from the
 256 MB last-level cache), and the CPU oracle timed on a bounded sample of the
 same workload on this host's cores.
 """
@@ -46,6 +46,8 @@ def main():
     ap.add_argument("--cold-reps", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -65,6 +67,17 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        # A copy of known size: its FETCH_SIZE / WRITE_SIZE counters read what
+        # 1 GiB of HBM traffic looks like on this device.
+        a = torch.ones(1 << 27, dtype=torch.float64, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": a.numel() * 8, "launches": 3}), flush=True)
+        return
 
     t0 = time.time()
     p = inputs.workload(args.workload)
@@ -115,14 +128,16 @@ def main():
     mode_avg = [float(np.mean(v)) for v in mode_ms]
     value = d * flops_mode / (wall / args.steps) / 1e9
 
-    # ---- cold cache: a 1 GiB write before each mode, outside the event pair ----
+    # ---- cold cache: a 1 GiB read of another buffer before each mode, outside
+    # the event pair, evicts the tensor from the last-level cache ----
     cold = None
     if args.cold_reps > 0:
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        sink = torch.empty((), dtype=torch.float32, device=dev)
         cms = [[] for _ in range(d)]
         for _ in range(args.cold_reps):
             for n in range(d):
-                flush.zero_()
+                torch.sum(flush, out=sink)
                 a = torch.cuda.Event(enable_timing=True)
                 b = torch.cuda.Event(enable_timing=True)
                 a.record(stream)
@@ -130,7 +145,7 @@ def main():
                 b.record(stream)
                 torch.cuda.synchronize()
                 cms[n].append(a.elapsed_time(b))
-        del flush
+        del flush, sink
         cold_med = [float(np.median(v)) for v in cms]
         cold = {
             "ms_per_mode_median": [round(v, 5) for v in cold_med],

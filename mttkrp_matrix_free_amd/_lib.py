@@ -48,6 +48,7 @@ class PlanInfo(ctypes.Structure):
         ("grid", ctypes.c_int64),
         ("lds_bytes", ctypes.c_size_t),
         ("ws_bytes", ctypes.c_size_t),
+        ("kchunks", ctypes.c_int64),
     ]
 
     def as_dict(self):

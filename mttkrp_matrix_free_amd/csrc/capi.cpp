@@ -391,6 +391,7 @@ int mttkrp_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem
     info->grid = pl.grid;
     info->lds_bytes = pl.lds_bytes;
     info->ws_bytes = pl.ws_bytes;
+    info->kchunks = pl.kp.nkch;
     return MTTKRP_OK;
 }
 

@@ -10,29 +10,32 @@
 //   form 0 (rho = i_n):   M(rho, r) += T computed with B scaled by W_o(r)
 //   form 1 (i_n in o):    M(i_n, r) += sum_rho Z(rho, r) W_o(r) T(rho, r)
 //
-// where B is the (at most two-factor) Khatri-Rao tile of the contracted modes
-// staged in LDS, W_o the Hadamard product of the outer factor rows and Z that
-// of the row factors -- the "tile Hadamard product" of the GenTen page, Fig. 2.
+// where B is the (at most two-factor) Khatri-Rao tile of the contracted modes,
+// W_o the Hadamard product of the outer factor rows and Z that of the row
+// factors -- the "tile Hadamard product" of the GenTen page, Fig. 2.
 //
-// Operand delivery.  Each lane loads four consecutive tensor elements with
-// 16-byte global loads straight into registers (no LDS round trip for X):
+// Tensor loads.  X is read with buffer loads whose per-lane byte offsets are
+// fixed for a wave and whose per-step advance is a scalar offset.  A lane
+// whose element lies outside the tile (ragged rows, the tail of the
+// contraction, steps past the end of the wave's work) gets an offset past the
+// buffer's range, for which the hardware returns zero without touching memory.
+// The loads therefore carry no branches, and the loop keeps exactly one step
+// of loads in flight while the matrix cores work on the previous step:
 //   layout 0 (contraction index contiguous): a lane holds X(row, k0+4q..k0+4q+3)
 //     and feeds them to four successive MFMA k-steps; the k order inside the
 //     matrix-core reduction is permuted consistently for A and B, which leaves
 //     the sum unchanged;
 //   layout 1 (rows contiguous, output = last mode): a lane holds four
 //     consecutive rows at one k and feeds four interleaved 16-row blocks.
-// The next step's loads are issued before the current step's MFMAs (register
-// double buffering), so HBM latency hides behind matrix-core work.
 //
 // 16x16x4 MFMA lane layout (CDNA3/CDNA4): lane l supplies A(row l%16, k l/16)
 // and B(k l/16, col l%16), and receives D(Mfma<T>::row(l/16, e), l%16) in
 // element e.
 //
-// Workgroups: 256 threads (4 waves) sharing one B tile; the workgroup index is
-// remapped so that consecutive logical workgroups run on the same XCD (the
-// hardware deals workgroups round-robin over the 8 XCDs), keeping the rank
-// tiles of one tensor chunk in one L2.
+// Workgroups: 256 threads (4 waves) sharing one B tile, two workgroups per
+// compute unit; the workgroup index is remapped so that consecutive logical
+// workgroups run on the same XCD (the hardware deals workgroups round-robin
+// over the 8 XCDs), keeping the rank tiles of one tensor chunk in one L2.
 #include <hip/hip_runtime.h>
 
 #include "plan.hpp"
@@ -42,6 +45,15 @@ namespace mttkrp {
 typedef double dx4 __attribute__((ext_vector_type(4)));
 typedef double dx2 __attribute__((ext_vector_type(2)));
 typedef float fx4 __attribute__((ext_vector_type(4)));
+typedef float fx2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Third descriptor word of a raw (unstructured) buffer on gfx9-family parts.
+constexpr unsigned kRsrcWord3 = 0x00020000u;
+// Byte offset past every descriptor's range (ranges are kept below 2^31):
+// a load at this offset returns zero.
+constexpr unsigned kOOB = 0x80000000u;
 
 template <typename T>
 struct Mfma;
@@ -68,22 +80,43 @@ struct Mfma<float> {
     static __device__ __forceinline__ int row(int q, int e) { return 4 * q + e; }
 };
 
-__device__ __forceinline__ void load4(const double *p, double *v)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes)
 {
-    const dx2 a = *reinterpret_cast<const dx2 *>(p);
-    const dx2 b = *reinterpret_cast<const dx2 *>(p + 2);
+    const int n = bytes >= 0x7fffffff ? 0x7fffffff : (int)(bytes < 0 ? 0 : bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, kRsrcWord3);
+}
+
+// Four consecutive elements at byte offset voff (+ soff).
+__device__ __forceinline__ void bload4(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff,
+                                       double *v)
+{
+    const dx2 a = __builtin_bit_cast(dx2, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+    const dx2 b =
+        __builtin_bit_cast(dx2, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, soff, 0));
     v[0] = a[0];
     v[1] = a[1];
     v[2] = b[0];
     v[3] = b[1];
 }
-__device__ __forceinline__ void load4(const float *p, float *v)
+__device__ __forceinline__ void bload4(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff,
+                                       float *v)
 {
-    const fx4 a = *reinterpret_cast<const fx4 *>(p);
+    const fx4 a = __builtin_bit_cast(fx4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
     v[0] = a[0];
     v[1] = a[1];
     v[2] = a[2];
     v[3] = a[3];
+}
+// One element at byte offset voff (+ soff).
+__device__ __forceinline__ double bload1(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff,
+                                         double)
+{
+    return __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+__device__ __forceinline__ float bload1(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff,
+                                        float)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
 
 // Decoded work item: tensor offset of the tile origin, first tile row,
@@ -117,22 +150,39 @@ __device__ __forceinline__ Item decode_item(const KParams &p, int64_t it, int64_
     return r;
 }
 
-template <typename T, int MB, int NB, bool RC, bool VEC, bool FORM1, bool BLDS>
-__global__ __launch_bounds__(kThreads) void mttkrp_tile_kernel(KParams p)
+// Waves per SIMD the register budget allows: two when the accumulators, the
+// two tensor buffers and the fp64 flush of a tile leave room for the rest in
+// 256 registers, else one (512 registers).
+template <typename T, int MB, int NB, bool FORM1>
+constexpr int tile_min_waves()
+{
+    constexpr int acc = MB * NB * 4 * (int)sizeof(T) / 4;
+    constexpr int flush = (!FORM1 && sizeof(T) == 4) ? MB * NB * 4 * 2 : 0;
+    constexpr int abuf = 2 * 4 * MB * (int)sizeof(T) / 4;
+    constexpr int percol = 10;  // B operand, multiplier, column index, row sum
+    return acc + flush + abuf + percol * NB + 64 <= 256 ? 2 : 1;
+}
+
+template <typename T, int MB, int NB, bool RC, bool VEC, bool FORM1>
+__global__ __launch_bounds__(kThreads, (tile_min_waves<T, MB, NB, FORM1>())) void mttkrp_tile_kernel(KParams p)
 {
     static_assert(!RC || (MB % 4 == 0), "row-contiguous layout uses 64-row groups");
     static_assert(!RC || !FORM1, "row-contiguous layout has the output as rows");
     typedef typename Mfma<T>::acc_t acc_t;
     constexpr int BN = 16 * NB;
     constexpr int ROWS = 16 * MB;
-    constexpr int G = MB / 4;  // 64-row groups (layout 1)
+    constexpr int G = MB / 4;   // 64-row groups (layout 1)
+    constexpr int NA = 4 * MB;  // tensor elements per lane per step
+    constexpr unsigned SZ = sizeof(T);
 
     extern __shared__ __align__(16) unsigned char smem[];
     T *Bs = reinterpret_cast<T *>(smem);
     double *red = reinterpret_cast<double *>(smem);
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    // The wave index is uniform across the wave: keep it (and everything
+    // derived from it) in scalar registers.
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int q = lane >> 4;
     const int c16 = lane & 15;
@@ -143,30 +193,37 @@ __global__ __launch_bounds__(kThreads) void mttkrp_tile_kernel(KParams p)
     if (logical >= p.grid_real) return;
     const int64_t rtile = logical % p.nrtiles;
     const int64_t rest = logical / p.nrtiles;
-    const int64_t split = rest % p.nsplit;
+    const int64_t split = rest % p.nsplit;  // output partial written by this workgroup
     const int64_t unit = rest / p.nsplit;
+    const int64_t kch = split / p.nsplit_it;    // contraction chunk
+    const int64_t isplit = split - kch * p.nsplit_it;  // chunk of the work items
     const int64_t r0 = rtile * BN;
+    const int64_t kbase = kch * p.Kc;
+    const int64_t Kloc = min(p.Kc, p.K - kbase);
+    const int64_t nkc = (Kloc + 15) / 16;
 
     const T *__restrict__ X = reinterpret_cast<const T *>(p.X);
     const int64_t R = p.R;
 
-    // ---- stage the contraction-side Khatri-Rao tile B(k, r0:r0+BN) in LDS ----
-    if (BLDS) {
+    // ---- stage the contraction-side Khatri-Rao tile B(kbase + k, r0:r0+BN)
+    // in LDS, rows past the chunk zero-filled to a multiple of 16 ----
+    {
         const T *Ua = reinterpret_cast<const T *>(p.Uk0);
         const T *Ub = reinterpret_cast<const T *>(p.Uk1);
-        const int64_t total = p.Kpad * BN;
+        const int64_t total = nkc * 16 * BN;
         for (int64_t idx = tid; idx < total; idx += kThreads) {
             const int64_t kk = idx / BN;
             const int c = (int)(idx - kk * BN);
-            const int64_t col = r0 + c;
+            const int64_t colg = r0 + c;
             T v = T(0);
-            if (kk < p.K && col < R) {
+            if (kk < Kloc && colg < R) {
+                const int64_t kg = kbase + kk;
                 if (Ub == nullptr) {
-                    v = Ua[kk * R + col];
+                    v = Ua[kg * R + colg];
                 } else {
-                    const int64_t a = kk / p.IkB;
-                    const int64_t b = kk - a * p.IkB;
-                    v = Ua[a * R + col] * Ub[b * R + col];
+                    const int64_t a = kg / p.IkB;
+                    const int64_t b = kg - a * p.IkB;
+                    v = Ua[a * R + colg] * Ub[b * R + colg];
                 }
             }
             Bs[kk * p.bpitch + c] = v;
@@ -174,22 +231,26 @@ __global__ __launch_bounds__(kThreads) void mttkrp_tile_kernel(KParams p)
         __syncthreads();
     }
 
-    // Per-lane rank columns.
-    int64_t col[NB];
+    // Per-lane rank columns (R < 2^24, so 32 bits suffice).
+    int col[NB];
     bool colok[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-        col[nb] = r0 + nb * 16 + c16;
+        col[nb] = (int)r0 + nb * 16 + c16;
         colok[nb] = col[nb] < R;
     }
 
-    // Work range of this workgroup and wave.
-    const int64_t it_lo = split * p.chunk;
+    // Work range of this workgroup: items [it_lo, it_hi), each of nkc steps.
+    // The waves split the flattened step sequence evenly; a wave's range may
+    // start or end inside an item (every item result is linear in its steps,
+    // so a partial item is reduced like a whole one).
+    const int64_t it_lo = isplit * p.chunk;
     const int64_t it_hi = min(p.nitems, it_lo + p.chunk);
-    const int64_t my_first = it_lo + wave;
-    const int64_t my_items = my_first < it_hi ? (it_hi - my_first + kWaves - 1) / kWaves : 0;
-    const int64_t nkc = p.Kpad / 16;
-    const int64_t nsteps = my_items * nkc;
+    const int64_t wg_steps = it_hi > it_lo ? (it_hi - it_lo) * nkc : 0;
+    const int64_t per_wave = (wg_steps + kWaves - 1) / kWaves;
+    const int64_t s_lo = min(wg_steps, wave * per_wave);
+    const int64_t s_hi = min(wg_steps, s_lo + per_wave);
+    const int64_t nsteps = s_hi - s_lo;
 
     // Unit: form 1 -> output row i_n; form 0 -> tile of output rows.
     int64_t unit_off, out_row0;
@@ -222,73 +283,143 @@ __global__ __launch_bounds__(kThreads) void mttkrp_tile_kernel(KParams p)
                 for (int e = 0; e < (FLUSH64 ? 4 : 1); ++e) acc64[i][j][e] = 0.0;
     }
 
-    // ---- loads of one 16-wide contraction step ----
-    auto load_step = [&](T *a, const Item &itm, int64_t kc) {
+    // ---- per-lane byte offsets of the tensor elements inside a tile ----
+    // layout 0: row block mb, elements 4q..4q+3 of the contraction step;
+    // layout 1: substep s, 64-row group g, rows 4*c16..4*c16+3.
+    constexpr int NV = RC ? 4 * G : MB;
+    unsigned vbase[NV];
+    if (!RC) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+            vbase[mb] = (unsigned)(((int64_t)(mb * 16 + c16) * p.row_stride + 4 * q) * SZ);
+    } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+                vbase[s * G + g] =
+                    (unsigned)(((int64_t)(64 * g + 4 * c16) + (int64_t)(4 * s + q) * p.k_stride) * SZ);
+    }
+    // Row validity (form 0: fixed for the workgroup; form 1: per item).
+    auto row_offsets = [&](int64_t row0, unsigned *vo) {
         if (!RC) {
-            const int64_t kk = kc * 16 + 4 * q;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                vo[mb] = (row0 + mb * 16 + c16 < nrows_lim) ? vbase[mb] : kOOB;
+        } else {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    vo[s * G + g] = (out_row0 + 64 * g + 4 * c16 < p.In) ? vbase[s * G + g] : kOOB;
+        }
+    };
+
+    // Load cursor state: descriptor of the current item and its offsets.
+    struct LoadCursor {
+        __amdgpu_buffer_rsrc_t rsrc;
+        unsigned vo[NV];
+        int64_t it, kc, step;  // item, step in the item, step in the workgroup
+        int64_t orow[3];       // element offsets of the outer factor rows (i_o * R)
+        bool live;             // step < s_hi: past it, loads return zeros
+    };
+    const int64_t x_elems = p.x_bytes / SZ;
+    const int64_t kshift = RC ? kbase * p.k_stride : kbase;  // start of the chunk
+    auto enter_item = [&](LoadCursor &lc) {
+        if (lc.step < s_hi) {
+            const Item itm = decode_item(p, lc.it, unit_off, ROWS, FORM1);
+            const int64_t o = itm.off + kshift;
+            lc.rsrc = make_rsrc(X + o, (x_elems - o) * (int64_t)SZ);
+            row_offsets(FORM1 ? itm.row0 : out_row0, lc.vo);
+#pragma unroll
+            for (int j = 0; j < 3; ++j) lc.orow[j] = j < p.nouter ? itm.oidx[j] * R : 0;
+            lc.live = true;
+        } else {
+            lc.live = false;
+        }
+    };
+    // Columns of this lane clamped into the factor (loads need no branch).
+    int colc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) colc[nb] = colok[nb] ? col[nb] : 0;
+    // Outer factors; unused slots read the first row of the contraction factor
+    // and are replaced by 1 below, so every step issues the same loads.
+    const T *Uo[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+        Uo[j] = reinterpret_cast<const T *>(j < p.nouter ? p.Uo[j] : p.Uk0);
+
+    // Issue the loads of the cursor's step: its outer multiplier (the product
+    // of the outer factor rows, W_o) into wq, then its tensor elements into a.
+    // Each step carries the multiplier of its own item, so the multiplier is
+    // double-buffered with the tensor and no load depends on a branch.
+    auto load_step = [&](T *a, T *wq, const LoadCursor &lc) {
+        {
+            T f[3][NB];
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) f[j][nb] = Uo[j][lc.orow[j] + colc[nb]];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                T v = colok[nb] ? T(1) : T(0);
+#pragma unroll
+                for (int j = 0; j < 3; ++j) v *= (j < p.nouter) ? f[j][nb] : T(1);
+                wq[nb] = v;
+            }
+        }
+        const int64_t krem = Kloc - lc.kc * 16;  // contraction elements left in this item
+        if (!RC) {
+            const unsigned soff = (unsigned)(lc.kc * 16 * SZ);
+            const bool kin = lc.live && (4 * q < krem);
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
-                const int64_t rr = (FORM1 ? itm.row0 : out_row0) + mb * 16 + c16;
-                const T *src = X + itm.off + (int64_t)(mb * 16 + c16) * p.row_stride + kk;
                 if (VEC) {
-                    if (rr < nrows_lim && kk < p.K) {
-                        load4(src, a + mb * 4);
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) a[mb * 4 + e] = T(0);
-                    }
+                    bload4(lc.rsrc, kin ? lc.vo[mb] : kOOB, soff, a + mb * 4);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        a[mb * 4 + e] = (rr < nrows_lim && kk + e < p.K) ? src[e] : T(0);
+                        a[mb * 4 + e] = bload1(
+                            lc.rsrc, (lc.live && 4 * q + e < krem) ? lc.vo[mb] + e * SZ : kOOB,
+                            soff, T(0));
                 }
             }
         } else {
+            const unsigned soff = (unsigned)(lc.kc * 16 * p.k_stride * SZ);
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const int64_t kk = kc * 16 + 4 * s + q;
+                const bool kin = lc.live && (4 * s + q < krem);
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
-                    const int64_t rr = out_row0 + 64 * g + 4 * c16;
-                    const T *src = X + itm.off + kk * p.k_stride + 64 * g + 4 * c16;
                     T *dst = a + (s * G + g) * 4;
+                    const unsigned vo = kin ? lc.vo[s * G + g] : kOOB;
                     if (VEC) {
-                        if (kk < p.K && rr < p.In) {
-                            load4(src, dst);
-                        } else {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) dst[e] = T(0);
-                        }
+                        bload4(lc.rsrc, vo, soff, dst);
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            dst[e] = (kk < p.K && rr + e < p.In) ? src[e] : T(0);
+                            dst[e] = bload1(lc.rsrc,
+                                            (vo != kOOB && out_row0 + 64 * g + 4 * c16 + e < p.In)
+                                                ? vo + e * SZ
+                                                : kOOB,
+                                            soff, T(0));
                     }
                 }
             }
         }
     };
-
-    // Outer multiplier of an item (product of the outer factor rows).
-    auto outer_w = [&](const Item &itm, T *w) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) w[nb] = T(1);
-#pragma unroll
-        for (int j = 0; j < 3; ++j) {
-            if (j < p.nouter) {
-                const T *Uo = reinterpret_cast<const T *>(p.Uo[j]) + itm.oidx[j] * R;
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-                    if (colok[nb]) w[nb] *= Uo[col[nb]];
-            }
+    auto advance = [&](LoadCursor &lc) {
+        ++lc.step;
+        if (++lc.kc == nkc) {
+            lc.kc = 0;
+            ++lc.it;
+            enter_item(lc);
+        } else if (lc.step == s_hi) {
+            lc.live = false;
         }
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-            if (!colok[nb]) w[nb] = T(0);
     };
 
     // ---- matrix-core work of one step ----
-    const T *Ug = reinterpret_cast<const T *>(p.Uk0);
     auto compute_step = [&](const T *a, int64_t kc, const T *wb) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -296,11 +427,7 @@ __global__ __launch_bounds__(kThreads) void mttkrp_tile_kernel(KParams p)
             T b[NB];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                if (BLDS) {
-                    b[nb] = Bs[kk * p.bpitch + nb * 16 + c16];
-                } else {
-                    b[nb] = (kk < p.K && colok[nb]) ? Ug[kk * R + col[nb]] : T(0);
-                }
+                b[nb] = Bs[kk * p.bpitch + nb * 16 + c16];
                 if (!FORM1) b[nb] *= wb[nb];
             }
             if (!RC) {
@@ -323,30 +450,36 @@ __global__ __launch_bounds__(kThreads) void mttkrp_tile_kernel(KParams p)
     };
 
     // ---- end of a work item ----
-    auto finish_item = [&](const Item &itm, const T *w) {
+    auto finish_item = [&](int64_t row0, const T *w) {
         if (FORM1) {
-            // Reduce the tile rows against their factor rows and the outer multiplier.
+            // Reduce the tile rows against their factor rows and the outer
+            // multiplier, one accumulator row at a time: its factor loads use
+            // clamped indices (no branches) and rows past the tile's end are
+            // masked afterwards.
             const T *Ura = reinterpret_cast<const T *>(p.Ur0);
             const T *Urb = reinterpret_cast<const T *>(p.Ur1);
+            const bool two = Urb != nullptr;
+            const unsigned IrB = (unsigned)p.IrB;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int64_t rr = itm.row0 + mb * 16 + Mfma<T>::row(q, e);
-                    if (rr < p.nrows) {
-                        int64_t ia = rr, ib = 0;
-                        if (Urb) {
-                            ia = rr / p.IrB;
-                            ib = rr - ia * p.IrB;
-                        }
+                    const int64_t rr = row0 + mb * 16 + Mfma<T>::row(q, e);
+                    const bool rok = rr < p.nrows;
+                    const unsigned rc = rok ? (unsigned)rr : 0u;
+                    const unsigned ia = two ? rc / IrB : rc;
+                    const unsigned ib = two ? rc - ia * IrB : 0u;
+                    T za[NB], zb[NB];
 #pragma unroll
-                        for (int nb = 0; nb < NB; ++nb) {
-                            if (colok[nb]) {
-                                double z = (double)Ura[ia * R + col[nb]] * (double)w[nb];
-                                if (Urb) z *= (double)Urb[ib * R + col[nb]];
-                                accrow[nb] += z * (double)acc[mb][nb][e];
-                            }
-                        }
+                    for (int nb = 0; nb < NB; ++nb) {
+                        za[nb] = Ura[(int64_t)ia * R + colc[nb]];
+                        zb[nb] = two ? Urb[(int64_t)ib * R + colc[nb]] : T(1);
+                    }
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        const double z = (double)za[nb] * (double)zb[nb] * (double)w[nb];
+                        const double t = z * (double)acc[mb][nb][e];
+                        accrow[nb] += (rok && colok[nb]) ? t : 0.0;
                     }
                 }
 #pragma unroll
@@ -364,59 +497,51 @@ __global__ __launch_bounds__(kThreads) void mttkrp_tile_kernel(KParams p)
         }
     };
 
-    // ---- main loop: steps over (item, k-chunk), loads one step ahead ----
+    // ---- main loop: steps over (item, k-chunk); the loads of step t+1 are
+    // in flight while step t runs on the matrix cores ----
     if (nsteps > 0) {
-        T abuf0[MB * 4], abuf1[MB * 4];
-        // load cursor
-        int64_t l_it = my_first, l_kc = 0;
-        Item l_itm = decode_item(p, l_it, unit_off, ROWS, FORM1);
+        T abuf0[NA], abuf1[NA];
+        LoadCursor lc;
+        lc.it = it_lo + s_lo / nkc;
+        lc.kc = s_lo - (lc.it - it_lo) * nkc;
+        lc.step = s_lo;
+        enter_item(lc);
+        T wbuf0[NB], wbuf1[NB];
         // compute cursor
-        int64_t c_kc = 0;
-        Item c_itm = l_itm;
-        T w[NB];
-        outer_w(c_itm, w);
+        int64_t c_it = lc.it, c_kc = lc.kc, c_step = s_lo;
+        int64_t c_row0 = FORM1 ? decode_item(p, c_it, unit_off, ROWS, FORM1).row0 : 0;
 
-        auto advance_load = [&]() {
-            if (++l_kc == nkc) {
-                l_kc = 0;
-                l_it += kWaves;
-                if (l_it < it_hi) l_itm = decode_item(p, l_it, unit_off, ROWS, FORM1);
+        // After each step: reduce the item when it ends or when the wave's
+        // range ends inside it.
+        auto after_compute = [&](const T *w) {
+            ++c_step;
+            const bool item_end = ++c_kc == nkc;
+            if (c_step <= s_hi && (item_end || c_step == s_hi)) {
+                finish_item(c_row0, w);
+                if (item_end) {
+                    c_kc = 0;
+                    ++c_it;
+                    if (FORM1 && c_step < s_hi)
+                        c_row0 = decode_item(p, c_it, unit_off, ROWS, FORM1).row0;
+                }
             }
         };
-        // Items of the compute cursor are re-decoded from a counter.
-        int64_t c_it = my_first;
-        load_step(abuf0, l_itm, l_kc);
-        advance_load();
-        for (int64_t j = 0; j < nsteps; j += 2) {
-            if (j + 1 < nsteps) {
-                load_step(abuf1, l_itm, l_kc);
-                advance_load();
-            }
-            compute_step(abuf0, c_kc, w);
-            if (++c_kc == nkc) {
-                finish_item(c_itm, w);
-                c_kc = 0;
-                c_it += kWaves;
-                if (c_it < it_hi) {
-                    c_itm = decode_item(p, c_it, unit_off, ROWS, FORM1);
-                    outer_w(c_itm, w);
-                }
-            }
-            if (j + 1 >= nsteps) break;
-            if (j + 2 < nsteps) {
-                load_step(abuf0, l_itm, l_kc);
-                advance_load();
-            }
-            compute_step(abuf1, c_kc, w);
-            if (++c_kc == nkc) {
-                finish_item(c_itm, w);
-                c_kc = 0;
-                c_it += kWaves;
-                if (c_it < it_hi) {
-                    c_itm = decode_item(p, c_it, unit_off, ROWS, FORM1);
-                    outer_w(c_itm, w);
-                }
-            }
+
+        // Two steps per iteration with the buffers swapped by name, so that each
+        // buffer keeps its own registers.  An odd step count runs one extra step
+        // whose loads return zeros (past the wave's range), which adds nothing
+        // to the accumulators.
+        load_step(abuf0, wbuf0, lc);
+        advance(lc);
+        for (int64_t t = 0; t < nsteps; t += 2) {
+            load_step(abuf1, wbuf1, lc);  // step t+1
+            advance(lc);
+            compute_step(abuf0, c_kc, wbuf0);
+            after_compute(wbuf0);
+            load_step(abuf0, wbuf0, lc);  // step t+2
+            advance(lc);
+            compute_step(abuf1, c_kc, wbuf1);
+            after_compute(wbuf1);
         }
     }
 
@@ -500,19 +625,33 @@ __global__ __launch_bounds__(kThreads) void mttkrp_tile_kernel(KParams p)
 }
 
 // Fixed-order sum of the split partials: out[i] = sum_{s=0}^{S-1} partial[s][i].
-template <typename T>
+// A workgroup covers EW consecutive outputs with 256/EW thread groups; group g
+// sums the partials s = g, g + 256/EW, ... and the group sums are added in
+// the order g = 0, 1, ..., so the result does not depend on scheduling.
+template <typename T, int EW>
 __global__ __launch_bounds__(256) void split_reduce_kernel(const double *__restrict__ partial,
                                                            int64_t nsplit, int64_t count,
                                                            void *out, int out64)
 {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= count) return;
+    constexpr int NG = 256 / EW;
+    __shared__ double sh[NG][EW];
+    const int c = threadIdx.x % EW;
+    const int g = threadIdx.x / EW;
+    const int64_t i = (int64_t)blockIdx.x * EW + c;
     double v = 0.0;
-    for (int64_t s = 0; s < nsplit; ++s) v += partial[s * count + i];
-    if (out64)
-        reinterpret_cast<double *>(out)[i] = v;
-    else
-        reinterpret_cast<T *>(out)[i] = (T)v;
+    if (i < count) {
+        for (int64_t s = g; s < nsplit; s += NG) v += partial[s * count + i];
+    }
+    sh[g][c] = v;
+    __syncthreads();
+    if (g == 0 && i < count) {
+        double t = sh[0][c];
+        for (int j = 1; j < NG; ++j) t += sh[j][c];
+        if (out64)
+            reinterpret_cast<double *>(out)[i] = t;
+        else
+            reinterpret_cast<T *>(out)[i] = (T)t;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -521,49 +660,40 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const double *__restr
 
 typedef void (*TileKernel)(KParams);
 
-template <typename T, int MB, int NB, bool RC, bool VEC, bool FORM1, bool BLDS>
-TileKernel pick()
-{
-    return mttkrp_tile_kernel<T, MB, NB, RC, VEC, FORM1, BLDS>;
-}
-
-template <typename T, int MB, int NB, bool RC, bool FORM1, bool BLDS>
+template <typename T, int MB, int NB, bool RC, bool FORM1>
 TileKernel pick_vec(bool vec)
 {
-    return vec ? pick<T, MB, NB, RC, true, FORM1, BLDS>() : pick<T, MB, NB, RC, false, FORM1, BLDS>();
+    return vec ? mttkrp_tile_kernel<T, MB, NB, RC, true, FORM1>
+               : mttkrp_tile_kernel<T, MB, NB, RC, false, FORM1>;
 }
 
-template <typename T, int MB, bool RC, bool FORM1, bool BLDS>
+template <typename T, int MB, bool RC, bool FORM1, bool WIDE>
 TileKernel pick_nb(int nb, bool vec)
 {
     switch (nb) {
-    case 1: return pick_vec<T, MB, 1, RC, FORM1, BLDS>(vec);
-    case 2: return pick_vec<T, MB, 2, RC, FORM1, BLDS>(vec);
-    case 4: return pick_vec<T, MB, 4, RC, FORM1, BLDS>(vec);
+    case 1: return pick_vec<T, MB, 1, RC, FORM1>(vec);
+    case 2: return pick_vec<T, MB, 2, RC, FORM1>(vec);
+    case 4: return pick_vec<T, MB, 4, RC, FORM1>(vec);
+    case 8: return WIDE ? pick_vec<T, MB, (WIDE ? 8 : 4), RC, FORM1>(vec) : nullptr;
     default: return nullptr;
     }
 }
 
+// Instantiated tiles: layout 1 uses 64-row groups (mb = 4); layout 0 uses
+// mb = 2 or 4 in either form.
 template <typename T>
 TileKernel select_kernel(const Plan &pl)
 {
     if (pl.layout == 1) {
         if (pl.mb != 4 || pl.form != 0) return nullptr;
-        return pl.b_in_lds ? pick_nb<T, 4, true, false, true>(pl.nb, pl.vec)
-                           : pick_nb<T, 4, true, false, false>(pl.nb, pl.vec);
+        return pick_nb<T, 4, true, false, false>(pl.nb, pl.vec);
     }
-    if (pl.form == 0) {
-        if (pl.mb != 2 || !pl.b_in_lds) return nullptr;
-        return pick_nb<T, 2, false, false, true>(pl.nb, pl.vec);
-    }
-    if (!pl.b_in_lds) {
-        if (pl.mb != 2) return nullptr;
-        if (pl.nb == 8) return pick_vec<T, 2, 8, false, true, false>(pl.vec);
-        return pick_nb<T, 2, false, true, false>(pl.nb, pl.vec);
-    }
-    if (pl.nb == 8) return pl.mb == 2 ? pick_vec<T, 2, 8, false, true, true>(pl.vec) : nullptr;
-    if (pl.mb == 4) return pick_nb<T, 4, false, true, true>(pl.nb, pl.vec);
-    if (pl.mb == 2) return pick_nb<T, 2, false, true, true>(pl.nb, pl.vec);
+    if (pl.mb == 2)
+        return pl.form ? pick_nb<T, 2, false, true, true>(pl.nb, pl.vec)
+                       : pick_nb<T, 2, false, false, true>(pl.nb, pl.vec);
+    if (pl.mb == 4)
+        return pl.form ? pick_nb<T, 4, false, true, false>(pl.nb, pl.vec)
+                       : pick_nb<T, 4, false, false, false>(pl.nb, pl.vec);
     return nullptr;
 }
 
@@ -584,10 +714,15 @@ hipError_t launch_mttkrp(const Plan &pl, hipStream_t stream)
     if (e != hipSuccess) return e;
     if (pl.kp.nsplit > 1) {
         const int64_t count = pl.kp.In * pl.kp.R;
-        const unsigned blocks = (unsigned)((count + 255) / 256);
-        hipLaunchKernelGGL(split_reduce_kernel<T>, dim3(blocks), dim3(256), 0, stream,
-                           (const double *)pl.kp.partial, pl.kp.nsplit, count, pl.kp.out,
-                           pl.kp.out64);
+        if (pl.kp.nsplit >= 32) {
+            hipLaunchKernelGGL((split_reduce_kernel<T, 16>), dim3((unsigned)((count + 15) / 16)),
+                               dim3(256), 0, stream, (const double *)pl.kp.partial, pl.kp.nsplit,
+                               count, pl.kp.out, pl.kp.out64);
+        } else {
+            hipLaunchKernelGGL((split_reduce_kernel<T, 64>), dim3((unsigned)((count + 63) / 64)),
+                               dim3(256), 0, stream, (const double *)pl.kp.partial, pl.kp.nsplit,
+                               count, pl.kp.out, pl.kp.out64);
+        }
         e = hipGetLastError();
     }
     return e;

@@ -117,6 +117,11 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
         } else if (n >= 1) {
             rlast = n - 1;
         }
+        // At high rank the per-tile row reduction of form 1 (one factor load
+        // and one fma per accumulator element) costs more than scaling the
+        // contraction tile by the outer multiplier, so the output rows become
+        // the tile rows (form 0).
+        if (rank >= 256) rlast = -1;
         if (rlast >= 0) {
             p.form = 1;
             int rfirst = rlast;
@@ -131,7 +136,8 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
             k.row_stride = S[rlast];
             for (int m = rfirst; m <= rlast; ++m) in_rows[m] = true;
         } else {
-            // n == 0 and every other mode is contracted: rows are the output.
+            // The output rows are the tile rows; every other mode is contracted
+            // or outer.
             p.form = 0;
             k.nrows = dims[n];
             k.row_stride = S[n];
@@ -172,39 +178,37 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
             if (k.o_stride[j] % 4 != 0) p.vec = false;
     }
 
-    // Wave tile: mb x 16 rows, nb x 16 rank columns.
+    // Wave tile: mb x 16 rows, nb x 16 rank columns.  Wide rank tiles (nb = 8)
+    // reuse each tensor element for 128 columns when the rank is large; the
+    // row tile is 32 rows unless there is work for many more waves than the
+    // chip holds.
     const int64_t ncb = ceil_div(rank, 16);  // 16-wide rank blocks
-    int nb_pref = ncb >= 4 ? 4 : (ncb >= 2 ? 2 : 1);
-    if (elem_bytes == 4 && ncb >= 8 && p.layout == 0 && p.form == 1) nb_pref = 8;
-    if (p.layout == 1)
-        p.mb = 4;
-    else if (p.form == 1)
-        p.mb = (k.nrows >= 64 && nb_pref <= 2) ? 4 : 2;
+    if (ncb >= 8 && p.layout == 0 && (p.form == 0 || elem_bytes == 4))
+        p.nb = 8;
     else
+        p.nb = ncb >= 4 ? 4 : (ncb >= 2 ? 2 : 1);
+    if (p.layout == 1) {
+        p.mb = 4;
+    } else if (p.nb > 4) {
         p.mb = 2;
-
-    k.Kpad = ceil_div(k.K, 16) * 16;
-    auto bpitch_for = [&](int nb) { return 16 * nb + (elem_bytes == 8 ? 4 : 8); };
-    auto b_bytes = [&](int nb) { return (size_t)k.Kpad * bpitch_for(nb) * elem_bytes; };
-    p.nb = nb_pref;
-    p.b_in_lds = b_bytes(p.nb) <= kLdsBudget;
-    if (!p.b_in_lds) {
-        if (k.k_mode1 < 0) {
-            // Contraction factor read through L1/L2 instead of LDS; wide rank
-            // tile so X is re-read fewer times.
-            if (p.layout == 0) {
-                p.mb = 2;
-                p.nb = ncb >= 8 ? 8 : nb_pref;
-            } else {
-                p.nb = nb_pref;
-            }
-        } else {
-            while (p.nb > 1 && b_bytes(p.nb) > kLdsBudget) p.nb /= 2;
-            if (b_bytes(p.nb) > kLdsBudget) return MTTKRP_ERANGE;
-            p.b_in_lds = true;
-        }
+    } else if (p.form == 1) {
+        const int64_t tiles64 = k.In * k.nbatch * ceil_div(k.nrows, 64);
+        p.mb = (p.nb <= 2 && tiles64 >= 8192) ? 4 : 2;
+    } else {
+        p.mb = (k.In >= 64 && p.nb <= 2) ? 4 : 2;
     }
-    k.bpitch = p.b_in_lds ? bpitch_for(p.nb) : 0;
+
+    // Contraction chunks: the Khatri-Rao tile of one chunk (Kc x 16nb) must
+    // fit in the workgroup's LDS; longer contractions are split into chunks
+    // whose results are summed by the reduction pass.
+    const int bpitch = 16 * p.nb + (elem_bytes == 8 ? 4 : 8);
+    const int64_t Kpad = ceil_div(k.K, 16) * 16;
+    const int64_t kc_max = (int64_t)(kLdsBudget / ((size_t)bpitch * elem_bytes)) / 16 * 16;
+    if (kc_max < 16) return MTTKRP_ERANGE;
+    k.Kc = std::min<int64_t>(Kpad, kc_max);
+    k.nkch = ceil_div(k.K, k.Kc);
+    k.bpitch = bpitch;
+    p.b_in_lds = true;
 
     // Work decomposition.
     const int64_t rows_per_tile = 16 * p.mb;
@@ -218,28 +222,46 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
         k.nrowtiles = 1;
         k.nitems = k.nbatch;
     }
-    const int64_t base = k.nunits * k.nrtiles;
-    const int64_t target = 4 * kNumCU;
+    // Split the work items of a unit so that the grid holds two workgroups
+    // per compute unit (four when the staged Khatri-Rao tile is small, so
+    // that restaging it is cheap), while the partial sums (written and read
+    // once each) stay under an eighth of the tensor traffic.  The waves of a
+    // workgroup share its steps evenly, so a chunk may hold any number of
+    // items.
+    const size_t b_tile = (size_t)k.Kc * k.bpitch * elem_bytes;
+    const int64_t base = k.nunits * k.nrtiles * k.nkch;
+    const int64_t target = (b_tile > 32 * 1024 ? 2 : 4) * kNumCU;
     int64_t want = std::max<int64_t>(1, ceil_div(target, base));
-    // Partial-sum traffic cap: 2 * nsplit * I_n * R * 8 <= N * elem / 10.
     const int64_t out_bytes = k.In * rank * 8;
-    const int64_t cap_traffic = std::max<int64_t>(1, (N * elem_bytes / 10) / std::max<int64_t>(1, 2 * out_bytes));
+    const int64_t cap_traffic = std::max<int64_t>(
+        1, (N * elem_bytes / 8) / std::max<int64_t>(1, 2 * out_bytes * k.nkch));
     want = std::min<int64_t>(want, std::min<int64_t>(cap_traffic, 1024));
-    int64_t chunk = ceil_div(k.nitems, want);
-    if (k.nitems >= kWaves) chunk = ceil_div(chunk, kWaves) * kWaves;
-    k.chunk = std::max<int64_t>(1, chunk);
-    k.nsplit = ceil_div(k.nitems, k.chunk);
+    k.chunk = std::max<int64_t>(1, ceil_div(k.nitems, want));
+    k.nsplit_it = ceil_div(k.nitems, k.chunk);
+    k.nsplit = k.nsplit_it * k.nkch;
     k.grid_real = k.nunits * k.nsplit * k.nrtiles;
     k.grid_per_xcd = ceil_div(k.grid_real, kNumXCD);
     p.grid = k.grid_per_xcd * kNumXCD;
     if (p.grid > INT_MAX) return MTTKRP_ERANGE;
+
+    // Buffer loads address a tile with 32-bit byte offsets below 2^31: the
+    // span of one tile (its rows and its whole contraction) must fit.
+    {
+        int64_t span;
+        if (p.layout == 0)
+            span = ((rows_per_tile - 1) * k.row_stride + k.Kc) * elem_bytes;
+        else
+            span = (rows_per_tile + (k.Kc - 1) * k.k_stride) * elem_bytes;
+        if (span >= (INT64_C(1) << 31) - 64) return MTTKRP_ERANGE;
+    }
+    k.x_bytes = N * elem_bytes;
 
     size_t red = 0;
     if (p.form == 1)
         red = (size_t)kWaves * 16 * p.nb * 8;
     else
         red = (size_t)rows_per_tile * 16 * p.nb * 8;
-    p.lds_bytes = std::max(p.b_in_lds ? b_bytes(p.nb) : (size_t)0, red);
+    p.lds_bytes = std::max((size_t)k.Kc * k.bpitch * elem_bytes, red);
     p.ws_bytes = k.nsplit > 1 ? (size_t)k.nsplit * (size_t)out_bytes : 0;
     p.ws_bytes = (p.ws_bytes + 255) / 256 * 256;
 

@@ -38,6 +38,7 @@ constexpr size_t kLdsBudget = 80 * 1024;  // dynamic LDS per workgroup (2 WGs / 
 
 struct KParams {
     const void *X;
+    int64_t x_bytes;           // bytes of X (bounds of its buffer descriptor)
     // factor rows by role (device): contraction group, tile rows, outer modes
     const void *Uk0, *Uk1;     // Uk1 = null when the contraction group is one mode
     const void *Ur0, *Ur1;     // form 1 only; Ur1 = null for one row mode
@@ -48,7 +49,8 @@ struct KParams {
     int64_t In;                // output rows
     // contraction group
     int64_t K;                 // contraction length
-    int64_t Kpad;              // K rounded up to 16
+    int64_t Kc;                // contraction chunk of one workgroup (multiple of 16)
+    int64_t nkch;              // contraction chunks (each writes its own partial)
     int64_t k_stride;          // element stride of k in X
     int k_mode0, k_mode1;      // k = i_{k_mode0} * IkB + i_{k_mode1}; k_mode1 = -1: single mode
     int64_t IkB;
@@ -69,7 +71,8 @@ struct KParams {
     int64_t nrowtiles;         // form 1: row tiles per batch
     int64_t nitems;            // work items per unit (form 1: batches x row tiles; form 0: batches)
     int64_t chunk;             // items per workgroup
-    int64_t nsplit;            // chunks per unit
+    int64_t nsplit;            // partial outputs per unit: nsplit_it * nkch
+    int64_t nsplit_it;         // chunks of the work items per unit
     int64_t nrtiles;           // rank tiles
     int64_t grid_real;         // nunits * nsplit * nrtiles
     int64_t grid_per_xcd;      // ceil(grid_real / kNumXCD)

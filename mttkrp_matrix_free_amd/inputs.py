@@ -55,7 +55,7 @@ def cp_tensor(factors: Sequence[np.ndarray]) -> np.ndarray:
     d = len(factors)
     letters = "abcdefgh"[:d]
     spec = ",".join(f"{c}z" for c in letters) + "->" + letters
-    return np.einsum(spec, *factors, optimize=True)
+    return np.ascontiguousarray(np.einsum(spec, *factors, optimize=True))
 
 
 # ---------------------------------------------------------------------------
