@@ -133,11 +133,10 @@ def main():
     cold = None
     if args.cold_reps > 0:
         flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-        sink = torch.empty((), dtype=torch.float32, device=dev)
         cms = [[] for _ in range(d)]
         for _ in range(args.cold_reps):
             for n in range(d):
-                torch.sum(flush, out=sink)
+                sink = flush.sum()
                 a = torch.cuda.Event(enable_timing=True)
                 b = torch.cuda.Event(enable_timing=True)
                 a.record(stream)
@@ -145,7 +144,7 @@ def main():
                 b.record(stream)
                 torch.cuda.synchronize()
                 cms[n].append(a.elapsed_time(b))
-        del flush, sink
+        del flush
         cold_med = [float(np.median(v)) for v in cms]
         cold = {
             "ms_per_mode_median": [round(v, 5) for v in cold_med],

@@ -80,10 +80,17 @@ struct Mfma<float> {
     static __device__ __forceinline__ int row(int q, int e) { return 4 * q + e; }
 };
 
+// Descriptor of [base, base + bytes) (range capped below 2^31).  The base and
+// the range are wave-uniform; they are read from the first lane so that the
+// compiler keeps the descriptor in scalar registers.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes)
 {
     const int n = bytes >= 0x7fffffff ? 0x7fffffff : (int)(bytes < 0 ? 0 : bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, kRsrcWord3);
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(lo | (hi << 32)), 0,
+                                             __builtin_amdgcn_readfirstlane(n), kRsrcWord3);
 }
 
 // Four consecutive elements at byte offset voff (+ soff).
@@ -154,13 +161,28 @@ __device__ __forceinline__ Item decode_item(const KParams &p, int64_t it, int64_
 // two tensor buffers and the fp64 flush of a tile leave room for the rest in
 // 256 registers, else one (512 registers).
 template <typename T, int MB, int NB, bool FORM1>
+constexpr int tile_regs(int buffers)
+{
+    const int acc = MB * NB * 4 * (int)sizeof(T) / 4;
+    const int flush = (!FORM1 && sizeof(T) == 4) ? MB * NB * 4 * 2 : 0;
+    const int buf = (4 * MB + 3 * NB) * (int)sizeof(T) / 4;  // tensor elements + factor values
+    // B operand, column index, row sum; form 1 also holds the row factors of
+    // the tile reduction and their addresses.
+    const int percol = FORM1 ? 16 : 10;
+    const int fixed = FORM1 ? 96 : 64;
+    return acc + flush + buffers * buf + percol * NB + fixed;
+}
+template <typename T, int MB, int NB, bool FORM1>
 constexpr int tile_min_waves()
 {
-    constexpr int acc = MB * NB * 4 * (int)sizeof(T) / 4;
-    constexpr int flush = (!FORM1 && sizeof(T) == 4) ? MB * NB * 4 * 2 : 0;
-    constexpr int abuf = 2 * 4 * MB * (int)sizeof(T) / 4;
-    constexpr int percol = 10;  // B operand, multiplier, column index, row sum
-    return acc + flush + abuf + percol * NB + 64 <= 256 ? 2 : 1;
+    return tile_regs<T, MB, NB, FORM1>(2) <= 256 ? 2 : 1;
+}
+// Steps of tensor loads kept in flight ahead of the matrix cores: two when a
+// third register buffer fits the budget the occupancy above leaves, else one.
+template <typename T, int MB, int NB, bool FORM1>
+constexpr int tile_prefetch()
+{
+    return tile_regs<T, MB, NB, FORM1>(3) <= 512 / tile_min_waves<T, MB, NB, FORM1>() ? 2 : 1;
 }
 
 template <typename T, int MB, int NB, bool RC, bool VEC, bool FORM1>
@@ -204,32 +226,6 @@ __global__ __launch_bounds__(kThreads, (tile_min_waves<T, MB, NB, FORM1>())) voi
 
     const T *__restrict__ X = reinterpret_cast<const T *>(p.X);
     const int64_t R = p.R;
-
-    // ---- stage the contraction-side Khatri-Rao tile B(kbase + k, r0:r0+BN)
-    // in LDS, rows past the chunk zero-filled to a multiple of 16 ----
-    {
-        const T *Ua = reinterpret_cast<const T *>(p.Uk0);
-        const T *Ub = reinterpret_cast<const T *>(p.Uk1);
-        const int64_t total = nkc * 16 * BN;
-        for (int64_t idx = tid; idx < total; idx += kThreads) {
-            const int64_t kk = idx / BN;
-            const int c = (int)(idx - kk * BN);
-            const int64_t colg = r0 + c;
-            T v = T(0);
-            if (kk < Kloc && colg < R) {
-                const int64_t kg = kbase + kk;
-                if (Ub == nullptr) {
-                    v = Ua[kg * R + colg];
-                } else {
-                    const int64_t a = kg / p.IkB;
-                    const int64_t b = kg - a * p.IkB;
-                    v = Ua[a * R + colg] * Ub[b * R + colg];
-                }
-            }
-            Bs[kk * p.bpitch + c] = v;
-        }
-        __syncthreads();
-    }
 
     // Per-lane rank columns (R < 2^24, so 32 bits suffice).
     int col[NB];
@@ -317,7 +313,7 @@ __global__ __launch_bounds__(kThreads, (tile_min_waves<T, MB, NB, FORM1>())) voi
 
     // Load cursor state: descriptor of the current item and its offsets.
     struct LoadCursor {
-        __amdgpu_buffer_rsrc_t rsrc;
+        int64_t base;  // element offset of the descriptor's start in X
         unsigned vo[NV];
         int64_t it, kc, step;  // item, step in the item, step in the workgroup
         int64_t orow[3];       // element offsets of the outer factor rows (i_o * R)
@@ -328,8 +324,7 @@ __global__ __launch_bounds__(kThreads, (tile_min_waves<T, MB, NB, FORM1>())) voi
     auto enter_item = [&](LoadCursor &lc) {
         if (lc.step < s_hi) {
             const Item itm = decode_item(p, lc.it, unit_off, ROWS, FORM1);
-            const int64_t o = itm.off + kshift;
-            lc.rsrc = make_rsrc(X + o, (x_elems - o) * (int64_t)SZ);
+            lc.base = itm.off + kshift;
             row_offsets(FORM1 ? itm.row0 : out_row0, lc.vo);
 #pragma unroll
             for (int j = 0; j < 3; ++j) lc.orow[j] = j < p.nouter ? itm.oidx[j] * R : 0;
@@ -342,32 +337,24 @@ __global__ __launch_bounds__(kThreads, (tile_min_waves<T, MB, NB, FORM1>())) voi
     int colc[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) colc[nb] = colok[nb] ? col[nb] : 0;
-    // Outer factors; unused slots read the first row of the contraction factor
-    // and are replaced by 1 below, so every step issues the same loads.
+    // Outer factors; unused slots read the first row of the contraction
+    // factor (always present) and count as 1 in the product.
     const T *Uo[3];
 #pragma unroll
     for (int j = 0; j < 3; ++j)
         Uo[j] = reinterpret_cast<const T *>(j < p.nouter ? p.Uo[j] : p.Uk0);
 
-    // Issue the loads of the cursor's step: its outer multiplier (the product
-    // of the outer factor rows, W_o) into wq, then its tensor elements into a.
-    // Each step carries the multiplier of its own item, so the multiplier is
-    // double-buffered with the tensor and no load depends on a branch.
-    auto load_step = [&](T *a, T *wq, const LoadCursor &lc) {
-        {
-            T f[3][NB];
+    // Issue the loads of the cursor's step: its three outer factor values
+    // (whose product is the multiplier W_o of the step's item) into wq, then
+    // its tensor elements into a.  Each step carries the factor values of its
+    // own item, so they are buffered with the tensor and no load depends on a
+    // branch; the product is formed only when the step is used.
+    auto load_step = [&](T *a, T (*wq)[NB], const LoadCursor &lc) {
 #pragma unroll
-            for (int j = 0; j < 3; ++j)
+        for (int j = 0; j < 3; ++j)
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) f[j][nb] = Uo[j][lc.orow[j] + colc[nb]];
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                T v = colok[nb] ? T(1) : T(0);
-#pragma unroll
-                for (int j = 0; j < 3; ++j) v *= (j < p.nouter) ? f[j][nb] : T(1);
-                wq[nb] = v;
-            }
-        }
+            for (int nb = 0; nb < NB; ++nb) wq[j][nb] = Uo[j][lc.orow[j] + colc[nb]];
+        const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(X + lc.base, (x_elems - lc.base) * (int64_t)SZ);
         const int64_t krem = Kloc - lc.kc * 16;  // contraction elements left in this item
         if (!RC) {
             const unsigned soff = (unsigned)(lc.kc * 16 * SZ);
@@ -375,12 +362,12 @@ __global__ __launch_bounds__(kThreads, (tile_min_waves<T, MB, NB, FORM1>())) voi
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 if (VEC) {
-                    bload4(lc.rsrc, kin ? lc.vo[mb] : kOOB, soff, a + mb * 4);
+                    bload4(rsrc, kin ? lc.vo[mb] : kOOB, soff, a + mb * 4);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         a[mb * 4 + e] = bload1(
-                            lc.rsrc, (lc.live && 4 * q + e < krem) ? lc.vo[mb] + e * SZ : kOOB,
+                            rsrc, (lc.live && 4 * q + e < krem) ? lc.vo[mb] + e * SZ : kOOB,
                             soff, T(0));
                 }
             }
@@ -394,11 +381,11 @@ __global__ __launch_bounds__(kThreads, (tile_min_waves<T, MB, NB, FORM1>())) voi
                     T *dst = a + (s * G + g) * 4;
                     const unsigned vo = kin ? lc.vo[s * G + g] : kOOB;
                     if (VEC) {
-                        bload4(lc.rsrc, vo, soff, dst);
+                        bload4(rsrc, vo, soff, dst);
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            dst[e] = bload1(lc.rsrc,
+                            dst[e] = bload1(rsrc,
                                             (vo != kOOB && out_row0 + 64 * g + 4 * c16 + e < p.In)
                                                 ? vo + e * SZ
                                                 : kOOB,
@@ -420,7 +407,25 @@ __global__ __launch_bounds__(kThreads, (tile_min_waves<T, MB, NB, FORM1>())) voi
     };
 
     // ---- matrix-core work of one step ----
-    auto compute_step = [&](const T *a, int64_t kc, const T *wb) {
+    // Multiplier of a step from its buffered factor values.  The empty asm
+    // pins the values to this point, so the product (and the wait for its
+    // loads) is not moved up to where the loads are issued.
+    auto multiplier = [&](T (*wq)[NB], T *w) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+v"(wq[j][nb]));
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            T v = colok[nb] ? T(1) : T(0);
+#pragma unroll
+            for (int j = 0; j < 3; ++j) v *= j < p.nouter ? wq[j][nb] : T(1);
+            w[nb] = v;
+        }
+    };
+    auto compute_step = [&](const T *a, int64_t kc, T (*wq)[NB]) {
+        T wb[NB];
+        if (!FORM1) multiplier(wq, wb);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int64_t kk = RC ? (kc * 16 + 4 * s + q) : (kc * 16 + 4 * q + s);
@@ -450,8 +455,10 @@ __global__ __launch_bounds__(kThreads, (tile_min_waves<T, MB, NB, FORM1>())) voi
     };
 
     // ---- end of a work item ----
-    auto finish_item = [&](int64_t row0, const T *w) {
+    auto finish_item = [&](int64_t row0, T (*wq)[NB]) {
         if (FORM1) {
+            T w[NB];
+            multiplier(wq, w);
             // Reduce the tile rows against their factor rows and the outer
             // multiplier, one accumulator row at a time: its factor loads use
             // clamped indices (no branches) and rows past the tile's end are
@@ -497,51 +504,102 @@ __global__ __launch_bounds__(kThreads, (tile_min_waves<T, MB, NB, FORM1>())) voi
         }
     };
 
-    // ---- main loop: steps over (item, k-chunk); the loads of step t+1 are
-    // in flight while step t runs on the matrix cores ----
-    if (nsteps > 0) {
-        T abuf0[NA], abuf1[NA];
-        LoadCursor lc;
-        lc.it = it_lo + s_lo / nkc;
-        lc.kc = s_lo - (lc.it - it_lo) * nkc;
-        lc.step = s_lo;
-        enter_item(lc);
-        T wbuf0[NB], wbuf1[NB];
-        // compute cursor
-        int64_t c_it = lc.it, c_kc = lc.kc, c_step = s_lo;
-        int64_t c_row0 = FORM1 ? decode_item(p, c_it, unit_off, ROWS, FORM1).row0 : 0;
+    // ---- main loop: steps over (item, k-chunk); the loads of the next PD
+    // steps are in flight while a step runs on the matrix cores ----
+    constexpr int PD = tile_prefetch<T, MB, NB, FORM1>();
+    T abuf[PD + 1][NA];
+    T wbuf[PD + 1][3][NB];
+    LoadCursor lc;
+    lc.base = 0;  // with every offset out of range until an item is entered
+#pragma unroll
+    for (int v = 0; v < NV; ++v) lc.vo[v] = kOOB;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) lc.orow[j] = 0;
+    lc.it = it_lo + (nkc > 0 ? s_lo / nkc : 0);
+    lc.kc = s_lo - (lc.it - it_lo) * nkc;
+    lc.step = s_lo;
+    lc.live = false;
+    enter_item(lc);
+    // compute cursor
+    int64_t c_it = lc.it, c_kc = lc.kc, c_step = s_lo;
+    int64_t c_row0 = (FORM1 && nsteps > 0) ? decode_item(p, c_it, unit_off, ROWS, FORM1).row0 : 0;
 
-        // After each step: reduce the item when it ends or when the wave's
-        // range ends inside it.
-        auto after_compute = [&](const T *w) {
-            ++c_step;
-            const bool item_end = ++c_kc == nkc;
-            if (c_step <= s_hi && (item_end || c_step == s_hi)) {
-                finish_item(c_row0, w);
-                if (item_end) {
-                    c_kc = 0;
-                    ++c_it;
-                    if (FORM1 && c_step < s_hi)
-                        c_row0 = decode_item(p, c_it, unit_off, ROWS, FORM1).row0;
+    // The first PD steps' loads go out before the Khatri-Rao tile is staged,
+    // so their latency overlaps the staging.
+#pragma unroll
+    for (int u = 0; u < PD; ++u) {
+        load_step(abuf[u], wbuf[u], lc);
+        advance(lc);
+    }
+
+    // ---- stage the contraction-side Khatri-Rao tile B(kbase + k, r0:r0+BN)
+    // in LDS, rows past the chunk zero-filled to a multiple of 16.  Four
+    // elements per thread are loaded before any is stored, with clamped
+    // indices and a select instead of branches. ----
+    {
+        const T *Ua = reinterpret_cast<const T *>(p.Uk0);
+        const T *Ub = reinterpret_cast<const T *>(p.Uk1);
+        const unsigned IkB = (unsigned)p.IkB;
+        const int64_t total = nkc * 16 * BN;
+        for (int64_t base = 0; base < total; base += 4 * kThreads) {
+            T v[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t idx = base + j * kThreads + tid;
+                const int kk = (int)(idx / BN);
+                const int c = (int)(idx - (int64_t)kk * BN);
+                const bool ok = idx < total && kk < Kloc && r0 + c < R;
+                const unsigned kg = ok ? (unsigned)(kbase + kk) : 0u;
+                const int64_t colg = ok ? r0 + c : 0;
+                T a, b = T(1);
+                if (Ub == nullptr) {
+                    a = Ua[(int64_t)kg * R + colg];
+                } else {
+                    const unsigned ia = kg / IkB;
+                    a = Ua[(int64_t)ia * R + colg];
+                    b = Ub[(int64_t)(kg - ia * IkB) * R + colg];
+                }
+                v[j] = ok ? a * b : T(0);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t idx = base + j * kThreads + tid;
+                if (idx < total) {
+                    const int kk = (int)(idx / BN);
+                    Bs[kk * p.bpitch + (int)(idx - (int64_t)kk * BN)] = v[j];
                 }
             }
-        };
+        }
+        __syncthreads();
+    }
 
-        // Two steps per iteration with the buffers swapped by name, so that each
-        // buffer keeps its own registers.  An odd step count runs one extra step
-        // whose loads return zeros (past the wave's range), which adds nothing
-        // to the accumulators.
-        load_step(abuf0, wbuf0, lc);
-        advance(lc);
-        for (int64_t t = 0; t < nsteps; t += 2) {
-            load_step(abuf1, wbuf1, lc);  // step t+1
+    // After each step: reduce the item when it ends or when the wave's
+    // range ends inside it.
+    auto after_compute = [&](T (*w)[NB]) {
+        ++c_step;
+        const bool item_end = ++c_kc == nkc;
+        if (c_step <= s_hi && (item_end || c_step == s_hi)) {
+            finish_item(c_row0, w);
+            if (item_end) {
+                c_kc = 0;
+                ++c_it;
+                if (FORM1 && c_step < s_hi)
+                    c_row0 = decode_item(p, c_it, unit_off, ROWS, FORM1).row0;
+            }
+        }
+    };
+
+    // PD + 1 steps per iteration over a ring of PD + 1 register buffers
+    // indexed by compile-time constants, so each buffer keeps its own
+    // registers.  Steps past the wave's range load zeros and skip the
+    // matrix cores.
+    for (int64_t t = 0; t < nsteps; t += PD + 1) {
+#pragma unroll
+        for (int u = 0; u <= PD; ++u) {
+            load_step(abuf[(u + PD) % (PD + 1)], wbuf[(u + PD) % (PD + 1)], lc);
             advance(lc);
-            compute_step(abuf0, c_kc, wbuf0);
-            after_compute(wbuf0);
-            load_step(abuf0, wbuf0, lc);  // step t+2
-            advance(lc);
-            compute_step(abuf1, c_kc, wbuf1);
-            after_compute(wbuf1);
+            if (c_step < s_hi) compute_step(abuf[u], c_kc, wbuf[u]);
+            after_compute(wbuf[u]);
         }
     }
 
@@ -667,33 +725,35 @@ TileKernel pick_vec(bool vec)
                : mttkrp_tile_kernel<T, MB, NB, RC, false, FORM1>;
 }
 
-template <typename T, int MB, bool RC, bool FORM1, bool WIDE>
+// Rank-tile widths instantiated up to MAXNB (the planner never asks for more).
+template <typename T, int MB, bool RC, bool FORM1, int MAXNB>
 TileKernel pick_nb(int nb, bool vec)
 {
     switch (nb) {
     case 1: return pick_vec<T, MB, 1, RC, FORM1>(vec);
-    case 2: return pick_vec<T, MB, 2, RC, FORM1>(vec);
-    case 4: return pick_vec<T, MB, 4, RC, FORM1>(vec);
-    case 8: return WIDE ? pick_vec<T, MB, (WIDE ? 8 : 4), RC, FORM1>(vec) : nullptr;
+    case 2: return MAXNB >= 2 ? pick_vec<T, MB, (MAXNB >= 2 ? 2 : 1), RC, FORM1>(vec) : nullptr;
+    case 4: return MAXNB >= 4 ? pick_vec<T, MB, (MAXNB >= 4 ? 4 : 1), RC, FORM1>(vec) : nullptr;
+    case 8: return MAXNB >= 8 ? pick_vec<T, MB, (MAXNB >= 8 ? 8 : 1), RC, FORM1>(vec) : nullptr;
     default: return nullptr;
     }
 }
 
-// Instantiated tiles: layout 1 uses 64-row groups (mb = 4); layout 0 uses
-// mb = 2 or 4 in either form.
+// Instantiated tiles: layout 1 uses 64-row groups (mb = 4, nb <= 4); layout 0
+// uses mb = 2 (nb <= 8; fp64 form 1: nb <= 4) or mb = 4 (nb <= 2).
 template <typename T>
 TileKernel select_kernel(const Plan &pl)
 {
+    constexpr int kWideForm1 = sizeof(T) == 4 ? 8 : 4;
     if (pl.layout == 1) {
         if (pl.mb != 4 || pl.form != 0) return nullptr;
-        return pick_nb<T, 4, true, false, false>(pl.nb, pl.vec);
+        return pick_nb<T, 4, true, false, 4>(pl.nb, pl.vec);
     }
     if (pl.mb == 2)
-        return pl.form ? pick_nb<T, 2, false, true, true>(pl.nb, pl.vec)
-                       : pick_nb<T, 2, false, false, true>(pl.nb, pl.vec);
+        return pl.form ? pick_nb<T, 2, false, true, kWideForm1>(pl.nb, pl.vec)
+                       : pick_nb<T, 2, false, false, 8>(pl.nb, pl.vec);
     if (pl.mb == 4)
-        return pl.form ? pick_nb<T, 4, false, true, false>(pl.nb, pl.vec)
-                       : pick_nb<T, 4, false, false, false>(pl.nb, pl.vec);
+        return pl.form ? pick_nb<T, 4, false, true, 2>(pl.nb, pl.vec)
+                       : pick_nb<T, 4, false, false, 2>(pl.nb, pl.vec);
     return nullptr;
 }
 
