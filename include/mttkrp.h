@@ -141,6 +141,7 @@ typedef struct {
     size_t lds_bytes;    /* dynamic LDS of the main kernel                            */
     size_t ws_bytes;     /* workspace of this mode                                    */
     int64_t kchunks;     /* contraction chunks (each sums into its own partial)       */
+    int waves;           /* waves per workgroup of the main kernel                    */
 } mttkrp_plan_info;
 
 int mttkrp_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_bytes,

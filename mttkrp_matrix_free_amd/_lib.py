@@ -49,6 +49,7 @@ class PlanInfo(ctypes.Structure):
         ("lds_bytes", ctypes.c_size_t),
         ("ws_bytes", ctypes.c_size_t),
         ("kchunks", ctypes.c_int64),
+        ("waves", ctypes.c_int),
     ]
 
     def as_dict(self):

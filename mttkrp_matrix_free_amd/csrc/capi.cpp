@@ -392,6 +392,7 @@ int mttkrp_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem
     info->lds_bytes = pl.lds_bytes;
     info->ws_bytes = pl.ws_bytes;
     info->kchunks = pl.kp.nkch;
+    info->waves = pl.waves;
     return MTTKRP_OK;
 }
 

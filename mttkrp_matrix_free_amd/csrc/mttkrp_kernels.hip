@@ -32,8 +32,8 @@
 // and B(k l/16, col l%16), and receives D(Mfma<T>::row(l/16, e), l%16) in
 // element e.
 //
-// Workgroups: 256 threads (4 waves) sharing one B tile, two workgroups per
-// compute unit; the workgroup index is remapped so that consecutive logical
+// Workgroups: four or eight waves sharing one B tile (eight waves per compute
+// unit in either case); the workgroup index is remapped so that consecutive logical
 // workgroups run on the same XCD (the hardware deals workgroups round-robin
 // over the 8 XCDs), keeping the rank tiles of one tensor chunk in one L2.
 #include <hip/hip_runtime.h>
@@ -157,37 +157,10 @@ __device__ __forceinline__ Item decode_item(const KParams &p, int64_t it, int64_
     return r;
 }
 
-// Waves per SIMD the register budget allows: two when the accumulators, the
-// two tensor buffers and the fp64 flush of a tile leave room for the rest in
-// 256 registers, else one (512 registers).
-template <typename T, int MB, int NB, bool FORM1>
-constexpr int tile_regs(int buffers)
+template <typename T, int MB, int NB, bool RC, bool VEC, bool FORM1, int W>
+__global__ __launch_bounds__(64 * W, (tile_min_waves(sizeof(T), MB, NB, FORM1))) void mttkrp_tile_kernel(KParams p)
 {
-    const int acc = MB * NB * 4 * (int)sizeof(T) / 4;
-    const int flush = (!FORM1 && sizeof(T) == 4) ? MB * NB * 4 * 2 : 0;
-    const int buf = (4 * MB + 3 * NB) * (int)sizeof(T) / 4;  // tensor elements + factor values
-    // B operand, column index, row sum; form 1 also holds the row factors of
-    // the tile reduction and their addresses.
-    const int percol = FORM1 ? 16 : 10;
-    const int fixed = FORM1 ? 96 : 64;
-    return acc + flush + buffers * buf + percol * NB + fixed;
-}
-template <typename T, int MB, int NB, bool FORM1>
-constexpr int tile_min_waves()
-{
-    return tile_regs<T, MB, NB, FORM1>(2) <= 256 ? 2 : 1;
-}
-// Steps of tensor loads kept in flight ahead of the matrix cores: two when a
-// third register buffer fits the budget the occupancy above leaves, else one.
-template <typename T, int MB, int NB, bool FORM1>
-constexpr int tile_prefetch()
-{
-    return tile_regs<T, MB, NB, FORM1>(3) <= 512 / tile_min_waves<T, MB, NB, FORM1>() ? 2 : 1;
-}
-
-template <typename T, int MB, int NB, bool RC, bool VEC, bool FORM1>
-__global__ __launch_bounds__(kThreads, (tile_min_waves<T, MB, NB, FORM1>())) void mttkrp_tile_kernel(KParams p)
-{
+    constexpr int NT = 64 * W;  // threads of the workgroup (W waves)
     static_assert(!RC || (MB % 4 == 0), "row-contiguous layout uses 64-row groups");
     static_assert(!RC || !FORM1, "row-contiguous layout has the output as rows");
     typedef typename Mfma<T>::acc_t acc_t;
@@ -243,7 +216,7 @@ __global__ __launch_bounds__(kThreads, (tile_min_waves<T, MB, NB, FORM1>())) voi
     const int64_t it_lo = isplit * p.chunk;
     const int64_t it_hi = min(p.nitems, it_lo + p.chunk);
     const int64_t wg_steps = it_hi > it_lo ? (it_hi - it_lo) * nkc : 0;
-    const int64_t per_wave = (wg_steps + kWaves - 1) / kWaves;
+    const int64_t per_wave = (wg_steps + W - 1) / W;
     const int64_t s_lo = min(wg_steps, wave * per_wave);
     const int64_t s_hi = min(wg_steps, s_lo + per_wave);
     const int64_t nsteps = s_hi - s_lo;
@@ -506,7 +479,7 @@ __global__ __launch_bounds__(kThreads, (tile_min_waves<T, MB, NB, FORM1>())) voi
 
     // ---- main loop: steps over (item, k-chunk); the loads of the next PD
     // steps are in flight while a step runs on the matrix cores ----
-    constexpr int PD = tile_prefetch<T, MB, NB, FORM1>();
+    constexpr int PD = tile_prefetch(sizeof(T), MB, NB, FORM1);
     T abuf[PD + 1][NA];
     T wbuf[PD + 1][3][NB];
     LoadCursor lc;
@@ -533,19 +506,21 @@ __global__ __launch_bounds__(kThreads, (tile_min_waves<T, MB, NB, FORM1>())) voi
     }
 
     // ---- stage the contraction-side Khatri-Rao tile B(kbase + k, r0:r0+BN)
-    // in LDS, rows past the chunk zero-filled to a multiple of 16.  Four
-    // elements per thread are loaded before any is stored, with clamped
-    // indices and a select instead of branches. ----
+    // in LDS, rows past the chunk zero-filled to a multiple of 16.  SB
+    // elements per thread are loaded before any is stored (one memory round
+    // trip per SB * 256 elements), with clamped indices and a select instead
+    // of branches. ----
     {
+        constexpr int SB = 16;
         const T *Ua = reinterpret_cast<const T *>(p.Uk0);
         const T *Ub = reinterpret_cast<const T *>(p.Uk1);
         const unsigned IkB = (unsigned)p.IkB;
         const int64_t total = nkc * 16 * BN;
-        for (int64_t base = 0; base < total; base += 4 * kThreads) {
-            T v[4];
+        for (int64_t base = 0; base < total; base += SB * NT) {
+            T v[SB];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t idx = base + j * kThreads + tid;
+            for (int j = 0; j < SB; ++j) {
+                const int64_t idx = base + j * NT + tid;
                 const int kk = (int)(idx / BN);
                 const int c = (int)(idx - (int64_t)kk * BN);
                 const bool ok = idx < total && kk < Kloc && r0 + c < R;
@@ -562,8 +537,8 @@ __global__ __launch_bounds__(kThreads, (tile_min_waves<T, MB, NB, FORM1>())) voi
                 v[j] = ok ? a * b : T(0);
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t idx = base + j * kThreads + tid;
+            for (int j = 0; j < SB; ++j) {
+                const int64_t idx = base + j * NT + tid;
                 if (idx < total) {
                     const int kk = (int)(idx / BN);
                     Bs[kk * p.bpitch + (int)(idx - (int64_t)kk * BN)] = v[j];
@@ -622,7 +597,7 @@ __global__ __launch_bounds__(kThreads, (tile_min_waves<T, MB, NB, FORM1>())) voi
         if (tid < BN) {
             double v = red[tid];
 #pragma unroll
-            for (int w2 = 1; w2 < kWaves; ++w2) v += red[w2 * BN + tid];
+            for (int w2 = 1; w2 < W; ++w2) v += red[w2 * BN + tid];
             const int64_t c = r0 + tid;
             if (c < R) {
                 if (split_out) {
@@ -640,7 +615,7 @@ __global__ __launch_bounds__(kThreads, (tile_min_waves<T, MB, NB, FORM1>())) voi
             return FLUSH64 ? acc64[FLUSH64 ? mb : 0][FLUSH64 ? nb : 0][FLUSH64 ? e : 0]
                            : (double)acc[mb][nb][e];
         };
-        for (int w2 = kWaves - 1; w2 >= 1; --w2) {
+        for (int w2 = W - 1; w2 >= 1; --w2) {
             if (wave == w2) {
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
@@ -649,7 +624,7 @@ __global__ __launch_bounds__(kThreads, (tile_min_waves<T, MB, NB, FORM1>())) voi
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int idx = ((mb * NB + nb) * 4 + e) * 64 + lane;
-                            red[idx] = (w2 == kWaves - 1) ? val(mb, nb, e) : red[idx] + val(mb, nb, e);
+                            red[idx] = (w2 == W - 1) ? val(mb, nb, e) : red[idx] + val(mb, nb, e);
                         }
             }
             __syncthreads();
@@ -662,7 +637,7 @@ __global__ __launch_bounds__(kThreads, (tile_min_waves<T, MB, NB, FORM1>())) voi
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int idx = ((mb * NB + nb) * 4 + e) * 64 + lane;
-                        const double v = val(mb, nb, e) + (kWaves > 1 ? red[idx] : 0.0);
+                        const double v = val(mb, nb, e) + (W > 1 ? red[idx] : 0.0);
                         int64_t row;
                         if (!RC)
                             row = out_row0 + mb * 16 + Mfma<T>::row(q, e);
@@ -718,42 +693,51 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const double *__restr
 
 typedef void (*TileKernel)(KParams);
 
-template <typename T, int MB, int NB, bool RC, bool FORM1>
+template <typename T, int MB, int NB, bool RC, bool FORM1, int W>
 TileKernel pick_vec(bool vec)
 {
-    return vec ? mttkrp_tile_kernel<T, MB, NB, RC, true, FORM1>
-               : mttkrp_tile_kernel<T, MB, NB, RC, false, FORM1>;
+    return vec ? mttkrp_tile_kernel<T, MB, NB, RC, true, FORM1, W>
+               : mttkrp_tile_kernel<T, MB, NB, RC, false, FORM1, W>;
 }
 
 // Rank-tile widths instantiated up to MAXNB (the planner never asks for more).
-template <typename T, int MB, bool RC, bool FORM1, int MAXNB>
+template <typename T, int MB, bool RC, bool FORM1, int MAXNB, int W>
 TileKernel pick_nb(int nb, bool vec)
 {
     switch (nb) {
-    case 1: return pick_vec<T, MB, 1, RC, FORM1>(vec);
-    case 2: return MAXNB >= 2 ? pick_vec<T, MB, (MAXNB >= 2 ? 2 : 1), RC, FORM1>(vec) : nullptr;
-    case 4: return MAXNB >= 4 ? pick_vec<T, MB, (MAXNB >= 4 ? 4 : 1), RC, FORM1>(vec) : nullptr;
-    case 8: return MAXNB >= 8 ? pick_vec<T, MB, (MAXNB >= 8 ? 8 : 1), RC, FORM1>(vec) : nullptr;
+    case 1: return pick_vec<T, MB, 1, RC, FORM1, W>(vec);
+    case 2: return MAXNB >= 2 ? pick_vec<T, MB, (MAXNB >= 2 ? 2 : 1), RC, FORM1, W>(vec) : nullptr;
+    case 4: return MAXNB >= 4 ? pick_vec<T, MB, (MAXNB >= 4 ? 4 : 1), RC, FORM1, W>(vec) : nullptr;
+    case 8: return MAXNB >= 8 ? pick_vec<T, MB, (MAXNB >= 8 ? 8 : 1), RC, FORM1, W>(vec) : nullptr;
     default: return nullptr;
     }
 }
 
 // Instantiated tiles: layout 1 uses 64-row groups (mb = 4, nb <= 4); layout 0
-// uses mb = 2 (nb <= 8; fp64 form 1: nb <= 4) or mb = 4 (nb <= 2).
+// uses mb = 2 (nb <= 8; fp64 form 1: nb <= 4) or mb = 4 (nb <= 2).  Form 1
+// workgroups have four or eight waves, the others four.
 template <typename T>
 TileKernel select_kernel(const Plan &pl)
 {
     constexpr int kWideForm1 = sizeof(T) == 4 ? 8 : 4;
     if (pl.layout == 1) {
-        if (pl.mb != 4 || pl.form != 0) return nullptr;
-        return pick_nb<T, 4, true, false, 4>(pl.nb, pl.vec);
+        if (pl.mb != 4 || pl.form != 0 || pl.waves != 4) return nullptr;
+        return pick_nb<T, 4, true, false, 4, 4>(pl.nb, pl.vec);
     }
-    if (pl.mb == 2)
-        return pl.form ? pick_nb<T, 2, false, true, kWideForm1>(pl.nb, pl.vec)
-                       : pick_nb<T, 2, false, false, 8>(pl.nb, pl.vec);
-    if (pl.mb == 4)
-        return pl.form ? pick_nb<T, 4, false, true, 2>(pl.nb, pl.vec)
-                       : pick_nb<T, 4, false, false, 2>(pl.nb, pl.vec);
+    if (pl.form == 1) {
+        // form 1: four or eight waves per workgroup (eight when a wave's
+        // registers fit two waves per SIMD)
+        if (pl.waves == 8)
+            return pl.mb == 2 ? pick_nb<T, 2, false, true, (sizeof(T) == 4 ? 4 : 2), 8>(pl.nb, pl.vec)
+                   : pl.mb == 4 ? pick_nb<T, 4, false, true, (sizeof(T) == 4 ? 2 : 1), 8>(pl.nb, pl.vec)
+                                : nullptr;
+        if (pl.waves != 4) return nullptr;
+        return pl.mb == 2 ? pick_nb<T, 2, false, true, kWideForm1, 4>(pl.nb, pl.vec)
+                          : pl.mb == 4 ? pick_nb<T, 4, false, true, 2, 4>(pl.nb, pl.vec) : nullptr;
+    }
+    if (pl.waves != 4) return nullptr;
+    if (pl.mb == 2) return pick_nb<T, 2, false, false, 8, 4>(pl.nb, pl.vec);
+    if (pl.mb == 4) return pick_nb<T, 4, false, false, 2, 4>(pl.nb, pl.vec);
     return nullptr;
 }
 
@@ -769,7 +753,7 @@ hipError_t launch_mttkrp(const Plan &pl, hipStream_t stream)
                                            (int)pl.lds_bytes);
         if (a != hipSuccess) return a;
     }
-    hipLaunchKernelGGL(k, dim3((unsigned)pl.grid), dim3(kThreads), pl.lds_bytes, stream, pl.kp);
+    hipLaunchKernelGGL(k, dim3((unsigned)pl.grid), dim3(64 * pl.waves), pl.lds_bytes, stream, pl.kp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (pl.kp.nsplit > 1) {

@@ -198,12 +198,20 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
         p.mb = (k.In >= 64 && p.nb <= 2) ? 4 : 2;
     }
 
+    // Workgroup size: form 1 runs eight waves per workgroup (when a wave's
+    // registers allow two waves per SIMD), one workgroup per compute unit, so
+    // one staged Khatri-Rao tile serves the whole unit and an output row is
+    // usually covered without splitting it; otherwise four waves, two
+    // workgroups per compute unit.
+    p.waves = (p.form == 1 && tile_min_waves(elem_bytes, p.mb, p.nb, true) == 2) ? 8 : 4;
+    const size_t lds_budget = p.waves == 8 ? kLdsBudgetWide : kLdsBudget;
+
     // Contraction chunks: the Khatri-Rao tile of one chunk (Kc x 16nb) must
     // fit in the workgroup's LDS; longer contractions are split into chunks
     // whose results are summed by the reduction pass.
     const int bpitch = 16 * p.nb + (elem_bytes == 8 ? 4 : 8);
     const int64_t Kpad = ceil_div(k.K, 16) * 16;
-    const int64_t kc_max = (int64_t)(kLdsBudget / ((size_t)bpitch * elem_bytes)) / 16 * 16;
+    const int64_t kc_max = (int64_t)(lds_budget / ((size_t)bpitch * elem_bytes)) / 16 * 16;
     if (kc_max < 16) return MTTKRP_ERANGE;
     k.Kc = std::min<int64_t>(Kpad, kc_max);
     k.nkch = ceil_div(k.K, k.Kc);
@@ -222,15 +230,15 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
         k.nrowtiles = 1;
         k.nitems = k.nbatch;
     }
-    // Split the work items of a unit so that the grid holds two workgroups
-    // per compute unit (four when the staged Khatri-Rao tile is small, so
-    // that restaging it is cheap), while the partial sums (written and read
-    // once each) stay under an eighth of the tensor traffic.  The waves of a
+    // Split the work items of a unit so that the grid holds eight waves per
+    // compute unit (sixteen when the staged Khatri-Rao tile is small, so that
+    // restaging it is cheap), while the partial sums (written and read once
+    // each) stay under an eighth of the tensor traffic.  The waves of a
     // workgroup share its steps evenly, so a chunk may hold any number of
     // items.
     const size_t b_tile = (size_t)k.Kc * k.bpitch * elem_bytes;
     const int64_t base = k.nunits * k.nrtiles * k.nkch;
-    const int64_t target = (b_tile > 32 * 1024 ? 2 : 4) * kNumCU;
+    const int64_t target = (b_tile > 32 * 1024 ? 8 : 16) / p.waves * kNumCU;
     int64_t want = std::max<int64_t>(1, ceil_div(target, base));
     const int64_t out_bytes = k.In * rank * 8;
     const int64_t cap_traffic = std::max<int64_t>(
@@ -258,7 +266,7 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
 
     size_t red = 0;
     if (p.form == 1)
-        red = (size_t)kWaves * 16 * p.nb * 8;
+        red = (size_t)p.waves * 16 * p.nb * 8;
     else
         red = (size_t)rows_per_tile * 16 * p.nb * 8;
     p.lds_bytes = std::max((size_t)k.Kc * k.bpitch * elem_bytes, red);

@@ -27,14 +27,41 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <hip/hip_runtime.h>
+
 namespace mttkrp {
 
 constexpr int kMaxOrder = 5;
-constexpr int kWaves = 4;              // waves per workgroup
-constexpr int kThreads = 64 * kWaves;  // threads per workgroup
+
 constexpr int kNumCU = 256;            // MI355X compute units
 constexpr int kNumXCD = 8;             // accelerator complex dies (L2 domains)
-constexpr size_t kLdsBudget = 80 * 1024;  // dynamic LDS per workgroup (2 WGs / CU of 160 KB)
+constexpr size_t kLdsBudget = 80 * 1024;       // dynamic LDS of a 4-wave workgroup (2 per CU)
+constexpr size_t kLdsBudgetWide = 144 * 1024;  // dynamic LDS of an 8-wave workgroup (1 per CU)
+
+// Register estimate of a tile kernel (per lane, 32-bit registers): the
+// accumulators, the fp64 flush of form-0 fp32 tiles, `buffers` step buffers
+// (tensor elements and outer factor values), per-column state and a fixed
+// part.  Shared by the kernels (launch bounds, prefetch depth) and the planner
+// (workgroup size).
+__host__ __device__ constexpr int tile_regs(int elem, int mb, int nb, bool form1, int buffers)
+{
+    return mb * nb * 4 * elem / 4 +                          // accumulators
+           ((!form1 && elem == 4) ? mb * nb * 4 * 2 : 0) +   // fp64 flush
+           buffers * (4 * mb + 3 * nb) * elem / 4 +          // step buffers
+           (form1 ? 16 : 10) * nb +                           // B operand, column, row sum
+           (form1 ? 96 : 64);                                 // addresses, cursors, row factors
+}
+// Waves per SIMD the registers allow: two within 256 registers, else one.
+__host__ __device__ constexpr int tile_min_waves(int elem, int mb, int nb, bool form1)
+{
+    return tile_regs(elem, mb, nb, form1, 2) <= 256 ? 2 : 1;
+}
+// Steps of tensor loads kept in flight: two when a third buffer fits the
+// budget of that occupancy, else one.
+__host__ __device__ constexpr int tile_prefetch(int elem, int mb, int nb, bool form1)
+{
+    return tile_regs(elem, mb, nb, form1, 3) <= 512 / tile_min_waves(elem, mb, nb, form1) ? 2 : 1;
+}
 
 struct KParams {
     const void *X;
@@ -85,6 +112,7 @@ struct Plan {
     int form = 1;
     int layout = 0;   // 0: contraction index contiguous; 1: rows contiguous
     int mb = 4, nb = 2;
+    int waves = 4;    // waves per workgroup (4 or 8)
     bool b_in_lds = true;
     bool vec = true;
     int k_modes[2] = {-1, -1};
