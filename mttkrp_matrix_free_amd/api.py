@@ -150,6 +150,36 @@ def mttkrp_all(X: torch.Tensor, factors: Sequence[torch.Tensor],
     return outs
 
 
+def prepare_all(X: torch.Tensor, factors: Sequence[torch.Tensor], outs: List[torch.Tensor],
+                ws: Optional[torch.Tensor] = None, stream=None):
+    """Check and marshal the arguments of mttkrp_all once; return a callable
+    that enqueues the all-mode sweep with them (no per-call Python checks, for
+    timing loops).  The tensors must stay alive and unchanged in shape."""
+    _check_tensor(X)
+    R = _check_factors(X, factors)
+    sfx, eb = _DT[X.dtype]
+    for m, o in enumerate(outs):
+        if o.shape != (X.shape[m], R) or o.dtype != X.dtype or not o.is_contiguous():
+            raise ValueError(f"output {m} must be a contiguous {X.shape[m]} x {R} tensor")
+    need = all_workspace_bytes(X.shape, R, X.dtype)
+    if ws is None:
+        ws = _workspace(need, X.device)
+    fn = getattr(_lib.lib(), f"mttkrp_all_{sfx}")
+    args = (ctypes.c_void_p(X.data_ptr()), _dims(X.shape), ctypes.c_int(X.dim()), _ptrs(factors),
+            ctypes.c_int64(R), _ptrs(outs), ctypes.c_void_p(None if ws is None else ws.data_ptr()),
+            ctypes.c_size_t(0 if ws is None else ws.numel()),
+            ctypes.c_void_p(_stream_handle(stream)))
+    keep = (X, list(factors), list(outs), ws)
+
+    def run():
+        st = fn(*args)
+        if st:
+            raise MttkrpError(st, f"mttkrp_all_{sfx}")
+        return keep[2]
+
+    return run
+
+
 def cp_als(X: torch.Tensor, factors: List[torch.Tensor], iters: int, tol: float = 0.0,
            ws: Optional[torch.Tensor] = None, stream=None):
     """CP-ALS from the given factors (updated in place).
