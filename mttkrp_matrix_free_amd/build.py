@@ -2,8 +2,10 @@
 
     python -m mttkrp_matrix_free_amd.build
 
-produces ``mttkrp_matrix_free_amd/libmttkrp_amd.so``.  Every HIP source is
-compiled with packed-fp32 instructions disabled ("Build").
+compiles every source under csrc/ to an object (in parallel; the tile-kernel
+instantiations are spread over several units for this) and links
+``mttkrp_matrix_free_amd/libmttkrp_amd.so``.  Every HIP source is compiled
+with packed-fp32 instructions disabled.
 """
 from __future__ import annotations
 
@@ -12,12 +14,19 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
+OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmttkrp_amd.so")
 ARCH = "gfx950"
+
+FLAGS = ["-O3", "-std=c++17", "-fPIC",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
+         "-Wno-unused-but-set-variable"]
 
 
 def hipcc() -> str:
@@ -31,20 +40,36 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def build(verbose: bool = False, extra=None) -> str:
-    """Compile every source into one shared library; returns its path."""
+def _compile(src: str, verbose: bool):
+    obj = os.path.join(OBJ, os.path.basename(src) + ".o")
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-c"] + FLAGS + [
+        "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", obj, src]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    return obj, res
+
+
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    """Compile every source (in parallel) and link the shared library; returns its path."""
+    os.makedirs(OBJ, exist_ok=True)
+    srcs = sources()
+    jobs = jobs or max(1, min(len(srcs), len(os.sched_getaffinity(0)), 16))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        results = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    failed = [(o, r) for o, r in results if r.returncode != 0]
+    for _, r in failed:
+        sys.stderr.write(r.stdout + r.stderr)
+    if failed:
+        raise RuntimeError("hipcc failed to compile " + ", ".join(os.path.basename(o) for o, _ in failed))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-Wall", "-Wno-unused-function", "-Wno-unused-variable", "-Wno-unused-but-set-variable",
-           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           "-o", tmp] + list(extra or []) + sources()
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + [o for o, _ in results]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed to build libmttkrp_amd.so")
+        raise RuntimeError("hipcc failed to link libmttkrp_amd.so")
     os.replace(tmp, LIB)
     return LIB
 

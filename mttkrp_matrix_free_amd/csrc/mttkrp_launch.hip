@@ -1,0 +1,89 @@
+// Launch of one MTTKRP mode: the tile kernel selected for the plan, then the
+// fixed-order reduction of the split partials when the plan has more than one.
+#include <hip/hip_runtime.h>
+
+#include "plan.hpp"
+#include "tile_select.hpp"
+
+namespace mttkrp {
+
+// Fixed-order sum of the split partials: out[i] = sum_{s=0}^{S-1} partial[s][i].
+// A workgroup covers EW consecutive outputs with 256/EW thread groups; group g
+// sums the partials s = g, g + 256/EW, ... and the group sums are added in
+// the order g = 0, 1, ..., so the result does not depend on scheduling.
+template <typename T, int EW>
+__global__ __launch_bounds__(256) void split_reduce_kernel(const double *__restrict__ partial,
+                                                           int64_t nsplit, int64_t count,
+                                                           void *out, int out64)
+{
+    constexpr int NG = 256 / EW;
+    __shared__ double sh[NG][EW];
+    const int c = threadIdx.x % EW;
+    const int g = threadIdx.x / EW;
+    const int64_t i = (int64_t)blockIdx.x * EW + c;
+    double v = 0.0;
+    if (i < count) {
+        for (int64_t s = g; s < nsplit; s += NG) v += partial[s * count + i];
+    }
+    sh[g][c] = v;
+    __syncthreads();
+    if (g == 0 && i < count) {
+        double t = sh[0][c];
+        for (int j = 1; j < NG; ++j) t += sh[j][c];
+        if (out64)
+            reinterpret_cast<double *>(out)[i] = t;
+        else
+            reinterpret_cast<T *>(out)[i] = (T)t;
+    }
+}
+
+template <typename T>
+TileKernel select_kernel(const Plan &pl);
+template <>
+TileKernel select_kernel<double>(const Plan &pl)
+{
+    if (pl.layout == 1) return select_tile_f64_rows(pl);
+    return pl.form ? select_tile_f64_form1(pl) : select_tile_f64_form0(pl);
+}
+template <>
+TileKernel select_kernel<float>(const Plan &pl)
+{
+    if (pl.layout == 1) return select_tile_f32_rows(pl);
+    return pl.form ? select_tile_f32_form1(pl) : select_tile_f32_form0(pl);
+}
+
+template <typename T>
+hipError_t launch_mttkrp(const Plan &pl, hipStream_t stream)
+{
+    TileKernel k = select_kernel<T>(pl);
+    if (!k) return hipErrorInvalidConfiguration;
+    if (pl.lds_bytes > 64 * 1024) {
+        // gfx950 has 160 KB of LDS per CU; dynamic sizes above 64 KB are opted into.
+        hipError_t a = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)pl.lds_bytes);
+        if (a != hipSuccess) return a;
+    }
+    hipLaunchKernelGGL(k, dim3((unsigned)pl.grid), dim3(64 * pl.waves), pl.lds_bytes, stream, pl.kp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (pl.kp.nsplit > 1) {
+        const int64_t count = pl.kp.In * pl.kp.R;
+        if (pl.kp.nsplit >= 32) {
+            hipLaunchKernelGGL((split_reduce_kernel<T, 16>), dim3((unsigned)((count + 15) / 16)),
+                               dim3(256), 0, stream, (const double *)pl.kp.partial, pl.kp.nsplit,
+                               count, pl.kp.out, pl.kp.out64);
+        } else {
+            hipLaunchKernelGGL((split_reduce_kernel<T, 64>), dim3((unsigned)((count + 63) / 64)),
+                               dim3(256), 0, stream, (const double *)pl.kp.partial, pl.kp.nsplit,
+                               count, pl.kp.out, pl.kp.out64);
+        }
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+template hipError_t launch_mttkrp<double>(const Plan &, hipStream_t);
+template hipError_t launch_mttkrp<float>(const Plan &, hipStream_t);
+
+}  // namespace mttkrp

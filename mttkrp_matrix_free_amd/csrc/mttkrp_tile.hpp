@@ -1,4 +1,6 @@
-// Matrix-free dense MTTKRP kernels for gfx950 (CDNA4).
+// Matrix-free dense MTTKRP tile kernel for gfx950 (CDNA4) -- template, included by the
+// instantiation units tile_*.hip.
+//
 //
 // One mode of M(i_n, r) = sum X(i) prod_{m != n} U_m(i_m, r) ("A Performance
 // Portable Matrix Free Dense MTTKRP in GenTen", abstract) is computed as a
@@ -36,9 +38,12 @@
 // unit in either case); the workgroup index is remapped so that consecutive logical
 // workgroups run on the same XCD (the hardware deals workgroups round-robin
 // over the 8 XCDs), keeping the rank tiles of one tensor chunk in one L2.
+#pragma once
+
 #include <hip/hip_runtime.h>
 
 #include "plan.hpp"
+#include "tile_select.hpp"
 
 namespace mttkrp {
 
@@ -157,9 +162,14 @@ __device__ __forceinline__ Item decode_item(const KParams &p, int64_t it, int64_
     return r;
 }
 
-template <typename T, int MB, int NB, bool RC, bool VEC, bool FORM1, int W>
-__global__ __launch_bounds__(64 * W, (tile_min_waves(sizeof(T), MB, NB, FORM1))) void mttkrp_tile_kernel(KParams p)
+template <typename T, int MB, int NB, bool RC, bool VEC, bool FORM1, int W, int S>
+__global__ __launch_bounds__(64 * W, (tile_min_waves(sizeof(T), MB, NB, FORM1, S))) void
+mttkrp_tile_kernel(KParams p)
 {
+    // S: outer-factor slots carried per step (0: no outer mode; else up to S
+    // outer modes, unused slots count as 1).
+    static_assert(S == 0 || S == 1 || S == 3, "outer slots");
+    constexpr int SS = S > 0 ? S : 1;  // array extent
     constexpr int NT = 64 * W;  // threads of the workgroup (W waves)
     static_assert(!RC || (MB % 4 == 0), "row-contiguous layout uses 64-row groups");
     static_assert(!RC || !FORM1, "row-contiguous layout has the output as rows");
@@ -312,9 +322,9 @@ __global__ __launch_bounds__(64 * W, (tile_min_waves(sizeof(T), MB, NB, FORM1)))
     for (int nb = 0; nb < NB; ++nb) colc[nb] = colok[nb] ? col[nb] : 0;
     // Outer factors; unused slots read the first row of the contraction
     // factor (always present) and count as 1 in the product.
-    const T *Uo[3];
+    const T *Uo[SS];
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
+    for (int j = 0; j < SS; ++j)
         Uo[j] = reinterpret_cast<const T *>(j < p.nouter ? p.Uo[j] : p.Uk0);
 
     // Issue the loads of the cursor's step: its three outer factor values
@@ -324,7 +334,7 @@ __global__ __launch_bounds__(64 * W, (tile_min_waves(sizeof(T), MB, NB, FORM1)))
     // branch; the product is formed only when the step is used.
     auto load_step = [&](T *a, T (*wq)[NB], const LoadCursor &lc) {
 #pragma unroll
-        for (int j = 0; j < 3; ++j)
+        for (int j = 0; j < S; ++j)
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) wq[j][nb] = Uo[j][lc.orow[j] + colc[nb]];
         const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(X + lc.base, (x_elems - lc.base) * (int64_t)SZ);
@@ -385,14 +395,14 @@ __global__ __launch_bounds__(64 * W, (tile_min_waves(sizeof(T), MB, NB, FORM1)))
     // loads) is not moved up to where the loads are issued.
     auto multiplier = [&](T (*wq)[NB], T *w) {
 #pragma unroll
-        for (int j = 0; j < 3; ++j)
+        for (int j = 0; j < S; ++j)
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+v"(wq[j][nb]));
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             T v = colok[nb] ? T(1) : T(0);
 #pragma unroll
-            for (int j = 0; j < 3; ++j) v *= j < p.nouter ? wq[j][nb] : T(1);
+            for (int j = 0; j < S; ++j) v *= j < p.nouter ? wq[j][nb] : T(1);
             w[nb] = v;
         }
     };
@@ -479,9 +489,9 @@ __global__ __launch_bounds__(64 * W, (tile_min_waves(sizeof(T), MB, NB, FORM1)))
 
     // ---- main loop: steps over (item, k-chunk); the loads of the next PD
     // steps are in flight while a step runs on the matrix cores ----
-    constexpr int PD = tile_prefetch(sizeof(T), MB, NB, FORM1);
+    constexpr int PD = tile_prefetch(sizeof(T), MB, NB, FORM1, S);
     T abuf[PD + 1][NA];
-    T wbuf[PD + 1][3][NB];
+    T wbuf[PD + 1][SS][NB];
     LoadCursor lc;
     lc.base = 0;  // with every offset out of range until an item is entered
 #pragma unroll
@@ -656,123 +666,5 @@ __global__ __launch_bounds__(64 * W, (tile_min_waves(sizeof(T), MB, NB, FORM1)))
         }
     }
 }
-
-// Fixed-order sum of the split partials: out[i] = sum_{s=0}^{S-1} partial[s][i].
-// A workgroup covers EW consecutive outputs with 256/EW thread groups; group g
-// sums the partials s = g, g + 256/EW, ... and the group sums are added in
-// the order g = 0, 1, ..., so the result does not depend on scheduling.
-template <typename T, int EW>
-__global__ __launch_bounds__(256) void split_reduce_kernel(const double *__restrict__ partial,
-                                                           int64_t nsplit, int64_t count,
-                                                           void *out, int out64)
-{
-    constexpr int NG = 256 / EW;
-    __shared__ double sh[NG][EW];
-    const int c = threadIdx.x % EW;
-    const int g = threadIdx.x / EW;
-    const int64_t i = (int64_t)blockIdx.x * EW + c;
-    double v = 0.0;
-    if (i < count) {
-        for (int64_t s = g; s < nsplit; s += NG) v += partial[s * count + i];
-    }
-    sh[g][c] = v;
-    __syncthreads();
-    if (g == 0 && i < count) {
-        double t = sh[0][c];
-        for (int j = 1; j < NG; ++j) t += sh[j][c];
-        if (out64)
-            reinterpret_cast<double *>(out)[i] = t;
-        else
-            reinterpret_cast<T *>(out)[i] = (T)t;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Dispatch
-// ---------------------------------------------------------------------------
-
-typedef void (*TileKernel)(KParams);
-
-template <typename T, int MB, int NB, bool RC, bool FORM1, int W>
-TileKernel pick_vec(bool vec)
-{
-    return vec ? mttkrp_tile_kernel<T, MB, NB, RC, true, FORM1, W>
-               : mttkrp_tile_kernel<T, MB, NB, RC, false, FORM1, W>;
-}
-
-// Rank-tile widths instantiated up to MAXNB (the planner never asks for more).
-template <typename T, int MB, bool RC, bool FORM1, int MAXNB, int W>
-TileKernel pick_nb(int nb, bool vec)
-{
-    switch (nb) {
-    case 1: return pick_vec<T, MB, 1, RC, FORM1, W>(vec);
-    case 2: return MAXNB >= 2 ? pick_vec<T, MB, (MAXNB >= 2 ? 2 : 1), RC, FORM1, W>(vec) : nullptr;
-    case 4: return MAXNB >= 4 ? pick_vec<T, MB, (MAXNB >= 4 ? 4 : 1), RC, FORM1, W>(vec) : nullptr;
-    case 8: return MAXNB >= 8 ? pick_vec<T, MB, (MAXNB >= 8 ? 8 : 1), RC, FORM1, W>(vec) : nullptr;
-    default: return nullptr;
-    }
-}
-
-// Instantiated tiles: layout 1 uses 64-row groups (mb = 4, nb <= 4); layout 0
-// uses mb = 2 (nb <= 8; fp64 form 1: nb <= 4) or mb = 4 (nb <= 2).  Form 1
-// workgroups have four or eight waves, the others four.
-template <typename T>
-TileKernel select_kernel(const Plan &pl)
-{
-    constexpr int kWideForm1 = sizeof(T) == 4 ? 8 : 4;
-    if (pl.layout == 1) {
-        if (pl.mb != 4 || pl.form != 0 || pl.waves != 4) return nullptr;
-        return pick_nb<T, 4, true, false, 4, 4>(pl.nb, pl.vec);
-    }
-    if (pl.form == 1) {
-        // form 1: four or eight waves per workgroup (eight when a wave's
-        // registers fit two waves per SIMD)
-        if (pl.waves == 8)
-            return pl.mb == 2 ? pick_nb<T, 2, false, true, (sizeof(T) == 4 ? 4 : 2), 8>(pl.nb, pl.vec)
-                   : pl.mb == 4 ? pick_nb<T, 4, false, true, (sizeof(T) == 4 ? 2 : 1), 8>(pl.nb, pl.vec)
-                                : nullptr;
-        if (pl.waves != 4) return nullptr;
-        return pl.mb == 2 ? pick_nb<T, 2, false, true, kWideForm1, 4>(pl.nb, pl.vec)
-                          : pl.mb == 4 ? pick_nb<T, 4, false, true, 2, 4>(pl.nb, pl.vec) : nullptr;
-    }
-    if (pl.waves != 4) return nullptr;
-    if (pl.mb == 2) return pick_nb<T, 2, false, false, 8, 4>(pl.nb, pl.vec);
-    if (pl.mb == 4) return pick_nb<T, 4, false, false, 2, 4>(pl.nb, pl.vec);
-    return nullptr;
-}
-
-template <typename T>
-hipError_t launch_mttkrp(const Plan &pl, hipStream_t stream)
-{
-    TileKernel k = select_kernel<T>(pl);
-    if (!k) return hipErrorInvalidConfiguration;
-    if (pl.lds_bytes > 64 * 1024) {
-        // gfx950 has 160 KB of LDS per CU; dynamic sizes above 64 KB are opted into.
-        hipError_t a = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)pl.lds_bytes);
-        if (a != hipSuccess) return a;
-    }
-    hipLaunchKernelGGL(k, dim3((unsigned)pl.grid), dim3(64 * pl.waves), pl.lds_bytes, stream, pl.kp);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (pl.kp.nsplit > 1) {
-        const int64_t count = pl.kp.In * pl.kp.R;
-        if (pl.kp.nsplit >= 32) {
-            hipLaunchKernelGGL((split_reduce_kernel<T, 16>), dim3((unsigned)((count + 15) / 16)),
-                               dim3(256), 0, stream, (const double *)pl.kp.partial, pl.kp.nsplit,
-                               count, pl.kp.out, pl.kp.out64);
-        } else {
-            hipLaunchKernelGGL((split_reduce_kernel<T, 64>), dim3((unsigned)((count + 63) / 64)),
-                               dim3(256), 0, stream, (const double *)pl.kp.partial, pl.kp.nsplit,
-                               count, pl.kp.out, pl.kp.out64);
-        }
-        e = hipGetLastError();
-    }
-    return e;
-}
-
-template hipError_t launch_mttkrp<double>(const Plan &, hipStream_t);
-template hipError_t launch_mttkrp<float>(const Plan &, hipStream_t);
 
 }  // namespace mttkrp

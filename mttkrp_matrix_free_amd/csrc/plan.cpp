@@ -203,7 +203,10 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
     // one staged Khatri-Rao tile serves the whole unit and an output row is
     // usually covered without splitting it; otherwise four waves, two
     // workgroups per compute unit.
-    p.waves = (p.form == 1 && tile_min_waves(elem_bytes, p.mb, p.nb, true) == 2) ? 8 : 4;
+    p.waves = (p.form == 1 &&
+               tile_min_waves(elem_bytes, p.mb, p.nb, true, plan_slots(1, k.nouter)) == 2)
+                  ? 8
+                  : 4;
     const size_t lds_budget = p.waves == 8 ? kLdsBudgetWide : kLdsBudget;
 
     // Contraction chunks: the Khatri-Rao tile of one chunk (Kc x 16nb) must

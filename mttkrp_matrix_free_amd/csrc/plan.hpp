@@ -38,29 +38,40 @@ constexpr int kNumXCD = 8;             // accelerator complex dies (L2 domains)
 constexpr size_t kLdsBudget = 80 * 1024;       // dynamic LDS of a 4-wave workgroup (2 per CU)
 constexpr size_t kLdsBudgetWide = 144 * 1024;  // dynamic LDS of an 8-wave workgroup (1 per CU)
 
+// Outer-factor slots a tile kernel carries per step: 0 when a form-1 plan has
+// no outer mode, else 1 (form 0, at most one outer mode) or 3.
+__host__ __device__ constexpr int plan_slots(int form, int nouter)
+{
+    return (form == 1 && nouter == 0) ? 0 : ((form == 0 && nouter <= 1) ? 1 : 3);
+}
+
 // Register estimate of a tile kernel (per lane, 32-bit registers): the
 // accumulators, the fp64 flush of form-0 fp32 tiles, `buffers` step buffers
-// (tensor elements and outer factor values), per-column state and a fixed
-// part.  Shared by the kernels (launch bounds, prefetch depth) and the planner
-// (workgroup size).
-__host__ __device__ constexpr int tile_regs(int elem, int mb, int nb, bool form1, int buffers)
+// (tensor elements and `slots` outer factor values per column), per-column
+// state and a fixed part.  Shared by the kernels (launch bounds, prefetch
+// depth) and the planner (workgroup size).
+__host__ __device__ constexpr int tile_regs(int elem, int mb, int nb, bool form1, int slots,
+                                            int buffers)
 {
     return mb * nb * 4 * elem / 4 +                          // accumulators
            ((!form1 && elem == 4) ? mb * nb * 4 * 2 : 0) +   // fp64 flush
-           buffers * (4 * mb + 3 * nb) * elem / 4 +          // step buffers
+           buffers * (4 * mb + slots * nb) * elem / 4 +      // step buffers
            (form1 ? 16 : 10) * nb +                           // B operand, column, row sum
            (form1 ? 96 : 64);                                 // addresses, cursors, row factors
 }
 // Waves per SIMD the registers allow: two within 256 registers, else one.
-__host__ __device__ constexpr int tile_min_waves(int elem, int mb, int nb, bool form1)
+__host__ __device__ constexpr int tile_min_waves(int elem, int mb, int nb, bool form1, int slots)
 {
-    return tile_regs(elem, mb, nb, form1, 2) <= 256 ? 2 : 1;
+    return tile_regs(elem, mb, nb, form1, slots, 2) <= 256 ? 2 : 1;
 }
 // Steps of tensor loads kept in flight: two when a third buffer fits the
 // budget of that occupancy, else one.
-__host__ __device__ constexpr int tile_prefetch(int elem, int mb, int nb, bool form1)
+__host__ __device__ constexpr int tile_prefetch(int elem, int mb, int nb, bool form1, int slots)
 {
-    return tile_regs(elem, mb, nb, form1, 3) <= 512 / tile_min_waves(elem, mb, nb, form1) ? 2 : 1;
+    return tile_regs(elem, mb, nb, form1, slots, 3) <=
+                   512 / tile_min_waves(elem, mb, nb, form1, slots)
+               ? 2
+               : 1;
 }
 
 struct KParams {
