@@ -68,9 +68,12 @@ int mttkrp_version(void);
 /* ---- workspace queries ----
  * Write to *bytes the device workspace the matching call needs (0 is possible)
  * for elem_bytes = 8 (fp64) or 4 (fp32).  It holds fp64 partial sums of the
- * output from at most 1024 independent chunks (four workgroups per compute
- * unit): at most 8 * 1024 * I_n * R + 256 bytes for one mode, so it grows
- * with R * I_n and never with the Khatri-Rao size R * prod_{m != n} I_m. */
+ * kernel's output rows from independent chunks of the work (at most
+ * max(1024, contraction chunks) of them).  The kernel's rows are the I_n
+ * output rows, or, when the output mode is a short unit-stride mode, the
+ * block of the last two modes (I_{d-2} * I_{d-1} rows with I_{d-1} < 64).  So
+ * the workspace grows like R * I_n (or R * 64 * I_{d-2}) and never with the
+ * Khatri-Rao size R * prod_{m != n} I_m. */
 int mttkrp_workspace_bytes(const int64_t *dims, int order, int64_t rank, int mode,
                            int elem_bytes, size_t *bytes);
 int mttkrp_all_workspace_bytes(const int64_t *dims, int order, int64_t rank, int elem_bytes,

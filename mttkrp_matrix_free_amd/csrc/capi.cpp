@@ -76,6 +76,11 @@ void bind_factors(KParams &k, const void *const *factors)
     for (int j = 0; j < 3; ++j) k.Uo[j] = j < k.nouter ? factors[k.o_mode[j]] : nullptr;
 }
 
+void bind_reduced(const Plan &pl, KParams &k, const void *const *factors)
+{
+    k.Ured = pl.red_mode >= 0 ? factors[pl.red_mode] : nullptr;
+}
+
 template <typename T>
 int mttkrp_one(const T *X, const int64_t *dims, int order, const T *const *factors, int64_t rank,
                int mode, void *out, int out64, void *ws, size_t ws_bytes, hipStream_t stream)
@@ -87,6 +92,7 @@ int mttkrp_one(const T *X, const int64_t *dims, int order, const T *const *facto
     if (pl.ws_bytes > 0 && !ws) return MTTKRP_EINVAL;
     pl.kp.X = X;
     bind_factors(pl.kp, reinterpret_cast<const void *const *>(factors));
+    bind_reduced(pl, pl.kp, reinterpret_cast<const void *const *>(factors));
     pl.kp.out = out;
     pl.kp.out64 = out64;
     pl.kp.partial = reinterpret_cast<double *>(ws);

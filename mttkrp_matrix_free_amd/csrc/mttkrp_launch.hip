@@ -37,6 +37,47 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const double *__restr
     }
 }
 
+// Trailing-rows reduction: out(i, r) = sum_s sum_j U_red(j, r) partial[s][row(i, j)][r]
+// with row(i, j) = i * inner + j (output = the outer row mode) or j * inner + i
+// (output = the inner one).  A workgroup covers EW consecutive outputs with
+// 256/EW thread groups striding over s (j ascending inside); the group sums
+// are added in order, so the result is independent of scheduling.
+template <typename T, int EW>
+__global__ __launch_bounds__(256) void trailing_reduce_kernel(const double *__restrict__ partial,
+                                                              KParams p)
+{
+    constexpr int NG = 256 / EW;
+    __shared__ double sh[NG][EW];
+    const int c = threadIdx.x % EW;
+    const int g = threadIdx.x / EW;
+    const int64_t R = p.R;
+    const int64_t o = (int64_t)blockIdx.x * EW + c;
+    const int64_t count = p.In_out * R;
+    const T *U = reinterpret_cast<const T *>(p.Ured);
+    double v = 0.0;
+    if (o < count) {
+        const int64_t i = o / R;
+        const int64_t r = o - i * R;
+        for (int64_t s = g; s < p.nsplit; s += NG) {
+            const double *P = partial + s * p.In * R;
+            for (int64_t j = 0; j < p.tr_J; ++j) {
+                const int64_t row = p.tr_div ? i * p.tr_inner + j : j * p.tr_inner + i;
+                v += (double)U[j * R + r] * P[row * R + r];
+            }
+        }
+    }
+    sh[g][c] = v;
+    __syncthreads();
+    if (g == 0 && o < count) {
+        double t = sh[0][c];
+        for (int j = 1; j < NG; ++j) t += sh[j][c];
+        if (p.out64)
+            reinterpret_cast<double *>(p.out)[o] = t;
+        else
+            reinterpret_cast<T *>(p.out)[o] = (T)t;
+    }
+}
+
 template <typename T>
 TileKernel select_kernel(const Plan &pl);
 template <>
@@ -67,7 +108,17 @@ hipError_t launch_mttkrp(const Plan &pl, hipStream_t stream)
     hipLaunchKernelGGL(k, dim3((unsigned)pl.grid), dim3(64 * pl.waves), pl.lds_bytes, stream, pl.kp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (pl.kp.nsplit > 1) {
+    if (pl.kp.tr) {
+        const int64_t count = pl.kp.In_out * pl.kp.R;
+        if (pl.kp.nsplit >= 16) {
+            hipLaunchKernelGGL((trailing_reduce_kernel<T, 16>), dim3((unsigned)((count + 15) / 16)),
+                               dim3(256), 0, stream, (const double *)pl.kp.partial, pl.kp);
+        } else {
+            hipLaunchKernelGGL((trailing_reduce_kernel<T, 64>), dim3((unsigned)((count + 63) / 64)),
+                               dim3(256), 0, stream, (const double *)pl.kp.partial, pl.kp);
+        }
+        e = hipGetLastError();
+    } else if (pl.kp.nsplit > 1) {
         const int64_t count = pl.kp.In * pl.kp.R;
         if (pl.kp.nsplit >= 32) {
             hipLaunchKernelGGL((split_reduce_kernel<T, 16>), dim3((unsigned)((count + 15) / 16)),

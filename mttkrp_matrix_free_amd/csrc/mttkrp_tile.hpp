@@ -589,7 +589,7 @@ mttkrp_tile_kernel(KParams p)
     }
 
     // ---- workgroup reduction and store ----
-    const bool split_out = p.nsplit > 1;
+    const bool split_out = p.to_partial != 0;
     __syncthreads();  // every wave is done with the B tile: LDS is reused below
     if (FORM1) {
 #pragma unroll

@@ -100,7 +100,47 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
         return first;
     };
 
-    if (n == d - 1) {
+    // Trailing rows: when the output is the unit-stride mode and shorter than
+    // a 64-row tile, or the second-to-last mode while the last mode is too
+    // short to be a contraction on its own, the tile rows are the contiguous
+    // block of the last two modes (rows have unit stride), the contraction
+    // runs over the mode before them (merged with its left neighbour when it
+    // is not a multiple of 16), and the reduction pass contracts the row mode
+    // that is not the output against its factor.
+    // (Tiny tensors keep the plain plan: the extra reduction launch would
+    // cost more than the padded rows.)
+    const bool trailing = d >= 3 && N >= (INT64_C(1) << 20) &&
+                          ((n == d - 1 && dims[d - 1] < 64) || (n == d - 2 && dims[d - 1] < 32));
+    k.tr = 0;
+    k.tr_div = 0;
+    k.tr_inner = 1;
+    k.tr_J = 1;
+    k.In_out = dims[n];
+    if (trailing) {
+        p.layout = 1;
+        p.form = 0;
+        const int last = d - 3;
+        int first = last;
+        if ((dims[last] % 16 != 0 || dims[last] < 32) && last - 1 >= 0) first = last - 1;
+        k.k_mode0 = first;
+        k.K = dims[last];
+        if (first != last) {
+            k.k_mode1 = last;
+            k.IkB = dims[last];
+            k.K = dims[first] * dims[last];
+        }
+        k.k_stride = S[last];
+        for (int m = first; m <= last; ++m) in_k[m] = true;
+        k.nrows = dims[d - 2] * dims[d - 1];
+        k.row_stride = 1;
+        in_rows[d - 2] = in_rows[d - 1] = true;
+        k.tr = 1;
+        k.tr_inner = dims[d - 1];
+        k.tr_div = n == d - 2;
+        p.red_mode = n == d - 2 ? d - 1 : d - 2;
+        k.tr_J = dims[p.red_mode];
+        k.In = k.nrows;  // the kernel's rows are the block
+    } else if (n == d - 1) {
         // Output mode has unit stride: tile rows are the output rows.
         p.layout = 1;
         p.form = 0;
@@ -145,7 +185,7 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
         }
     }
 
-    // Outer modes: everything else except the output mode.
+    // Outer modes: everything else except the output mode (and the rows).
     k.nouter = 0;
     k.nbatch = 1;
     for (int m = 0; m < d; ++m) {
@@ -241,8 +281,35 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
     // items.
     const size_t b_tile = (size_t)k.Kc * k.bpitch * elem_bytes;
     const int64_t base = k.nunits * k.nrtiles * k.nkch;
-    const int64_t target = (b_tile > 32 * 1024 ? 8 : 16) / p.waves * kNumCU;
-    int64_t want = std::max<int64_t>(1, ceil_div(target, base));
+    // Workgroups resident at once: by waves (two or one per SIMD, from the
+    // register model) and by LDS.  A grid that needs a second, partial round
+    // leaves most of the chip idle in it, so the split is rounded down to
+    // whole rounds.
+    const int slots = plan_slots(p.form, k.nouter);
+    const int per_cu_waves = 4 * tile_min_waves(elem_bytes, p.mb, p.nb, p.form == 1, slots);
+    const size_t lds_est = std::max((size_t)k.Kc * k.bpitch * elem_bytes,
+                                    (size_t)p.waves * 16 * p.nb * 8);
+    const int64_t per_cu = std::max<int64_t>(
+        1, std::min<int64_t>(per_cu_waves / p.waves, (int64_t)(160 * 1024 / lds_est)));
+    const int64_t resident = per_cu * kNumCU;
+    (void)b_tile;
+    // The split that best fills whole rounds of resident workgroups (the
+    // smallest one among equals), up to two rounds' worth.
+    int64_t want = 1;
+    {
+        const int64_t wmax = std::max<int64_t>(1, std::min<int64_t>(k.nitems, ceil_div(2 * resident, base)));
+        auto util = [&](int64_t w) {  // with the split the chunk rounding yields
+            const int64_t g = base * ceil_div(k.nitems, ceil_div(k.nitems, w));
+            return (double)g / (double)(ceil_div(g, resident) * resident);
+        };
+        double best = 0.0;
+        for (int64_t w = 1; w <= wmax; ++w) best = std::max(best, util(w));
+        for (int64_t w = 1; w <= wmax; ++w)
+            if (util(w) >= best - 0.01) {
+                want = w;
+                break;
+            }
+    }
     const int64_t out_bytes = k.In * rank * 8;
     const int64_t cap_traffic = std::max<int64_t>(
         1, (N * elem_bytes / 8) / std::max<int64_t>(1, 2 * out_bytes * k.nkch));
@@ -273,12 +340,16 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
     else
         red = (size_t)rows_per_tile * 16 * p.nb * 8;
     p.lds_bytes = std::max((size_t)k.Kc * k.bpitch * elem_bytes, red);
-    p.ws_bytes = k.nsplit > 1 ? (size_t)k.nsplit * (size_t)out_bytes : 0;
+    k.to_partial = (k.nsplit > 1 || k.tr) ? 1 : 0;
+    p.ws_bytes = k.to_partial ? (size_t)k.nsplit * (size_t)out_bytes : 0;
     p.ws_bytes = (p.ws_bytes + 255) / 256 * 256;
 
     p.k_modes[0] = k.k_mode0;
     p.k_modes[1] = k.k_mode1;
-    if (p.form == 1) {
+    if (k.tr) {
+        p.row_modes[0] = d - 2;
+        p.row_modes[1] = d - 1;
+    } else if (p.form == 1) {
         p.row_modes[0] = k.r_mode0;
         p.row_modes[1] = k.r_mode1;
     } else {

@@ -116,6 +116,16 @@ struct KParams {
     int64_t grid_per_xcd;      // ceil(grid_real / kNumXCD)
     int bpitch;                // LDS row pitch of B (elements)
     int out64;                 // 1: `out` is fp64 whatever the element type
+    int to_partial;            // 1: the tile kernel writes fp64 partials (split or trailing rows)
+    // Trailing rows (layout 1 with the last two modes as tile rows): the kernel
+    // rows are the block (i_{d-2}, i_{d-1}); the reduction pass contracts the
+    // row mode that is not the output against its factor U_red.
+    int tr;                    // 1: trailing-rows plan
+    int tr_div;                // 1: output index = row / tr_inner; 0: = row % tr_inner
+    int64_t tr_inner;          // I_{d-1}
+    int64_t tr_J;              // extent of the reduced row mode
+    int64_t In_out;            // output rows I_n (In is the kernel's row count)
+    const void *Ured;          // factor of the reduced row mode
 };
 
 struct Plan {
@@ -129,6 +139,7 @@ struct Plan {
     int k_modes[2] = {-1, -1};
     int row_modes[2] = {-1, -1};
     int outer_modes[3] = {-1, -1, -1};
+    int red_mode = -1;  // trailing rows: the row mode reduced after the tile pass
     KParams kp{};
     int64_t grid = 0;        // launched grid (multiple of kNumXCD)
     size_t lds_bytes = 0;

@@ -170,7 +170,14 @@ def test_plans_within_limits_and_matrix_free_memory(L, dims, R, eb):
         ws = ctypes.c_size_t()
         assert L.mttkrp_workspace_bytes(dims_arr(dims), d, R, n, eb, ctypes.byref(ws)) == 0
         assert ws.value == info.ws_bytes
-        assert ws.value <= 8 * 1024 * dims[n] * R + 256
+        # partials: at most max(1024, contraction chunks) copies of the kernel's
+        # output rows (I_n, or the trailing block I_{d-2} I_{d-1} with
+        # I_{d-1} < 64 for a layout-1 plan) times R, in fp64
+        rows_k = info.rows if info.layout == 1 else dims[n]
+        if info.layout == 1:
+            assert rows_k in (dims[n], dims[d - 2] * dims[d - 1])
+            assert rows_k <= 64 * max(dims)
+        assert ws.value <= 8 * max(1024, info.kchunks) * rows_k * R + 256
         kr = 1
         for m in range(d):
             if m != n:
