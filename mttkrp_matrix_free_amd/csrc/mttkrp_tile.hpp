@@ -42,6 +42,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "plan.hpp"
 #include "tile_select.hpp"
 
@@ -443,38 +445,49 @@ mttkrp_tile_kernel(KParams p)
             T w[NB];
             multiplier(wq, w);
             // Reduce the tile rows against their factor rows and the outer
-            // multiplier, one accumulator row at a time: its factor loads use
-            // clamped indices (no branches) and rows past the tile's end are
-            // masked afterwards.
+            // multiplier, one accumulator row g = (mb, e) at a time.  The
+            // factor loads of row g + 1 are issued before row g is used, so
+            // the round trips overlap while only two rows of factor values
+            // are held.  Indices are clamped and a missing second row factor
+            // reads the first and counts as 1, so no load sits under a
+            // branch; rows past the tile's end are masked afterwards.
             const T *Ura = reinterpret_cast<const T *>(p.Ur0);
-            const T *Urb = reinterpret_cast<const T *>(p.Ur1);
-            const bool two = Urb != nullptr;
+            const bool two = p.Ur1 != nullptr;
+            const T *Urb = two ? reinterpret_cast<const T *>(p.Ur1) : Ura;
             const unsigned IrB = (unsigned)p.IrB;
+            constexpr int NG = MB * 4;
+            T za[2][NB], zb[2][NB];
+            auto zload = [&](int g, T *a, T *b) {
+                const int64_t rr = row0 + (g >> 2) * 16 + Mfma<T>::row(q, g & 3);
+                const unsigned rc = rr < p.nrows ? (unsigned)rr : 0u;
+                const unsigned ia = two ? rc / IrB : rc;
+                const unsigned ib = two ? rc - ia * IrB : 0u;
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int64_t rr = row0 + mb * 16 + Mfma<T>::row(q, e);
-                    const bool rok = rr < p.nrows;
-                    const unsigned rc = rok ? (unsigned)rr : 0u;
-                    const unsigned ia = two ? rc / IrB : rc;
-                    const unsigned ib = two ? rc - ia * IrB : 0u;
-                    T za[NB], zb[NB];
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) {
-                        za[nb] = Ura[(int64_t)ia * R + colc[nb]];
-                        zb[nb] = two ? Urb[(int64_t)ib * R + colc[nb]] : T(1);
-                    }
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) {
-                        const double z = (double)za[nb] * (double)zb[nb] * (double)w[nb];
-                        const double t = z * (double)acc[mb][nb][e];
-                        accrow[nb] += (rok && colok[nb]) ? t : 0.0;
-                    }
+                for (int nb = 0; nb < NB; ++nb) {
+                    a[nb] = Ura[(int64_t)ia * R + colc[nb]];
+                    b[nb] = Urb[(int64_t)ib * R + colc[nb]];
                 }
+            };
+            zload(0, za[0], zb[0]);
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                asm volatile("" ::: "memory");
+                if (g + 1 < NG) zload(g + 1, za[(g + 1) & 1], zb[(g + 1) & 1]);
+                const int mb = g >> 2, e = g & 3;
+                const int64_t rr = row0 + mb * 16 + Mfma<T>::row(q, e);
+                const bool rok = rr < p.nrows;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const double zbv = two ? (double)zb[g & 1][nb] : 1.0;
+                    const double z = (double)za[g & 1][nb] * zbv * (double)w[nb];
+                    const double t = z * (double)acc[mb][nb][e];
+                    accrow[nb] += (rok && colok[nb]) ? t : 0.0;
+                }
+            }
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = acc_t{};
-            }
         } else if (FLUSH64) {
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
@@ -507,56 +520,105 @@ mttkrp_tile_kernel(KParams p)
     int64_t c_it = lc.it, c_kc = lc.kc, c_step = s_lo;
     int64_t c_row0 = (FORM1 && nsteps > 0) ? decode_item(p, c_it, unit_off, ROWS, FORM1).row0 : 0;
 
-    // The first PD steps' loads go out before the Khatri-Rao tile is staged,
-    // so their latency overlaps the staging.
+    // ---- stage the contraction-side Khatri-Rao tile B(kbase + k, r0:r0+BN)
+    // in LDS, rows past the chunk zero-filled to a multiple of 16.  A thread
+    // owns VW consecutive columns (16 bytes) of every RPP-th row; SP rows are
+    // loaded before any is stored (one memory round trip per SP * RPP rows).
+    // Factor values are read with buffer loads, elements outside the chunk or
+    // the rank range at an offset past the descriptor (they read as zero),
+    // so no load sits under a branch; a two-factor tile takes one index
+    // division per row.  The staging runs before the first tensor loads are
+    // issued: loads return in order, so tensor loads issued first would delay
+    // every store. ----
+    {
+        constexpr int VW = 16 / (int)SZ;
+        constexpr int TPR = BN / VW;  // threads per tile row
+        static_assert(NT % TPR == 0, "tile row split over whole threads");
+        constexpr int RPP = NT / TPR;  // rows per pass
+        constexpr int SP = 8;          // rows per thread per batch
+        typedef typename std::conditional<sizeof(T) == 8, dx2, fx4>::type vec_t;
+        const int scol = (tid % TPR) * VW;
+        const int srow = tid / TPR;
+        const int nstage = (int)(nkc * 16);
+        const bool two = p.Uk1 != nullptr;
+        const unsigned IkB = (unsigned)p.IkB;
+        // Descriptors: the first factor from the chunk's first row on, the
+        // second (if any) whole; spans are kept below 2^31 bytes by the planner.
+        const int64_t ia0 = two ? kbase / (int64_t)IkB : kbase;
+        const int64_t na = two ? p.K / (int64_t)IkB : p.K;
+        const __amdgpu_buffer_rsrc_t ra =
+            make_rsrc(reinterpret_cast<const T *>(p.Uk0) + ia0 * R, (na - ia0) * R * (int64_t)SZ);
+        const __amdgpu_buffer_rsrc_t rb2 =
+            make_rsrc(two ? p.Uk1 : p.Uk0, two ? (int64_t)IkB * R * (int64_t)SZ : 0);
+        unsigned cofs[VW];
+        bool cok[VW];
+#pragma unroll
+        for (int v = 0; v < VW; ++v) {
+            cok[v] = r0 + scol + v < R;
+            cofs[v] = (unsigned)((r0 + scol + v) * SZ);
+        }
+        auto stage = [&](auto two_c, auto vec_c) {
+            constexpr bool TWO = decltype(two_c)::value;
+            constexpr bool V16 = decltype(vec_c)::value;
+            for (int rbase = 0; rbase < nstage; rbase += SP * RPP) {
+                T sv[SP][VW];
+#pragma unroll
+                for (int j = 0; j < SP; ++j) {
+                    const int kk = rbase + j * RPP + srow;
+                    const bool rok = kk < Kloc;
+                    const unsigned kg = (unsigned)(kbase + kk);
+                    const unsigned ia = TWO ? kg / IkB : kg;
+                    const unsigned ib = TWO ? kg - ia * IkB : 0u;
+                    const unsigned oa = (unsigned)((int64_t)(ia - (unsigned)ia0) * R * SZ);
+                    const unsigned ob = (unsigned)((int64_t)ib * R * SZ);
+                    if (V16) {
+                        // R is a multiple of VW: a 16-byte group is wholly in or out.
+                        const bool ok = rok && cok[0];
+                        const vec_t xa = __builtin_bit_cast(
+                            vec_t, __builtin_amdgcn_raw_buffer_load_b128(ra, ok ? oa + cofs[0] : kOOB, 0, 0));
+                        vec_t xb;
+                        if (TWO)
+                            xb = __builtin_bit_cast(vec_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                               rb2, ok ? ob + cofs[0] : kOOB, 0, 0));
+#pragma unroll
+                        for (int v = 0; v < VW; ++v) sv[j][v] = TWO ? xa[v] * xb[v] : xa[v];
+                    } else {
+#pragma unroll
+                        for (int v = 0; v < VW; ++v) {
+                            const bool ok = rok && cok[v];
+                            T x = bload1(ra, ok ? oa + cofs[v] : kOOB, 0, T(0));
+                            if (TWO) x *= bload1(rb2, ok ? ob + cofs[v] : kOOB, 0, T(0));
+                            sv[j][v] = x;
+                        }
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < SP; ++j) {
+                    const int kk = rbase + j * RPP + srow;
+                    if (kk < nstage) {
+                        vec_t t;
+#pragma unroll
+                        for (int v = 0; v < VW; ++v) t[v] = sv[j][v];
+                        *reinterpret_cast<vec_t *>(&Bs[kk * p.bpitch + scol]) = t;
+                    }
+                }
+            }
+        };
+        typedef std::integral_constant<bool, true> yes;
+        typedef std::integral_constant<bool, false> no;
+        const bool v16 = (R % VW) == 0;
+        if (two) {
+            if (v16) stage(yes(), yes()); else stage(yes(), no());
+        } else {
+            if (v16) stage(no(), yes()); else stage(no(), no());
+        }
+    }
 #pragma unroll
     for (int u = 0; u < PD; ++u) {
         load_step(abuf[u], wbuf[u], lc);
         advance(lc);
     }
-
-    // ---- stage the contraction-side Khatri-Rao tile B(kbase + k, r0:r0+BN)
-    // in LDS, rows past the chunk zero-filled to a multiple of 16.  SB
-    // elements per thread are loaded before any is stored (one memory round
-    // trip per SB * 256 elements), with clamped indices and a select instead
-    // of branches. ----
-    {
-        constexpr int SB = 16;
-        const T *Ua = reinterpret_cast<const T *>(p.Uk0);
-        const T *Ub = reinterpret_cast<const T *>(p.Uk1);
-        const unsigned IkB = (unsigned)p.IkB;
-        const int64_t total = nkc * 16 * BN;
-        for (int64_t base = 0; base < total; base += SB * NT) {
-            T v[SB];
-#pragma unroll
-            for (int j = 0; j < SB; ++j) {
-                const int64_t idx = base + j * NT + tid;
-                const int kk = (int)(idx / BN);
-                const int c = (int)(idx - (int64_t)kk * BN);
-                const bool ok = idx < total && kk < Kloc && r0 + c < R;
-                const unsigned kg = ok ? (unsigned)(kbase + kk) : 0u;
-                const int64_t colg = ok ? r0 + c : 0;
-                T a, b = T(1);
-                if (Ub == nullptr) {
-                    a = Ua[(int64_t)kg * R + colg];
-                } else {
-                    const unsigned ia = kg / IkB;
-                    a = Ua[(int64_t)ia * R + colg];
-                    b = Ub[(int64_t)(kg - ia * IkB) * R + colg];
-                }
-                v[j] = ok ? a * b : T(0);
-            }
-#pragma unroll
-            for (int j = 0; j < SB; ++j) {
-                const int64_t idx = base + j * NT + tid;
-                if (idx < total) {
-                    const int kk = (int)(idx / BN);
-                    Bs[kk * p.bpitch + (int)(idx - (int64_t)kk * BN)] = v[j];
-                }
-            }
-        }
-        __syncthreads();
-    }
+    __syncthreads();
 
     // After each step: reduce the item when it ends or when the wave's
     // range ends inside it.

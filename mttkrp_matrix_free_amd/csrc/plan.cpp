@@ -331,6 +331,12 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
         else
             span = (rows_per_tile + (k.Kc - 1) * k.k_stride) * elem_bytes;
         if (span >= (INT64_C(1) << 31) - 64) return MTTKRP_ERANGE;
+        // The contraction factor rows one chunk stages are read the same
+        // way: the first factor from the chunk's first row, the second whole.
+        const int64_t rows_a = (k.k_mode1 >= 0) ? k.Kc / k.IkB + 2 : k.Kc;
+        if ((rows_a * rank + 16) * elem_bytes >= (INT64_C(1) << 31)) return MTTKRP_ERANGE;
+        if ((k.k_mode1 >= 0) && (k.IkB * rank + 16) * elem_bytes >= (INT64_C(1) << 31))
+            return MTTKRP_ERANGE;
     }
     k.x_bytes = N * elem_bytes;
 
