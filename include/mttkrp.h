@@ -65,6 +65,14 @@ const char *mttkrp_strerror(int status);
 /* Library version, major * 10000 + minor * 100 + patch. */
 int mttkrp_version(void);
 
+/* Host-only self-check of the integer helpers the kernels rely on: the
+ * multiply-high division constants the planner computes for the index decode
+ * ("Division by Invariant Integers using Multiplication", Granlund and
+ * Montgomery, Sec. 4) are checked against plain division over a fixed set of
+ * divisors in [1, 2^31) and dividends in [0, 2^31).  Needs no GPU.  Returns 0,
+ * or 1 + the index of the first failing (divisor, dividend) pair. */
+int mttkrp_selftest(void);
+
 /* ---- workspace queries ----
  * Write to *bytes the device workspace the matching call needs (0 is possible)
  * for elem_bytes = 8 (fp64) or 4 (fp32).  It holds fp64 partial sums of the

@@ -22,7 +22,7 @@ ENOTSPD = -7
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTS = (
-    "mttkrp_strerror", "mttkrp_version",
+    "mttkrp_strerror", "mttkrp_version", "mttkrp_selftest",
     "mttkrp_workspace_bytes", "mttkrp_all_workspace_bytes", "cp_als_workspace_bytes",
     "mttkrp_f64", "mttkrp_f32", "mttkrp_all_f64", "mttkrp_all_f32",
     "cp_als_f64", "cp_als_f32", "mttkrp_plan",
@@ -85,6 +85,8 @@ def lib():
         L.mttkrp_strerror.argtypes = [I]
         L.mttkrp_strerror.restype = ctypes.c_char_p
         L.mttkrp_version.restype = I
+        L.mttkrp_selftest.restype = I
+        L.mttkrp_selftest.argtypes = []
         for f in ("mttkrp_workspace_bytes",):
             getattr(L, f).argtypes = [P, I, i64, I, I, ctypes.POINTER(sz)]
             getattr(L, f).restype = I

@@ -8,10 +8,14 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <vector>
+
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <limits>
+#include <vector>
 
 #include "../../include/mttkrp.h"
 #include "plan.hpp"
@@ -295,6 +299,40 @@ const char *mttkrp_strerror(int status)
 }
 
 int mttkrp_version(void) { return 100; }
+
+int mttkrp_selftest(void)
+{
+    // Divisors: every value up to 4096, powers of two and their neighbours,
+    // and values near 2^31; dividends: the edges around multiples of the
+    // divisor, the top of the range and a fixed linear-congruential sample.
+    std::vector<int64_t> ds;
+    for (int64_t d = 1; d <= 4096; ++d) ds.push_back(d);
+    for (int k = 12; k <= 30; ++k)
+        for (int64_t e = -1; e <= 1; ++e) ds.push_back((INT64_C(1) << k) + e);
+    for (int64_t d : {INT64_C(2147483647), INT64_C(2147483646), INT64_C(2147483629), INT64_C(1000000007),
+                      INT64_C(65537), INT64_C(46341), INT64_C(99991)})
+        ds.push_back(d);
+    uint64_t lcg = 0x9e3779b97f4a7c15ull;
+    int64_t idx = 0;
+    for (int64_t d : ds) {
+        const mttkrp::FastDiv f = mttkrp::make_fastdiv(d);
+        std::vector<uint32_t> xs = {0u, 1u, 2u, 0x7fffffffu, 0x7ffffffeu};
+        for (int64_t k : {INT64_C(1), INT64_C(2), INT64_C(3), INT64_C(1000), (INT64_C(0x7fffffff) / d)}) {
+            const int64_t base = k * d;
+            for (int64_t e = -1; e <= 1; ++e)
+                if (base + e >= 0 && base + e < (INT64_C(1) << 31)) xs.push_back((uint32_t)(base + e));
+        }
+        for (int j = 0; j < 64; ++j) {
+            lcg = lcg * 6364136223846793005ull + 1442695040888963407ull;
+            xs.push_back((uint32_t)(lcg >> 33));
+        }
+        for (uint32_t x : xs) {
+            ++idx;
+            if (mttkrp::fdiv(x, f) != (uint32_t)(x / (uint64_t)d)) return (int)std::min<int64_t>(idx, INT32_MAX);
+        }
+    }
+    return 0;
+}
 
 int mttkrp_workspace_bytes(const int64_t *dims, int order, int64_t rank, int mode, int elem_bytes,
                            size_t *bytes)

@@ -21,9 +21,20 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const double *__restr
     const int c = threadIdx.x % EW;
     const int g = threadIdx.x / EW;
     const int64_t i = (int64_t)blockIdx.x * EW + c;
+    // Eight partials are loaded before any is added (one memory round trip per
+    // eight, not per partial); out-of-range ones read as zero.
     double v = 0.0;
     if (i < count) {
-        for (int64_t s = g; s < nsplit; s += NG) v += partial[s * count + i];
+        for (int64_t s0 = g; s0 < nsplit; s0 += 8 * NG) {
+            double t[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int64_t s = s0 + (int64_t)u * NG;
+                t[u] = s < nsplit ? partial[s * count + i] : 0.0;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v += t[u];
+        }
     }
     sh[g][c] = v;
     __syncthreads();
@@ -58,11 +69,22 @@ __global__ __launch_bounds__(256) void trailing_reduce_kernel(const double *__re
     if (o < count) {
         const int64_t i = o / R;
         const int64_t r = o - i * R;
+        // Eight (factor, partial) pairs are loaded before any is used.
         for (int64_t s = g; s < p.nsplit; s += NG) {
             const double *P = partial + s * p.In * R;
-            for (int64_t j = 0; j < p.tr_J; ++j) {
-                const int64_t row = p.tr_div ? i * p.tr_inner + j : j * p.tr_inner + i;
-                v += (double)U[j * R + r] * P[row * R + r];
+            for (int64_t j0 = 0; j0 < p.tr_J; j0 += 8) {
+                double u[8], w[8];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const int64_t j = j0 + t;
+                    const bool ok = j < p.tr_J;
+                    const int64_t jj = ok ? j : 0;
+                    const int64_t row = p.tr_div ? i * p.tr_inner + jj : jj * p.tr_inner + i;
+                    u[t] = ok ? (double)U[jj * R + r] : 0.0;
+                    w[t] = ok ? P[row * R + r] : 0.0;
+                }
+#pragma unroll
+                for (int t = 0; t < 8; ++t) v += u[t] * w[t];
             }
         }
     }

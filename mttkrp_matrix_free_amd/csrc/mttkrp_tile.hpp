@@ -144,20 +144,21 @@ struct Item {
 __device__ __forceinline__ Item decode_item(const KParams &p, int64_t it, int64_t unit_off,
                                             int64_t rows_per_tile, bool form1)
 {
+    // (item indices are below 2^31: 32-bit divisions by planner constants)
     Item r;
-    int64_t b;
+    uint32_t b;
     if (form1) {
-        b = it / p.nrowtiles;
-        r.row0 = (it - b * p.nrowtiles) * rows_per_tile;
+        b = fdiv((uint32_t)it, p.fd_nrowtiles);
+        r.row0 = (int64_t)((uint32_t)it - b * p.fd_nrowtiles.d) * rows_per_tile;
     } else {
-        b = it;
+        b = (uint32_t)it;
         r.row0 = 0;
     }
     // unused outer slots have dimension 1 and stride 0
-    const int64_t q2 = b / p.o_dim[2];
-    r.oidx[2] = b - q2 * p.o_dim[2];
-    const int64_t q1 = q2 / p.o_dim[1];
-    r.oidx[1] = q2 - q1 * p.o_dim[1];
+    const uint32_t q2 = fdiv(b, p.fd_odim2);
+    r.oidx[2] = b - q2 * p.fd_odim2.d;
+    const uint32_t q1 = fdiv(q2, p.fd_odim1);
+    r.oidx[1] = q2 - q1 * p.fd_odim1.d;
     r.oidx[0] = q1;
     r.off = unit_off + r.oidx[0] * p.o_stride[0] + r.oidx[1] * p.o_stride[1] +
             r.oidx[2] * p.o_stride[2] + r.row0 * p.row_stride;
@@ -175,6 +176,7 @@ mttkrp_tile_kernel(KParams p)
     constexpr int NT = 64 * W;  // threads of the workgroup (W waves)
     static_assert(!RC || (MB % 4 == 0), "row-contiguous layout uses 64-row groups");
     static_assert(!RC || !FORM1, "row-contiguous layout has the output as rows");
+    static_assert(W == 4 || W == 8, "four or eight waves");
     typedef typename Mfma<T>::acc_t acc_t;
     constexpr int BN = 16 * NB;
     constexpr int ROWS = 16 * MB;
@@ -198,16 +200,22 @@ mttkrp_tile_kernel(KParams p)
     const int64_t bid = blockIdx.x;
     const int64_t logical = (bid % kNumXCD) * p.grid_per_xcd + bid / kNumXCD;
     if (logical >= p.grid_real) return;
-    const int64_t rtile = logical % p.nrtiles;
-    const int64_t rest = logical / p.nrtiles;
-    const int64_t split = rest % p.nsplit;  // output partial written by this workgroup
-    const int64_t unit = rest / p.nsplit;
-    const int64_t kch = split / p.nsplit_it;    // contraction chunk
-    const int64_t isplit = split - kch * p.nsplit_it;  // chunk of the work items
+    // Workgroup decode in 32 bits (the grid is below 2^31).
+    const uint32_t lg = (uint32_t)logical;
+    const uint32_t rest = fdiv(lg, p.fd_nrtiles);
+    const int64_t rtile = lg - rest * p.fd_nrtiles.d;
+    const uint32_t unit32 = fdiv(rest, p.fd_nsplit);
+    const int64_t split = rest - unit32 * p.fd_nsplit.d;  // output partial written by this workgroup
+    const int64_t unit = unit32;
+    const uint32_t kch32 = fdiv((uint32_t)split, p.fd_nsplit_it);
+    const int64_t kch = kch32;                                   // contraction chunk
+    const int64_t isplit = split - (int64_t)kch32 * p.fd_nsplit_it.d;  // chunk of the work items
     const int64_t r0 = rtile * BN;
     const int64_t kbase = kch * p.Kc;
     const int64_t Kloc = min(p.Kc, p.K - kbase);
-    const int64_t nkc = (Kloc + 15) / 16;
+    // steps per item (the last contraction chunk may be shorter)
+    const FastDiv fd_nkc = kch == p.nkch - 1 ? p.fd_nkc_last : p.fd_nkc_full;
+    const int64_t nkc = fd_nkc.d;
 
     const T *__restrict__ X = reinterpret_cast<const T *>(p.X);
     const int64_t R = p.R;
@@ -460,7 +468,7 @@ mttkrp_tile_kernel(KParams p)
             auto zload = [&](int g, T *a, T *b) {
                 const int64_t rr = row0 + (g >> 2) * 16 + Mfma<T>::row(q, g & 3);
                 const unsigned rc = rr < p.nrows ? (unsigned)rr : 0u;
-                const unsigned ia = two ? rc / IrB : rc;
+                const unsigned ia = two ? fdiv(rc, p.fd_IrB) : rc;
                 const unsigned ib = two ? rc - ia * IrB : 0u;
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
@@ -511,7 +519,7 @@ mttkrp_tile_kernel(KParams p)
     for (int v = 0; v < NV; ++v) lc.vo[v] = kOOB;
 #pragma unroll
     for (int j = 0; j < 3; ++j) lc.orow[j] = 0;
-    lc.it = it_lo + (nkc > 0 ? s_lo / nkc : 0);
+    lc.it = it_lo + fdiv((uint32_t)s_lo, fd_nkc);
     lc.kc = s_lo - (lc.it - it_lo) * nkc;
     lc.step = s_lo;
     lc.live = false;
@@ -527,9 +535,10 @@ mttkrp_tile_kernel(KParams p)
     // Factor values are read with buffer loads, elements outside the chunk or
     // the rank range at an offset past the descriptor (they read as zero),
     // so no load sits under a branch; a two-factor tile takes one index
-    // division per row.  The staging runs before the first tensor loads are
-    // issued: loads return in order, so tensor loads issued first would delay
-    // every store. ----
+    // division per row.  The tensor loads of the first PD steps are issued
+    // right after the first batch's factor loads: loads return in order, so
+    // that batch's stores wait for the factor values only, while the tensor
+    // loads stay in flight. ----
     {
         constexpr int VW = 16 / (int)SZ;
         constexpr int TPR = BN / VW;  // threads per tile row
@@ -560,14 +569,14 @@ mttkrp_tile_kernel(KParams p)
         auto stage = [&](auto two_c, auto vec_c) {
             constexpr bool TWO = decltype(two_c)::value;
             constexpr bool V16 = decltype(vec_c)::value;
-            for (int rbase = 0; rbase < nstage; rbase += SP * RPP) {
-                T sv[SP][VW];
+            T sv[SP][VW];
+            auto load_batch = [&](int rbase) {
 #pragma unroll
                 for (int j = 0; j < SP; ++j) {
                     const int kk = rbase + j * RPP + srow;
                     const bool rok = kk < Kloc;
                     const unsigned kg = (unsigned)(kbase + kk);
-                    const unsigned ia = TWO ? kg / IkB : kg;
+                    const unsigned ia = TWO ? fdiv(kg, p.fd_IkB) : kg;
                     const unsigned ib = TWO ? kg - ia * IkB : 0u;
                     const unsigned oa = (unsigned)((int64_t)(ia - (unsigned)ia0) * R * SZ);
                     const unsigned ob = (unsigned)((int64_t)ib * R * SZ);
@@ -592,6 +601,8 @@ mttkrp_tile_kernel(KParams p)
                         }
                     }
                 }
+            };
+            auto store_batch = [&](int rbase) {
 #pragma unroll
                 for (int j = 0; j < SP; ++j) {
                     const int kk = rbase + j * RPP + srow;
@@ -602,6 +613,20 @@ mttkrp_tile_kernel(KParams p)
                         *reinterpret_cast<vec_t *>(&Bs[kk * p.bpitch + scol]) = t;
                     }
                 }
+            };
+            // First batch, then the tensor loads of the first PD steps, then
+            // the first batch's stores (which wait for its loads only).
+            load_batch(0);
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int u = 0; u < PD; ++u) {
+                load_step(abuf[u], wbuf[u], lc);
+                advance(lc);
+            }
+            store_batch(0);
+            for (int rbase = SP * RPP; rbase < nstage; rbase += SP * RPP) {
+                load_batch(rbase);
+                store_batch(rbase);
             }
         };
         typedef std::integral_constant<bool, true> yes;
@@ -612,11 +637,6 @@ mttkrp_tile_kernel(KParams p)
         } else {
             if (v16) stage(no(), yes()); else stage(no(), no());
         }
-    }
-#pragma unroll
-    for (int u = 0; u < PD; ++u) {
-        load_step(abuf[u], wbuf[u], lc);
-        advance(lc);
     }
     __syncthreads();
 
@@ -687,19 +707,40 @@ mttkrp_tile_kernel(KParams p)
             return FLUSH64 ? acc64[FLUSH64 ? mb : 0][FLUSH64 ? nb : 0][FLUSH64 ? e : 0]
                            : (double)acc[mb][nb][e];
         };
-        for (int w2 = W - 1; w2 >= 1; --w2) {
-            if (wave == w2) {
+        auto add_val = [&](int mb, int nb, int e, double x) {
+            if (FLUSH64)
+                acc64[FLUSH64 ? mb : 0][FLUSH64 ? nb : 0][FLUSH64 ? e : 0] += x;
+            else
+                acc[mb][nb][e] += (T)x;
+        };
+        // Fixed-order pairwise tree over the waves: in the round with h
+        // slots, waves h..2h-1 write their sums and waves 0..h-1 add them, so
+        // W waves take log2(W) rounds and W/2 slots of LDS.
+        constexpr int SLOT = MB * NB * 4 * 64;
+#pragma unroll
+        for (int h = W / 2; h >= 1; h /= 2) {
+            if (wave >= h && wave < 2 * h) {
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int idx = ((mb * NB + nb) * 4 + e) * 64 + lane;
-                            red[idx] = (w2 == W - 1) ? val(mb, nb, e) : red[idx] + val(mb, nb, e);
-                        }
+                        for (int e = 0; e < 4; ++e)
+                            red[(wave - h) * SLOT + ((mb * NB + nb) * 4 + e) * 64 + lane] =
+                                val(mb, nb, e);
             }
             __syncthreads();
+            if (wave < h) {
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            add_val(mb, nb, e,
+                                    red[wave * SLOT + ((mb * NB + nb) * 4 + e) * 64 + lane]);
+            }
+            if (h > 1) __syncthreads();
         }
         if (wave == 0) {
 #pragma unroll
@@ -708,8 +749,7 @@ mttkrp_tile_kernel(KParams p)
                 for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const int idx = ((mb * NB + nb) * 4 + e) * 64 + lane;
-                        const double v = val(mb, nb, e) + (W > 1 ? red[idx] : 0.0);
+                        const double v = val(mb, nb, e);
                         int64_t row;
                         if (!RC)
                             row = out_row0 + mb * 16 + Mfma<T>::row(q, e);

@@ -238,13 +238,13 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
         p.mb = (k.In >= 64 && p.nb <= 2) ? 4 : 2;
     }
 
-    // Workgroup size: form 1 runs eight waves per workgroup (when a wave's
-    // registers allow two waves per SIMD), one workgroup per compute unit, so
-    // one staged Khatri-Rao tile serves the whole unit and an output row is
-    // usually covered without splitting it; otherwise four waves, two
-    // workgroups per compute unit.
-    p.waves = (p.form == 1 &&
-               tile_min_waves(elem_bytes, p.mb, p.nb, true, plan_slots(1, k.nouter)) == 2)
+    // Workgroup size: form 1 and the row-contiguous layout run eight waves per
+    // workgroup (when a wave's registers allow two waves per SIMD), one
+    // workgroup per compute unit, so one staged Khatri-Rao tile serves the
+    // whole unit and fewer splits (partial sums) are needed; otherwise four
+    // waves, two workgroups per compute unit.
+    p.waves = ((p.form == 1 || p.layout == 1) &&
+               tile_min_waves(elem_bytes, p.mb, p.nb, p.form == 1, plan_slots(p.form, k.nouter)) == 2)
                   ? 8
                   : 4;
     const size_t lds_budget = p.waves == 8 ? kLdsBudgetWide : kLdsBudget;
@@ -287,8 +287,11 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
     // whole rounds.
     const int slots = plan_slots(p.form, k.nouter);
     const int per_cu_waves = 4 * tile_min_waves(elem_bytes, p.mb, p.nb, p.form == 1, slots);
-    const size_t lds_est = std::max((size_t)k.Kc * k.bpitch * elem_bytes,
-                                    (size_t)p.waves * 16 * p.nb * 8);
+    // Cross-wave reduction space: one row of column sums per wave (form 1) or
+    // W/2 wave tiles of fp64 sums (form 0, a pairwise tree over the waves).
+    const size_t red = p.form == 1 ? (size_t)p.waves * 16 * p.nb * 8
+                                   : (size_t)(p.waves / 2) * rows_per_tile * 16 * p.nb * 8;
+    const size_t lds_est = std::max((size_t)k.Kc * k.bpitch * elem_bytes, red);
     const int64_t per_cu = std::max<int64_t>(
         1, std::min<int64_t>(per_cu_waves / p.waves, (int64_t)(160 * 1024 / lds_est)));
     const int64_t resident = per_cu * kNumCU;
@@ -340,12 +343,27 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
     }
     k.x_bytes = N * elem_bytes;
 
-    size_t red = 0;
-    if (p.form == 1)
-        red = (size_t)p.waves * 16 * p.nb * 8;
-    else
-        red = (size_t)rows_per_tile * 16 * p.nb * 8;
-    p.lds_bytes = std::max((size_t)k.Kc * k.bpitch * elem_bytes, red);
+    // Index decode in 32 bits: every dividend and divisor below 2^31.
+    {
+        const int64_t lim = INT64_C(1) << 31;
+        const int64_t nkc_full = k.Kc / 16;
+        if (k.K >= lim || k.nrows >= lim || k.nbatch >= lim || k.nitems >= lim ||
+            k.chunk * nkc_full >= lim || k.IrB >= lim || k.IkB >= lim)
+            return MTTKRP_ERANGE;
+        const int64_t klast = k.K - (k.nkch - 1) * k.Kc;
+        k.fd_nrtiles = make_fastdiv(k.nrtiles);
+        k.fd_nsplit = make_fastdiv(k.nsplit);
+        k.fd_nsplit_it = make_fastdiv(k.nsplit_it);
+        k.fd_nkc_full = make_fastdiv(nkc_full);
+        k.fd_nkc_last = make_fastdiv((klast + 15) / 16);
+        k.fd_nrowtiles = make_fastdiv(k.nrowtiles);
+        k.fd_odim1 = make_fastdiv(k.o_dim[1]);
+        k.fd_odim2 = make_fastdiv(k.o_dim[2]);
+        k.fd_IrB = make_fastdiv(k.IrB);
+        k.fd_IkB = make_fastdiv(k.IkB);
+    }
+
+    p.lds_bytes = lds_est;
     k.to_partial = (k.nsplit > 1 || k.tr) ? 1 : 0;
     p.ws_bytes = k.to_partial ? (size_t)k.nsplit * (size_t)out_bytes : 0;
     p.ws_bytes = (p.ws_bytes + 255) / 256 * 256;

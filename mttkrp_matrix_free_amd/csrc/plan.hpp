@@ -74,6 +74,31 @@ __host__ __device__ constexpr int tile_prefetch(int elem, int mb, int nb, bool f
                : 1;
 }
 
+// Division by a divisor d in [1, 2^31) fixed for a launch, for dividends
+// below 2^31: q = (mulhi(x, m) + x) >> s with s = ceil(log2 d) and
+// m = floor(2^32 (2^s - d) / d) + 1 -- the round-up method of Granlund and
+// Montgomery, "Division by Invariant Integers using Multiplication" (1994),
+// Sec. 4, with the add kept in 32 bits because x < 2^31.  The constants are
+// computed once on the host; a division costs a multiply-high, an add and a
+// shift instead of a software 64-bit division.
+struct FastDiv {
+    uint32_t d, m, s;
+};
+inline FastDiv make_fastdiv(int64_t d)
+{
+    FastDiv f;
+    f.d = (uint32_t)d;
+    f.s = 0;
+    while ((UINT64_C(1) << f.s) < (uint64_t)d) ++f.s;
+    f.m = (uint32_t)(((UINT64_C(1) << 32) * ((UINT64_C(1) << f.s) - (uint64_t)d)) / (uint64_t)d + 1);
+    return f;
+}
+__host__ __device__ inline uint32_t fdiv(uint32_t x, const FastDiv &f)
+{
+    const uint32_t t = (uint32_t)(((uint64_t)x * f.m) >> 32);
+    return (t + x) >> f.s;
+}
+
 struct KParams {
     const void *X;
     int64_t x_bytes;           // bytes of X (bounds of its buffer descriptor)
@@ -126,6 +151,10 @@ struct KParams {
     int64_t tr_J;              // extent of the reduced row mode
     int64_t In_out;            // output rows I_n (In is the kernel's row count)
     const void *Ured;          // factor of the reduced row mode
+    // divisors of the index decode (every dividend is below 2^31)
+    FastDiv fd_nrtiles, fd_nsplit, fd_nsplit_it;
+    FastDiv fd_nkc_full, fd_nkc_last;  // steps per item: full chunk, last chunk
+    FastDiv fd_nrowtiles, fd_odim1, fd_odim2, fd_IrB, fd_IkB;
 };
 
 struct Plan {

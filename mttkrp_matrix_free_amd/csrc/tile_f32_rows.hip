@@ -1,5 +1,6 @@
 // Tile-kernel instantiations: f32, layout 1 (rows contiguous, output = the
-// unit-stride mode), form 0; four waves, 64-row groups (mb = 4), nb <= 4;
+// unit-stride mode), form 0; four waves or eight (when two waves per SIMD
+// fit the registers), 64-row groups (mb = 4), nb <= 4;
 // one or three outer slots.
 #include "mttkrp_tile.hpp"
 
@@ -34,13 +35,15 @@ TileKernel pick_nb(int nb, bool vec)
 template <int S>
 TileKernel sel(const Plan &pl)
 {
-    return pl.mb == 4 ? pick_nb<float, 4, true, false, 4, 4, S>(pl.nb, pl.vec) : nullptr;
+    if (pl.mb != 4) return nullptr;
+    if (pl.waves == 8) return pick_nb<float, 4, true, false, 4, 8, S>(pl.nb, pl.vec);
+    return pl.waves == 4 ? pick_nb<float, 4, true, false, 4, 4, S>(pl.nb, pl.vec) : nullptr;
 }
 }  // namespace
 
 TileKernel select_tile_f32_rows(const Plan &pl)
 {
-    if (pl.layout != 1 || pl.form != 0 || pl.waves != 4) return nullptr;
+    if (pl.layout != 1 || pl.form != 0) return nullptr;
     const int s = tile_slots(pl);
     return s == 1 ? sel<1>(pl) : s == 3 ? sel<3>(pl) : nullptr;
 }

@@ -57,6 +57,13 @@ def test_strerror_and_version(L):
     assert L.mttkrp_version() >= 100
 
 
+def test_fast_division_constants(L):
+    """The planner's multiply-high division constants (Granlund and Montgomery,
+    "Division by Invariant Integers using Multiplication", Sec. 4) agree with
+    plain division over the library's fixed set of divisors and dividends."""
+    assert L.mttkrp_selftest() == 0
+
+
 def call_f64(L, X=FAKE, dims=(4, 5, 6), order=None, factors=None, rank=3, mode=0, out=FAKE,
              ws=None, ws_bytes=0):
     order = len(dims) if order is None else order
