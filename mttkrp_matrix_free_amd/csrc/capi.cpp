@@ -8,9 +8,6 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <vector>
-
-#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
