@@ -21,8 +21,9 @@
 // whose element lies outside the tile (ragged rows, the tail of the
 // contraction, steps past the end of the wave's work) gets an offset past the
 // buffer's range, for which the hardware returns zero without touching memory.
-// The loads therefore carry no branches, and the loop keeps exactly one step
-// of loads in flight while the matrix cores work on the previous step:
+// The loads therefore carry no branches, and the loop keeps the loads of the
+// next steps (two when the registers allow) in flight while the matrix cores
+// work on the current one:
 //   layout 0 (contraction index contiguous): a lane holds X(row, k0+4q..k0+4q+3)
 //     and feeds them to four successive MFMA k-steps; the k order inside the
 //     matrix-core reduction is permuted consistently for A and B, which leaves

@@ -4,11 +4,11 @@
 // tile rows, the outer (Hadamard) modes, the wave tile, and the split of the
 // work over workgroups.  The split rule follows a plain cache/traffic model:
 // X is streamed once per rank tile; a split adds 2 * nsplit * I_n * R * 8
-// bytes of partial sums, kept under a tenth of the tensor traffic; the grid
-// aims at four workgroups per compute unit.  (The GenTen page names a tile-size
-// heuristic and cache models for this choice; their formulas are not given,
-// so this is a reading for gfx950: 160 KB LDS and 512 registers per lane per
-// SIMD.)
+// bytes of partial sums, kept under an eighth of the tensor traffic; the grid
+// is sized to fill whole rounds of the workgroups the chip holds at once.
+// (The GenTen page names a tile-size heuristic and cache models for this
+// choice; their formulas are not given, so this is a reading for gfx950:
+// 160 KB LDS and 512 registers per lane per SIMD.)
 #include "plan.hpp"
 
 #include <algorithm>
