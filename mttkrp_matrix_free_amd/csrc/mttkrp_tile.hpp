@@ -714,58 +714,84 @@ mttkrp_tile_kernel(KParams p)
             else
                 acc[mb][nb][e] += (T)x;
         };
-        // Fixed-order pairwise tree over the waves: in the round with h
-        // slots, waves h..2h-1 write their sums and waves 0..h-1 add them, so
-        // W waves take log2(W) rounds and W/2 slots of LDS.
         constexpr int SLOT = MB * NB * 4 * 64;
-#pragma unroll
-        for (int h = W / 2; h >= 1; h /= 2) {
-            if (wave >= h && wave < 2 * h) {
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            red[(wave - h) * SLOT + ((mb * NB + nb) * 4 + e) * 64 + lane] =
-                                val(mb, nb, e);
+        // Output element (mb, nb, e) of lane ln: its row and column.
+        auto put = [&](int mb, int nb, int e, int ln, double v) {
+            const int64_t c = r0 + nb * 16 + (ln & 15);
+            int64_t row;
+            if (!RC)
+                row = out_row0 + mb * 16 + Mfma<T>::row(ln >> 4, e);
+            else
+                row = out_row0 + 64 * (mb / 4) + 4 * Mfma<T>::row(ln >> 4, e) + (mb % 4);
+            if (row < p.In && c < R) {
+                if (split_out) {
+                    p.partial[(split * p.In + row) * R + c] = v;
+                } else if (p.out64) {
+                    reinterpret_cast<double *>(p.out)[row * R + c] = v;
+                } else {
+                    reinterpret_cast<T *>(p.out)[row * R + c] = (T)v;
+                }
             }
-            __syncthreads();
-            if (wave < h) {
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            add_val(mb, nb, e,
-                                    red[wave * SLOT + ((mb * NB + nb) * 4 + e) * 64 + lane]);
-            }
-            if (h > 1) __syncthreads();
-        }
-        if (wave == 0) {
+        };
+        if (p.red_all) {
+            // Every wave writes its tile to a slot of its own; after one barrier
+            // each thread adds the W slots of its elements in wave order and
+            // stores them, so the store is spread over the whole workgroup.
+            static_assert(SLOT % NT == 0, "slot split over whole threads");
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const double v = val(mb, nb, e);
-                        int64_t row;
-                        if (!RC)
-                            row = out_row0 + mb * 16 + Mfma<T>::row(q, e);
-                        else
-                            row = out_row0 + 64 * (mb / 4) + 4 * Mfma<T>::row(q, e) + (mb % 4);
-                        if (row < p.In && colok[nb]) {
-                            if (split_out) {
-                                p.partial[(split * p.In + row) * R + col[nb]] = v;
-                            } else if (p.out64) {
-                                reinterpret_cast<double *>(p.out)[row * R + col[nb]] = v;
-                            } else {
-                                reinterpret_cast<T *>(p.out)[row * R + col[nb]] = (T)v;
-                            }
-                        }
-                    }
+                    for (int e = 0; e < 4; ++e)
+                        red[wave * SLOT + ((mb * NB + nb) * 4 + e) * 64 + lane] = val(mb, nb, e);
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < SLOT / NT; ++k) {
+                const int i = k * NT + tid;
+                double v = red[i];
+#pragma unroll
+                for (int w2 = 1; w2 < W; ++w2) v += red[w2 * SLOT + i];
+                const int g = i >> 6;
+                put(g / (4 * NB), (g >> 2) % NB, g & 3, i & 63, v);
+            }
+        } else {
+            // Fixed-order pairwise tree over the waves: in the round with h
+            // slots, waves h..2h-1 write their sums and waves 0..h-1 add them, so
+            // W waves take log2(W) rounds and W/2 slots of LDS.
+#pragma unroll
+            for (int h = W / 2; h >= 1; h /= 2) {
+                if (wave >= h && wave < 2 * h) {
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                red[(wave - h) * SLOT + ((mb * NB + nb) * 4 + e) * 64 + lane] =
+                                    val(mb, nb, e);
+                }
+                __syncthreads();
+                if (wave < h) {
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                add_val(mb, nb, e,
+                                        red[wave * SLOT + ((mb * NB + nb) * 4 + e) * 64 + lane]);
+                }
+                if (h > 1) __syncthreads();
+            }
+            if (wave == 0) {
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) put(mb, nb, e, lane, val(mb, nb, e));
+            }
         }
     }
 }

@@ -287,10 +287,14 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
     // whole rounds.
     const int slots = plan_slots(p.form, k.nouter);
     const int per_cu_waves = 4 * tile_min_waves(elem_bytes, p.mb, p.nb, p.form == 1, slots);
-    // Cross-wave reduction space: one row of column sums per wave (form 1) or
-    // W/2 wave tiles of fp64 sums (form 0, a pairwise tree over the waves).
+    // Cross-wave reduction space: one row of column sums per wave (form 1);
+    // for form 0 every wave's tile of fp64 sums when that fits the LDS budget
+    // (one round, the store spread over the workgroup), else W/2 tiles (a
+    // pairwise tree over the waves).
+    const size_t wave_tile = (size_t)rows_per_tile * 16 * p.nb * 8;
+    k.red_all = (p.form == 0 && (size_t)p.waves * wave_tile <= lds_budget) ? 1 : 0;
     const size_t red = p.form == 1 ? (size_t)p.waves * 16 * p.nb * 8
-                                   : (size_t)(p.waves / 2) * rows_per_tile * 16 * p.nb * 8;
+                                   : (size_t)(k.red_all ? p.waves : p.waves / 2) * wave_tile;
     const size_t lds_est = std::max((size_t)k.Kc * k.bpitch * elem_bytes, red);
     const int64_t per_cu = std::max<int64_t>(
         1, std::min<int64_t>(per_cu_waves / p.waves, (int64_t)(160 * 1024 / lds_est)));

@@ -142,6 +142,7 @@ struct KParams {
     int bpitch;                // LDS row pitch of B (elements)
     int out64;                 // 1: `out` is fp64 whatever the element type
     int to_partial;            // 1: the tile kernel writes fp64 partials (split or trailing rows)
+    int red_all;               // form 0: every wave's tile goes to LDS at once (else a pairwise tree)
     // Trailing rows (layout 1 with the last two modes as tile rows): the kernel
     // rows are the block (i_{d-2}, i_{d-1}); the reduction pass contracts the
     // row mode that is not the output against its factor U_red.
