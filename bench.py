@@ -146,22 +146,22 @@ def main():
         sweep()
     torch.cuda.synchronize()
 
-    # ---- timed region: exactly `steps` all-mode sweeps, back to back, each
-    # bracketed by HIP events on the library's stream ----
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    # ---- timed region: exactly `steps` all-mode sweeps, back to back, between
+    # two HIP events on the library's stream (an event between sweeps would
+    # drain the GPU's queue there) ----
+    ev_a = torch.cuda.Event(enable_timing=True)
+    ev_b = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for k in range(args.steps):
-        ev[k][0].record(stream)
+    ev_a.record(stream)
+    for _ in range(args.steps):
         sweep()
-        ev[k][1].record(stream)
+    ev_b.record(stream)
     torch.cuda.synchronize()
     t_end = time.perf_counter()
     wall = t_end - t_start
     ms_per_step = wall * 1e3 / args.steps
-    sweep_ms = [a.elapsed_time(b) for a, b in ev]
-    sweep_avg = float(np.mean(sweep_ms))
+    sweep_avg = ev_a.elapsed_time(ev_b) / args.steps
     value = d * flops_mode / (wall / args.steps) / 1e9
 
     # ---- cold cache: a 1 GiB read of another buffer before each mode, outside
@@ -189,9 +189,9 @@ def main():
             "reps": args.cold_reps,
         }
 
-    # ---- roofline of the MTTKRP launches: the sweep's d mode launches (tile
-    # kernel + split reduction each) over the sweep's event time, i.e. the
-    # algorithmic bytes (or flops) per launch over the average launch time ----
+    # ---- roofline of the MTTKRP launches: the sweeps' mode launches over the
+    # event time of the timed region, i.e. the algorithmic bytes (or flops)
+    # per launch over the average launch time ----
     ai = [flops_mode / b for b in bytes_mode]
     peak_f = PEAK_TFLOPS[dt_name] * 1e12
     ridge = peak_f / (HBM_PEAK_GBS * 1e9)

@@ -20,7 +20,7 @@
 namespace mttkrp {
 
 template <typename T>
-hipError_t launch_mttkrp(const Plan &pl, hipStream_t stream);
+hipError_t launch_mttkrp(const Plan &pl, hipStream_t stream, bool with_reduce);
 
 template <typename T>
 hipError_t launch_sumsq(const T *X, int64_t N, double *partial, int nparts, double *out,
@@ -82,11 +82,11 @@ void bind_reduced(const Plan &pl, KParams &k, const void *const *factors)
     k.Ured = pl.red_mode >= 0 ? factors[pl.red_mode] : nullptr;
 }
 
+// Plan of one mode with every pointer bound.
 template <typename T>
-int mttkrp_one(const T *X, const int64_t *dims, int order, const T *const *factors, int64_t rank,
-               int mode, void *out, int out64, void *ws, size_t ws_bytes, hipStream_t stream)
+int bound_plan(const T *X, const int64_t *dims, int order, const T *const *factors, int64_t rank,
+               int mode, void *out, int out64, void *ws, size_t ws_bytes, Plan &pl)
 {
-    Plan pl;
     int st = make_plan(dims, order, rank, mode, (int)sizeof(T), pl);
     if (st) return st;
     if (pl.ws_bytes > ws_bytes) return MTTKRP_EWORKSPACE;
@@ -97,8 +97,29 @@ int mttkrp_one(const T *X, const int64_t *dims, int order, const T *const *facto
     pl.kp.out = out;
     pl.kp.out64 = out64;
     pl.kp.partial = reinterpret_cast<double *>(ws);
-    return launch_mttkrp<T>(pl, stream) == hipSuccess ? MTTKRP_OK : MTTKRP_EHIP;
+    return MTTKRP_OK;
 }
+
+template <typename T>
+int mttkrp_one(const T *X, const int64_t *dims, int order, const T *const *factors, int64_t rank,
+               int mode, void *out, int out64, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    Plan pl;
+    const int st = bound_plan<T>(X, dims, order, factors, rank, mode, out, out64, ws, ws_bytes, pl);
+    if (st) return st;
+    return launch_mttkrp<T>(pl, stream, true) == hipSuccess ? MTTKRP_OK : MTTKRP_EHIP;
+}
+
+// A plain split plan (partials summed by split_reduce_kernel) and a plan that
+// writes no partials, whose launch can carry that sum instead.
+// (The partner reads the partials with 32-bit offsets: their span must stay
+// below 2^31 bytes.)
+bool plain_split(const Plan &pl)
+{
+    return pl.kp.nsplit > 1 && !pl.kp.tr &&
+           pl.kp.nsplit * pl.kp.In * pl.kp.R * 8 < (INT64_C(1) << 31) - 64;
+}
+bool no_partials(const Plan &pl) { return !pl.kp.to_partial; }
 
 template <typename T>
 int mttkrp_entry(const T *X, const int64_t *dims, int order, const T *const *factors,
@@ -143,11 +164,39 @@ int mttkrp_all_entry(const T *X, const int64_t *dims, int order, const T *const 
     if (st) return st;
     if (need > ws_bytes) return MTTKRP_EWORKSPACE;
     if (need > 0 && !ws) return MTTKRP_EINVAL;
+    // Every plan first (so that nothing is launched when one fails), then the
+    // launches: each mode with a plain split goes first and hands its partial
+    // sums to the tile kernel of a mode that writes none, which adds them in
+    // split_reduce_kernel's order (the results do not change, one launch per
+    // split mode is saved); a split mode without such a partner keeps its own
+    // reduction launch.  The modes are independent, so the order is free.
+    Plan pl[kMaxOrder];
     for (int m = 0; m < order; ++m) {
-        st = mttkrp_one<T>(X, dims, order, factors, rank, m, outs[m], 0, ws, ws_bytes,
-                           reinterpret_cast<hipStream_t>(stream));
+        st = bound_plan<T>(X, dims, order, factors, rank, m, outs[m], 0, ws, ws_bytes, pl[m]);
         if (st) return st;
     }
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    bool done[kMaxOrder] = {false, false, false, false, false};
+    for (int a = 0; a < order; ++a) {
+        if (!plain_split(pl[a])) continue;
+        int b = -1;
+        for (int m = 0; m < order && b < 0; ++m)
+            if (!done[m] && m != a && no_partials(pl[m])) b = m;
+        if (launch_mttkrp<T>(pl[a], s, b < 0) != hipSuccess) return MTTKRP_EHIP;
+        done[a] = true;
+        if (b >= 0) {
+            KParams &k = pl[b].kp;
+            k.pend_partial = pl[a].kp.partial;
+            k.pend_nsplit = pl[a].kp.nsplit;
+            k.pend_count = pl[a].kp.In * pl[a].kp.R;
+            k.pend_out = pl[a].kp.out;
+            k.pend_ng = pl[a].kp.nsplit >= 32 ? 16 : 4;
+            if (launch_mttkrp<T>(pl[b], s, true) != hipSuccess) return MTTKRP_EHIP;
+            done[b] = true;
+        }
+    }
+    for (int m = 0; m < order; ++m)
+        if (!done[m] && launch_mttkrp<T>(pl[m], s, true) != hipSuccess) return MTTKRP_EHIP;
     return MTTKRP_OK;
 }
 

@@ -2,6 +2,8 @@
 // fixed-order reduction of the split partials when the plan has more than one.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "plan.hpp"
 #include "tile_select.hpp"
 
@@ -100,6 +102,30 @@ __global__ __launch_bounds__(256) void trailing_reduce_kernel(const double *__re
     }
 }
 
+// gfx950 has 160 KB of LDS per compute unit; a kernel opts into dynamic sizes
+// above 64 KB once per device (the limit is raised to the whole 160 KB, and
+// each launch still asks only for what its plan needs).  Launches are often
+// issued back to back from the host, so the opt-in is not repeated.
+hipError_t allow_large_lds(const void *k)
+{
+    constexpr int kMaxDev = 64;
+    constexpr int kMaxKernels = 256;
+    static std::mutex mu;
+    static const void *done[kMaxDev][kMaxKernels];
+    static int ndone[kMaxDev];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    const bool cache = dev >= 0 && dev < kMaxDev;
+    if (cache)
+        for (int j = 0; j < ndone[dev]; ++j)
+            if (done[dev][j] == k) return hipSuccess;
+    e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e == hipSuccess && cache && ndone[dev] < kMaxKernels) done[dev][ndone[dev]++] = k;
+    return e;
+}
+
 template <typename T>
 TileKernel select_kernel(const Plan &pl);
 template <>
@@ -115,16 +141,15 @@ TileKernel select_kernel<float>(const Plan &pl)
     return pl.form ? select_tile_f32_form1(pl) : select_tile_f32_form0(pl);
 }
 
+// with_reduce = false leaves a split plan's partials for a later launch to
+// sum (the all-mode sweep hands them to the next mode's tile kernel).
 template <typename T>
-hipError_t launch_mttkrp(const Plan &pl, hipStream_t stream)
+hipError_t launch_mttkrp(const Plan &pl, hipStream_t stream, bool with_reduce)
 {
     TileKernel k = select_kernel<T>(pl);
     if (!k) return hipErrorInvalidConfiguration;
     if (pl.lds_bytes > 64 * 1024) {
-        // gfx950 has 160 KB of LDS per CU; dynamic sizes above 64 KB are opted into.
-        hipError_t a = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)pl.lds_bytes);
+        hipError_t a = allow_large_lds(reinterpret_cast<const void *>(k));
         if (a != hipSuccess) return a;
     }
     hipLaunchKernelGGL(k, dim3((unsigned)pl.grid), dim3(64 * pl.waves), pl.lds_bytes, stream, pl.kp);
@@ -140,7 +165,7 @@ hipError_t launch_mttkrp(const Plan &pl, hipStream_t stream)
                                dim3(256), 0, stream, (const double *)pl.kp.partial, pl.kp);
         }
         e = hipGetLastError();
-    } else if (pl.kp.nsplit > 1) {
+    } else if (pl.kp.nsplit > 1 && with_reduce) {
         const int64_t count = pl.kp.In * pl.kp.R;
         if (pl.kp.nsplit >= 32) {
             hipLaunchKernelGGL((split_reduce_kernel<T, 16>), dim3((unsigned)((count + 15) / 16)),
@@ -156,7 +181,7 @@ hipError_t launch_mttkrp(const Plan &pl, hipStream_t stream)
     return e;
 }
 
-template hipError_t launch_mttkrp<double>(const Plan &, hipStream_t);
-template hipError_t launch_mttkrp<float>(const Plan &, hipStream_t);
+template hipError_t launch_mttkrp<double>(const Plan &, hipStream_t, bool);
+template hipError_t launch_mttkrp<float>(const Plan &, hipStream_t, bool);
 
 }  // namespace mttkrp

@@ -671,6 +671,59 @@ mttkrp_tile_kernel(KParams p)
         }
     }
 
+    // ---- a split reduction of another mode (all-mode sweep) ----
+    // Done here, before the workgroup barrier, so that waves which finish
+    // their steps early do it while the others still run.  Thread gid takes
+    // group g = gid mod NG of output gid / NG and sums partials g, g + NG, ...
+    // in blocks of eight (as split_reduce_kernel does); the NG group sums of
+    // an output sit in consecutive lanes and are added in group order.
+    // The partials are read through a buffer descriptor (their span is below
+    // 2^31 bytes): a slot past the last split reads as zero, so the eight
+    // loads of a block go out together with no branch.
+    if (p.pend_partial != nullptr) {
+        const int NGp = p.pend_ng;  // 4 or 16
+        const int lg = NGp == 16 ? 4 : 2;
+        const int64_t total = p.pend_count * NGp;
+        const int64_t stride = p.grid_real * (int64_t)NT;
+        const int64_t npass = (total + stride - 1) / stride;
+        const __amdgpu_buffer_rsrc_t rp =
+            make_rsrc(p.pend_partial, p.pend_nsplit * p.pend_count * (int64_t)sizeof(double));
+        for (int64_t k = 0; k < npass; ++k) {
+            const int64_t gid = k * stride + logical * NT + tid;
+            const bool ok = gid < total;
+            const int64_t i = ok ? (gid >> lg) : 0;
+            const int g = (int)(gid & (NGp - 1));
+            double v = 0.0;
+            for (int64_t s0 = g; s0 < p.pend_nsplit; s0 += 8 * NGp) {
+                double t[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int64_t sp = s0 + (int64_t)u * NGp;
+                    const unsigned off =
+                        (ok && sp < p.pend_nsplit) ? (unsigned)((sp * p.pend_count + i) * 8) : kOOB;
+                    t[u] = bload1(rp, off, 0u, 0.0);
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v += t[u];
+            }
+            // every shuffle is issued before the sums are added (in group order)
+            double tot = v;
+            auto combine = [&](auto ng_c) {
+                constexpr int NG = decltype(ng_c)::value;
+                double o[NG];
+#pragma unroll
+                for (int j = 1; j < NG; ++j) o[j] = __shfl(v, (lane & ~(NG - 1)) + j);
+#pragma unroll
+                for (int j = 1; j < NG; ++j) tot += o[j];
+            };
+            if (NGp == 16)
+                combine(std::integral_constant<int, 16>());
+            else
+                combine(std::integral_constant<int, 4>());
+            if (ok && g == 0) reinterpret_cast<T *>(p.pend_out)[i] = (T)tot;
+        }
+    }
+
     // ---- workgroup reduction and store ----
     const bool split_out = p.to_partial != 0;
     __syncthreads();  // every wave is done with the B tile: LDS is reused below

@@ -152,6 +152,14 @@ struct KParams {
     int64_t tr_J;              // extent of the reduced row mode
     int64_t In_out;            // output rows I_n (In is the kernel's row count)
     const void *Ured;          // factor of the reduced row mode
+    // A split reduction of another mode carried out by this launch (all-mode
+    // sweep): pend_out[i] = sum_s pend_partial[s][i] for i < pend_count, in
+    // the fixed order of split_reduce_kernel with pend_ng thread groups.
+    // pend_partial = null: none.
+    const double *pend_partial;
+    int64_t pend_nsplit, pend_count;
+    void *pend_out;
+    int pend_ng;
     // divisors of the index decode (every dividend is below 2^31)
     FastDiv fd_nrtiles, fd_nsplit, fd_nsplit_it;
     FastDiv fd_nkc_full, fd_nkc_last;  // steps per item: full chunk, last chunk

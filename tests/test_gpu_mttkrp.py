@@ -161,6 +161,32 @@ def test_all_modes_entry_and_determinism():
         assert rel_fro(outs[n].cpu().numpy(), oracle.mttkrp(p.X, p.factors, n, nthreads=NT)) <= 1e-12
 
 
+@pytest.mark.parametrize("dims,rank,dtype", [
+    ((256, 256, 256), 32, np.float64),   # 64 splits: 16 thread groups per output
+    ((128, 96, 256), 40, np.float64),    # 19 splits: 4 groups; two rank tiles
+    ((200, 256, 96), 40, np.float32),    # fp32, ragged rank
+])
+def test_all_modes_hand_split_sums_to_another_launch(dims, rank, dtype):
+    """In the all-mode call a mode whose plan splits hands its partial sums to
+    the tile kernel of a mode that writes none; the result must equal the
+    per-mode call (its own reduction kernel) bit for bit, and the oracle."""
+    plans = [api.plan(dims, rank, n, torch.float64 if dtype == np.float64 else torch.float32)
+             for n in range(len(dims))]
+    assert any(pl["splits"] > 1 for pl in plans) and any(pl["ws_bytes"] == 0 for pl in plans)
+    p = inputs.random_problem(dims, rank, seed=31, dtype=dtype)
+    say(f"  all-mode {dims} R={rank} {np.dtype(dtype).name}: splits {[pl['splits'] for pl in plans]}")
+    X = dev(p.X)
+    U = [dev(u) for u in p.factors]
+    outs = api.mttkrp_all(X, U)
+    for n in range(len(dims)):
+        single = api.mttkrp(X, U, n)
+        assert torch.equal(outs[n], single), n
+    n = int(np.argmax([pl["splits"] for pl in plans]))
+    rr = np.linspace(0, dims[n] - 1, 24).astype(np.int64)
+    Mo = oracle.mttkrp(p.X, p.factors, n, rows=rr, nthreads=NT)
+    assert rel_fro(outs[n].cpu().numpy()[rr], Mo) <= TOL[np.dtype(dtype)]
+
+
 def test_target_factor_not_read():
     p = inputs.random_problem((20, 30, 40), 9, seed=6)
     X = dev(p.X)
