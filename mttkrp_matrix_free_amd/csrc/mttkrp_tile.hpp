@@ -134,6 +134,15 @@ __device__ __forceinline__ float bload1(__amdgpu_buffer_rsrc_t r, unsigned voff,
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
 
+// Element offset of tile row r: r * stride, or, for two row modes that are
+// not adjacent, ia * stride_a + ib * stride_b with (ia, ib) = divmod(r, I_b).
+__device__ __forceinline__ int64_t row_offset(const KParams &p, int64_t r)
+{
+    if (!p.row_split) return r * p.row_stride;
+    const uint32_t ia = fdiv((uint32_t)r, p.fd_IrB);
+    return (int64_t)ia * p.row_stride_a + (int64_t)((uint32_t)r - ia * p.fd_IrB.d) * p.row_stride;
+}
+
 // Decoded work item: tensor offset of the tile origin, first tile row,
 // outer-mode indices.
 struct Item {
@@ -162,7 +171,7 @@ __device__ __forceinline__ Item decode_item(const KParams &p, int64_t it, int64_
     r.oidx[1] = q2 - q1 * p.fd_odim1.d;
     r.oidx[0] = q1;
     r.off = unit_off + r.oidx[0] * p.o_stride[0] + r.oidx[1] * p.o_stride[1] +
-            r.oidx[2] * p.o_stride[2] + r.row0 * p.row_stride;
+            r.oidx[2] * p.o_stride[2] + row_offset(p, r.row0);
     return r;
 }
 
@@ -291,11 +300,19 @@ mttkrp_tile_kernel(KParams p)
                     (unsigned)(((int64_t)(64 * g + 4 * c16) + (int64_t)(4 * s + q) * p.k_stride) * SZ);
     }
     // Row validity (form 0: fixed for the workgroup; form 1: per item).
+    // With two non-adjacent row modes the offsets depend on the item's first
+    // row and are recomputed per item.
     auto row_offsets = [&](int64_t row0, unsigned *vo) {
         if (!RC) {
+            const int64_t base0 = FORM1 && p.row_split ? row_offset(p, row0) : 0;
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-                vo[mb] = (row0 + mb * 16 + c16 < nrows_lim) ? vbase[mb] : kOOB;
+            for (int mb = 0; mb < MB; ++mb) {
+                const int64_t rr = row0 + mb * 16 + c16;
+                unsigned v = vbase[mb];
+                if (FORM1 && p.row_split)
+                    v = (unsigned)((row_offset(p, rr < nrows_lim ? rr : row0) - base0 + 4 * q) * SZ);
+                vo[mb] = rr < nrows_lim ? v : kOOB;
+            }
         } else {
 #pragma unroll
             for (int s = 0; s < 4; ++s)

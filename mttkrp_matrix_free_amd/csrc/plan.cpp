@@ -151,12 +151,14 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
     } else {
         p.layout = 0;
         const int kq = choose_k(d - 1);
+        // Tile rows: the free mode nearest the contraction group on its left
+        // (skipping the output mode), merged with the next free mode to its
+        // left when it is shorter than 64 rows.  The two need not be adjacent
+        // (the output mode may sit between them): row r = (ia, ib) is then
+        // addressed as ia * stride_a + ib * stride_b.
         int rlast = -1;
-        if (kq - 1 != n) {
-            rlast = kq - 1;
-        } else if (n >= 1) {
-            rlast = n - 1;
-        }
+        for (int m = kq - 1; m >= 0 && rlast < 0; --m)
+            if (m != n) rlast = m;
         // At high rank the per-tile row reduction of form 1 (one factor load
         // and one fma per accumulator element) costs more than scaling the
         // contraction tile by the outer multiplier, so the output rows become
@@ -165,16 +167,21 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
         if (rlast >= 0) {
             p.form = 1;
             int rfirst = rlast;
-            if (dims[rlast] < 64 && rlast - 1 >= 0 && rlast - 1 != n) rfirst = rlast - 1;
+            if (dims[rlast] < 64)
+                for (int m = rlast - 1; m >= 0 && rfirst == rlast; --m)
+                    if (m != n) rfirst = m;
             k.r_mode0 = rfirst;
             k.nrows = dims[rlast];
+            k.IrB = dims[rlast];
+            k.row_stride = S[rlast];
+            k.row_stride_a = S[rfirst];
+            k.row_split = 0;
             if (rfirst != rlast) {
                 k.r_mode1 = rlast;
-                k.IrB = dims[rlast];
                 k.nrows = dims[rfirst] * dims[rlast];
+                k.row_split = rfirst != rlast - 1 ? 1 : 0;
             }
-            k.row_stride = S[rlast];
-            for (int m = rfirst; m <= rlast; ++m) in_rows[m] = true;
+            in_rows[rfirst] = in_rows[rlast] = true;
         } else {
             // The output rows are the tile rows; every other mode is contracted
             // or outer.
@@ -206,7 +213,8 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
     // Vectorised loads need every 4-element group inside the tensor and
     // aligned with the row/fibre starts.
     if (p.layout == 0)
-        p.vec = (k.K % 4 == 0) && (k.row_stride % 4 == 0);
+        p.vec = (k.K % 4 == 0) && (k.row_stride % 4 == 0) &&
+                (!k.row_split || k.row_stride_a % 4 == 0);
     else
         p.vec = (k.nrows % 4 == 0) && (k.k_stride % 4 == 0);
     if (p.layout == 0) {
@@ -333,7 +341,10 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
     // span of one tile (its rows and its whole contraction) must fit.
     {
         int64_t span;
-        if (p.layout == 0)
+        if (p.layout == 0 && k.row_split)
+            span = ((ceil_div(rows_per_tile, k.IrB) + 1) * k.row_stride_a +
+                    k.IrB * k.row_stride + k.Kc) * elem_bytes;
+        else if (p.layout == 0)
             span = ((rows_per_tile - 1) * k.row_stride + k.Kc) * elem_bytes;
         else
             span = (rows_per_tile + (k.Kc - 1) * k.k_stride) * elem_bytes;

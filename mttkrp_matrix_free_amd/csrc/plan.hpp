@@ -119,7 +119,9 @@ struct KParams {
     int64_t IkB;
     // tile rows
     int64_t nrows;             // rows per batch
-    int64_t row_stride;        // element stride of the row index
+    int64_t row_stride;        // element stride of the row index (of i_{r_mode1} for two row modes)
+    int64_t row_stride_a;      // element stride of i_{r_mode0}
+    int row_split;             // 1: the two row modes are not adjacent (offsets per item and lane)
     int r_mode0, r_mode1;      // form 1 only; row = i_{r_mode0} * IrB + i_{r_mode1}
     int64_t IrB;
     // outer modes (decoded last-fastest from the batch index)
