@@ -157,7 +157,12 @@ hipError_t launch_mttkrp(const Plan &pl, hipStream_t stream, bool with_reduce)
     if (e != hipSuccess) return e;
     if (pl.kp.tr) {
         const int64_t count = pl.kp.In_out * pl.kp.R;
-        if (pl.kp.nsplit >= 16) {
+        // Few outputs (a short output mode): four per workgroup, so that the
+        // grid still spans the chip.
+        if (count < 16 * 1024) {
+            hipLaunchKernelGGL((trailing_reduce_kernel<T, 4>), dim3((unsigned)((count + 3) / 4)),
+                               dim3(256), 0, stream, (const double *)pl.kp.partial, pl.kp);
+        } else if (pl.kp.nsplit >= 16) {
             hipLaunchKernelGGL((trailing_reduce_kernel<T, 16>), dim3((unsigned)((count + 15) / 16)),
                                dim3(256), 0, stream, (const double *)pl.kp.partial, pl.kp);
         } else {

@@ -237,6 +237,15 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
         p.nb = ncb >= 4 ? 4 : (ncb >= 2 ? 2 : 1);
     if (p.layout == 1) {
         p.mb = 4;
+        // Trailing-rows tiles (a short block of rows, many contraction steps)
+        // keep the matrix cores fed only with two waves per SIMD: when four
+        // rank blocks do not fit the registers for that, two do, at the cost
+        // of one more pass over X per rank tile (served from the caches when
+        // X is small enough to stay there).
+        if (k.tr && p.nb == 4 &&
+            tile_min_waves(elem_bytes, 4, 4, false, plan_slots(0, k.nouter)) == 1 &&
+            tile_min_waves(elem_bytes, 4, 2, false, plan_slots(0, k.nouter)) == 2)
+            p.nb = 2;
     } else if (p.nb > 4) {
         p.mb = 2;
     } else if (p.form == 1) {
