@@ -151,17 +151,17 @@ struct Item {
     int64_t oidx[3];
 };
 
-__device__ __forceinline__ Item decode_item(const KParams &p, int64_t it, int64_t unit_off,
+__device__ __forceinline__ Item decode_item(const KParams &p, uint32_t it, int64_t unit_off,
                                             int64_t rows_per_tile, bool form1)
 {
     // (item indices are below 2^31: 32-bit divisions by planner constants)
     Item r;
     uint32_t b;
     if (form1) {
-        b = fdiv((uint32_t)it, p.fd_nrowtiles);
-        r.row0 = (int64_t)((uint32_t)it - b * p.fd_nrowtiles.d) * rows_per_tile;
+        b = fdiv(it, p.fd_nrowtiles);
+        r.row0 = (int64_t)(it - b * p.fd_nrowtiles.d) * rows_per_tile;
     } else {
-        b = (uint32_t)it;
+        b = it;
         r.row0 = 0;
     }
     // unused outer slots have dimension 1 and stride 0
@@ -182,6 +182,7 @@ mttkrp_tile_kernel(KParams p)
     // S: outer-factor slots carried per step (0: no outer mode; else up to S
     // outer modes, unused slots count as 1).
     static_assert(S == 0 || S == 1 || S == 3, "outer slots");
+    static_assert(!FORM1 || S == 0, "form 1 reads its outer factors once per item");
     constexpr int SS = S > 0 ? S : 1;  // array extent
     constexpr int NT = 64 * W;  // threads of the workgroup (W waves)
     static_assert(!RC || (MB % 4 == 0), "row-contiguous layout uses 64-row groups");
@@ -225,7 +226,7 @@ mttkrp_tile_kernel(KParams p)
     const int64_t Kloc = min(p.Kc, p.K - kbase);
     // steps per item (the last contraction chunk may be shorter)
     const FastDiv fd_nkc = kch == p.nkch - 1 ? p.fd_nkc_last : p.fd_nkc_full;
-    const int64_t nkc = fd_nkc.d;
+    const int nkc = (int)fd_nkc.d;
 
     const T *__restrict__ X = reinterpret_cast<const T *>(p.X);
     const int64_t R = p.R;
@@ -243,13 +244,14 @@ mttkrp_tile_kernel(KParams p)
     // The waves split the flattened step sequence evenly; a wave's range may
     // start or end inside an item (every item result is linear in its steps,
     // so a partial item is reduced like a whole one).
-    const int64_t it_lo = isplit * p.chunk;
-    const int64_t it_hi = min(p.nitems, it_lo + p.chunk);
-    const int64_t wg_steps = it_hi > it_lo ? (it_hi - it_lo) * nkc : 0;
-    const int64_t per_wave = (wg_steps + W - 1) / W;
-    const int64_t s_lo = min(wg_steps, wave * per_wave);
-    const int64_t s_hi = min(wg_steps, s_lo + per_wave);
-    const int64_t nsteps = s_hi - s_lo;
+    // (below 2^31: the planner bounds items and steps of a workgroup)
+    const int it_lo = (int)(isplit * p.chunk);
+    const int it_hi = (int)min(p.nitems, (int64_t)it_lo + p.chunk);
+    const int wg_steps = it_hi > it_lo ? (it_hi - it_lo) * nkc : 0;
+    const int per_wave = (wg_steps + W - 1) / W;
+    const int s_lo = min(wg_steps, wave * per_wave);
+    const int s_hi = min(wg_steps, s_lo + per_wave);
+    const int nsteps = s_hi - s_lo;
 
     // Unit: form 1 -> output row i_n; form 0 -> tile of output rows.
     int64_t unit_off, out_row0;
@@ -326,7 +328,7 @@ mttkrp_tile_kernel(KParams p)
     struct LoadCursor {
         int64_t base;  // element offset of the descriptor's start in X
         unsigned vo[NV];
-        int64_t it, kc, step;  // item, step in the item, step in the workgroup
+        int it, kc, step;      // item, step in the item, step in the workgroup
         int64_t orow[3];       // element offsets of the outer factor rows (i_o * R)
         bool live;             // step < s_hi: past it, loads return zeros
     };
@@ -366,7 +368,7 @@ mttkrp_tile_kernel(KParams p)
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) wq[j][nb] = Uo[j][lc.orow[j] + colc[nb]];
         const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(X + lc.base, (x_elems - lc.base) * (int64_t)SZ);
-        const int64_t krem = Kloc - lc.kc * 16;  // contraction elements left in this item
+        const int krem = (int)Kloc - lc.kc * 16;  // contraction elements left in this item
         if (!RC) {
             const unsigned soff = (unsigned)(lc.kc * 16 * SZ);
             const bool kin = lc.live && (4 * q < krem);
@@ -434,12 +436,12 @@ mttkrp_tile_kernel(KParams p)
             w[nb] = v;
         }
     };
-    auto compute_step = [&](const T *a, int64_t kc, T (*wq)[NB]) {
+    auto compute_step = [&](const T *a, int kc, T (*wq)[NB]) {
         T wb[NB];
         if (!FORM1) multiplier(wq, wb);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const int64_t kk = RC ? (kc * 16 + 4 * s + q) : (kc * 16 + 4 * q + s);
+            const int kk = RC ? (kc * 16 + 4 * s + q) : (kc * 16 + 4 * q + s);
             T b[NB];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
@@ -466,10 +468,20 @@ mttkrp_tile_kernel(KParams p)
     };
 
     // ---- end of a work item ----
-    auto finish_item = [&](int64_t row0, T (*wq)[NB]) {
+    // Outer factors of the form-1 item reduction; unused slots read the first
+    // row of the contraction factor and count as 1.
+    const T *Uf[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) Uf[j] = reinterpret_cast<const T *>(j < p.nouter ? p.Uo[j] : p.Uk0);
+    auto finish_item = [&](int64_t row0, const int64_t *orow) {
         if (FORM1) {
-            T w[NB];
-            multiplier(wq, w);
+            // The item's outer multiplier W_o (needed once per item, so read
+            // here rather than with every step's tensor loads).
+            T wv[3][NB];
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) wv[j][nb] = Uf[j][orow[j] + colc[nb]];
             // Reduce the tile rows against their factor rows and the outer
             // multiplier, one accumulator row g = (mb, e) at a time.  The
             // factor loads of row g + 1 are issued before row g is used, so
@@ -495,17 +507,27 @@ mttkrp_tile_kernel(KParams p)
                 }
             };
             zload(0, za[0], zb[0]);
+            double w[NB];
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
                 asm volatile("" ::: "memory");
                 if (g + 1 < NG) zload(g + 1, za[(g + 1) & 1], zb[(g + 1) & 1]);
+                if (g == 0) {
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        double v = 1.0;
+#pragma unroll
+                        for (int j = 0; j < 3; ++j) v *= j < p.nouter ? (double)wv[j][nb] : 1.0;
+                        w[nb] = v;
+                    }
+                }
                 const int mb = g >> 2, e = g & 3;
                 const int64_t rr = row0 + mb * 16 + Mfma<T>::row(q, e);
                 const bool rok = rr < p.nrows;
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
                     const double zbv = two ? (double)zb[g & 1][nb] : 1.0;
-                    const double z = (double)za[g & 1][nb] * zbv * (double)w[nb];
+                    const double z = (double)za[g & 1][nb] * zbv * w[nb];
                     const double t = z * (double)acc[mb][nb][e];
                     accrow[nb] += (rok && colok[nb]) ? t : 0.0;
                 }
@@ -537,14 +559,21 @@ mttkrp_tile_kernel(KParams p)
     for (int v = 0; v < NV; ++v) lc.vo[v] = kOOB;
 #pragma unroll
     for (int j = 0; j < 3; ++j) lc.orow[j] = 0;
-    lc.it = it_lo + fdiv((uint32_t)s_lo, fd_nkc);
+    lc.it = it_lo + (int)fdiv((uint32_t)s_lo, fd_nkc);
     lc.kc = s_lo - (lc.it - it_lo) * nkc;
     lc.step = s_lo;
     lc.live = false;
     enter_item(lc);
     // compute cursor
-    int64_t c_it = lc.it, c_kc = lc.kc, c_step = s_lo;
-    int64_t c_row0 = (FORM1 && nsteps > 0) ? decode_item(p, c_it, unit_off, ROWS, FORM1).row0 : 0;
+    int c_it = lc.it, c_kc = lc.kc, c_step = s_lo;
+    int64_t c_row0 = 0, c_orow[3] = {0, 0, 0};
+    auto compute_item = [&]() {  // form 1: first row and outer rows of item c_it
+        const Item itm = decode_item(p, c_it, unit_off, ROWS, FORM1);
+        c_row0 = itm.row0;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) c_orow[j] = j < p.nouter ? itm.oidx[j] * R : 0;
+    };
+    if (FORM1 && nsteps > 0) compute_item();
 
     // ---- stage the contraction-side Khatri-Rao tile B(kbase + k, r0:r0+BN)
     // in LDS, rows past the chunk zero-filled to a multiple of 16.  A thread
@@ -660,16 +689,15 @@ mttkrp_tile_kernel(KParams p)
 
     // After each step: reduce the item when it ends or when the wave's
     // range ends inside it.
-    auto after_compute = [&](T (*w)[NB]) {
+    auto after_compute = [&]() {
         ++c_step;
         const bool item_end = ++c_kc == nkc;
         if (c_step <= s_hi && (item_end || c_step == s_hi)) {
-            finish_item(c_row0, w);
+            finish_item(c_row0, c_orow);
             if (item_end) {
                 c_kc = 0;
                 ++c_it;
-                if (FORM1 && c_step < s_hi)
-                    c_row0 = decode_item(p, c_it, unit_off, ROWS, FORM1).row0;
+                if (FORM1 && c_step < s_hi) compute_item();
             }
         }
     };
@@ -678,13 +706,13 @@ mttkrp_tile_kernel(KParams p)
     // indexed by compile-time constants, so each buffer keeps its own
     // registers.  Steps past the wave's range load zeros and skip the
     // matrix cores.
-    for (int64_t t = 0; t < nsteps; t += PD + 1) {
+    for (int t = 0; t < nsteps; t += PD + 1) {
 #pragma unroll
         for (int u = 0; u <= PD; ++u) {
             load_step(abuf[(u + PD) % (PD + 1)], wbuf[(u + PD) % (PD + 1)], lc);
             advance(lc);
             if (c_step < s_hi) compute_step(abuf[u], c_kc, wbuf[u]);
-            after_compute(wbuf[u]);
+            after_compute();
         }
     }
 

@@ -1,7 +1,8 @@
 // Tile-kernel instantiations: f32, layout 0, form 1 (the output index fixed
 // per workgroup, tile rows reduced against their factor rows); four waves
 // (mb = 2: nb <= 8; mb = 4: nb <= 2) or eight waves when two waves per
-// SIMD fit the registers; no or three outer slots.
+// SIMD fit the registers; no outer slots (the item reduction reads the
+// outer factors).
 #include "mttkrp_tile.hpp"
 
 namespace mttkrp {
@@ -50,7 +51,7 @@ TileKernel select_tile_f32_form1(const Plan &pl)
 {
     if (pl.layout != 0 || pl.form != 1) return nullptr;
     const int s = tile_slots(pl);
-    return s == 0 ? sel<0>(pl) : s == 3 ? sel<3>(pl) : nullptr;
+    return s == 0 ? sel<0>(pl) : nullptr;
 }
 
 }  // namespace mttkrp
