@@ -486,13 +486,21 @@ mttkrp_tile_kernel(KParams p)
             // multiplier, one accumulator row g = (mb, e) at a time.  The
             // factor loads of row g + 1 are issued before row g is used, so
             // the round trips overlap while only two rows of factor values
-            // are held.  Indices are clamped and a missing second row factor
-            // reads the first and counts as 1, so no load sits under a
-            // branch; rows past the tile's end are masked afterwards.
-            const T *Ura = reinterpret_cast<const T *>(p.Ur0);
+            // are held.  They use 32-bit offsets from the factor's base (its
+            // span is below 2^31 bytes); indices are clamped (rows past the
+            // tile's end are masked afterwards) and a missing second row
+            // factor reads the first and counts as 1, so no load sits under a
+            // branch.
+            // For fp32 the weights and their products with the tile are formed
+            // in fp32; the row sums are fp64.
             const bool two = p.Ur1 != nullptr;
-            const T *Urb = two ? reinterpret_cast<const T *>(p.Ur1) : Ura;
             const unsigned IrB = (unsigned)p.IrB;
+            const unsigned RS = (unsigned)(R * SZ);
+            const char *za_base = reinterpret_cast<const char *>(p.Ur0);
+            const char *zb_base = reinterpret_cast<const char *>(two ? p.Ur1 : p.Ur0);
+            unsigned cofs_z[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) cofs_z[nb] = (unsigned)(colc[nb] * SZ);
             constexpr int NG = MB * 4;
             T za[2][NB], zb[2][NB];
             auto zload = [&](int g, T *a, T *b) {
@@ -500,14 +508,15 @@ mttkrp_tile_kernel(KParams p)
                 const unsigned rc = rr < p.nrows ? (unsigned)rr : 0u;
                 const unsigned ia = two ? fdiv(rc, p.fd_IrB) : rc;
                 const unsigned ib = two ? rc - ia * IrB : 0u;
+                const unsigned oa = ia * RS, ob = ib * RS;
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
-                    a[nb] = Ura[(int64_t)ia * R + colc[nb]];
-                    b[nb] = Urb[(int64_t)ib * R + colc[nb]];
+                    a[nb] = *reinterpret_cast<const T *>(za_base + (oa + cofs_z[nb]));
+                    b[nb] = *reinterpret_cast<const T *>(zb_base + (ob + cofs_z[nb]));
                 }
             };
             zload(0, za[0], zb[0]);
-            double w[NB];
+            T w[NB];
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
                 asm volatile("" ::: "memory");
@@ -515,21 +524,28 @@ mttkrp_tile_kernel(KParams p)
                 if (g == 0) {
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) {
-                        double v = 1.0;
+                        T v = T(1);
 #pragma unroll
-                        for (int j = 0; j < 3; ++j) v *= j < p.nouter ? (double)wv[j][nb] : 1.0;
+                        for (int j = 0; j < 3; ++j) v *= j < p.nouter ? wv[j][nb] : T(1);
                         w[nb] = v;
                     }
                 }
                 const int mb = g >> 2, e = g & 3;
-                const int64_t rr = row0 + mb * 16 + Mfma<T>::row(q, e);
-                const bool rok = rr < p.nrows;
+                const bool rok = row0 + mb * 16 + Mfma<T>::row(q, e) < p.nrows;
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
-                    const double zbv = two ? (double)zb[g & 1][nb] : 1.0;
-                    const double z = (double)za[g & 1][nb] * zbv * w[nb];
-                    const double t = z * (double)acc[mb][nb][e];
-                    accrow[nb] += (rok && colok[nb]) ? t : 0.0;
+                    if constexpr (sizeof(T) == 4) {
+                        // fp32: weight and product in fp32, the sum in fp64
+                        // (columns past the rank are never stored: no mask)
+                        T z = za[g & 1][nb] * (two ? zb[g & 1][nb] : T(1)) * w[nb];
+                        z = rok ? z : T(0);
+                        accrow[nb] += (double)(z * acc[mb][nb][e]);
+                    } else {
+                        const double zbv = two ? (double)zb[g & 1][nb] : 1.0;
+                        const double z = (double)za[g & 1][nb] * zbv * (double)w[nb];
+                        const double t = z * (double)acc[mb][nb][e];
+                        accrow[nb] += (rok && colok[nb]) ? t : 0.0;
+                    }
                 }
             }
 #pragma unroll

@@ -269,7 +269,9 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
     // Contraction chunks: the Khatri-Rao tile of one chunk (Kc x 16nb) must
     // fit in the workgroup's LDS; longer contractions are split into chunks
     // whose results are summed by the reduction pass.
-    const int bpitch = 16 * p.nb + (elem_bytes == 8 ? 4 : 8);
+    // LDS pitch of B rows: a lane group of four reads rows 4 apart, so the
+    // pitch is padded (4 elements) to put those rows on different banks.
+    const int bpitch = 16 * p.nb + 4;
     const int64_t Kpad = ceil_div(k.K, 16) * 16;
     const int64_t kc_max = (int64_t)(lds_budget / ((size_t)bpitch * elem_bytes)) / 16 * 16;
     if (kc_max < 16) return MTTKRP_ERANGE;
@@ -360,6 +362,13 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
         if (span >= (INT64_C(1) << 31) - 64) return MTTKRP_ERANGE;
         // The contraction factor rows one chunk stages are read the same
         // way: the first factor from the chunk's first row, the second whole.
+        // The row factors of a form-1 reduction likewise.
+        if (p.form == 1) {
+            const int64_t na = k.r_mode1 >= 0 ? k.nrows / k.IrB : k.nrows;
+            if ((na * rank + 16) * elem_bytes >= (INT64_C(1) << 31)) return MTTKRP_ERANGE;
+            if (k.r_mode1 >= 0 && (k.IrB * rank + 16) * elem_bytes >= (INT64_C(1) << 31))
+                return MTTKRP_ERANGE;
+        }
         const int64_t rows_a = (k.k_mode1 >= 0) ? k.Kc / k.IkB + 2 : k.Kc;
         if ((rows_a * rank + 16) * elem_bytes >= (INT64_C(1) << 31)) return MTTKRP_ERANGE;
         if ((k.k_mode1 >= 0) && (k.IkB * rank + 16) * elem_bytes >= (INT64_C(1) << 31))
