@@ -230,8 +230,16 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
     // reuse each tensor element for 128 columns when the rank is large; the
     // row tile is 32 rows unless there is work for many more waves than the
     // chip holds.
+    // fp32 form-0 tiles keep an fp64 copy of their accumulators, so eight
+    // rank blocks leave one wave per SIMD; four blocks with two waves per
+    // SIMD keep the matrix cores busier even though X is then read once per
+    // 64 rank columns (measured on the 4-way fp32 rank-512 tensor: -19%).
     const int64_t ncb = ceil_div(rank, 16);  // 16-wide rank blocks
-    if (ncb >= 8 && p.layout == 0 && (p.form == 0 || elem_bytes == 4))
+    const bool wide_ok =
+        p.form == 1 ? elem_bytes == 4
+                    : (elem_bytes == 8 ||
+                       tile_min_waves(elem_bytes, 2, 8, false, plan_slots(0, k.nouter)) == 2);
+    if (ncb >= 8 && p.layout == 0 && wide_ok)
         p.nb = 8;
     else
         p.nb = ncb >= 4 ? 4 : (ncb >= 2 ? 2 : 1);
