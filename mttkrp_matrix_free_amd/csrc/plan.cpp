@@ -162,8 +162,14 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
         // At high rank the per-tile row reduction of form 1 (one factor load
         // and one fma per accumulator element) costs more than scaling the
         // contraction tile by the outer multiplier, so the output rows become
-        // the tile rows (form 0).
-        if (rank >= 256) rlast = -1;
+        // the tile rows (form 0).  That reduction runs on the vector ALUs,
+        // which do not overlap the matrix cores, and it weighs twice as much
+        // against fp32 MFMAs as against fp64 ones: fp32 takes form 0 already
+        // at rank 64, and at lower rank when the output rows lie close
+        // together (stride up to 2^16 elements; measured on the 4-way fp32
+        // tensor: R=64 modes 0-2 258 -> 202-218 us, R=8 modes 1-2 -15/-23%).
+        if (rank >= 256 || (elem_bytes == 4 && (rank >= 64 || S[n] <= (INT64_C(1) << 16))))
+            rlast = -1;
         if (rlast >= 0) {
             p.form = 1;
             int rfirst = rlast;

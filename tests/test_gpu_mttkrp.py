@@ -164,7 +164,7 @@ def test_all_modes_entry_and_determinism():
 @pytest.mark.parametrize("dims,rank,dtype", [
     ((256, 256, 256), 32, np.float64),   # 64 splits: 16 thread groups per output
     ((128, 96, 256), 40, np.float64),    # 19 splits: 4 groups; two rank tiles
-    ((200, 256, 96), 40, np.float32),    # fp32, ragged rank
+    ((256, 384, 192), 24, np.float32),   # fp32, ragged rank; two split modes, one partner
 ])
 def test_all_modes_hand_split_sums_to_another_launch(dims, rank, dtype):
     """In the all-mode call a mode whose plan splits hands its partial sums to
