@@ -205,6 +205,14 @@ def main():
         achieved = d * flops_mode / tot_t / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS[dt_name],
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS[dt_name], 4)}
+    # The same fraction from the cold-cache medians (the tensor read from HBM
+    # rather than from the last-level cache it fits in between modes).
+    if cold is not None:
+        t_cold = sum(cold_med) / 1e3
+        if hbm_bound:
+            roof["frac_cold"] = round(sum(bytes_mode) / t_cold / 1e9 / HBM_PEAK_GBS, 4)
+        else:
+            roof["frac_cold"] = round(d * flops_mode / t_cold / 1e12 / PEAK_TFLOPS[dt_name], 4)
     tr = measured_traffic(p.name)
     roof["traffic"] = (round(float(np.mean(tr["bytes_per_mode"])), 0) if tr else None)
     roof["traffic_unit"] = "bytes/launch (FETCH_SIZE+WRITE_SIZE, copy-calibrated)"
