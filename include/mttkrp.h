@@ -81,7 +81,9 @@ int mttkrp_selftest(void);
  * output rows, or, when the output mode is a short unit-stride mode, the
  * block of the last two modes (I_{d-2} * I_{d-1} rows with I_{d-1} < 64).  So
  * the workspace grows like R * I_n (or R * 64 * I_{d-2}) and never with the
- * Khatri-Rao size R * prod_{m != n} I_m. */
+ * Khatri-Rao size R * prod_{m != n} I_m.  The all-mode call needs twice the
+ * largest mode's workspace: it holds one mode's partials while the next mode
+ * writes its own. */
 int mttkrp_workspace_bytes(const int64_t *dims, int order, int64_t rank, int mode,
                            int elem_bytes, size_t *bytes);
 int mttkrp_all_workspace_bytes(const int64_t *dims, int order, int64_t rank, int elem_bytes,

@@ -110,8 +110,8 @@ int mttkrp_one(const T *X, const int64_t *dims, int order, const T *const *facto
     return launch_mttkrp<T>(pl, stream, true) == hipSuccess ? MTTKRP_OK : MTTKRP_EHIP;
 }
 
-// A plain split plan (partials summed by split_reduce_kernel) and a plan that
-// writes no partials, whose launch can carry that sum instead.
+// A plain split plan: partials summed by split_reduce_kernel, or by the tile
+// kernel of another launch.
 // (The partner reads the partials with 32-bit offsets: their span must stay
 // below 2^31 bytes.)
 bool plain_split(const Plan &pl)
@@ -119,7 +119,6 @@ bool plain_split(const Plan &pl)
     return pl.kp.nsplit > 1 && !pl.kp.tr &&
            pl.kp.nsplit * pl.kp.In * pl.kp.R * 8 < (INT64_C(1) << 31) - 64;
 }
-bool no_partials(const Plan &pl) { return !pl.kp.to_partial; }
 
 template <typename T>
 int mttkrp_entry(const T *X, const int64_t *dims, int order, const T *const *factors,
@@ -134,7 +133,8 @@ int mttkrp_entry(const T *X, const int64_t *dims, int order, const T *const *fac
                          reinterpret_cast<hipStream_t>(stream));
 }
 
-int all_ws(const int64_t *dims, int order, int64_t rank, int elem, size_t *bytes)
+// Largest workspace of one mode (each a multiple of 256 bytes).
+int mode_ws_max(const int64_t *dims, int order, int64_t rank, int elem, size_t *bytes)
 {
     size_t mx = 0;
     for (int m = 0; m < order; ++m) {
@@ -144,6 +144,17 @@ int all_ws(const int64_t *dims, int order, int64_t rank, int elem, size_t *bytes
         mx = std::max(mx, pl.ws_bytes);
     }
     *bytes = mx;
+    return MTTKRP_OK;
+}
+
+// The all-mode call holds two modes' partials at once (one pending while the
+// next mode writes its own): two halves of the largest mode workspace.
+int all_ws(const int64_t *dims, int order, int64_t rank, int elem, size_t *bytes)
+{
+    size_t mx = 0;
+    const int st = mode_ws_max(dims, order, rank, elem, &mx);
+    if (st) return st;
+    *bytes = 2 * mx;
     return MTTKRP_OK;
 }
 
@@ -165,38 +176,45 @@ int mttkrp_all_entry(const T *X, const int64_t *dims, int order, const T *const 
     if (need > ws_bytes) return MTTKRP_EWORKSPACE;
     if (need > 0 && !ws) return MTTKRP_EINVAL;
     // Every plan first (so that nothing is launched when one fails), then the
-    // launches: each mode with a plain split goes first and hands its partial
-    // sums to the tile kernel of a mode that writes none, which adds them in
-    // split_reduce_kernel's order (the results do not change, one launch per
-    // split mode is saved); a split mode without such a partner keeps its own
-    // reduction launch.  The modes are independent, so the order is free.
+    // launches, the modes with a plain split first.  A split mode does not
+    // launch its own reduction: the next launch's tile kernel adds its partial
+    // sums in split_reduce_kernel's order (so the results do not change and a
+    // launch per split mode is saved), while writing its own partials, if
+    // any, to the other half of the workspace.  Only the last launch, when it
+    // splits, keeps its reduction kernel.  The modes are independent given the
+    // factors, so the order is free.
     Plan pl[kMaxOrder];
     for (int m = 0; m < order; ++m) {
         st = bound_plan<T>(X, dims, order, factors, rank, m, outs[m], 0, ws, ws_bytes, pl[m]);
         if (st) return st;
     }
-    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    bool done[kMaxOrder] = {false, false, false, false, false};
-    for (int a = 0; a < order; ++a) {
-        if (!plain_split(pl[a])) continue;
-        int b = -1;
-        for (int m = 0; m < order && b < 0; ++m)
-            if (!done[m] && m != a && no_partials(pl[m])) b = m;
-        if (launch_mttkrp<T>(pl[a], s, b < 0) != hipSuccess) return MTTKRP_EHIP;
-        done[a] = true;
-        if (b >= 0) {
-            KParams &k = pl[b].kp;
-            k.pend_partial = pl[a].kp.partial;
-            k.pend_nsplit = pl[a].kp.nsplit;
-            k.pend_count = pl[a].kp.In * pl[a].kp.R;
-            k.pend_out = pl[a].kp.out;
-            k.pend_ng = pl[a].kp.nsplit >= 32 ? 16 : 4;
-            if (launch_mttkrp<T>(pl[b], s, true) != hipSuccess) return MTTKRP_EHIP;
-            done[b] = true;
-        }
-    }
+    int ord[kMaxOrder];
+    int no = 0;
     for (int m = 0; m < order; ++m)
-        if (!done[m] && launch_mttkrp<T>(pl[m], s, true) != hipSuccess) return MTTKRP_EHIP;
+        if (plain_split(pl[m])) ord[no++] = m;
+    for (int m = 0; m < order; ++m)
+        if (!plain_split(pl[m])) ord[no++] = m;
+    const size_t half = need / 2;
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    int prev = -1;    // split mode whose partials are pending
+    int prev_half = 0;
+    for (int i = 0; i < order; ++i) {
+        Plan &cur = pl[ord[i]];
+        const int h = prev >= 0 ? 1 - prev_half : 0;
+        cur.kp.partial = reinterpret_cast<double *>(static_cast<char *>(ws) + h * half);
+        if (prev >= 0) {
+            const KParams &a = pl[prev].kp;
+            cur.kp.pend_partial = a.partial;
+            cur.kp.pend_nsplit = a.nsplit;
+            cur.kp.pend_count = a.In * a.R;
+            cur.kp.pend_out = a.out;
+            cur.kp.pend_ng = a.nsplit >= 32 ? 16 : 4;
+        }
+        const bool hand_on = plain_split(cur) && i + 1 < order;
+        if (launch_mttkrp<T>(cur, s, !hand_on) != hipSuccess) return MTTKRP_EHIP;
+        prev = hand_on ? ord[i] : -1;
+        prev_half = h;
+    }
     return MTTKRP_OK;
 }
 
@@ -210,7 +228,7 @@ struct AlsLayout {
 int als_layout(const int64_t *dims, int order, int64_t rank, int elem, AlsLayout &L)
 {
     size_t mt = 0;
-    int st = all_ws(dims, order, rank, elem, &mt);
+    int st = mode_ws_max(dims, order, rank, elem, &mt);
     if (st) return st;
     int64_t maxI = 0;
     for (int m = 0; m < order; ++m) maxI = std::max<int64_t>(maxI, dims[m]);

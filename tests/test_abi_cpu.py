@@ -156,6 +156,7 @@ WORKLOADS = [
 def test_plans_within_limits_and_matrix_free_memory(L, dims, R, eb):
     d = len(dims)
     kr_bytes_max = 0
+    max_ws = 0
     for n in range(d):
         info = _lib.PlanInfo()
         assert L.mttkrp_plan(dims_arr(dims), d, R, n, eb, ctypes.byref(info)) == 0
@@ -177,6 +178,7 @@ def test_plans_within_limits_and_matrix_free_memory(L, dims, R, eb):
         ws = ctypes.c_size_t()
         assert L.mttkrp_workspace_bytes(dims_arr(dims), d, R, n, eb, ctypes.byref(ws)) == 0
         assert ws.value == info.ws_bytes
+        max_ws = max(max_ws, ws.value)
         # partials: at most max(1024, contraction chunks) copies of the kernel's
         # output rows (I_n, or the trailing block I_{d-2} I_{d-1} with
         # I_{d-1} < 64 for a layout-1 plan) times R, in fp64
@@ -192,10 +194,12 @@ def test_plans_within_limits_and_matrix_free_memory(L, dims, R, eb):
         kr_bytes_max = max(kr_bytes_max, kr * R * eb)
     allws = ctypes.c_size_t()
     assert L.mttkrp_all_workspace_bytes(dims_arr(dims), d, R, eb, ctypes.byref(allws)) == 0
+    # two halves: one mode's pending partials and the next mode's own
+    assert allws.value == 2 * max_ws
     als = ctypes.c_size_t()
     if R <= 4096:
         assert L.cp_als_workspace_bytes(dims_arr(dims), d, R, eb, ctypes.byref(als)) == 0
-        assert als.value >= allws.value
+        assert als.value >= max_ws
 
 
 def test_workspace_far_below_khatri_rao_at_rank_2000(L):
