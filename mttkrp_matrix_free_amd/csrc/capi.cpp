@@ -12,6 +12,7 @@
 #include <cstdint>
 #include <cstring>
 #include <limits>
+#include <mutex>
 #include <vector>
 
 #include "../../include/mttkrp.h"
@@ -48,6 +49,30 @@ constexpr int kSumsqParts = 1024;
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+// Second stream of the current device for the all-mode call: created on first
+// use (default priority, not synchronising with the null stream) and kept
+// until the process ends.
+hipError_t side_stream(hipStream_t *out)
+{
+    constexpr int kMaxDev = 64;
+    static std::mutex mu;
+    static hipStream_t ss[kMaxDev];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ss[dev]) {
+        e = hipStreamCreateWithFlags(&ss[dev], hipStreamNonBlocking);
+        if (e != hipSuccess) {
+            ss[dev] = nullptr;
+            return e;
+        }
+    }
+    *out = ss[dev];
+    return hipSuccess;
+}
 
 // Checks shared by the MTTKRP entry points.  `factors` may hold NULL at `mode`
 // (mode < 0: every factor must be present).
@@ -110,6 +135,26 @@ int mttkrp_one(const T *X, const int64_t *dims, int order, const T *const *facto
     return launch_mttkrp<T>(pl, stream, true) == hipSuccess ? MTTKRP_OK : MTTKRP_EHIP;
 }
 
+// Rough time of an all-mode sweep: each mode bounded by streaming X at
+// 5 TB/s or by the matrix cores at 60 (fp64) or 120 (fp32) TFLOP/s.
+double sweep_seconds(const Plan *pl, int order)
+{
+    double t = 0.0;
+    for (int m = 0; m < order; ++m) {
+        const KParams &k = pl[m].kp;
+        const double N = (double)k.x_bytes / pl[m].elem_bytes;
+        const double mem = (double)k.x_bytes / 5e12;
+        const double mma = 2.0 * N * (double)k.R / (pl[m].elem_bytes == 8 ? 60e12 : 120e12);
+        t += std::max(mem, mma);
+    }
+    return t;
+}
+// Two streams in the all-mode call only pay off when the sweep hides the
+// cost of the cross-stream dependencies (two per call, about 10 us each):
+// measured faster on the 4-way fp32 rank-8 tensor (-8%, ~440 us) and the
+// 5-way tensor (-1.5%), slower on the 256^3 fp64 rank-32 one (+6%, ~90 us).
+constexpr double kTwoStreamSweep = 200e-6;
+
 // A plain split plan: partials summed by split_reduce_kernel, or by the tile
 // kernel of another launch.
 // (The partner reads the partials with 32-bit offsets: their span must stay
@@ -147,8 +192,9 @@ int mode_ws_max(const int64_t *dims, int order, int64_t rank, int elem, size_t *
     return MTTKRP_OK;
 }
 
-// The all-mode call holds two modes' partials at once (one pending while the
-// next mode writes its own): two halves of the largest mode workspace.
+// The all-mode call holds two modes' partials at once (two streams, or one
+// mode's partials pending while the next writes its own): two halves of the
+// largest mode workspace.
 int all_ws(const int64_t *dims, int order, int64_t rank, int elem, size_t *bytes)
 {
     size_t mx = 0;
@@ -176,32 +222,65 @@ int mttkrp_all_entry(const T *X, const int64_t *dims, int order, const T *const 
     if (need > ws_bytes) return MTTKRP_EWORKSPACE;
     if (need > 0 && !ws) return MTTKRP_EINVAL;
     // Every plan first (so that nothing is launched when one fails), then the
-    // launches, the modes with a plain split first.  A split mode does not
-    // launch its own reduction: the next launch's tile kernel adds its partial
-    // sums in split_reduce_kernel's order (so the results do not change and a
-    // launch per split mode is saved), while writing its own partials, if
-    // any, to the other half of the workspace.  Only the last launch, when it
-    // splits, keeps its reduction kernel.  The modes are independent given the
-    // factors, so the order is free.
+    // launches.  The modes are independent given the factors, so the order is
+    // free.
     Plan pl[kMaxOrder];
     for (int m = 0; m < order; ++m) {
         st = bound_plan<T>(X, dims, order, factors, rank, m, outs[m], 0, ws, ws_bytes, pl[m]);
         if (st) return st;
     }
+    const size_t half = need / 2;
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    auto in_half = [&](int h) {
+        return reinterpret_cast<double *>(static_cast<char *>(ws) + (size_t)h * half);
+    };
+    if (sweep_seconds(pl, order) >= kTwoStreamSweep) {
+        // A long sweep alternates between the caller's stream and a second
+        // one, so that one mode's last workgroups, its split reduction and
+        // the next mode's first workgroups run side by side.  Each stream has
+        // its own half of the workspace.
+        hipStream_t side = nullptr;
+        if (side_stream(&side) != hipSuccess) return MTTKRP_EHIP;
+        hipEvent_t fork = nullptr, join = nullptr;
+        if (hipEventCreateWithFlags(&fork, hipEventDisableTiming) != hipSuccess) return MTTKRP_EHIP;
+        if (hipEventCreateWithFlags(&join, hipEventDisableTiming) != hipSuccess) {
+            (void)hipEventDestroy(fork);
+            return MTTKRP_EHIP;
+        }
+        // The second stream starts after the work already on the caller's
+        // stream, and the caller's stream continues after both.
+        hipError_t e = hipEventRecord(fork, s);
+        if (e == hipSuccess) e = hipStreamWaitEvent(side, fork, 0);
+        for (int m = 0; m < order && e == hipSuccess; ++m) {
+            const int lane = m & 1;
+            pl[m].kp.partial = in_half(lane);
+            e = launch_mttkrp<T>(pl[m], lane ? side : s, true);
+        }
+        if (e == hipSuccess) e = hipEventRecord(join, side);
+        if (e == hipSuccess) e = hipStreamWaitEvent(s, join, 0);
+        (void)hipEventDestroy(fork);
+        (void)hipEventDestroy(join);
+        return e == hipSuccess ? MTTKRP_OK : MTTKRP_EHIP;
+    }
+    // A short sweep stays on the caller's stream, the modes with a plain split
+    // first.  A split mode launches no reduction of its own: the next
+    // launch's tile kernel adds its partial sums in split_reduce_kernel's
+    // order (so the results do not change and a launch per split mode is
+    // saved), while writing its own partials, if any, to the other half of
+    // the workspace.  Only the last launch, when it splits, keeps its
+    // reduction kernel.
     int ord[kMaxOrder];
     int no = 0;
     for (int m = 0; m < order; ++m)
         if (plain_split(pl[m])) ord[no++] = m;
     for (int m = 0; m < order; ++m)
         if (!plain_split(pl[m])) ord[no++] = m;
-    const size_t half = need / 2;
-    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    int prev = -1;    // split mode whose partials are pending
+    int prev = -1;  // split mode whose partials are pending
     int prev_half = 0;
     for (int i = 0; i < order; ++i) {
         Plan &cur = pl[ord[i]];
         const int h = prev >= 0 ? 1 - prev_half : 0;
-        cur.kp.partial = reinterpret_cast<double *>(static_cast<char *>(ws) + h * half);
+        cur.kp.partial = in_half(h);
         if (prev >= 0) {
             const KParams &a = pl[prev].kp;
             cur.kp.pend_partial = a.partial;
