@@ -436,9 +436,12 @@ mttkrp_tile_kernel(KParams p)
             w[nb] = v;
         }
     };
+    // fp32 form 0 applies the outer multiplier once per item instead (at the
+    // item end, with the fp64 flush), so its steps use B as staged.
+    constexpr bool SCALE_B = !FORM1 && !FLUSH64;
     auto compute_step = [&](const T *a, int kc, T (*wq)[NB]) {
         T wb[NB];
-        if (!FORM1) multiplier(wq, wb);
+        if (SCALE_B) multiplier(wq, wb);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int kk = RC ? (kc * 16 + 4 * s + q) : (kc * 16 + 4 * q + s);
@@ -446,7 +449,7 @@ mttkrp_tile_kernel(KParams p)
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 b[nb] = Bs[kk * p.bpitch + nb * 16 + c16];
-                if (!FORM1) b[nb] *= wb[nb];
+                if (SCALE_B) b[nb] *= wb[nb];
             }
             if (!RC) {
 #pragma unroll
@@ -473,7 +476,7 @@ mttkrp_tile_kernel(KParams p)
     const T *Uf[3];
 #pragma unroll
     for (int j = 0; j < 3; ++j) Uf[j] = reinterpret_cast<const T *>(j < p.nouter ? p.Uo[j] : p.Uk0);
-    auto finish_item = [&](int64_t row0, const int64_t *orow) {
+    auto finish_item = [&](int64_t row0, const int64_t *orow, T (*wq)[NB]) {
         if (FORM1) {
             // The item's outer multiplier W_o (needed once per item, so read
             // here rather than with every step's tensor loads).
@@ -553,12 +556,17 @@ mttkrp_tile_kernel(KParams p)
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = acc_t{};
         } else if (FLUSH64) {
+            // The item's tile, weighted by its outer multiplier (from the
+            // factor values buffered with its last step), joins the fp64 sums.
+            T w[NB];
+            multiplier(wq, w);
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) acc64[mb][nb][e] += (double)acc[mb][nb][e];
+                    for (int e = 0; e < 4; ++e)
+                        acc64[mb][nb][e] += (double)(w[nb] * acc[mb][nb][e]);
                     acc[mb][nb] = acc_t{};
                 }
         }
@@ -705,11 +713,11 @@ mttkrp_tile_kernel(KParams p)
 
     // After each step: reduce the item when it ends or when the wave's
     // range ends inside it.
-    auto after_compute = [&]() {
+    auto after_compute = [&](T (*wq)[NB]) {
         ++c_step;
         const bool item_end = ++c_kc == nkc;
         if (c_step <= s_hi && (item_end || c_step == s_hi)) {
-            finish_item(c_row0, c_orow);
+            finish_item(c_row0, c_orow, wq);
             if (item_end) {
                 c_kc = 0;
                 ++c_it;
@@ -728,7 +736,7 @@ mttkrp_tile_kernel(KParams p)
             load_step(abuf[(u + PD) % (PD + 1)], wbuf[(u + PD) % (PD + 1)], lc);
             advance(lc);
             if (c_step < s_hi) compute_step(abuf[u], c_kc, wbuf[u]);
-            after_compute();
+            after_compute(wbuf[u]);
         }
     }
 
