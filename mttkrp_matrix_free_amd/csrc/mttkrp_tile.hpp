@@ -10,6 +10,7 @@
 //   for every outer tuple o and tile of rows rho:
 //       T(rho, r) = sum_k X(o, rho, k) B(k, r)              (MFMA, 16x16x4)
 //   form 0 (rho = i_n):   M(rho, r) += T computed with B scaled by W_o(r)
+//                         (fp32: M += W_o(r) T, once per item, in fp64)
 //   form 1 (i_n in o):    M(i_n, r) += sum_rho Z(rho, r) W_o(r) T(rho, r)
 //
 // where B is the (at most two-factor) Khatri-Rao tile of the contracted modes,
