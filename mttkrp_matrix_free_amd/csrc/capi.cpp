@@ -22,6 +22,8 @@ namespace mttkrp {
 
 template <typename T>
 hipError_t launch_mttkrp(const Plan &pl, hipStream_t stream, bool with_reduce);
+template <typename T>
+hipError_t launch_mttkrp_multi(const Plan *const *pls, int np, hipStream_t stream);
 
 template <typename T>
 hipError_t launch_sumsq(const T *X, int64_t N, double *partial, int nparts, double *out,
@@ -155,6 +157,22 @@ double sweep_seconds(const Plan *pl, int order)
 // 5-way tensor (-1.5%), slower on the 256^3 fp64 rank-32 one (+6%, ~90 us).
 constexpr double kTwoStreamSweep = 200e-6;
 
+// Two form-1 plans one multi-mode launch can run in turn: the same tile
+// shape, the same B tile for every workgroup (contraction group, chunking,
+// rank tiles, decomposition) and no partials.
+bool fusable(const Plan &a, const Plan &b)
+{
+    const KParams &x = a.kp, &y = b.kp;
+    return a.form == 1 && b.form == 1 && a.layout == 0 && b.layout == 0 && a.waves == 8 &&
+           b.waves == 8 && a.mb == b.mb && a.nb == b.nb && a.vec == b.vec &&
+           a.elem_bytes == b.elem_bytes && !x.to_partial && !y.to_partial && !x.tr && !y.tr &&
+           x.k_mode0 == y.k_mode0 && x.k_mode1 == y.k_mode1 && x.K == y.K && x.Kc == y.Kc &&
+           x.nkch == y.nkch && x.IkB == y.IkB && x.bpitch == y.bpitch && x.R == y.R &&
+           x.grid_real == y.grid_real && x.grid_per_xcd == y.grid_per_xcd &&
+           x.nrtiles == y.nrtiles && x.nsplit == y.nsplit && x.nsplit_it == y.nsplit_it &&
+           a.grid == b.grid;
+}
+
 // A plain split plan: partials summed by split_reduce_kernel, or by the tile
 // kernel of another launch.
 // (The partner reads the partials with 32-bit offsets: their span must stay
@@ -275,9 +293,11 @@ int mttkrp_all_entry(const T *X, const int64_t *dims, int order, const T *const 
         if (plain_split(pl[m])) ord[no++] = m;
     for (int m = 0; m < order; ++m)
         if (!plain_split(pl[m])) ord[no++] = m;
+    // Consecutive form-1 modes that share their B tile and decomposition and
+    // write no partials run as the passes of one multi-mode launch.
     int prev = -1;  // split mode whose partials are pending
     int prev_half = 0;
-    for (int i = 0; i < order; ++i) {
+    for (int i = 0; i < order;) {
         Plan &cur = pl[ord[i]];
         const int h = prev >= 0 ? 1 - prev_half : 0;
         cur.kp.partial = in_half(h);
@@ -289,10 +309,23 @@ int mttkrp_all_entry(const T *X, const int64_t *dims, int order, const T *const 
             cur.kp.pend_out = a.out;
             cur.kp.pend_ng = a.nsplit >= 32 ? 16 : 4;
         }
+        const Plan *grp[kMaxPasses] = {&cur};
+        int np = 1;
+        while (np < kMaxPasses && i + np < order && fusable(cur, pl[ord[i + np]])) {
+            grp[np] = &pl[ord[i + np]];
+            ++np;
+        }
+        if (np > 1) {
+            if (launch_mttkrp_multi<T>(grp, np, s) != hipSuccess) return MTTKRP_EHIP;
+            prev = -1;
+            i += np;
+            continue;
+        }
         const bool hand_on = plain_split(cur) && i + 1 < order;
         if (launch_mttkrp<T>(cur, s, !hand_on) != hipSuccess) return MTTKRP_EHIP;
         prev = hand_on ? ord[i] : -1;
         prev_half = h;
+        ++i;
     }
     return MTTKRP_OK;
 }

@@ -186,7 +186,33 @@ hipError_t launch_mttkrp(const Plan &pl, hipStream_t stream, bool with_reduce)
     return e;
 }
 
+// Two form-1 modes in one launch, one pass each (plans checked by fusable():
+// same B tile and decomposition, no partials).  The reduction
+// space follows the B tile in LDS.
+template <typename T>
+hipError_t launch_mttkrp_multi(const Plan *const *pls, int np, hipStream_t stream)
+{
+    if (np != kMaxPasses) return hipErrorInvalidValue;
+    const Plan &pl = *pls[0];
+    MultiKernel k = sizeof(T) == 8 ? select_multi_f64(pl) : select_multi_f32(pl);
+    if (!k) return hipErrorInvalidConfiguration;
+    KPack pk{};
+    for (int i = 0; i < np; ++i) pk.p[i] = pls[i]->kp;
+    const size_t b_tile = (size_t)pl.kp.Kc * pl.kp.bpitch * sizeof(T);
+    pk.red_off = (int64_t)((b_tile + 15) / 16 * 16);
+    const size_t lds = (size_t)pk.red_off + (size_t)pl.waves * 16 * pl.nb * sizeof(double);
+    if (lds > 160 * 1024) return hipErrorInvalidConfiguration;
+    if (lds > 64 * 1024) {
+        hipError_t a = allow_large_lds(reinterpret_cast<const void *>(k));
+        if (a != hipSuccess) return a;
+    }
+    hipLaunchKernelGGL(k, dim3((unsigned)pl.grid), dim3(64 * pl.waves), lds, stream, pk);
+    return hipGetLastError();
+}
+
 template hipError_t launch_mttkrp<double>(const Plan &, hipStream_t, bool);
 template hipError_t launch_mttkrp<float>(const Plan &, hipStream_t, bool);
+template hipError_t launch_mttkrp_multi<double>(const Plan *const *, int, hipStream_t);
+template hipError_t launch_mttkrp_multi<float>(const Plan *const *, int, hipStream_t);
 
 }  // namespace mttkrp

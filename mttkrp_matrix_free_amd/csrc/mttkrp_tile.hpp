@@ -176,9 +176,13 @@ __device__ __forceinline__ Item decode_item(const KParams &p, uint32_t it, int64
     return r;
 }
 
+// One mode's work for the calling workgroup.  stage_b = false: the B tile of
+// this pass is already in LDS (staged by an earlier pass of the same launch
+// with the same contraction chunk and rank tile); red_off: byte offset of the
+// cross-wave reduction space in LDS.
 template <typename T, int MB, int NB, bool RC, bool VEC, bool FORM1, int W, int S>
-__global__ __launch_bounds__(64 * W, (tile_min_waves(sizeof(T), MB, NB, FORM1, S))) void
-mttkrp_tile_kernel(KParams p)
+__device__ __forceinline__ void tile_pass(const KParams &p, unsigned char *smem, bool stage_b,
+                                          size_t red_off)
 {
     // S: outer-factor slots carried per step (0: no outer mode; else up to S
     // outer modes, unused slots count as 1).
@@ -196,9 +200,8 @@ mttkrp_tile_kernel(KParams p)
     constexpr int NA = 4 * MB;  // tensor elements per lane per step
     constexpr unsigned SZ = sizeof(T);
 
-    extern __shared__ __align__(16) unsigned char smem[];
     T *Bs = reinterpret_cast<T *>(smem);
-    double *red = reinterpret_cast<double *>(smem);
+    double *red = reinterpret_cast<double *>(smem + red_off);
 
     const int tid = threadIdx.x;
     // The wave index is uniform across the wave: keep it (and everything
@@ -704,7 +707,14 @@ mttkrp_tile_kernel(KParams p)
         typedef std::integral_constant<bool, true> yes;
         typedef std::integral_constant<bool, false> no;
         const bool v16 = (R % VW) == 0;
-        if (two) {
+        if (!stage_b) {
+            // B is in LDS already: only the tensor loads of the first steps.
+#pragma unroll
+            for (int u = 0; u < PD; ++u) {
+                load_step(abuf[u], wbuf[u], lc);
+                advance(lc);
+            }
+        } else if (two) {
             if (v16) stage(yes(), yes()); else stage(yes(), no());
         } else {
             if (v16) stage(no(), yes()); else stage(no(), no());
@@ -917,6 +927,31 @@ mttkrp_tile_kernel(KParams p)
             }
         }
     }
+}
+
+template <typename T, int MB, int NB, bool RC, bool VEC, bool FORM1, int W, int S>
+__global__ __launch_bounds__(64 * W, (tile_min_waves(sizeof(T), MB, NB, FORM1, S))) void
+mttkrp_tile_kernel(KParams p)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    tile_pass<T, MB, NB, RC, VEC, FORM1, W, S>(p, smem, true, 0);
+}
+
+// Two form-1 modes whose plans share the contraction group, the chunking,
+// the rank tiles and the workgroup decomposition (so every workgroup needs
+// the same B tile in both), one after the other in each workgroup of a
+// single launch: the B tile is staged once, and the second mode's work does
+// not wait for the first mode's last workgroups.  The reduction space sits
+// after the B tile.  (The passes are written out, not indexed at run time,
+// so the parameter blocks stay in scalar registers.)
+template <typename T, int MB, int NB, bool VEC, int W>
+__global__ __launch_bounds__(64 * W, (tile_min_waves(sizeof(T), MB, NB, true, 0))) void
+mttkrp_tile_multi_kernel(KPack pk)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    tile_pass<T, MB, NB, false, VEC, true, W, 0>(pk.p[0], smem, true, pk.red_off);
+    __syncthreads();
+    tile_pass<T, MB, NB, false, VEC, true, W, 0>(pk.p[1], smem, false, pk.red_off);
 }
 
 }  // namespace mttkrp

@@ -187,6 +187,15 @@ struct Plan {
     size_t ws_bytes = 0;
 };
 
+// Parameter blocks of the two modes one multi-mode launch runs in turn
+// (form 1, same B tile and decomposition); red_off: LDS byte offset of the
+// reduction space (after the B tile).
+constexpr int kMaxPasses = 2;
+struct KPack {
+    KParams p[kMaxPasses];
+    int64_t red_off;
+};
+
 // Fills `plan` for mode `mode`.  Returns 0 or a MTTKRP_* status.  Pure host
 // code: no HIP call.  Pointers in plan.kp are left null.
 int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_bytes, Plan &plan);

@@ -2,7 +2,7 @@
 // per workgroup, tile rows reduced against their factor rows); four waves
 // (mb = 2: nb <= 8; mb = 4: nb <= 2) or eight waves when two waves per
 // SIMD fit the registers; no outer slots (the item reduction reads the
-// outer factors).
+// outer factors).  Also the multi-mode launches of eight-wave form-1 plans.
 #include "mttkrp_tile.hpp"
 
 namespace mttkrp {
@@ -45,7 +45,30 @@ TileKernel sel(const Plan &pl)
            : pl.mb == 4 ? pick_nb<float, 4, false, true, 2, 4, S>(pl.nb, pl.vec)
                         : nullptr;
 }
+template <int MB, int NB>
+MultiKernel multi_vec(bool vec)
+{
+    if constexpr (tile_min_waves(sizeof(float), MB, NB, true, 0) != 2)
+        return nullptr;
+    else
+        return vec ? mttkrp_tile_multi_kernel<float, MB, NB, true, 8>
+                   : mttkrp_tile_multi_kernel<float, MB, NB, false, 8>;
+}
 }  // namespace
+
+MultiKernel select_multi_f32(const Plan &pl)
+{
+    if (pl.layout != 0 || pl.form != 1 || pl.waves != 8 || tile_slots(pl) != 0) return nullptr;
+    if (pl.mb == 2)
+        return pl.nb == 1 ? multi_vec<2, 1>(pl.vec)
+               : pl.nb == 2 ? multi_vec<2, 2>(pl.vec)
+               : pl.nb == 4 ? multi_vec<2, 4>(pl.vec)
+               : pl.nb == 8 ? multi_vec<2, 8>(pl.vec)
+                            : nullptr;
+    if (pl.mb == 4)
+        return pl.nb == 1 ? multi_vec<4, 1>(pl.vec) : pl.nb == 2 ? multi_vec<4, 2>(pl.vec) : nullptr;
+    return nullptr;
+}
 
 TileKernel select_tile_f32_form1(const Plan &pl)
 {

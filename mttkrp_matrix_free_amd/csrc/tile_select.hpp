@@ -18,6 +18,11 @@ TileKernel select_tile_f32_form0(const Plan &pl);
 TileKernel select_tile_f32_form1(const Plan &pl);
 TileKernel select_tile_f32_rows(const Plan &pl);
 
+// Multi-mode launches (several form-1 modes sharing a B tile, one pass each).
+typedef void (*MultiKernel)(KPack);
+MultiKernel select_multi_f64(const Plan &pl);
+MultiKernel select_multi_f32(const Plan &pl);
+
 inline int tile_slots(const Plan &pl) { return plan_slots(pl.form, pl.kp.nouter); }
 
 }  // namespace mttkrp
