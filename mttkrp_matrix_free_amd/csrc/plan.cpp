@@ -272,9 +272,12 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
     // Workgroup size: form 1 and the row-contiguous layout run eight waves per
     // workgroup (when a wave's registers allow two waves per SIMD), one
     // workgroup per compute unit, so one staged Khatri-Rao tile serves the
-    // whole unit and fewer splits (partial sums) are needed; otherwise four
-    // waves, two workgroups per compute unit.
-    p.waves = ((p.form == 1 || p.layout == 1) &&
+    // whole unit and fewer splits (partial sums) are needed -- when that tile
+    // is big enough (32 KiB) for its staging to matter; otherwise four waves,
+    // two workgroups per compute unit, which interleave better with the other
+    // stream's launch in an all-mode sweep (4-way fp32 rank 8: 442 -> 414 us).
+    const bool big_b = ceil_div(k.K, 16) * 16 * (16 * p.nb + 4) * elem_bytes >= 32 * 1024;
+    p.waves = ((p.form == 1 || p.layout == 1) && big_b &&
                tile_min_waves(elem_bytes, p.mb, p.nb, p.form == 1, plan_slots(p.form, k.nouter)) == 2)
                   ? 8
                   : 4;
