@@ -80,12 +80,22 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
     // (when that neighbour is free) so that the matrix-core K dimension is not
     // mostly padding; the merged Khatri-Rao tile must fit in LDS at one
     // 16-column rank block.
+    // fp32 at rank 64 and above also merges a last mode of at most 64 into a
+    // long contraction, chunked through LDS: an item then spans a chunk of
+    // many steps instead of 4, so its per-item work (decode, the multiplier,
+    // the fp64 flush) is spread over more matrix-core work (4-way fp32
+    // tensor: rank 512 modes 0-1 -5%, rank 64 mode 1 -5%; at rank 64 the
+    // output mode with a 4 MiB row stride lost 4%, so that case keeps the
+    // short contraction).
     const int64_t kMergeMax = (int64_t)(kLdsBudget / ((16 + 8) * (size_t)elem_bytes));
     auto choose_k = [&](int last) {
         int first = last;
-        if (dims[last] < 32 && last - 1 >= 0 && last - 1 != n &&
-            dims[last - 1] * dims[last] <= kMergeMax)
-            first = last - 1;
+        const bool free_left = last - 1 >= 0 && last - 1 != n;
+        const bool short_last =
+            free_left && dims[last] < 32 && dims[last - 1] * dims[last] <= kMergeMax;
+        const bool long_fp32 = elem_bytes == 4 && dims[last] <= 64 && rank >= 64 &&
+                               (rank >= 128 || S[n] <= (INT64_C(1) << 16));
+        if (free_left && (short_last || long_fp32)) first = last - 1;
         if (first == last) {
             k.k_mode0 = last;
             k.K = dims[last];

@@ -72,6 +72,7 @@ SWEEP = [
     ((64, 64, 96), 130, np.float32),     # several rank tiles, 8-block tiles in fp32
     ((17, 19, 23, 4), 19, np.float64),   # short last mode merged into the contraction
     ((9, 10, 11, 12, 13), 7, np.float32),
+    ((24, 20, 50, 48), 72, np.float32),  # fp32 long merged contraction: 9 chunks, ragged last
 ]
 
 
