@@ -244,14 +244,27 @@ __device__ __forceinline__ void tile_pass(const KParams &p, unsigned char *smem,
         colok[nb] = col[nb] < R;
     }
 
-    // Work range of this workgroup: items [it_lo, it_hi), each of nkc steps.
-    // The waves split the flattened step sequence evenly; a wave's range may
-    // start or end inside an item (every item result is linear in its steps,
-    // so a partial item is reduced like a whole one).
-    // (below 2^31: the planner bounds items and steps of a workgroup)
-    const int it_lo = (int)(isplit * p.chunk);
-    const int it_hi = (int)min(p.nitems, (int64_t)it_lo + p.chunk);
-    const int wg_steps = it_hi > it_lo ? (it_hi - it_lo) * nkc : 0;
+    // Work range of this workgroup: steps [g_lo, g_lo + wg_steps) of the
+    // unit's sequence of (item, step) pairs, nkc steps per item.  Form 0 cuts
+    // the sequence into nsplit_it equal ranges; form 1 into ranges of whole
+    // items (p.chunk items each), because every item a range touches costs a
+    // row reduction.  The waves split the workgroup's range evenly in turn.  A
+    // range may start or end inside an item (every item result is linear in
+    // its steps, so a partial item is reduced like a whole one).
+    // (below 2^31: the planner bounds the unit's steps)
+    const int tot_steps = (int)p.nitems * nkc;
+    int g_lo, wg_steps;
+    if (FORM1) {
+        const int it_lo = min((int)p.nitems, (int)(isplit * p.chunk));
+        const int it_hi = min((int)p.nitems, it_lo + (int)p.chunk);
+        g_lo = it_lo * nkc;
+        wg_steps = (it_hi - it_lo) * nkc;
+    } else {
+        const int wg_chunk =
+            (int)fdiv((uint32_t)(tot_steps + (int)p.fd_nsplit_it.d - 1), p.fd_nsplit_it);
+        g_lo = min(tot_steps, (int)isplit * wg_chunk);
+        wg_steps = min(tot_steps, g_lo + wg_chunk) - g_lo;
+    }
     const int per_wave = (wg_steps + W - 1) / W;
     const int s_lo = min(wg_steps, wave * per_wave);
     const int s_hi = min(wg_steps, s_lo + per_wave);
@@ -587,8 +600,8 @@ __device__ __forceinline__ void tile_pass(const KParams &p, unsigned char *smem,
     for (int v = 0; v < NV; ++v) lc.vo[v] = kOOB;
 #pragma unroll
     for (int j = 0; j < 3; ++j) lc.orow[j] = 0;
-    lc.it = it_lo + (int)fdiv((uint32_t)s_lo, fd_nkc);
-    lc.kc = s_lo - (lc.it - it_lo) * nkc;
+    lc.it = (int)fdiv((uint32_t)(g_lo + s_lo), fd_nkc);
+    lc.kc = g_lo + s_lo - lc.it * nkc;
     lc.step = s_lo;
     lc.live = false;
     enter_item(lc);

@@ -347,12 +347,23 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
     const int64_t resident = per_cu * kNumCU;
     (void)b_tile;
     // The split that best fills whole rounds of resident workgroups (the
-    // smallest one among equals), up to two rounds' worth.
+    // smallest one among equals), up to two rounds' worth.  Form 0 cuts the
+    // unit's sequence of (item, step) pairs into equal ranges, not whole
+    // items, so every workgroup of a round has the same work (each range
+    // keeps at least two steps per wave; 5-way trailing rows: 50 items in 6
+    // ranges, 90 -> 87 us).  Form 1 keeps whole items per range: every item a
+    // range touches costs a row reduction (5-way modes 0-2: +4% otherwise).
+    const int64_t unit_steps = k.nitems * (k.Kc / 16);
     int64_t want = 1;
     {
-        const int64_t wmax = std::max<int64_t>(1, std::min<int64_t>(k.nitems, ceil_div(2 * resident, base)));
-        auto util = [&](int64_t w) {  // with the split the chunk rounding yields
-            const int64_t g = base * ceil_div(k.nitems, ceil_div(k.nitems, w));
+        const int64_t wmax =
+            p.form == 1
+                ? std::max<int64_t>(1, std::min<int64_t>(k.nitems, ceil_div(2 * resident, base)))
+                : std::max<int64_t>(1, std::min<int64_t>(unit_steps / (2 * p.waves),
+                                                         ceil_div(2 * resident, base)));
+        auto util = [&](int64_t w) {
+            const int64_t g =
+                p.form == 1 ? base * ceil_div(k.nitems, ceil_div(k.nitems, w)) : base * w;
             return (double)g / (double)(ceil_div(g, resident) * resident);
         };
         double best = 0.0;
@@ -367,8 +378,13 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
     const int64_t cap_traffic = std::max<int64_t>(
         1, (N * elem_bytes / 8) / std::max<int64_t>(1, 2 * out_bytes * k.nkch));
     want = std::min<int64_t>(want, std::min<int64_t>(cap_traffic, 1024));
-    k.chunk = std::max<int64_t>(1, ceil_div(k.nitems, want));
-    k.nsplit_it = ceil_div(k.nitems, k.chunk);
+    if (p.form == 1) {
+        k.chunk = std::max<int64_t>(1, ceil_div(k.nitems, want));  // items per workgroup
+        k.nsplit_it = ceil_div(k.nitems, k.chunk);
+    } else {
+        k.nsplit_it = want;
+        k.chunk = ceil_div(unit_steps, want);  // steps per workgroup (full contraction chunk)
+    }
     k.nsplit = k.nsplit_it * k.nkch;
     k.grid_real = k.nunits * k.nsplit * k.nrtiles;
     k.grid_per_xcd = ceil_div(k.grid_real, kNumXCD);
@@ -408,7 +424,7 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
         const int64_t lim = INT64_C(1) << 31;
         const int64_t nkc_full = k.Kc / 16;
         if (k.K >= lim || k.nrows >= lim || k.nbatch >= lim || k.nitems >= lim ||
-            k.chunk * nkc_full >= lim || k.IrB >= lim || k.IkB >= lim)
+            k.nitems * nkc_full + k.nsplit_it >= lim || k.IrB >= lim || k.IkB >= lim)
             return MTTKRP_ERANGE;
         const int64_t klast = k.K - (k.nkch - 1) * k.Kc;
         k.fd_nrtiles = make_fastdiv(k.nrtiles);

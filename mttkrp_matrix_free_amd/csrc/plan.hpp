@@ -136,7 +136,7 @@ struct KParams {
     int64_t nunits;            // form 1: I_n; form 0: row tiles of the output
     int64_t nrowtiles;         // form 1: row tiles per batch
     int64_t nitems;            // work items per unit (form 1: batches x row tiles; form 0: batches)
-    int64_t chunk;             // items per workgroup
+    int64_t chunk;             // form 1: items per workgroup; form 0: steps (full chunk)
     int64_t nsplit;            // partial outputs per unit: nsplit_it * nkch
     int64_t nsplit_it;         // chunks of the work items per unit
     int64_t nrtiles;           // rank tiles
