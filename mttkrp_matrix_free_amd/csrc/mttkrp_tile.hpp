@@ -29,8 +29,9 @@
 //     and feeds them to four successive MFMA k-steps; the k order inside the
 //     matrix-core reduction is permuted consistently for A and B, which leaves
 //     the sum unchanged;
-//   layout 1 (rows contiguous, output = last mode): a lane holds four
-//     consecutive rows at one k and feeds four interleaved 16-row blocks.
+//   layout 1 (rows contiguous, output = last mode): a lane holds RL = 4 (or,
+//     for 32-row tiles, 2) consecutive rows at one k and feeds RL interleaved
+//     16-row blocks.
 //
 // 16x16x4 MFMA lane layout (CDNA3/CDNA4): lane l supplies A(row l%16, k l/16)
 // and B(k l/16, col l%16), and receives D(Mfma<T>::row(l/16, e), l%16) in
@@ -123,6 +124,21 @@ __device__ __forceinline__ void bload4(__amdgpu_buffer_rsrc_t r, unsigned voff, 
     v[2] = a[2];
     v[3] = a[3];
 }
+// Two consecutive elements at byte offset voff (+ soff).
+__device__ __forceinline__ void bload2(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff,
+                                       double *v)
+{
+    const dx2 a = __builtin_bit_cast(dx2, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+    v[0] = a[0];
+    v[1] = a[1];
+}
+__device__ __forceinline__ void bload2(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff,
+                                       float *v)
+{
+    const fx2 a = __builtin_bit_cast(fx2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+    v[0] = a[0];
+    v[1] = a[1];
+}
 // One element at byte offset voff (+ soff).
 __device__ __forceinline__ double bload1(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff,
                                          double)
@@ -190,13 +206,15 @@ __device__ __forceinline__ void tile_pass(const KParams &p, unsigned char *smem,
     static_assert(!FORM1 || S == 0, "form 1 reads its outer factors once per item");
     constexpr int SS = S > 0 ? S : 1;  // array extent
     constexpr int NT = 64 * W;  // threads of the workgroup (W waves)
-    static_assert(!RC || (MB % 4 == 0), "row-contiguous layout uses 64-row groups");
+    static_assert(!RC || MB == 2 || MB % 4 == 0, "row-contiguous layout: 32- or 64-row groups");
     static_assert(!RC || !FORM1, "row-contiguous layout has the output as rows");
     static_assert(W == 4 || W == 8, "four or eight waves");
     typedef typename Mfma<T>::acc_t acc_t;
     constexpr int BN = 16 * NB;
     constexpr int ROWS = 16 * MB;
-    constexpr int G = MB / 4;   // 64-row groups (layout 1)
+    // layout 1: a lane holds RL consecutive rows of each 16*RL-row group
+    constexpr int RL = MB < 4 ? MB : 4;
+    constexpr int G = MB / RL;  // row groups
     constexpr int NA = 4 * MB;  // tensor elements per lane per step
     constexpr unsigned SZ = sizeof(T);
 
@@ -315,8 +333,9 @@ __device__ __forceinline__ void tile_pass(const KParams &p, unsigned char *smem,
         for (int s = 0; s < 4; ++s)
 #pragma unroll
             for (int g = 0; g < G; ++g)
-                vbase[s * G + g] =
-                    (unsigned)(((int64_t)(64 * g + 4 * c16) + (int64_t)(4 * s + q) * p.k_stride) * SZ);
+                vbase[s * G + g] = (unsigned)(((int64_t)(16 * RL * g + RL * c16) +
+                                               (int64_t)(4 * s + q) * p.k_stride) *
+                                              SZ);
     }
     // Row validity (form 0: fixed for the workgroup; form 1: per item).
     // With two non-adjacent row modes the offsets depend on the item's first
@@ -337,7 +356,8 @@ __device__ __forceinline__ void tile_pass(const KParams &p, unsigned char *smem,
             for (int s = 0; s < 4; ++s)
 #pragma unroll
                 for (int g = 0; g < G; ++g)
-                    vo[s * G + g] = (out_row0 + 64 * g + 4 * c16 < p.In) ? vbase[s * G + g] : kOOB;
+                    vo[s * G + g] =
+                        (out_row0 + 16 * RL * g + RL * c16 < p.In) ? vbase[s * G + g] : kOOB;
         }
     };
 
@@ -408,15 +428,18 @@ __device__ __forceinline__ void tile_pass(const KParams &p, unsigned char *smem,
                 const bool kin = lc.live && (4 * s + q < krem);
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
-                    T *dst = a + (s * G + g) * 4;
+                    T *dst = a + (s * G + g) * RL;
                     const unsigned vo = kin ? lc.vo[s * G + g] : kOOB;
                     if (VEC) {
-                        bload4(rsrc, vo, soff, dst);
+                        if (RL == 4)
+                            bload4(rsrc, vo, soff, dst);
+                        else
+                            bload2(rsrc, vo, soff, dst);
                     } else {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
+                        for (int e = 0; e < RL; ++e)
                             dst[e] = bload1(rsrc,
-                                            (vo != kOOB && out_row0 + 64 * g + 4 * c16 + e < p.In)
+                                            (vo != kOOB && out_row0 + 16 * RL * g + RL * c16 + e < p.In)
                                                 ? vo + e * SZ
                                                 : kOOB,
                                             soff, T(0));
@@ -480,9 +503,9 @@ __device__ __forceinline__ void tile_pass(const KParams &p, unsigned char *smem,
 #pragma unroll
                     for (int g = 0; g < G; ++g)
 #pragma unroll
-                        for (int jj = 0; jj < 4; ++jj)
-                            acc[4 * g + jj][nb] =
-                                Mfma<T>::mma(a[(s * G + g) * 4 + jj], b[nb], acc[4 * g + jj][nb]);
+                        for (int jj = 0; jj < RL; ++jj)
+                            acc[RL * g + jj][nb] =
+                                Mfma<T>::mma(a[(s * G + g) * RL + jj], b[nb], acc[RL * g + jj][nb]);
             }
         }
     };
@@ -868,7 +891,7 @@ __device__ __forceinline__ void tile_pass(const KParams &p, unsigned char *smem,
             if (!RC)
                 row = out_row0 + mb * 16 + Mfma<T>::row(ln >> 4, e);
             else
-                row = out_row0 + 64 * (mb / 4) + 4 * Mfma<T>::row(ln >> 4, e) + (mb % 4);
+                row = out_row0 + 16 * RL * (mb / RL) + RL * Mfma<T>::row(ln >> 4, e) + (mb % RL);
             if (row < p.In && c < R) {
                 if (split_out) {
                     p.partial[(split * p.In + row) * R + c] = v;

@@ -262,14 +262,18 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
     if (p.layout == 1) {
         p.mb = 4;
         // Trailing-rows tiles (a short block of rows, many contraction steps)
-        // keep the matrix cores fed only with two waves per SIMD: when four
-        // rank blocks do not fit the registers for that, two do, at the cost
-        // of one more pass over X per rank tile (served from the caches when
-        // X is small enough to stay there).
-        if (k.tr && p.nb == 4 &&
-            tile_min_waves(elem_bytes, 4, 4, false, plan_slots(0, k.nouter)) == 1 &&
-            tile_min_waves(elem_bytes, 4, 2, false, plan_slots(0, k.nouter)) == 2)
-            p.nb = 2;
+        // keep the matrix cores fed only with two waves per SIMD.  When four
+        // rank blocks of 64 rows do not fit the registers for that, 32-row
+        // tiles with four rank blocks are taken: every 64 rank columns then
+        // read X once, and a short row block is padded less (200 rows: 224
+        // instead of 256).  Failing that, 64-row tiles with two rank blocks.
+        const int sl = plan_slots(0, k.nouter);
+        if (k.tr && p.nb == 4 && tile_min_waves(elem_bytes, 4, 4, false, sl) == 1) {
+            if (tile_min_waves(elem_bytes, 2, 4, false, sl) == 2)
+                p.mb = 2;
+            else if (tile_min_waves(elem_bytes, 4, 2, false, sl) == 2)
+                p.nb = 2;
+        }
     } else if (p.nb > 4) {
         p.mb = 2;
     } else if (p.form == 1) {
@@ -326,7 +330,6 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
     // workgroup share its steps evenly, so a chunk may hold any number of
     // items.
     const size_t b_tile = (size_t)k.Kc * k.bpitch * elem_bytes;
-    const int64_t base = k.nunits * k.nrtiles * k.nkch;
     // Workgroups resident at once: by waves (two or one per SIMD, from the
     // register model) and by LDS.  A grid that needs a second, partial round
     // leaves most of the chip idle in it, so the split is rounded down to
@@ -353,6 +356,34 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
     // keeps at least two steps per wave; 5-way trailing rows: 50 items in 6
     // ranges, 90 -> 87 us).  Form 1 keeps whole items per range: every item a
     // range touches costs a row reduction (5-way modes 0-2: +4% otherwise).
+    // Trailing-rows plans have few units and few, long items (the outer
+    // tuples): their contraction is cut into more chunks than LDS requires
+    // when that fills the rounds better (fewer chunks among equals).
+    // (Each chunk count is paired with the best split of the items into
+    // 1..4 step ranges, up to two rounds of workgroups; among equal fills the
+    // fewest partial outputs win.)
+    if (k.tr) {
+        int64_t best_kc = k.Kc, best_parts = 0;
+        double best_u = -1.0;
+        const int64_t nk0 = k.nkch;
+        for (int64_t nk = nk0; nk <= std::max<int64_t>(nk0, 64); ++nk) {
+            const int64_t kc = ceil_div(ceil_div(k.K, nk), 16) * 16;
+            const int64_t nke = ceil_div(k.K, kc);
+            for (int64_t w = 1; w <= 4; ++w) {
+                const int64_t g = k.nunits * k.nrtiles * nke * w;
+                if (g > 2 * resident && !(nk == nk0 && w == 1)) continue;
+                const double u = (double)g / (double)(ceil_div(g, resident) * resident);
+                if (u > best_u + 0.01 || (u > best_u - 0.01 && nke * w < best_parts)) {
+                    best_u = std::max(best_u, u);
+                    best_kc = kc;
+                    best_parts = nke * w;
+                }
+            }
+        }
+        k.Kc = best_kc;
+        k.nkch = ceil_div(k.K, k.Kc);
+    }
+    const int64_t base = k.nunits * k.nrtiles * k.nkch;
     const int64_t unit_steps = k.nitems * (k.Kc / 16);
     int64_t want = 1;
     {
@@ -439,7 +470,7 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
         k.fd_IkB = make_fastdiv(k.IkB);
     }
 
-    p.lds_bytes = lds_est;
+    p.lds_bytes = std::max((size_t)k.Kc * k.bpitch * elem_bytes, red);
     k.to_partial = (k.nsplit > 1 || k.tr) ? 1 : 0;
     p.ws_bytes = k.to_partial ? (size_t)k.nsplit * (size_t)out_bytes : 0;
     p.ws_bytes = (p.ws_bytes + 255) / 256 * 256;

@@ -1,6 +1,7 @@
 // Tile-kernel instantiations: f32, layout 1 (rows contiguous, output = the
 // unit-stride mode), form 0; four waves or eight (when two waves per SIMD
-// fit the registers), 64-row groups (mb = 4), nb <= 4;
+// fit the registers), 64-row groups (mb = 4) with nb <= 4, or 32-row
+// groups (mb = 2) with nb = 4;
 // one or three outer slots.
 #include "mttkrp_tile.hpp"
 
@@ -35,6 +36,14 @@ TileKernel pick_nb(int nb, bool vec)
 template <int S>
 TileKernel sel(const Plan &pl)
 {
+    // 32-row tiles (mb = 2) with four rank blocks: short trailing row blocks,
+    // where 64-row tiles would be mostly padding or need two rank tiles.
+    if (pl.mb == 2) {
+        if (pl.nb != 4) return nullptr;
+        return pl.waves == 8   ? pick_vec<float, 2, 4, true, false, 8, S>(pl.vec)
+               : pl.waves == 4 ? pick_vec<float, 2, 4, true, false, 4, S>(pl.vec)
+                               : nullptr;
+    }
     if (pl.mb != 4) return nullptr;
     if (pl.waves == 8) return pick_nb<float, 4, true, false, 4, 8, S>(pl.nb, pl.vec);
     return pl.waves == 4 ? pick_nb<float, 4, true, false, 4, 4, S>(pl.nb, pl.vec) : nullptr;

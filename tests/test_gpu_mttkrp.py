@@ -142,6 +142,33 @@ def test_fourway_f32_sampled(R):
     assert all(e <= 1e-5 for e in errs.values()), errs
 
 
+TRAILING = [
+    ((37, 41, 23, 19, 7), 64, np.float64),   # 133 rows: ragged 32-row tiles, scalar loads
+    ((37, 41, 23, 20, 6), 80, np.float32),   # 120 rows, vector loads, ragged rank tile
+    ((31, 29, 17, 24, 40), 64, np.float64),  # 960 rows
+]
+
+
+@pytest.mark.parametrize("dims,R,dt", TRAILING, ids=[f"{'x'.join(map(str, d))}-R{r}-{np.dtype(t).name}"
+                                                     for d, r, t in TRAILING])
+def test_trailing_rows_32row_tiles(dims, R, dt):
+    """Outputs that are one of the two short trailing modes: the tile rows are
+    the contiguous block of the last two modes, in 32-row tiles, and the
+    contraction is cut into many chunks."""
+    p = inputs.random_problem(dims, R, dtype=dt, seed=sum(dims) + R)
+    d = len(dims)
+    tdt = torch.float64 if dt == np.float64 else torch.float32
+    modes = [n for n in (d - 2, d - 1) if api.plan(dims, R, n, tdt)["rows"] == dims[-2] * dims[-1]]
+    assert modes, "no trailing-rows plan for this shape"
+    for n in modes:
+        pl = api.plan(dims, R, n, tdt)
+        assert pl["layout"] == 1 and pl["mb"] == 2 and pl["nb"] == 4 and pl["kchunks"] > 1, pl
+    errs = run_modes(p, modes=modes)
+    say("  errors", errs)
+    for n, e in errs.items():
+        assert e <= TOL[np.dtype(dt)], (dims, R, n, e)
+
+
 def test_fiveway_workload_full():
     p = inputs.fiveway_als()
     errs = run_modes(p)
