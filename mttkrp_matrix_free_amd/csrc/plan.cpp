@@ -302,7 +302,12 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
     // whose results are summed by the reduction pass.
     // LDS pitch of B rows: a lane group of four reads rows 4 apart, so the
     // pitch is padded (4 elements) to put those rows on different banks.
-    const int bpitch = 16 * p.nb + 4;
+    // In the row-contiguous layout the four lane groups read consecutive
+    // rows instead: for fp32 a pitch of 16 (mod 32) elements puts each pair
+    // of groups on disjoint banks (with a pad of 4, the 4-way fp32 R=64 mode-3
+    // kernel stalled half a cycle per MFMA on bank conflicts).
+    const int bpitch =
+        16 * p.nb + ((p.layout == 1 && elem_bytes == 4) ? (p.nb % 2 ? 32 : 16) : 4);
     const int64_t Kpad = ceil_div(k.K, 16) * 16;
     const int64_t kc_max = (int64_t)(lds_budget / ((size_t)bpitch * elem_bytes)) / 16 * 16;
     if (kc_max < 16) return MTTKRP_ERANGE;
