@@ -387,12 +387,18 @@ __device__ __forceinline__ void tile_pass(const KParams &p, unsigned char *smem,
     int colc[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) colc[nb] = colok[nb] ? col[nb] : 0;
-    // Outer factors; unused slots read the first row of the contraction
-    // factor (always present) and count as 1 in the product.
-    const T *Uo[SS];
+    // Outer factors, read through buffer descriptors: the lane's column is a
+    // fixed vector offset and the item's row a scalar offset, so a step's
+    // factor loads need no address arithmetic.  Unused slots have an empty
+    // range (their loads return zero) and count as 1 in the product.
+    __amdgpu_buffer_rsrc_t ro[SS];
 #pragma unroll
     for (int j = 0; j < SS; ++j)
-        Uo[j] = reinterpret_cast<const T *>(j < p.nouter ? p.Uo[j] : p.Uk0);
+        ro[j] = make_rsrc(j < p.nouter ? p.Uo[j] : p.Uk0,
+                          j < p.nouter ? p.o_dim[j] * R * (int64_t)SZ : 0);
+    unsigned ocol[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) ocol[nb] = (unsigned)colc[nb] * SZ;
 
     // Issue the loads of the cursor's step: its three outer factor values
     // (whose product is the multiplier W_o of the step's item) into wq, then
@@ -401,9 +407,11 @@ __device__ __forceinline__ void tile_pass(const KParams &p, unsigned char *smem,
     // branch; the product is formed only when the step is used.
     auto load_step = [&](T *a, T (*wq)[NB], const LoadCursor &lc) {
 #pragma unroll
-        for (int j = 0; j < S; ++j)
+        for (int j = 0; j < S; ++j) {
+            const unsigned srow = (unsigned)(lc.orow[j] * SZ);
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) wq[j][nb] = Uo[j][lc.orow[j] + colc[nb]];
+            for (int nb = 0; nb < NB; ++nb) wq[j][nb] = bload1(ro[j], ocol[nb], srow, T(0));
+        }
         const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(X + lc.base, (x_elems - lc.base) * (int64_t)SZ);
         const int krem = (int)Kloc - lc.kc * 16;  // contraction elements left in this item
         if (!RC) {

@@ -448,6 +448,9 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
             if (k.r_mode1 >= 0 && (k.IrB * rank + 16) * elem_bytes >= (INT64_C(1) << 31))
                 return MTTKRP_ERANGE;
         }
+        // Outer factors are read through descriptors over the whole factor.
+        for (int j = 0; j < k.nouter; ++j)
+            if ((k.o_dim[j] * rank + 16) * elem_bytes >= (INT64_C(1) << 31)) return MTTKRP_ERANGE;
         const int64_t rows_a = (k.k_mode1 >= 0) ? k.Kc / k.IkB + 2 : k.Kc;
         if ((rows_a * rank + 16) * elem_bytes >= (INT64_C(1) << 31)) return MTTKRP_ERANGE;
         if ((k.k_mode1 >= 0) && (k.IkB * rank + 16) * elem_bytes >= (INT64_C(1) << 31))
