@@ -605,16 +605,21 @@ __device__ __forceinline__ void tile_pass(const KParams &p, unsigned char *smem,
                 for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = acc_t{};
         } else if (FLUSH64) {
             // The item's tile, weighted by its outer multiplier (from the
-            // factor values buffered with its last step), joins the fp64 sums.
+            // factor values buffered with its last step), joins the fp64 sums
+            // (the product formed in fp64).
             T w[NB];
             multiplier(wq, w);
+            double wd[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) wd[nb] = (double)w[nb];
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        acc64[mb][nb][e] += (double)(w[nb] * acc[mb][nb][e]);
+                        acc64[mb][nb][e] =
+                            __builtin_fma((double)acc[mb][nb][e], wd[nb], acc64[mb][nb][e]);
                     acc[mb][nb] = acc_t{};
                 }
         }
