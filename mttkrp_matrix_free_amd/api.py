@@ -133,7 +133,9 @@ def mttkrp(X: torch.Tensor, factors: Sequence[Optional[torch.Tensor]], mode: int
 def mttkrp_all(X: torch.Tensor, factors: Sequence[torch.Tensor],
                outs: Optional[List[torch.Tensor]] = None, ws: Optional[torch.Tensor] = None,
                stream=None) -> List[torch.Tensor]:
-    """MTTKRP of every mode, in mode order, on one stream."""
+    """MTTKRP of every mode, ordered on the caller's stream (a long sweep also
+    runs part of its modes on a second stream, forked from and joined back to
+    the caller's)."""
     _check_tensor(X)
     R = _check_factors(X, factors)
     sfx, eb = _DT[X.dtype]

@@ -273,3 +273,35 @@ def test_workspace_reuse_across_calls():
     for n in (2, 0, 1, 2):
         M = api.mttkrp(X, U, n, ws=ws).cpu().numpy()
         assert rel_fro(M, oracle.mttkrp(p.X, p.factors, n, nthreads=NT)) <= 1e-12
+
+
+def test_two_stream_sweep_orders_with_caller_stream():
+    """A long all-mode sweep runs on the caller's stream and a second stream;
+    work queued on the caller's stream after the call must see every output
+    complete, and work queued before it must finish before the sweep reads its
+    inputs."""
+    p = inputs.fiveway_als()
+    X = dev(p.X)
+    U = [dev(u) for u in p.factors]
+    ref = [api.mttkrp(X, U, n) for n in range(5)]
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    outs = [torch.zeros_like(r) for r in ref]
+    ws = torch.empty(api.all_workspace_bytes(X.shape, p.rank, X.dtype), dtype=torch.uint8,
+                     device="cuda")
+    U2 = [torch.zeros_like(u) for u in U]
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            # factors written on the caller's stream right before the call
+            for a, b in zip(U2, U):
+                a.copy_(b)
+            api.mttkrp_all(X, U2, outs=outs, ws=ws, stream=s)
+            # read back on the caller's stream right after the call
+            copies = [o.clone() for o in outs]
+            for o in outs:
+                o.zero_()
+            for a in U2:
+                a.zero_()
+    s.synchronize()
+    for n in range(5):
+        assert torch.equal(copies[n], ref[n]), n
