@@ -528,11 +528,17 @@ __device__ __forceinline__ void tile_pass(const KParams &p, unsigned char *smem,
         if (FORM1) {
             // The item's outer multiplier W_o (needed once per item, so read
             // here rather than with every step's tensor loads).
+            // (Only the outer modes the plan has are read.)
             T wv[3][NB];
 #pragma unroll
-            for (int j = 0; j < 3; ++j)
+            for (int j = 0; j < 3; ++j) {
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) wv[j][nb] = Uf[j][orow[j] + colc[nb]];
+                for (int nb = 0; nb < NB; ++nb) wv[j][nb] = T(1);
+                if (j < p.nouter) {
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) wv[j][nb] = Uf[j][orow[j] + colc[nb]];
+                }
+            }
             // Reduce the tile rows against their factor rows and the outer
             // multiplier, one accumulator row g = (mb, e) at a time.  The
             // factor loads of row g + 1 are issued before row g is used, so
