@@ -200,9 +200,9 @@ template <typename T, int MB, int NB, bool RC, bool VEC, bool FORM1, int W, int 
 __device__ __forceinline__ void tile_pass(const KParams &p, unsigned char *smem, bool stage_b,
                                           size_t red_off)
 {
-    // S: outer-factor slots carried per step (0: no outer mode; else up to S
-    // outer modes, unused slots count as 1).
-    static_assert(S == 0 || S == 1 || S == 3, "outer slots");
+    // S: outer-factor slots carried per step (0: no outer mode; else one per
+    // outer mode, with unused slots counting as 1).
+    static_assert(S >= 0 && S <= 3, "outer slots");
     static_assert(!FORM1 || S == 0, "form 1 reads its outer factors once per item");
     constexpr int SS = S > 0 ? S : 1;  // array extent
     constexpr int NT = 64 * W;  // threads of the workgroup (W waves)

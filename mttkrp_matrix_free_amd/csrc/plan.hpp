@@ -39,11 +39,11 @@ constexpr size_t kLdsBudget = 80 * 1024;       // dynamic LDS of a 4-wave workgr
 constexpr size_t kLdsBudgetWide = 144 * 1024;  // dynamic LDS of an 8-wave workgroup (1 per CU)
 
 // Outer-factor slots a tile kernel carries per step: none for form 1 (its
-// outer multiplier is read once per item, at the item's reduction), else 1
-// (at most one outer mode) or 3.
+// outer multiplier is read once per item, at the item's reduction), else one
+// per outer mode (at least one).
 __host__ __device__ constexpr int plan_slots(int form, int nouter)
 {
-    return form == 1 ? 0 : (nouter <= 1 ? 1 : 3);
+    return form == 1 ? 0 : (nouter <= 1 ? 1 : nouter);
 }
 
 // Register estimate of a tile kernel (per lane, 32-bit registers): the

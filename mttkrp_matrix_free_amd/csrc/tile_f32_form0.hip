@@ -1,6 +1,6 @@
 // Tile-kernel instantiations: f32, layout 0 (contraction index contiguous),
 // form 0 (tile rows are the output rows); four waves, mb = 2 (nb <= 8) or
-// mb = 4 (nb <= 2); one or three outer slots.
+// mb = 4 (nb <= 2); one to three outer slots.
 #include "mttkrp_tile.hpp"
 
 namespace mttkrp {
@@ -44,7 +44,7 @@ TileKernel select_tile_f32_form0(const Plan &pl)
 {
     if (pl.layout != 0 || pl.form != 0 || pl.waves != 4) return nullptr;
     const int s = tile_slots(pl);
-    return s == 1 ? sel<1>(pl) : s == 3 ? sel<3>(pl) : nullptr;
+    return s == 1 ? sel<1>(pl) : s == 2 ? sel<2>(pl) : s == 3 ? sel<3>(pl) : nullptr;
 }
 
 }  // namespace mttkrp

@@ -2,7 +2,7 @@
 // unit-stride mode), form 0; four waves or eight (when two waves per SIMD
 // fit the registers), 64-row groups (mb = 4) with nb <= 4, or 32-row
 // groups (mb = 2) with nb = 4;
-// one or three outer slots.
+// one to three outer slots.
 #include "mttkrp_tile.hpp"
 
 namespace mttkrp {
@@ -54,7 +54,7 @@ TileKernel select_tile_f64_rows(const Plan &pl)
 {
     if (pl.layout != 1 || pl.form != 0) return nullptr;
     const int s = tile_slots(pl);
-    return s == 1 ? sel<1>(pl) : s == 3 ? sel<3>(pl) : nullptr;
+    return s == 1 ? sel<1>(pl) : s == 2 ? sel<2>(pl) : s == 3 ? sel<3>(pl) : nullptr;
 }
 
 }  // namespace mttkrp
