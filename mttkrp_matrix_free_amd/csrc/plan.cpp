@@ -366,7 +366,8 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
     // when that fills the rounds better (fewer chunks among equals).
     // (Each chunk count is paired with the best split of the items into
     // 1..4 step ranges, up to two rounds of workgroups; among equal fills the
-    // fewest partial outputs win.)
+    // fewest partial outputs win, and among those the shortest chunks, whose
+    // B tiles are the quickest to stage.)
     if (k.tr) {
         int64_t best_kc = k.Kc, best_parts = 0;
         double best_u = -1.0;
@@ -378,7 +379,7 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
                 const int64_t g = k.nunits * k.nrtiles * nke * w;
                 if (g > 2 * resident && !(nk == nk0 && w == 1)) continue;
                 const double u = (double)g / (double)(ceil_div(g, resident) * resident);
-                if (u > best_u + 0.01 || (u > best_u - 0.01 && nke * w < best_parts)) {
+                if (u > best_u + 0.01 || (u > best_u - 0.01 && nke * w <= best_parts)) {
                     best_u = std::max(best_u, u);
                     best_kc = kc;
                     best_parts = nke * w;
