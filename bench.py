@@ -84,6 +84,7 @@ def main():
                     choices=["c1", "c2", "c3", "c4r8", "c4r64", "c4r512", "c5"])
     ap.add_argument("--cold-reps", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-als", action="store_true", help="skip the CP-ALS timing (5-way workload)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
@@ -265,6 +266,41 @@ def main():
                          f"({t_cpu:.1f} s; long-double oracle, OpenMP over rows)"}
         log(f"[bench] cpu oracle {cpu}")
 
+    # ---- CP-ALS (the workload that is a CP-ALS run): time per iteration of the
+    # whole driver (per mode: MTTKRP, Hadamard of Grams, Cholesky, row
+    # solves, normalization, Gram refresh; then the fit, one read-back), and
+    # the share of it that the per-mode MTTKRP launches take ----
+    als = None
+    if p.als_iters and not args.no_als:
+        iters = 10
+        ws_als = torch.empty(api.cp_als_workspace_bytes(dims, R, X.dtype), dtype=torch.uint8,
+                             device=dev)
+        U0 = [u.clone() for u in U]
+        Ua = [u.clone() for u in U0]
+        api.cp_als(X, Ua, iters=2, ws=ws_als, stream=stream)  # warm-up
+        torch.cuda.synchronize()
+        Ua = [u.clone() for u in U0]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        _, hist, done, st = api.cp_als(X, Ua, iters=iters, ws=ws_als, stream=stream)
+        torch.cuda.synchronize()
+        t_als = (time.perf_counter() - t0) / max(1, done)
+        # the same iterations' MTTKRP launches alone, mode after mode on one
+        # stream as the driver issues them
+        ev_c = torch.cuda.Event(enable_timing=True)
+        ev_d = torch.cuda.Event(enable_timing=True)
+        ev_c.record(stream)
+        for _ in range(iters):
+            for n in range(d):
+                api.mttkrp(X, Ua, n, out=outs[n], ws=ws, stream=stream)
+        ev_d.record(stream)
+        torch.cuda.synchronize()
+        t_mt = ev_c.elapsed_time(ev_d) / 1e3 / iters
+        als = {"ms_per_iter": round(t_als * 1e3, 4), "iters": int(done), "status": int(st),
+               "final_fit": round(float(hist[done - 1]), 6) if done else None,
+               "mttkrp_ms_per_iter": round(t_mt * 1e3, 4),
+               "mttkrp_share": round(t_mt / t_als, 3)}
+
     cfg = {"workload": p.name, "dims": list(dims), "rank": R, "modes": list(range(d)),
            "step": "all-mode MTTKRP sweep", "cache": "warm (back-to-back sweeps)"}
     line = {
@@ -285,6 +321,7 @@ def main():
         "roofline": roof,
         "cold_cache": cold,
         "cpu_baseline": cpu,
+        "cp_als": als,
     }
     print(json.dumps(line), flush=True)
 

@@ -94,33 +94,47 @@ __global__ __launch_bounds__(1024) void als_chol_kernel(const double *__restrict
     __shared__ int fail;
     const int tid = threadIdx.x, nt = blockDim.x;
     const int64_t RR = R * R;
+    // Row pitch of A: R + 1 in LDS (a column read by consecutive threads
+    // then falls on different banks), R in the global fallback.
+    const int64_t P = use_lds ? R + 1 : R;
     for (int64_t e = tid; e < RR; e += nt) {
         double v = 1.0;
         for (int m = 0; m < order; ++m)
             if (m != n) v *= Gall[(int64_t)m * RR + e];
-        A[e] = v;
+        A[(e / R) * P + (e - (e / R) * R)] = v;
     }
     if (tid == 0) fail = 0;
     __syncthreads();
-    // Column by column (textbook order, as the reference solve):
-    //   L_jj = sqrt(V_jj - sum_{k<j} L_jk^2);  L_ij = (V_ij - sum_{k<j} L_ik L_jk) / L_jj.
+    // Column by column, right-looking: once column j of L is known, every
+    // entry below the diagonal of the trailing block takes its update
+    //   A_ik -= L_ij L_kj  (i >= k > j)
+    // at once.  Each entry receives its subtractions in the order j = 0, 1,
+    // ... exactly as in the textbook dot products
+    //   L_jj = sqrt(V_jj - sum_{k<j} L_jk^2),  L_ij = (V_ij - sum_{k<j} L_ik L_jk) / L_jj,
+    // so the factor is the same; the work per column is spread over the
+    // workgroup instead of running as one thread's dot product.
     for (int64_t j = 0; j < R; ++j) {
         if (tid == 0) {
-            double d = A[j * R + j];
-            for (int64_t k = 0; k < j; ++k) d -= A[j * R + k] * A[j * R + k];
-            if (!(d > 0.0)) {
+            const double d = A[j * P + j];
+            if (!(d > 0.0))
                 fail = 1;
-            } else {
-                A[j * R + j] = sqrt(d);
-            }
+            else
+                A[j * P + j] = sqrt(d);
         }
         __syncthreads();
         if (fail) break;
-        const double ljj = A[j * R + j];
-        for (int64_t i = j + 1 + tid; i < R; i += nt) {
-            double s = A[i * R + j];
-            for (int64_t k = 0; k < j; ++k) s -= A[i * R + k] * A[j * R + k];
-            A[i * R + j] = s / ljj;
+        const double ljj = A[j * P + j];
+        for (int64_t i = j + 1 + tid; i < R; i += nt) A[i * P + j] = A[i * P + j] / ljj;
+        __syncthreads();
+        // trailing block (rows and columns j+1..R-1, lower triangle): thread
+        // (ti, tk) of a 32 x 32 grid takes rows ti, ti+32, ... and columns
+        // tk, tk+32, ... (32-bit indices: R is at most 4096)
+        const int Ri = (int)P, jj = (int)j;
+        const int ti = tid >> 5, tk = tid & 31, ni = nt >> 5;
+        for (int i = jj + 1 + ti; i < (int)R; i += ni) {
+            const double lij = A[i * Ri + jj];
+            for (int k = jj + 1 + tk; k <= i; k += 32)
+                A[i * Ri + k] = __builtin_fma(-lij, A[k * Ri + jj], A[i * Ri + k]);
         }
         __syncthreads();
     }
@@ -131,7 +145,7 @@ __global__ __launch_bounds__(1024) void als_chol_kernel(const double *__restrict
     // zero the strict upper triangle and copy out
     for (int64_t e = tid; e < RR; e += nt) {
         const int64_t i = e / R, c = e - (e / R) * R;
-        Lout[e] = c > i ? 0.0 : A[e];
+        Lout[e] = c > i ? 0.0 : A[i * P + c];
     }
 }
 
@@ -217,6 +231,104 @@ __global__ __launch_bounds__(256) void als_normalize_kernel(const double *__rest
     if (lamT) lamT[r] = (T)lam;
 }
 
+// The solve, normalization and Gram refresh of one mode in one workgroup,
+// for a mode whose M (I x R) and L (R x R, R <= 64) fit in LDS together.  The
+// arithmetic is that of als_solve_wave_kernel, als_normalize_kernel and
+// gram_kernel, in the same order (the results are the same); only the
+// operands come from LDS and the three launches become one.
+template <typename T>
+__global__ __launch_bounds__(1024) void als_update_small_kernel(
+    const double *__restrict__ M, const double *__restrict__ L, int64_t I64, int64_t R64,
+    T *__restrict__ Uout, double *__restrict__ lam64, T *__restrict__ lamT,
+    double *__restrict__ G, const int *__restrict__ flag)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    if (*flag) return;
+    const int I = (int)I64, R = (int)R64;  // R <= 64, I * R small (checked by the host)
+    const int P = R + 1;                            // pitch of L: columns read across lanes
+    double *Ls = reinterpret_cast<double *>(smem);  // R x P
+    double *x = Ls + R * P;                         // I x R
+    const int tid = threadIdx.x, nt = blockDim.x;
+    const int lane = tid & 63, wave = tid >> 6, nw = nt >> 6;
+    for (int e = tid; e < R * R; e += nt) Ls[(e / R) * P + (e - (e / R) * R)] = L[e];
+    for (int e = tid; e < I * R; e += nt) x[e] = M[e];
+    __syncthreads();
+    // row solves (L L^T) u = m, one wave per row, lane l holding component l;
+    // the pivot component is broadcast with a lane read (uniform index), and
+    // the next step's factor entry is read ahead
+    for (int row = wave; row < I; row += nw) {
+        double b = lane < R ? x[row * R + lane] : 0.0;
+        double lnext = lane < R ? Ls[lane * P] : 0.0;
+        for (int j = 0; j < R; ++j) {
+            const double lcur = lnext;
+            if (j + 1 < R) lnext = lane < R ? Ls[lane * P + j + 1] : 0.0;
+            const double bj = __builtin_bit_cast(
+                double, ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(
+                             (int)(__builtin_bit_cast(uint64_t, b) >> 32), j) << 32) |
+                            (uint32_t)__builtin_amdgcn_readlane(
+                                (int)(uint32_t)__builtin_bit_cast(uint64_t, b), j));
+            const double xj = bj / Ls[j * P + j];
+            if (lane == j) b = xj;
+            if (lane > j && lane < R) b -= lcur * xj;
+        }
+        double unext = Ls[(R - 1) * P + (lane < R ? lane : 0)];
+        for (int j = R - 1; j >= 0; --j) {
+            const double ucur = unext;
+            if (j > 0) unext = Ls[(j - 1) * P + (lane < R ? lane : 0)];
+            const double bj = __builtin_bit_cast(
+                double, ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(
+                             (int)(__builtin_bit_cast(uint64_t, b) >> 32), j) << 32) |
+                            (uint32_t)__builtin_amdgcn_readlane(
+                                (int)(uint32_t)__builtin_bit_cast(uint64_t, b), j));
+            const double xj = bj / Ls[j * P + j];
+            if (lane == j) b = xj;
+            if (lane < j) b -= ucur * xj;
+        }
+        if (lane < R) x[row * R + lane] = b;
+    }
+    __syncthreads();
+    // column norms and the normalized factor; the LDS copy keeps the stored
+    // (element-type) values for the Gram below
+    for (int r = tid; r < R; r += nt) {
+        double sq = 0.0;
+        for (int i = 0; i < I; ++i) sq += x[i * R + r] * x[i * R + r];
+        const double lam = sqrt(sq);
+        for (int i = 0; i < I; ++i) {
+            const double v = x[i * R + r];
+            const T u = (T)(lam > 0.0 ? v / lam : v);
+            Uout[i * R + r] = u;
+            x[i * R + r] = (double)u;
+        }
+        lam64[r] = lam;
+        if (lamT) lamT[r] = (T)lam;
+    }
+    __syncthreads();
+    // G = U^T U: a thread takes a 4 x 4 block of entries (each summed over i
+    // in order), so a pair of LDS reads feeds four products
+    const int nb4 = (R + 3) / 4;
+    for (int blk = tid; blk < nb4 * nb4; blk += nt) {
+        const int a0 = (blk / nb4) * 4, c0 = (blk - (blk / nb4) * nb4) * 4;
+        double g[4][4] = {};
+        for (int i = 0; i < I; ++i) {
+            double ua[4], uc[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                ua[t] = a0 + t < R ? x[i * R + a0 + t] : 0.0;
+                uc[t] = c0 + t < R ? x[i * R + c0 + t] : 0.0;
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) g[t][u] += ua[t] * uc[u];
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (a0 + t < R && c0 + u < R) G[(a0 + t) * R + c0 + u] = g[t][u];
+    }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void fill_kernel(T *__restrict__ p, int64_t n, T v)
 {
@@ -285,7 +397,7 @@ hipError_t launch_gram(const T *U, int64_t I, int64_t R, double *G, const int *f
 hipError_t launch_chol(const double *Gall, int order, int n, int64_t R, double *L, int *flag,
                        hipStream_t s)
 {
-    const size_t bytes = (size_t)R * R * sizeof(double);
+    const size_t bytes = (size_t)R * (R + 1) * sizeof(double);
     const int use_lds = bytes <= 64 * 1024;
     hipLaunchKernelGGL(als_chol_kernel, dim3(1), dim3(1024), use_lds ? bytes : 0, s, Gall, order,
                        n, R, L, flag, use_lds);
@@ -314,6 +426,25 @@ hipError_t launch_normalize(const double *Unew, int64_t I, int64_t R, T *Uout, d
     return hipGetLastError();
 }
 
+// Bytes of LDS the one-workgroup update of a mode needs (0: not usable).
+size_t update_small_lds(int64_t I, int64_t R)
+{
+    if (R > 64) return 0;
+    const size_t b = (size_t)(R * (R + 1) + I * R) * sizeof(double);
+    return b <= 64 * 1024 ? b : 0;
+}
+
+template <typename T>
+hipError_t launch_update_small(const double *M, const double *L, int64_t I, int64_t R, T *Uout,
+                               double *lam64, T *lamT, double *G, const int *flag, hipStream_t s)
+{
+    const size_t lds = update_small_lds(I, R);
+    if (!lds) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(als_update_small_kernel<T>, dim3(1), dim3(1024), lds, s, M, L, I, R, Uout,
+                       lam64, lamT, G, flag);
+    return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_fill(T *p, int64_t n, T v, hipStream_t s)
 {
@@ -336,6 +467,8 @@ template hipError_t launch_sumsq<double>(const double *, int64_t, double *, int,
 template hipError_t launch_sumsq<float>(const float *, int64_t, double *, int, double *, hipStream_t);
 template hipError_t launch_gram<double>(const double *, int64_t, int64_t, double *, const int *, hipStream_t);
 template hipError_t launch_gram<float>(const float *, int64_t, int64_t, double *, const int *, hipStream_t);
+template hipError_t launch_update_small<double>(const double *, const double *, int64_t, int64_t, double *, double *, double *, double *, const int *, hipStream_t);
+template hipError_t launch_update_small<float>(const double *, const double *, int64_t, int64_t, float *, double *, float *, double *, const int *, hipStream_t);
 template hipError_t launch_normalize<double>(const double *, int64_t, int64_t, double *, double *, double *, const int *, hipStream_t);
 template hipError_t launch_normalize<float>(const double *, int64_t, int64_t, float *, double *, float *, const int *, hipStream_t);
 template hipError_t launch_fill<double>(double *, int64_t, double, hipStream_t);

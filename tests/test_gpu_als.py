@@ -43,6 +43,7 @@ def rel(a, b):
 @pytest.mark.parametrize("dims,true_rank,R,iters", [
     ((12, 10, 8), 3, 4, 1), ((12, 10, 8), 3, 4, 6), ((9, 8, 7, 6), 2, 5, 5),
     ((6, 5, 7, 4, 3), 2, 3, 4), ((40, 35, 30), 5, 70, 3),
+    ((80, 12, 10), 3, 64, 2),  # mode 0 too tall for the one-workgroup update, modes 1-2 not
 ])
 def test_als_small_vs_oracle(dims, true_rank, R, iters):
     p = inputs.random_cp_problem(dims, true_rank, R, sigma=0.05, seed=31)
