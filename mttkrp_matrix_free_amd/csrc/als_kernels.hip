@@ -234,8 +234,10 @@ __global__ __launch_bounds__(256) void als_normalize_kernel(const double *__rest
 // The solve, normalization and Gram refresh of one mode in one workgroup,
 // for a mode whose M (I x R) and L (R x R, R <= 64) fit in LDS together.  The
 // arithmetic is that of als_solve_wave_kernel, als_normalize_kernel and
-// gram_kernel, in the same order (the results are the same); only the
-// operands come from LDS and the three launches become one.
+// gram_kernel, in the same order, except that the substitutions multiply by
+// the reciprocals of L's diagonal instead of dividing by it (results within
+// a rounding of the divisions); the operands come from LDS and the three
+// launches become one.
 template <typename T>
 __global__ __launch_bounds__(1024) void als_update_small_kernel(
     const double *__restrict__ M, const double *__restrict__ L, int64_t I64, int64_t R64,
@@ -252,10 +254,15 @@ __global__ __launch_bounds__(1024) void als_update_small_kernel(
     const int lane = tid & 63, wave = tid >> 6, nw = nt >> 6;
     for (int e = tid; e < R * R; e += nt) Ls[(e / R) * P + (e - (e / R) * R)] = L[e];
     for (int e = tid; e < I * R; e += nt) x[e] = M[e];
+    __shared__ double rd[64];  // reciprocals of the diagonal of L
+    __syncthreads();
+    if (tid < R) rd[tid] = 1.0 / Ls[tid * P + tid];
     __syncthreads();
     // row solves (L L^T) u = m, one wave per row, lane l holding component l;
-    // the pivot component is broadcast with a lane read (uniform index), and
-    // the next step's factor entry is read ahead
+    // the pivot component is broadcast with a lane read (uniform index), the
+    // next step's factor entry is read ahead, and the pivot division is a
+    // product with the diagonal's reciprocal (a serial chain of divisions
+    // dominated the kernel)
     for (int row = wave; row < I; row += nw) {
         double b = lane < R ? x[row * R + lane] : 0.0;
         double lnext = lane < R ? Ls[lane * P] : 0.0;
@@ -267,7 +274,7 @@ __global__ __launch_bounds__(1024) void als_update_small_kernel(
                              (int)(__builtin_bit_cast(uint64_t, b) >> 32), j) << 32) |
                             (uint32_t)__builtin_amdgcn_readlane(
                                 (int)(uint32_t)__builtin_bit_cast(uint64_t, b), j));
-            const double xj = bj / Ls[j * P + j];
+            const double xj = bj * rd[j];
             if (lane == j) b = xj;
             if (lane > j && lane < R) b -= lcur * xj;
         }
@@ -280,7 +287,7 @@ __global__ __launch_bounds__(1024) void als_update_small_kernel(
                              (int)(__builtin_bit_cast(uint64_t, b) >> 32), j) << 32) |
                             (uint32_t)__builtin_amdgcn_readlane(
                                 (int)(uint32_t)__builtin_bit_cast(uint64_t, b), j));
-            const double xj = bj / Ls[j * P + j];
+            const double xj = bj * rd[j];
             if (lane == j) b = xj;
             if (lane < j) b -= ucur * xj;
         }
