@@ -149,6 +149,141 @@ __global__ __launch_bounds__(1024) void als_chol_kernel(const double *__restrict
     }
 }
 
+// Lane read of a double (the lane index is wave-uniform).
+__device__ __forceinline__ double lane_read(double v, int l)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(u >> 32), l);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// One step of the one-wave factorization below with a frame of W registers
+// (columns j .. j + W - 1; every column past the frame is past R - 1).
+// Publishes this lane's entry l of column j (to the column buffer c and to
+// its place Lij in L), applies the column to the frame, shifting it by one,
+// and returns the next column's entry in l.
+template <int W, int RM>
+__device__ __forceinline__ void chol_wave_step(double (&a)[RM], double &l, bool &bad, int i, int j,
+                                               int R, double *__restrict__ c,
+                                               double *__restrict__ Lij)
+{
+    c[i] = l;
+    *Lij = i >= j ? l : 0.0;
+    // the wave's LDS operations are performed in issue order, so the reads
+    // below see every lane's entry
+    __builtin_amdgcn_wave_barrier();
+    double cv[W];
+#pragma unroll
+    for (int k = 1; k < W - 1; ++k) cv[k] = c[j + 1 + k];
+    // the next pivot's path: the one entry it needs comes by lane read
+    const int jn = j + 1;
+    const double t0 = __builtin_fma(-l, lane_read(l, jn & 63), a[1]);
+    const double piv = lane_read(t0, jn & 63);
+    bad = bad || (jn < R && !(piv > 0.0));
+    const double d = sqrt(piv);
+    const double ln = i == jn ? d : t0 / d;
+    a[0] = t0;
+#pragma unroll
+    for (int k = 1; k < W - 1; ++k) a[k] = __builtin_fma(-l, cv[k], a[k + 1]);
+    a[W - 1] = 0.0;
+    l = ln;
+}
+
+// The same factorization for R <= RM <= 64 by one wave.  Lane i keeps row i
+// of the trailing matrix in registers, in a frame that moves one column per
+// step (at step j register k holds column j + k), so the trailing update is
+// a fixed, unrolled set of fused multiply-adds whose destinations carry the
+// shift; the frame narrows in steps of 16 as the trailing matrix shrinks.
+// The finished column goes through LDS, where every lane reads its entries
+// with broadcast reads (all issued before the first is used).  The next
+// column's pivot, square root and divisions come from the first updated
+// register before the rest of the update, so their latency overlaps it.
+// Every entry of L receives the operations of als_chol_kernel in the same
+// order (the factors are equal); entries above the diagonal take throwaway
+// updates and are written as zeros.  All four waves assemble V (every load
+// in flight at once) and copy L out; wave 0 factors.  One wave per SIMD: the
+// factoring wave may use the whole register file.
+template <int RM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
+als_chol_wave_kernel(const double *__restrict__ Gall, int order, int n, int R,
+                     double *__restrict__ Lout, int *__restrict__ flag)
+{
+    constexpr int P = RM + 1;
+    constexpr int EPT = (RM * RM + 255) / 256;
+    struct Smem {
+        double col[2 * 128];  // two column buffers; entries past row R - 1 stay zero
+        double A[RM * P + 1];  // V, then L; the last entry takes writes of rows past R - 1
+        int fail;
+    };
+    __shared__ Smem sm;
+    if (*flag) return;
+    const int tid = threadIdx.x;
+    const int RR = R * R;
+    {
+        double v[EPT];
+#pragma unroll
+        for (int q = 0; q < EPT; ++q) v[q] = 1.0;
+        // factors in mode order; a skipped mode multiplies by 1 (exact)
+#pragma unroll
+        for (int m = 0; m < 5; ++m) {
+            const bool use = m < order && m != n;
+            const double *Gm = Gall + (use ? (int64_t)m * RR : 0);
+#pragma unroll
+            for (int q = 0; q < EPT; ++q) {
+                const int e = tid + 256 * q;
+                const double g = Gm[e < RR ? e : 0];
+                v[q] *= use ? g : 1.0;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < EPT; ++q) {
+            const int e = tid + 256 * q;
+            if (e < RR) {
+                const int r = e / R;
+                sm.A[r * P + (e - r * R)] = v[q];
+            }
+        }
+    }
+    sm.col[tid] = 0.0;
+    __syncthreads();
+    if (tid < 64) {
+        const int i = tid;
+        const bool row = i < R;
+        double a[RM];
+#pragma unroll
+        for (int k = 0; k < RM; ++k) a[k] = row && k < R ? sm.A[i * P + k] : 0.0;
+        const double piv = lane_read(a[0], 0);
+        bool bad = !(piv > 0.0);
+        const double d = sqrt(piv);
+        double l = i == 0 ? d : a[0] / d;  // this lane's entry of column j
+        double *const Lrow = sm.A + (row ? i * P : RM * P);
+        const int lastw = row ? 1 : 0;  // rows past R - 1 keep writing the spare entry
+        int j = 0;
+        if constexpr (RM >= 64)
+            for (; j < R - 48; ++j)
+                chol_wave_step<64>(a, l, bad, i, j, R, sm.col + (j & 1) * 128, Lrow + j * lastw);
+        if constexpr (RM >= 48)
+            for (; j < R - 32; ++j)
+                chol_wave_step<48>(a, l, bad, i, j, R, sm.col + (j & 1) * 128, Lrow + j * lastw);
+        if constexpr (RM >= 32)
+            for (; j < R - 16; ++j)
+                chol_wave_step<32>(a, l, bad, i, j, R, sm.col + (j & 1) * 128, Lrow + j * lastw);
+        for (; j < R; ++j)
+            chol_wave_step<16>(a, l, bad, i, j, R, sm.col + (j & 1) * 128, Lrow + j * lastw);
+        if (i == 0) sm.fail = bad;
+    }
+    __syncthreads();
+    if (sm.fail) {
+        if (tid == 0) *flag = 1;
+        return;
+    }
+    for (int e = tid; e < RR; e += 256) {
+        const int r = e / R;
+        Lout[e] = sm.A[r * P + (e - r * R)];
+    }
+}
+
 // Row solves (L L^T) x = m for every row of M; one wave per row, R <= 64:
 // lane l holds component l.
 __global__ __launch_bounds__(256) void als_solve_wave_kernel(const double *__restrict__ M,
@@ -231,89 +366,126 @@ __global__ __launch_bounds__(256) void als_normalize_kernel(const double *__rest
     if (lamT) lamT[r] = (T)lam;
 }
 
-// The solve, normalization and Gram refresh of one mode in one workgroup,
-// for a mode whose M (I x R) and L (R x R, R <= 64) fit in LDS together.  The
-// arithmetic is that of als_solve_wave_kernel, als_normalize_kernel and
-// gram_kernel, in the same order, except that the substitutions multiply by
-// the reciprocals of L's diagonal instead of dividing by it (results within
-// a rounding of the divisions); the operands come from LDS and the three
-// launches become one.
-template <typename T>
-__global__ __launch_bounds__(1024) void als_update_small_kernel(
-    const double *__restrict__ M, const double *__restrict__ L, int64_t I64, int64_t R64,
-    T *__restrict__ Uout, double *__restrict__ lam64, T *__restrict__ lamT,
-    double *__restrict__ G, const int *__restrict__ flag)
+// One substitution step for a wave whose lanes hold one row each, with a
+// frame of W registers (a[k] holds component j + S k, S = +1 forward, -1
+// back; every component past the frame is out of range).  The component
+// a[0] is final after the pivot product: it is stored to xj, and its
+// multiples e[S k] (k >= 1, uniform across lanes) are taken off the rest of
+// the frame, which shifts by one.
+template <int W, int S, int RM>
+__device__ __forceinline__ void subst_step(double (&a)[RM], double rdj,
+                                           const double *__restrict__ e, double *__restrict__ xj)
+{
+    double cv[W];
+#pragma unroll
+    for (int k = 1; k < W; ++k) cv[k] = e[S * k];
+    const double x = a[0] * rdj;
+    *xj = x;
+#pragma unroll
+    for (int k = 1; k < W; ++k) a[k - 1] = __builtin_fma(-cv[k], x, a[k]);
+    a[W - 1] = 0.0;
+}
+
+// The solve, normalization and Gram refresh of one mode in one workgroup
+// (four waves, one per SIMD), for R <= RM <= 64 and a mode whose solution,
+// L and L^T fit in LDS together.  The arithmetic is that of
+// als_solve_wave_kernel, als_normalize_kernel and gram_kernel, in the same
+// order, except that the substitutions multiply by the reciprocals of L's
+// diagonal instead of dividing by it (results within a rounding of the
+// divisions).
+//  - Substitutions: a lane per row (64 rows per wave and pass), the row's
+//    unknowns in registers in a frame that shifts by one per step and narrows
+//    in steps of 16 as the unsolved part shrinks; L's entries of a step are
+//    the same for every row and come from LDS as broadcast reads (L^T rows
+//    for the forward pass, L rows backward, zero padding past both ends).
+//    There is no exchange between lanes, so the only serial chain per step
+//    is one product and one fused multiply-add.
+//  - Normalization: a thread per column forms the norm (rows in order); then
+//    every thread scales a share of the entries.
+//  - Gram: a thread per 4 x 4 block of entries (rows in order).
+template <typename T, int RM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
+als_update_small_kernel(const double *__restrict__ M, const double *__restrict__ L, int64_t I64,
+                        int64_t R64, T *__restrict__ Uout, double *__restrict__ lam64,
+                        T *__restrict__ lamT, double *__restrict__ G,
+                        const int *__restrict__ flag)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     if (*flag) return;
-    const int I = (int)I64, R = (int)R64;  // R <= 64, I * R small (checked by the host)
-    const int P = R + 1;                            // pitch of L: columns read across lanes
-    double *Ls = reinterpret_cast<double *>(smem);  // R x P
-    double *x = Ls + R * P;                         // I x R
-    const int tid = threadIdx.x, nt = blockDim.x;
-    const int lane = tid & 63, wave = tid >> 6, nw = nt >> 6;
-    for (int e = tid; e < R * R; e += nt) Ls[(e / R) * P + (e - (e / R) * R)] = L[e];
-    for (int e = tid; e < I * R; e += nt) x[e] = M[e];
-    __shared__ double rd[64];  // reciprocals of the diagonal of L
-    __syncthreads();
-    if (tid < R) rd[tid] = 1.0 / Ls[tid * P + tid];
-    __syncthreads();
-    // row solves (L L^T) u = m, one wave per row, lane l holding component l;
-    // the pivot component is broadcast with a lane read (uniform index), the
-    // next step's factor entry is read ahead, and the pivot division is a
-    // product with the diagonal's reciprocal (a serial chain of divisions
-    // dominated the kernel)
-    for (int row = wave; row < I; row += nw) {
-        double b = lane < R ? x[row * R + lane] : 0.0;
-        double lnext = lane < R ? Ls[lane * P] : 0.0;
-        for (int j = 0; j < R; ++j) {
-            const double lcur = lnext;
-            if (j + 1 < R) lnext = lane < R ? Ls[lane * P + j + 1] : 0.0;
-            const double bj = __builtin_bit_cast(
-                double, ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(
-                             (int)(__builtin_bit_cast(uint64_t, b) >> 32), j) << 32) |
-                            (uint32_t)__builtin_amdgcn_readlane(
-                                (int)(uint32_t)__builtin_bit_cast(uint64_t, b), j));
-            const double xj = bj * rd[j];
-            if (lane == j) b = xj;
-            if (lane > j && lane < R) b -= lcur * xj;
-        }
-        double unext = Ls[(R - 1) * P + (lane < R ? lane : 0)];
-        for (int j = R - 1; j >= 0; --j) {
-            const double ucur = unext;
-            if (j > 0) unext = Ls[(j - 1) * P + (lane < R ? lane : 0)];
-            const double bj = __builtin_bit_cast(
-                double, ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(
-                             (int)(__builtin_bit_cast(uint64_t, b) >> 32), j) << 32) |
-                            (uint32_t)__builtin_amdgcn_readlane(
-                                (int)(uint32_t)__builtin_bit_cast(uint64_t, b), j));
-            const double xj = bj * rd[j];
-            if (lane == j) b = xj;
-            if (lane < j) b -= ucur * xj;
-        }
-        if (lane < R) x[row * R + lane] = b;
+    const int I = (int)I64, R = (int)R64;  // R <= RM, sizes checked by the host
+    const int RR = R * R;
+    double *Lr = reinterpret_cast<double *>(smem) + 64;  // L, rows; 64 zeros before
+    double *Lt = Lr + RR;                                // L^T, rows; 64 zeros after
+    double *x = Lt + RR + 64;                            // I x R solution, then U
+    double *rd = x + (size_t)I * R;                      // 1 / L_jj, then lambda
+    double *spare = rd + 64;                             // writes of rows past I - 1
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int e = tid; e < 64; e += 256) {
+        Lr[e - 64] = 0.0;
+        Lt[RR + e] = 0.0;
+    }
+    for (int e = tid; e < RR; e += 256) {
+        const int r = e / R, c = e - (e / R) * R;
+        const double v = L[e];
+        Lr[e] = v;
+        Lt[c * R + r] = v;
     }
     __syncthreads();
-    // column norms and the normalized factor; the LDS copy keeps the stored
-    // (element-type) values for the Gram below
-    for (int r = tid; r < R; r += nt) {
+    if (tid < R) rd[tid] = 1.0 / Lr[tid * R + tid];
+    __syncthreads();
+    for (int r0 = 64 * wave; r0 < I; r0 += 256) {
+        const int row = r0 + lane;
+        const bool ok = row < I;
+        double *xrow = ok ? x + (size_t)row * R : spare;
+        const int xs = ok ? 1 : 0;  // rows past I - 1 keep writing the spare entry
+        double a[RM];
+        // forward, L y = m: a[k] holds component j + k
+#pragma unroll
+        for (int k = 0; k < RM; ++k) a[k] = ok && k < R ? M[(size_t)(ok ? row : 0) * R + k] : 0.0;
+        int j = 0;
+        if constexpr (RM >= 64)
+            for (; j < R - 48; ++j) subst_step<64, 1>(a, rd[j], Lt + j * R + j, xrow + j * xs);
+        if constexpr (RM >= 48)
+            for (; j < R - 32; ++j) subst_step<48, 1>(a, rd[j], Lt + j * R + j, xrow + j * xs);
+        if constexpr (RM >= 32)
+            for (; j < R - 16; ++j) subst_step<32, 1>(a, rd[j], Lt + j * R + j, xrow + j * xs);
+        for (; j < R; ++j) subst_step<16, 1>(a, rd[j], Lt + j * R + j, xrow + j * xs);
+        // back, L^T u = y: a[k] holds component j - k (this lane's own row
+        // of x, so no exchange is needed)
+#pragma unroll
+        for (int k = 0; k < RM; ++k) a[k] = ok && k < R ? x[(size_t)(ok ? row : 0) * R + R - 1 - k] : 0.0;
+        j = R - 1;
+        if constexpr (RM >= 64)
+            for (; j >= 48; --j) subst_step<64, -1>(a, rd[j], Lr + j * R + j, xrow + j * xs);
+        if constexpr (RM >= 48)
+            for (; j >= 32; --j) subst_step<48, -1>(a, rd[j], Lr + j * R + j, xrow + j * xs);
+        if constexpr (RM >= 32)
+            for (; j >= 16; --j) subst_step<32, -1>(a, rd[j], Lr + j * R + j, xrow + j * xs);
+        for (; j >= 0; --j) subst_step<16, -1>(a, rd[j], Lr + j * R + j, xrow + j * xs);
+    }
+    __syncthreads();
+    // column norms (rows in order), then the normalized factor; the LDS copy
+    // keeps the stored (element-type) values for the Gram below
+    if (tid < R) {
         double sq = 0.0;
-        for (int i = 0; i < I; ++i) sq += x[i * R + r] * x[i * R + r];
+        for (int i = 0; i < I; ++i) sq += x[i * R + tid] * x[i * R + tid];
         const double lam = sqrt(sq);
-        for (int i = 0; i < I; ++i) {
-            const double v = x[i * R + r];
-            const T u = (T)(lam > 0.0 ? v / lam : v);
-            Uout[i * R + r] = u;
-            x[i * R + r] = (double)u;
-        }
-        lam64[r] = lam;
-        if (lamT) lamT[r] = (T)lam;
+        rd[tid] = lam;
+        lam64[tid] = lam;
+        if (lamT) lamT[tid] = (T)lam;
+    }
+    __syncthreads();
+    for (int e = tid; e < I * R; e += 256) {
+        const double lam = rd[e - (e / R) * R];
+        const T u = (T)(lam > 0.0 ? x[e] / lam : x[e]);
+        Uout[e] = u;
+        x[e] = (double)u;
     }
     __syncthreads();
     // G = U^T U: a thread takes a 4 x 4 block of entries (each summed over i
     // in order), so a pair of LDS reads feeds four products
     const int nb4 = (R + 3) / 4;
-    for (int blk = tid; blk < nb4 * nb4; blk += nt) {
+    for (int blk = tid; blk < nb4 * nb4; blk += 256) {
         const int a0 = (blk / nb4) * 4, c0 = (blk - (blk / nb4) * nb4) * 4;
         double g[4][4] = {};
         for (int i = 0; i < I; ++i) {
@@ -404,6 +576,13 @@ hipError_t launch_gram(const T *U, int64_t I, int64_t R, double *G, const int *f
 hipError_t launch_chol(const double *Gall, int order, int n, int64_t R, double *L, int *flag,
                        hipStream_t s)
 {
+    if (R <= 64) {
+        auto k = R <= 16 ? als_chol_wave_kernel<16>
+                 : R <= 32 ? als_chol_wave_kernel<32>
+                           : als_chol_wave_kernel<64>;
+        hipLaunchKernelGGL(k, dim3(1), dim3(256), 0, s, Gall, order, n, (int)R, L, flag);
+        return hipGetLastError();
+    }
     const size_t bytes = (size_t)R * (R + 1) * sizeof(double);
     const int use_lds = bytes <= 64 * 1024;
     hipLaunchKernelGGL(als_chol_kernel, dim3(1), dim3(1024), use_lds ? bytes : 0, s, Gall, order,
@@ -436,10 +615,12 @@ hipError_t launch_normalize(const double *Unew, int64_t I, int64_t R, T *Uout, d
 // Bytes of LDS the one-workgroup update of a mode needs (0: not usable).
 size_t update_small_lds(int64_t I, int64_t R)
 {
-    if (R > 64) return 0;
-    const size_t b = (size_t)(R * (R + 1) + I * R) * sizeof(double);
-    return b <= 64 * 1024 ? b : 0;
+    if (R > 64 || I > (1 << 20)) return 0;
+    const size_t b = (size_t)(2 * R * R + I * R + 4 * 64 + 1) * sizeof(double);
+    return b <= 160 * 1024 ? b : 0;
 }
+
+hipError_t allow_large_lds(const void *k);
 
 template <typename T>
 hipError_t launch_update_small(const double *M, const double *L, int64_t I, int64_t R, T *Uout,
@@ -447,8 +628,14 @@ hipError_t launch_update_small(const double *M, const double *L, int64_t I, int6
 {
     const size_t lds = update_small_lds(I, R);
     if (!lds) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(als_update_small_kernel<T>, dim3(1), dim3(1024), lds, s, M, L, I, R, Uout,
-                       lam64, lamT, G, flag);
+    auto k = R <= 16 ? als_update_small_kernel<T, 16>
+             : R <= 32 ? als_update_small_kernel<T, 32>
+                       : als_update_small_kernel<T, 64>;
+    if (lds > 64 * 1024) {
+        const hipError_t a = allow_large_lds(reinterpret_cast<const void *>(k));
+        if (a != hipSuccess) return a;
+    }
+    hipLaunchKernelGGL(k, dim3(1), dim3(256), lds, s, M, L, I, R, Uout, lam64, lamT, G, flag);
     return hipGetLastError();
 }
 
