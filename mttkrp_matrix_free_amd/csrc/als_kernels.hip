@@ -16,8 +16,10 @@
 //   fit = 1 - sqrt(max(0, ||X||^2 + ||model||^2 - 2 <X, model>)) / ||X||
 // with <X, model> = sum_r lambda_r sum_i M(i, r) U_{d-1}(i, r) and
 // ||model||^2 = sum_{a,b} lambda_a lambda_b prod_m G_m(a, b).
-// Every kernel after a failed Cholesky returns without writing, so the
-// factors keep the values of the failing step's start.
+// Every kernel after a failed Cholesky (flag 1) returns without writing, so
+// the factors keep the values of the failing step's start; the same holds
+// after a converged sweep (flag 2, set by als_fit), so sweeps queued ahead of
+// the host's check change nothing.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -248,6 +250,9 @@ als_chol_wave_kernel(const double *__restrict__ Gall, int order, int n, int R,
     sm.col[tid] = 0.0;
     __syncthreads();
     if (tid < 64) {
+        // this kernel usually shares its compute unit with MTTKRP waves;
+        // its one serial wave goes first at instruction issue
+        __builtin_amdgcn_s_setprio(3);
         const int i = tid;
         const bool row = i < R;
         double a[RM];
@@ -517,14 +522,25 @@ __global__ __launch_bounds__(256) void fill_kernel(T *__restrict__ p, int64_t n,
 
 // Fit after the last mode of a sweep; one workgroup.  scal[0] = ||X||^2 in,
 // scal[1] = fit out.
+// The fit after a sweep, and the stop decision: a sweep whose fit changed by
+// less than tol (tol > 0, a previous sweep's fit in scal[2]) sets the flag
+// to 2, so every later kernel of the run returns without writing, just as
+// after a failed Cholesky (flag 1).  The fit and the flag are also stored to
+// the host-visible slot (out_fit, out_flag), so the host learns the outcome
+// without a copy, while the next sweep is already queued.
 template <typename T>
 __global__ __launch_bounds__(kRedThreads) void als_fit_kernel(
     const double *__restrict__ M, const T *__restrict__ Ulast, int64_t Ilast,
     const double *__restrict__ lam64, const double *__restrict__ Gall, int order, int64_t R,
-    double *__restrict__ scal, const int *__restrict__ flag)
+    double *__restrict__ scal, int *__restrict__ flag, double tol, int have_prev,
+    double *__restrict__ out_fit, int *__restrict__ out_flag)
 {
     __shared__ double sh[kRedThreads / 64];
-    if (*flag) return;
+    const int f0 = *flag;
+    if (f0) {
+        if (threadIdx.x == 0) *out_flag = f0;
+        return;
+    }
     double inner = 0.0;
     for (int64_t r = threadIdx.x; r < R; r += kRedThreads) {
         double s = 0.0;
@@ -532,20 +548,48 @@ __global__ __launch_bounds__(kRedThreads) void als_fit_kernel(
         inner += lam64[r] * s;
     }
     inner = block_sum(inner, sh);
+    // ||model||^2: eight entries per thread and round, every load of a round
+    // in flight at once; each thread still adds its entries in index order
     const int64_t RR = R * R;
     double nrm2 = 0.0;
-    for (int64_t e = threadIdx.x; e < RR; e += kRedThreads) {
-        const int64_t a = e / R, b = e - (e / R) * R;
-        double v = lam64[a] * lam64[b];
-        for (int m = 0; m < order; ++m) v *= Gall[(int64_t)m * RR + e];
-        nrm2 += v;
+    constexpr int Q = 8;
+    for (int64_t e0 = threadIdx.x; e0 < RR; e0 += (int64_t)kRedThreads * Q) {
+        double v[Q];
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            int64_t e = e0 + (int64_t)kRedThreads * q;
+            e = e < RR ? e : RR - 1;
+            const int64_t a = e / R, b = e - (e / R) * R;
+            v[q] = lam64[a] * lam64[b];
+        }
+        // modes past the order multiply by 1 (exact), so no load waits on a branch
+#pragma unroll
+        for (int m = 0; m < 5; ++m) {
+            const bool use = m < order;
+            const double *Gm = Gall + (use ? (int64_t)m * RR : 0);
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                const int64_t e = e0 + (int64_t)kRedThreads * q;
+                const double g = Gm[e < RR ? e : RR - 1];
+                v[q] *= use ? g : 1.0;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < Q; ++q)
+            if (e0 + (int64_t)kRedThreads * q < RR) nrm2 += v[q];
     }
     nrm2 = block_sum(nrm2, sh);
     if (threadIdx.x == 0) {
         const double nx2 = scal[0];
         double resid = nx2 + nrm2 - 2.0 * inner;
         if (resid < 0.0) resid = 0.0;
-        scal[1] = nx2 > 0.0 ? 1.0 - sqrt(resid) / sqrt(nx2) : __builtin_nan("");
+        const double fit = nx2 > 0.0 ? 1.0 - sqrt(resid) / sqrt(nx2) : __builtin_nan("");
+        const int stop = tol > 0.0 && have_prev && fabs(fit - scal[2]) < tol;
+        scal[1] = fit;
+        scal[2] = fit;
+        if (stop) *flag = 2;
+        *out_fit = fit;
+        *out_flag = stop ? 2 : 0;
     }
 }
 
@@ -649,11 +693,11 @@ hipError_t launch_fill(T *p, int64_t n, T v, hipStream_t s)
 
 template <typename T>
 hipError_t launch_fit(const double *M, const T *Ulast, int64_t Ilast, const double *lam64,
-                      const double *Gall, int order, int64_t R, double *scal, const int *flag,
-                      hipStream_t s)
+                      const double *Gall, int order, int64_t R, double *scal, int *flag,
+                      double tol, int have_prev, double *out_fit, int *out_flag, hipStream_t s)
 {
     hipLaunchKernelGGL(als_fit_kernel<T>, dim3(1), dim3(kRedThreads), 0, s, M, Ulast, Ilast, lam64,
-                       Gall, order, R, scal, flag);
+                       Gall, order, R, scal, flag, tol, have_prev, out_fit, out_flag);
     return hipGetLastError();
 }
 
@@ -668,7 +712,7 @@ template hipError_t launch_normalize<float>(const double *, int64_t, int64_t, fl
 template hipError_t launch_fill<double>(double *, int64_t, double, hipStream_t);
 template hipError_t launch_fill<float>(float *, int64_t, float, hipStream_t);
 template hipError_t launch_fill<int>(int *, int64_t, int, hipStream_t);
-template hipError_t launch_fit<double>(const double *, const double *, int64_t, const double *, const double *, int, int64_t, double *, const int *, hipStream_t);
-template hipError_t launch_fit<float>(const double *, const float *, int64_t, const double *, const double *, int, int64_t, double *, const int *, hipStream_t);
+template hipError_t launch_fit<double>(const double *, const double *, int64_t, const double *, const double *, int, int64_t, double *, int *, double, int, double *, int *, hipStream_t);
+template hipError_t launch_fit<float>(const double *, const float *, int64_t, const double *, const double *, int, int64_t, double *, int *, double, int, double *, int *, hipStream_t);
 
 }  // namespace mttkrp

@@ -45,8 +45,8 @@ hipError_t launch_update_small(const double *M, const double *L, int64_t I, int6
                                double *lam64, T *lamT, double *G, const int *flag, hipStream_t s);
 template <typename T>
 hipError_t launch_fit(const double *M, const T *Ulast, int64_t Ilast, const double *lam64,
-                      const double *Gall, int order, int64_t R, double *scal, const int *flag,
-                      hipStream_t s);
+                      const double *Gall, int order, int64_t R, double *scal, int *flag,
+                      double tol, int have_prev, double *out_fit, int *out_flag, hipStream_t s);
 
 namespace {
 
@@ -435,9 +435,55 @@ int cp_als_entry(const T *X, const int64_t *dims, int order, int64_t rank, T *co
     if (!ok(hipEventCreateWithFlags(&ev.fork, hipEventDisableTiming))) return MTTKRP_EHIP;
     if (!ok(hipEventCreateWithFlags(&ev.join, hipEventDisableTiming))) return MTTKRP_EHIP;
 
+    // Each sweep's fit and flag land in host-visible pinned memory (two
+    // slots, written by the fit kernel).  The host reads sweep it - 1's slot
+    // only after sweep it is queued, so the device never waits for the host;
+    // a sweep queued past a stop (convergence or a failed Cholesky) changes
+    // nothing, since its kernels see the flag and return.
+    struct Slot {
+        double fit;
+        int flag;
+        int pad;
+    };
+    struct Pinned {
+        hipStream_t s;
+        Slot *p = nullptr;
+        hipEvent_t done[2] = {nullptr, nullptr};
+        ~Pinned()
+        {
+            // queued fit kernels may still write the slots
+            if (p) (void)hipStreamSynchronize(s);
+            for (hipEvent_t e : done)
+                if (e) (void)hipEventDestroy(e);
+            if (p) (void)hipHostFree(p);
+        }
+    } pin{s};
+    if (!ok(hipHostMalloc(reinterpret_cast<void **>(&pin.p), 2 * sizeof(Slot),
+                          hipHostMallocDefault)))
+        return MTTKRP_EHIP;
+    for (hipEvent_t &e : pin.done)
+        if (!ok(hipEventCreateWithFlags(&e, hipEventDisableTiming))) return MTTKRP_EHIP;
+    // Outcome of sweep k: 1 = go on, 0 = stopped after it (converged), or an
+    // error status.
+    auto consume = [&](int k) -> int {
+        if (!ok(hipEventSynchronize(pin.done[k & 1]))) return MTTKRP_EHIP;
+        const Slot &h = pin.p[k & 1];
+        if (h.flag == 1) {
+            *iters_done = k;
+            return MTTKRP_ENOTSPD;
+        }
+        fit_hist[k] = h.fit;
+        *iters_done = k + 1;
+        return h.flag == 2 ? 0 : 1;
+    };
+    auto finish = [&](int r) -> int {
+        // later sweeps may still be queued (their kernels return at once)
+        if (!ok(hipStreamSynchronize(s))) return MTTKRP_EHIP;
+        return r;
+    };
+
     const T *cf[kMaxOrder];
     for (int m = 0; m < order; ++m) cf[m] = factors[m];
-    double prev = std::numeric_limits<double>::quiet_NaN();
     for (int it = 0; it < iters; ++it) {
         for (int n = 0; n < order; ++n) {
             if (!ok(hipEventRecord(ev.fork, s))) return MTTKRP_EHIP;
@@ -460,26 +506,19 @@ int cp_als_entry(const T *X, const int64_t *dims, int order, int64_t rank, T *co
             if (!ok(launch_gram<T>(factors[n], dims[n], R, G + (size_t)n * R * R, flag, s)))
                 return MTTKRP_EHIP;
         }
+        Slot *slot = pin.p + (it & 1);
         if (!ok(launch_fit<T>(M, factors[order - 1], dims[order - 1], lam64, G, order, R, scal,
-                              flag, s)))
+                              flag, tol, it > 0, &slot->fit, &slot->flag, s)))
             return MTTKRP_EHIP;
-        struct {
-            double fit;
-            int flag;
-        } host;
-        if (!ok(hipMemcpyAsync(&host.fit, scal + 1, sizeof(double), hipMemcpyDeviceToHost, s)))
-            return MTTKRP_EHIP;
-        if (!ok(hipMemcpyAsync(&host.flag, flag, sizeof(int), hipMemcpyDeviceToHost, s)))
-            return MTTKRP_EHIP;
-        if (!ok(hipStreamSynchronize(s))) return MTTKRP_EHIP;
-        if (host.flag) {
-            *iters_done = it;
-            return MTTKRP_ENOTSPD;
+        if (!ok(hipEventRecord(pin.done[it & 1], s))) return MTTKRP_EHIP;
+        if (it > 0) {
+            const int r = consume(it - 1);
+            if (r != 1) return finish(r);
         }
-        fit_hist[it] = host.fit;
-        *iters_done = it + 1;
-        if (tol > 0.0 && it > 0 && std::fabs(host.fit - prev) < tol) break;
-        prev = host.fit;
+    }
+    if (iters > 0) {
+        const int r = consume(iters - 1);
+        if (r != 1) return finish(r);
     }
     return MTTKRP_OK;
 }

@@ -105,6 +105,15 @@ def test_als_tolerance_stops_early():
     lam, fit, done, st = api.cp_als(X, U, 50, tol=1e-10)
     assert st == 0 and 1 < done < 50
     assert all(np.isnan(f) for f in fit[done:])
+    # the sweep queued past the stop changes nothing: the result equals that
+    # of a run of exactly `done` sweeps
+    U2 = [dev(u) for u in p.factors]
+    lam2, fit2, done2, st2 = api.cp_als(X, U2, done)
+    assert st2 == 0 and done2 == done
+    assert np.array_equal(fit2, fit[:done])
+    assert torch.equal(lam2, lam)
+    for a, b in zip(U, U2):
+        assert torch.equal(a, b)
 
 
 def test_als_float32():
