@@ -23,6 +23,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 namespace mttkrp {
 
 constexpr int kRedThreads = 256;
@@ -163,15 +165,17 @@ __device__ __forceinline__ double lane_read(double v, int l)
 // One step of the one-wave factorization below with a frame of W registers
 // (columns j .. j + W - 1; every column past the frame is past R - 1).
 // Publishes this lane's entry l of column j (to the column buffer c and to
-// its place Lij in L), applies the column to the frame, shifting it by one,
-// and returns the next column's entry in l.
+// its places L1 and L2 in the outputs), applies the column to the frame,
+// shifting it by one, and returns the next column's entry in l.
 template <int W, int RM>
 __device__ __forceinline__ void chol_wave_step(double (&a)[RM], double &l, bool &bad, int i, int j,
                                                int R, double *__restrict__ c,
-                                               double *__restrict__ Lij)
+                                               double *__restrict__ L1, double *__restrict__ L2)
 {
     c[i] = l;
-    *Lij = i >= j ? l : 0.0;
+    const double lo = i >= j ? l : 0.0;
+    *L1 = lo;
+    *L2 = lo;
     // the wave's LDS operations are performed in issue order, so the reads
     // below see every lane's entry
     __builtin_amdgcn_wave_barrier();
@@ -192,29 +196,102 @@ __device__ __forceinline__ void chol_wave_step(double (&a)[RM], double &l, bool 
     l = ln;
 }
 
-// The same factorization for R <= RM <= 64 by one wave.  Lane i keeps row i
-// of the trailing matrix in registers, in a frame that moves one column per
-// step (at step j register k holds column j + k), so the trailing update is
-// a fixed, unrolled set of fused multiply-adds whose destinations carry the
-// shift; the frame narrows in steps of 16 as the trailing matrix shrinks.
-// The finished column goes through LDS, where every lane reads its entries
-// with broadcast reads (all issued before the first is used).  The next
-// column's pivot, square root and divisions come from the first updated
-// register before the rest of the update, so their latency overlaps it.
-// Every entry of L receives the operations of als_chol_kernel in the same
-// order (the factors are equal); entries above the diagonal take throwaway
-// updates and are written as zeros.  All four waves assemble V (every load
-// in flight at once) and copy L out; wave 0 factors.  One wave per SIMD: the
-// factoring wave may use the whole register file.
+// V = Hadamard_{m != n} G_m into A (R x R, pitch P; all threads of the
+// workgroup take part, every load of a thread in flight at once).  Factors
+// are multiplied in mode order; a skipped mode multiplies by 1 (exact).
+template <int RM, int NT>
+__device__ __forceinline__ void hadamard_to_lds(const double *__restrict__ Gall, int order, int n,
+                                                int R, double *__restrict__ A, int P)
+{
+    constexpr int EPT = (RM * RM + NT - 1) / NT;
+    const int tid = threadIdx.x;
+    const int RR = R * R;
+    double v[EPT];
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) v[q] = 1.0;
+#pragma unroll
+    for (int m = 0; m < 5; ++m) {
+        const bool use = m < order && m != n;
+        const double *Gm = Gall + (use ? (int64_t)m * RR : 0);
+#pragma unroll
+        for (int q = 0; q < EPT; ++q) {
+            const int e = tid + NT * q;
+            const double g = Gm[e < RR ? e : 0];
+            v[q] *= use ? g : 1.0;
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+        const int e = tid + NT * q;
+        if (e < RR) {
+            const int r = e / R;
+            A[r * P + (e - r * R)] = v[q];
+        }
+    }
+}
+
+// The factorization of V (in A, pitch RM + 1, R <= RM <= 64) by one wave
+// (called by the whole first wave).  Lane i keeps row i of the trailing
+// matrix in registers, in a frame that moves one column per step (at step j
+// register k holds column j + k), so the trailing update is a fixed,
+// unrolled set of fused multiply-adds whose destinations carry the shift;
+// the frame narrows in steps of 16 as the trailing matrix shrinks.  The
+// finished column goes through LDS (col, 256 entries, zero on entry), where
+// every lane reads its entries with broadcast reads, all issued before the
+// first is used.  The next column's pivot, square root and divisions come
+// from the first updated register before the rest of the update, so their
+// latency overlaps it.  Every entry of L receives the operations of
+// als_chol_kernel in the same order (the factors are equal); entries above
+// the diagonal take throwaway updates and are written as zeros.  L_ij goes
+// to out1[i * s1r + j * s1c] and out2[i * s2r + j * s2c]; rows past R - 1
+// write to spare.  Returns (in every lane) whether a pivot was not positive.
+template <int RM>
+__device__ __forceinline__ bool chol_wave_factor(const double *__restrict__ A, int R,
+                                                 double *__restrict__ col,
+                                                 double *__restrict__ out1, int s1r, int s1c,
+                                                 double *__restrict__ out2, int s2r, int s2c,
+                                                 double *__restrict__ spare)
+{
+    constexpr int P = RM + 1;
+    const int i = threadIdx.x & 63;
+    const bool row = i < R;
+    double a[RM];
+#pragma unroll
+    for (int k = 0; k < RM; ++k) a[k] = row && k < R ? A[(row ? i : 0) * P + k] : 0.0;
+    const double piv = lane_read(a[0], 0);
+    bool bad = !(piv > 0.0);
+    const double d = sqrt(piv);
+    double l = i == 0 ? d : a[0] / d;  // this lane's entry of column j
+    double *const b1 = row ? out1 + i * s1r : spare;
+    double *const b2 = row ? out2 + i * s2r : spare;
+    const int c1 = row ? s1c : 0, c2 = row ? s2c : 0;
+    int j = 0;
+    if constexpr (RM >= 64)
+        for (; j < R - 48; ++j)
+            chol_wave_step<64>(a, l, bad, i, j, R, col + (j & 1) * 128, b1 + j * c1, b2 + j * c2);
+    if constexpr (RM >= 48)
+        for (; j < R - 32; ++j)
+            chol_wave_step<48>(a, l, bad, i, j, R, col + (j & 1) * 128, b1 + j * c1, b2 + j * c2);
+    if constexpr (RM >= 32)
+        for (; j < R - 16; ++j)
+            chol_wave_step<32>(a, l, bad, i, j, R, col + (j & 1) * 128, b1 + j * c1, b2 + j * c2);
+    for (; j < R; ++j)
+        chol_wave_step<16>(a, l, bad, i, j, R, col + (j & 1) * 128, b1 + j * c1, b2 + j * c2);
+    return bad;
+}
+
+// The Cholesky factor alone (for modes the one-workgroup update below does
+// not take), R <= RM <= 64: all four waves assemble V and copy L out, the
+// first factors it.  One wave per SIMD: the factoring wave may use the whole
+// register file.
 template <int RM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 als_chol_wave_kernel(const double *__restrict__ Gall, int order, int n, int R,
                      double *__restrict__ Lout, int *__restrict__ flag)
 {
     constexpr int P = RM + 1;
-    constexpr int EPT = (RM * RM + 255) / 256;
     struct Smem {
-        double col[2 * 128];  // two column buffers; entries past row R - 1 stay zero
+        double col[256];       // two column buffers
         double A[RM * P + 1];  // V, then L; the last entry takes writes of rows past R - 1
         int fail;
     };
@@ -222,61 +299,15 @@ als_chol_wave_kernel(const double *__restrict__ Gall, int order, int n, int R,
     if (*flag) return;
     const int tid = threadIdx.x;
     const int RR = R * R;
-    {
-        double v[EPT];
-#pragma unroll
-        for (int q = 0; q < EPT; ++q) v[q] = 1.0;
-        // factors in mode order; a skipped mode multiplies by 1 (exact)
-#pragma unroll
-        for (int m = 0; m < 5; ++m) {
-            const bool use = m < order && m != n;
-            const double *Gm = Gall + (use ? (int64_t)m * RR : 0);
-#pragma unroll
-            for (int q = 0; q < EPT; ++q) {
-                const int e = tid + 256 * q;
-                const double g = Gm[e < RR ? e : 0];
-                v[q] *= use ? g : 1.0;
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < EPT; ++q) {
-            const int e = tid + 256 * q;
-            if (e < RR) {
-                const int r = e / R;
-                sm.A[r * P + (e - r * R)] = v[q];
-            }
-        }
-    }
+    hadamard_to_lds<RM, 256>(Gall, order, n, R, sm.A, P);
     sm.col[tid] = 0.0;
     __syncthreads();
     if (tid < 64) {
-        // this kernel usually shares its compute unit with MTTKRP waves;
-        // its one serial wave goes first at instruction issue
-        __builtin_amdgcn_s_setprio(3);
-        const int i = tid;
-        const bool row = i < R;
-        double a[RM];
-#pragma unroll
-        for (int k = 0; k < RM; ++k) a[k] = row && k < R ? sm.A[i * P + k] : 0.0;
-        const double piv = lane_read(a[0], 0);
-        bool bad = !(piv > 0.0);
-        const double d = sqrt(piv);
-        double l = i == 0 ? d : a[0] / d;  // this lane's entry of column j
-        double *const Lrow = sm.A + (row ? i * P : RM * P);
-        const int lastw = row ? 1 : 0;  // rows past R - 1 keep writing the spare entry
-        int j = 0;
-        if constexpr (RM >= 64)
-            for (; j < R - 48; ++j)
-                chol_wave_step<64>(a, l, bad, i, j, R, sm.col + (j & 1) * 128, Lrow + j * lastw);
-        if constexpr (RM >= 48)
-            for (; j < R - 32; ++j)
-                chol_wave_step<48>(a, l, bad, i, j, R, sm.col + (j & 1) * 128, Lrow + j * lastw);
-        if constexpr (RM >= 32)
-            for (; j < R - 16; ++j)
-                chol_wave_step<32>(a, l, bad, i, j, R, sm.col + (j & 1) * 128, Lrow + j * lastw);
-        for (; j < R; ++j)
-            chol_wave_step<16>(a, l, bad, i, j, R, sm.col + (j & 1) * 128, Lrow + j * lastw);
-        if (i == 0) sm.fail = bad;
+        // L overwrites V in place: a row's entries are read into registers
+        // before any is written
+        const bool bad = chol_wave_factor<RM>(sm.A, R, sm.col, sm.A, P, 1, sm.A, P, 1,
+                                              sm.A + RM * P);
+        if (tid == 0) sm.fail = bad;
     }
     __syncthreads();
     if (sm.fail) {
@@ -391,10 +422,11 @@ __device__ __forceinline__ void subst_step(double (&a)[RM], double rdj,
     a[W - 1] = 0.0;
 }
 
-// The solve, normalization and Gram refresh of one mode in one workgroup
-// (four waves, one per SIMD), for R <= RM <= 64 and a mode whose solution,
-// L and L^T fit in LDS together.  The arithmetic is that of
-// als_solve_wave_kernel, als_normalize_kernel and gram_kernel, in the same
+// A whole mode step after its MTTKRP in one workgroup (four waves, one per
+// SIMD), for R <= RM <= 64 and a mode whose solution, L and L^T fit in LDS
+// together: V and its Cholesky factor (as in als_chol_wave_kernel), then the
+// solve, normalization and Gram refresh, with the arithmetic of
+// als_solve_wave_kernel, als_normalize_kernel and gram_kernel in the same
 // order, except that the substitutions multiply by the reciprocals of L's
 // diagonal instead of dividing by it (results within a rounding of the
 // divisions).
@@ -408,34 +440,44 @@ __device__ __forceinline__ void subst_step(double (&a)[RM], double rdj,
 //  - Normalization: a thread per column forms the norm (rows in order); then
 //    every thread scales a share of the entries.
 //  - Gram: a thread per 4 x 4 block of entries (rows in order).
+// A non-positive pivot sets the flag to 1 and writes nothing else.
 template <typename T, int RM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
-als_update_small_kernel(const double *__restrict__ M, const double *__restrict__ L, int64_t I64,
-                        int64_t R64, T *__restrict__ Uout, double *__restrict__ lam64,
-                        T *__restrict__ lamT, double *__restrict__ G,
-                        const int *__restrict__ flag)
+als_update_small_kernel(const double *__restrict__ Gall, int order, int n,
+                        const double *__restrict__ M, int64_t I64, int64_t R64,
+                        T *__restrict__ Uout, double *__restrict__ lam64,
+                        T *__restrict__ lamT, double *__restrict__ G, int *__restrict__ flag)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     if (*flag) return;
     const int I = (int)I64, R = (int)R64;  // R <= RM, sizes checked by the host
     const int RR = R * R;
-    double *Lr = reinterpret_cast<double *>(smem) + 64;  // L, rows; 64 zeros before
+    constexpr int PV = RM + 1;  // pitch of V
+    double *col = reinterpret_cast<double *>(smem);      // 256: factorization's column buffers
+    double *Lr = col + 256 + 64;                         // L, rows; 64 zeros before
     double *Lt = Lr + RR;                                // L^T, rows; 64 zeros after
-    double *x = Lt + RR + 64;                            // I x R solution, then U
-    double *rd = x + (size_t)I * R;                      // 1 / L_jj, then lambda
-    double *spare = rd + 64;                             // writes of rows past I - 1
+    double *x = Lt + RR + 64;                            // V (pitch PV), then the I x R solution, then U
+    const int nx = RM * PV > I * R ? RM * PV : I * R;
+    double *rd = x + nx;                                 // 1 / L_jj, then lambda
+    double *spare = rd + 64;                             // writes of rows past the end
+    int &fail = *reinterpret_cast<int *>(spare + 1);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (int e = tid; e < 64; e += 256) {
-        Lr[e - 64] = 0.0;
-        Lt[RR + e] = 0.0;
-    }
-    for (int e = tid; e < RR; e += 256) {
-        const int r = e / R, c = e - (e / R) * R;
-        const double v = L[e];
-        Lr[e] = v;
-        Lt[c * R + r] = v;
+    hadamard_to_lds<RM, 256>(Gall, order, n, R, x, PV);
+    col[tid] = 0.0;
+    if (tid < 64) {
+        Lr[tid - 64] = 0.0;
+        Lt[RR + tid] = 0.0;
     }
     __syncthreads();
+    if (tid < 64) {
+        const bool bad = chol_wave_factor<RM>(x, R, col, Lr, R, 1, Lt, 1, R, spare);
+        if (tid == 0) fail = bad;
+    }
+    __syncthreads();
+    if (fail) {
+        if (tid == 0) *flag = 1;
+        return;
+    }
     if (tid < R) rd[tid] = 1.0 / Lr[tid * R + tid];
     __syncthreads();
     for (int r0 = 64 * wave; r0 < I; r0 += 256) {
@@ -660,15 +702,18 @@ hipError_t launch_normalize(const double *Unew, int64_t I, int64_t R, T *Uout, d
 size_t update_small_lds(int64_t I, int64_t R)
 {
     if (R > 64 || I > (1 << 20)) return 0;
-    const size_t b = (size_t)(2 * R * R + I * R + 4 * 64 + 1) * sizeof(double);
-    return b <= 160 * 1024 ? b : 0;
+    const int64_t rm = R <= 16 ? 16 : R <= 32 ? 32 : 64;
+    const int64_t nx = std::max(rm * (rm + 1), I * R);
+    const size_t b = (size_t)(256 + 128 + 2 * R * R + nx + 64 + 2) * sizeof(double);
+    return b <= 150 * 1024 ? b : 0;
 }
 
 hipError_t allow_large_lds(const void *k);
 
 template <typename T>
-hipError_t launch_update_small(const double *M, const double *L, int64_t I, int64_t R, T *Uout,
-                               double *lam64, T *lamT, double *G, const int *flag, hipStream_t s)
+hipError_t launch_update_small(const double *Gall, int order, int n, const double *M, int64_t I,
+                               int64_t R, T *Uout, double *lam64, T *lamT, double *G, int *flag,
+                               hipStream_t s)
 {
     const size_t lds = update_small_lds(I, R);
     if (!lds) return hipErrorInvalidValue;
@@ -679,7 +724,8 @@ hipError_t launch_update_small(const double *M, const double *L, int64_t I, int6
         const hipError_t a = allow_large_lds(reinterpret_cast<const void *>(k));
         if (a != hipSuccess) return a;
     }
-    hipLaunchKernelGGL(k, dim3(1), dim3(256), lds, s, M, L, I, R, Uout, lam64, lamT, G, flag);
+    hipLaunchKernelGGL(k, dim3(1), dim3(256), lds, s, Gall, order, n, M, I, R, Uout, lam64, lamT,
+                       G, flag);
     return hipGetLastError();
 }
 
@@ -705,8 +751,8 @@ template hipError_t launch_sumsq<double>(const double *, int64_t, double *, int,
 template hipError_t launch_sumsq<float>(const float *, int64_t, double *, int, double *, hipStream_t);
 template hipError_t launch_gram<double>(const double *, int64_t, int64_t, double *, const int *, hipStream_t);
 template hipError_t launch_gram<float>(const float *, int64_t, int64_t, double *, const int *, hipStream_t);
-template hipError_t launch_update_small<double>(const double *, const double *, int64_t, int64_t, double *, double *, double *, double *, const int *, hipStream_t);
-template hipError_t launch_update_small<float>(const double *, const double *, int64_t, int64_t, float *, double *, float *, double *, const int *, hipStream_t);
+template hipError_t launch_update_small<double>(const double *, int, int, const double *, int64_t, int64_t, double *, double *, double *, double *, int *, hipStream_t);
+template hipError_t launch_update_small<float>(const double *, int, int, const double *, int64_t, int64_t, float *, double *, float *, double *, int *, hipStream_t);
 template hipError_t launch_normalize<double>(const double *, int64_t, int64_t, double *, double *, double *, const int *, hipStream_t);
 template hipError_t launch_normalize<float>(const double *, int64_t, int64_t, float *, double *, float *, const int *, hipStream_t);
 template hipError_t launch_fill<double>(double *, int64_t, double, hipStream_t);

@@ -41,8 +41,9 @@ template <typename T>
 hipError_t launch_fill(T *p, int64_t n, T v, hipStream_t s);
 size_t update_small_lds(int64_t I, int64_t R);
 template <typename T>
-hipError_t launch_update_small(const double *M, const double *L, int64_t I, int64_t R, T *Uout,
-                               double *lam64, T *lamT, double *G, const int *flag, hipStream_t s);
+hipError_t launch_update_small(const double *Gall, int order, int n, const double *M, int64_t I,
+                               int64_t R, T *Uout, double *lam64, T *lamT, double *G, int *flag,
+                               hipStream_t s);
 template <typename T>
 hipError_t launch_fit(const double *M, const T *Ulast, int64_t Ilast, const double *lam64,
                       const double *Gall, int order, int64_t R, double *scal, int *flag,
@@ -418,23 +419,6 @@ int cp_als_entry(const T *X, const int64_t *dims, int order, int64_t rank, T *co
         if (!ok(launch_gram<T>(factors[m], dims[m], R, G + (size_t)m * R * R, flag, s)))
             return MTTKRP_EHIP;
 
-    // The Cholesky factor of mode n's V depends only on the Grams, not on the
-    // mode's MTTKRP: it runs on a second stream beside the MTTKRP launches
-    // (one workgroup, latency-bound), forked after the previous mode's Gram
-    // refresh and joined before the solve.
-    hipStream_t side = nullptr;
-    if (side_stream(&side) != hipSuccess) return MTTKRP_EHIP;
-    struct Events {
-        hipEvent_t fork = nullptr, join = nullptr;
-        ~Events()
-        {
-            if (fork) (void)hipEventDestroy(fork);
-            if (join) (void)hipEventDestroy(join);
-        }
-    } ev;
-    if (!ok(hipEventCreateWithFlags(&ev.fork, hipEventDisableTiming))) return MTTKRP_EHIP;
-    if (!ok(hipEventCreateWithFlags(&ev.join, hipEventDisableTiming))) return MTTKRP_EHIP;
-
     // Each sweep's fit and flag land in host-visible pinned memory (two
     // slots, written by the fit kernel).  The host reads sweep it - 1's slot
     // only after sweep it is queued, so the device never waits for the host;
@@ -486,20 +470,20 @@ int cp_als_entry(const T *X, const int64_t *dims, int order, int64_t rank, T *co
     for (int m = 0; m < order; ++m) cf[m] = factors[m];
     for (int it = 0; it < iters; ++it) {
         for (int n = 0; n < order; ++n) {
-            if (!ok(hipEventRecord(ev.fork, s))) return MTTKRP_EHIP;
-            if (!ok(hipStreamWaitEvent(side, ev.fork, 0))) return MTTKRP_EHIP;
-            if (!ok(launch_chol(G, order, n, R, Lc, flag, side))) return MTTKRP_EHIP;
-            if (!ok(hipEventRecord(ev.join, side))) return MTTKRP_EHIP;
             st = mttkrp_one<T>(X, dims, order, cf, R, n, M, 1, w + L.mt, L.M - L.mt, s);
             if (st) return st;
-            if (!ok(hipStreamWaitEvent(s, ev.join, 0))) return MTTKRP_EHIP;
             if (update_small_lds(dims[n], R)) {
-                // solve, normalization and Gram refresh in one workgroup
-                if (!ok(launch_update_small<T>(M, Lc, dims[n], R, factors[n], lam64, lambda,
-                                               G + (size_t)n * R * R, flag, s)))
+                // Cholesky, solve, normalization and Gram refresh in one
+                // workgroup
+                if (!ok(launch_update_small<T>(G, order, n, M, dims[n], R, factors[n], lam64,
+                                               lambda, G + (size_t)n * R * R, flag, s)))
                     return MTTKRP_EHIP;
                 continue;
             }
+            // (the factor is not hidden beside the MTTKRP on a second stream:
+            // sharing the chip with the MTTKRP slowed the one-workgroup
+            // factorization about threefold, more than the overlap gained)
+            if (!ok(launch_chol(G, order, n, R, Lc, flag, s))) return MTTKRP_EHIP;
             if (!ok(launch_solve(M, Lc, dims[n], R, Unew, flag, s))) return MTTKRP_EHIP;
             if (!ok(launch_normalize<T>(Unew, dims[n], R, factors[n], lam64, lambda, flag, s)))
                 return MTTKRP_EHIP;
