@@ -24,6 +24,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 
 namespace mttkrp {
 
@@ -402,24 +403,143 @@ __global__ __launch_bounds__(256) void als_normalize_kernel(const double *__rest
     if (lamT) lamT[r] = (T)lam;
 }
 
-// One substitution step for a wave whose lanes hold one row each, with a
-// frame of W registers (a[k] holds component j + S k, S = +1 forward, -1
-// back; every component past the frame is out of range).  The component
-// a[0] is final after the pivot product: it is stored to xj, and its
-// multiples e[S k] (k >= 1, uniform across lanes) are taken off the rest of
-// the frame, which shifts by one.
-template <int W, int S, int RM>
-__device__ __forceinline__ void subst_step(double (&a)[RM], double rdj,
-                                           const double *__restrict__ e, double *__restrict__ xj)
+// Quad-local lane moves (DPP quad permutations): the value of lane 0 of this
+// lane's group of four, and the value of the next lane of the group (lane 3
+// gets its own).
+__device__ __forceinline__ double quad_first(double v)
 {
-    double cv[W];
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)u, 0x00, 0xf, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(u >> 32), 0x00, 0xf, 0xf, false);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double quad_next(double v)
+{
+    constexpr int kNext = 1 | (2 << 2) | (3 << 4) | (3 << 6);
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)u, kNext, 0xf, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(u >> 32), kNext, 0xf, 0xf, false);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Substitution frames split over groups of four lanes: lane 4 r + q holds
+// quarter q of row r's frame (16 rows per wave).  With quarter width w,
+// register t of quarter q holds component j + S (q w + t) (S = +1 forward,
+// -1 back).
+
+// One step: x = (component j) / L_jj from quarter 0, handed to the group;
+// every quarter takes x times its L entries cv[t] (entries for offsets
+// q w + 1 + t) off its components, shifting by one, the top register taking
+// the next quarter's first component.  Quarter 0 of a valid row stores x.
+// The next step's reciprocal and entries (rdn, en) are read before this
+// step's arithmetic.
+template <int w, int S, int RQ>
+__device__ __forceinline__ void subst_step4(double (&a)[RQ], double (&cv)[RQ], double &rdj,
+                                            const double *__restrict__ rdn,
+                                            const double *__restrict__ en,
+                                            double *__restrict__ xj, int q)
+{
+    double cn[w];
 #pragma unroll
-    for (int k = 1; k < W; ++k) cv[k] = e[S * k];
-    const double x = a[0] * rdj;
+    for (int t = 0; t < w; ++t) cn[t] = en[S * t];
+    const double rn = *rdn;
+    const double x = quad_first(a[0] * rdj);
     *xj = x;
+    const double up = quad_next(a[0]);
+    const double nxt = q == 3 ? 0.0 : up;
 #pragma unroll
-    for (int k = 1; k < W; ++k) a[k - 1] = __builtin_fma(-cv[k], x, a[k]);
-    a[W - 1] = 0.0;
+    for (int t = 0; t < w - 1; ++t) a[t] = __builtin_fma(-cv[t], x, a[t + 1]);
+    a[w - 1] = __builtin_fma(-cv[w - 1], x, nxt);
+#pragma unroll
+    for (int t = 0; t < w; ++t) cv[t] = cn[t];
+    rdj = rn;
+}
+
+// Moves a frame from quarter width wf to wt (the frame narrows by 16
+// components) through the row's own LDS storage: every in-range component is
+// written at its place, then read back in the new layout.
+template <int wf, int wt, int S, int RQ>
+__device__ __forceinline__ void restage4(double (&a)[RQ], double *__restrict__ xrow, int j, int R,
+                                         bool ok, int q)
+{
+    if (wf > 0) {
+#pragma unroll
+        for (int t = 0; t < wf; ++t) {
+            const int c = j + S * (q * wf + t);
+            if (ok && c >= 0 && c < R) xrow[c] = a[t];
+        }
+    }
+    // the wave's LDS operations are performed in issue order
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int t = 0; t < wt; ++t) {
+        const int c = j + S * (q * wt + t);
+        a[t] = ok && c >= 0 && c < R ? xrow[c] : 0.0;
+    }
+#pragma unroll
+    for (int t = wt; t < RQ; ++t) a[t] = 0.0;
+}
+
+// One substitution pass (S = +1: L y = m from the row in xrow; S = -1:
+// L^T u = y) over rows of 4 lanes, the frame narrowing from 64 to 16
+// components as the unsolved part shrinks.  E: L^T rows forward, L rows back
+// (with 64 zero entries past the end the pass reads).
+template <int S, int RQ>
+__device__ __forceinline__ void subst_pass4(double *__restrict__ xrow, double *__restrict__ xout,
+                                            int xs, const double *__restrict__ E,
+                                            const double *__restrict__ rd, int R, bool ok, int q)
+{
+    double a[RQ], cv[RQ];
+    int j = S > 0 ? 0 : R - 1;
+    int w = 0;  // current quarter width (0: nothing loaded yet)
+    double rdj = 0.0;
+    // this step's operands (on entry to a segment) and the next step's
+    // (inside it; the index is clamped at the ends)
+    auto ent = [&](int jj, int ww) { return E + jj * R + jj + S * (q * ww + 1); };
+    auto nj = [&]() { const int t = j + S; return t < 0 ? 0 : (t >= R ? R - 1 : t); };
+    auto enter = [&](auto wc) {
+        constexpr int ww = decltype(wc)::value;
+        const double *e = ent(j, ww);
+#pragma unroll
+        for (int t = 0; t < ww; ++t) cv[t] = e[S * t];
+        rdj = rd[j];
+    };
+    if constexpr (RQ >= 16)
+        if (R > 48) {
+            restage4<0, 16, S>(a, xrow, j, R, ok, q);
+            enter(std::integral_constant<int, 16>());
+            w = 16;
+#pragma unroll 2
+            for (; S > 0 ? j < R - 48 : j >= 48; j += S)
+                subst_step4<16, S>(a, cv, rdj, rd + nj(), ent(nj(), 16), xout + j * xs, q);
+            restage4<16, 12, S>(a, xrow, j, R, ok, q);
+            w = 12;
+        }
+    if constexpr (RQ >= 16)
+        if (R > 32) {
+            if (w == 0) restage4<0, 12, S>(a, xrow, j, R, ok, q);
+            enter(std::integral_constant<int, 12>());
+#pragma unroll 2
+            for (; S > 0 ? j < R - 32 : j >= 32; j += S)
+                subst_step4<12, S>(a, cv, rdj, rd + nj(), ent(nj(), 12), xout + j * xs, q);
+            restage4<12, 8, S>(a, xrow, j, R, ok, q);
+            w = 8;
+        }
+    if constexpr (RQ >= 8)
+        if (R > 16) {
+            if (w == 0) restage4<0, 8, S>(a, xrow, j, R, ok, q);
+            enter(std::integral_constant<int, 8>());
+#pragma unroll 2
+            for (; S > 0 ? j < R - 16 : j >= 16; j += S)
+                subst_step4<8, S>(a, cv, rdj, rd + nj(), ent(nj(), 8), xout + j * xs, q);
+            restage4<8, 4, S>(a, xrow, j, R, ok, q);
+            w = 4;
+        }
+    if (w == 0) restage4<0, 4, S>(a, xrow, j, R, ok, q);
+    enter(std::integral_constant<int, 4>());
+#pragma unroll 2
+    for (; S > 0 ? j < R : j >= 0; j += S)
+        subst_step4<4, S>(a, cv, rdj, rd + nj(), ent(nj(), 4), xout + j * xs, q);
 }
 
 // A whole mode step after its MTTKRP in one workgroup (four waves, one per
@@ -480,35 +600,28 @@ als_update_small_kernel(const double *__restrict__ Gall, int order, int n,
     }
     if (tid < R) rd[tid] = 1.0 / Lr[tid * R + tid];
     __syncthreads();
-    for (int r0 = 64 * wave; r0 < I; r0 += 256) {
-        const int row = r0 + lane;
-        const bool ok = row < I;
-        double *xrow = ok ? x + (size_t)row * R : spare;
-        const int xs = ok ? 1 : 0;  // rows past I - 1 keep writing the spare entry
-        double a[RM];
-        // forward, L y = m: a[k] holds component j + k
+    {
+        const int q = lane & 3;  // quarter of the row's frame this lane holds
+        constexpr int RQ = RM / 4;
+        for (int r0 = 16 * wave; r0 < I; r0 += 64) {
+            const int row = r0 + (lane >> 2);
+            const bool ok = row < I;
+            double *xrow = x + (size_t)(ok ? row : 0) * R;
+            // quarter 0 of a valid row stores the unknowns; other lanes the
+            // spare entry
+            const bool st = ok && q == 0;
+            double *xout = st ? xrow : spare;
+            const int xs = st ? 1 : 0;
+            // the row of M into its LDS storage, a quarter per block
 #pragma unroll
-        for (int k = 0; k < RM; ++k) a[k] = ok && k < R ? M[(size_t)(ok ? row : 0) * R + k] : 0.0;
-        int j = 0;
-        if constexpr (RM >= 64)
-            for (; j < R - 48; ++j) subst_step<64, 1>(a, rd[j], Lt + j * R + j, xrow + j * xs);
-        if constexpr (RM >= 48)
-            for (; j < R - 32; ++j) subst_step<48, 1>(a, rd[j], Lt + j * R + j, xrow + j * xs);
-        if constexpr (RM >= 32)
-            for (; j < R - 16; ++j) subst_step<32, 1>(a, rd[j], Lt + j * R + j, xrow + j * xs);
-        for (; j < R; ++j) subst_step<16, 1>(a, rd[j], Lt + j * R + j, xrow + j * xs);
-        // back, L^T u = y: a[k] holds component j - k (this lane's own row
-        // of x, so no exchange is needed)
-#pragma unroll
-        for (int k = 0; k < RM; ++k) a[k] = ok && k < R ? x[(size_t)(ok ? row : 0) * R + R - 1 - k] : 0.0;
-        j = R - 1;
-        if constexpr (RM >= 64)
-            for (; j >= 48; --j) subst_step<64, -1>(a, rd[j], Lr + j * R + j, xrow + j * xs);
-        if constexpr (RM >= 48)
-            for (; j >= 32; --j) subst_step<48, -1>(a, rd[j], Lr + j * R + j, xrow + j * xs);
-        if constexpr (RM >= 32)
-            for (; j >= 16; --j) subst_step<32, -1>(a, rd[j], Lr + j * R + j, xrow + j * xs);
-        for (; j >= 0; --j) subst_step<16, -1>(a, rd[j], Lr + j * R + j, xrow + j * xs);
+            for (int t = 0; t < RQ; ++t) {
+                const int c = q * RQ + t;
+                if (ok && c < R) xrow[c] = M[(size_t)row * R + c];
+            }
+            subst_pass4<1, RQ>(xrow, xout, xs, Lt, rd, R, ok, q);
+            __builtin_amdgcn_wave_barrier();
+            subst_pass4<-1, RQ>(xrow, xout, xs, Lr, rd, R, ok, q);
+        }
     }
     __syncthreads();
     // column norms (rows in order), then the normalized factor; the LDS copy
@@ -535,6 +648,7 @@ als_update_small_kernel(const double *__restrict__ Gall, int order, int n,
     for (int blk = tid; blk < nb4 * nb4; blk += 256) {
         const int a0 = (blk / nb4) * 4, c0 = (blk - (blk / nb4) * nb4) * 4;
         double g[4][4] = {};
+#pragma unroll 4
         for (int i = 0; i < I; ++i) {
             double ua[4], uc[4];
 #pragma unroll

@@ -43,7 +43,9 @@ def rel(a, b):
 @pytest.mark.parametrize("dims,true_rank,R,iters", [
     ((12, 10, 8), 3, 4, 1), ((12, 10, 8), 3, 4, 6), ((9, 8, 7, 6), 2, 5, 5),
     ((6, 5, 7, 4, 3), 2, 3, 4), ((40, 35, 30), 5, 70, 3),
-    ((80, 12, 10), 3, 64, 2),  # mode 0 too tall for the one-workgroup update, modes 1-2 not
+    ((80, 12, 10), 3, 64, 2),  # mode 0: two 64-row passes of the one-workgroup update
+    ((200, 12, 10), 3, 64, 2),  # mode 0 too tall for the one-workgroup update, modes 1-2 not
+    ((70, 9, 8), 3, 40, 2), ((33, 21, 17), 3, 20, 2),  # frames that start 48 and 32 wide
 ])
 def test_als_small_vs_oracle(dims, true_rank, R, iters):
     p = inputs.random_cp_problem(dims, true_rank, R, sigma=0.05, seed=31)
