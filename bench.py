@@ -73,6 +73,45 @@ def measured_traffic(workload: str):
     return None
 
 
+def khatri_rao(U, modes):
+    """The explicit Khatri-Rao matrix of the factors of `modes` (in mode
+    order): row (i_a, i_b, ...) with the last index fastest, column r holds
+    prod_m U_m(i_m, r)."""
+    R = U[modes[0]].shape[1]
+    K = U[modes[0]]
+    for m in modes[1:]:
+        K = (K[:, None, :] * U[m][None, :, :]).reshape(-1, R)
+    return K
+
+
+def unfold(X, n):
+    """Mode-n unfolding of a row-major tensor (columns: the other indices in
+    mode order, the last fastest).  A view for the first and last modes (the
+    last as a transposed view), a permuted copy otherwise."""
+    d = X.dim()
+    if n == 0:
+        return X.reshape(X.shape[0], -1)
+    if n == d - 1:
+        return X.reshape(-1, X.shape[-1]).t()
+    others = [m for m in range(d) if m != n]
+    return X.permute(n, *others).contiguous().reshape(X.shape[n], -1)
+
+
+def explicit_kr_mttkrp(X, U, n):
+    """The matrix-based MTTKRP the GenTen page compares against (its Fig. 3):
+    form the Khatri-Rao product of the other factors explicitly, unfold X
+    along mode n, and multiply with the vendor GEMM (torch.matmul, i.e.
+    hipBLASLt / rocBLAS).  A comparison baseline only: the product path never
+    forms the Khatri-Rao matrix.  Returns (M_n, khatri_rao_bytes,
+    unfold_copy_bytes)."""
+    import torch
+    d = X.dim()
+    K = khatri_rao(U, [m for m in range(d) if m != n])
+    Xn = unfold(X, n)
+    copy_bytes = 0 if n in (0, d - 1) else Xn.numel() * Xn.element_size()
+    return torch.matmul(Xn, K), K.numel() * K.element_size(), copy_bytes
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -87,6 +126,8 @@ def main():
     ap.add_argument("--cold-reps", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-als", action="store_true", help="skip the CP-ALS timing (5-way workload)")
+    ap.add_argument("--no-gemm-baseline", action="store_true",
+                    help="skip the explicit Khatri-Rao + vendor GEMM comparison")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
@@ -303,6 +344,50 @@ def main():
                "mttkrp_ms_per_iter": round(t_mt * 1e3, 4),
                "mttkrp_share": round(t_mt / t_als, 3)}
 
+    # ---- the matrix-based comparison (explicit Khatri-Rao matrix, unfolded
+    # X, vendor GEMM): time per mode with its extra memory, and its largest
+    # difference from this library's outputs ----
+    gemm = None
+    if not args.no_gemm_baseline:
+        ms, kr_b, cp_b, diff = [], [], [], 0.0
+        parts = {"khatri_rao_ms": [], "unfold_ms": [], "gemm_ms": []}
+        for n in range(d):
+            explicit_kr_mttkrp(X, U, n)  # warm-up (library handles, allocations)
+            torch.cuda.synchronize()
+            reps = 3
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            t_parts = [0.0, 0.0, 0.0]
+            for _ in range(reps):
+                ev[0].record(stream)
+                K = khatri_rao(U, [m for m in range(d) if m != n])
+                ev[1].record(stream)
+                Xn = unfold(X, n)
+                ev[2].record(stream)
+                Mn = torch.matmul(Xn, K)
+                ev[3].record(stream)
+                torch.cuda.synchronize()
+                for i in range(3):
+                    t_parts[i] += ev[i].elapsed_time(ev[i + 1]) / reps
+            for key, v in zip(parts, t_parts):
+                parts[key].append(round(v, 4))
+            ms.append(sum(t_parts))
+            kr_b.append(K.numel() * K.element_size())
+            cp_b.append(0 if n in (0, d - 1) else Xn.numel() * Xn.element_size())
+            del K, Xn
+            api.mttkrp(X, U, n, out=outs[n], ws=ws, stream=stream)
+            torch.cuda.synchronize()
+            ref = outs[n].double()
+            diff = max(diff, float((Mn.double() - ref).norm() / ref.norm().clamp_min(1e-300)))
+            del Mn
+        torch.cuda.empty_cache()
+        gemm = {"kind": "explicit Khatri-Rao + torch.matmul (vendor GEMM)",
+                "ms_per_mode": [round(v, 4) for v in ms], **parts,
+                "gflops_all_mode": round(d * flops_mode / (sum(ms) / 1e3) / 1e9, 2),
+                "khatri_rao_bytes_per_mode": kr_b, "unfold_copy_bytes_per_mode": cp_b,
+                "library_workspace_bytes": ws_bytes,
+                "rel_diff_vs_library": diff}
+        log(f"[bench] explicit-KR GEMM baseline {gemm}")
+
     cfg = {"workload": p.name, "dims": list(dims), "rank": R, "modes": list(range(d)),
            "step": "all-mode MTTKRP sweep", "cache": "warm (back-to-back sweeps)"}
     line = {
@@ -324,6 +409,7 @@ def main():
         "cold_cache": cold,
         "cpu_baseline": cpu,
         "cp_als": als,
+        "gemm_baseline": gemm,
     }
     print(json.dumps(line), flush=True)
 
