@@ -126,6 +126,9 @@ def main():
     ap.add_argument("--cold-reps", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-als", action="store_true", help="skip the CP-ALS timing (5-way workload)")
+    ap.add_argument("--als-iters", type=int, default=0,
+                    help="time this many CP-ALS sweeps on any workload (default: ten on the "
+                         "5-way workload only)")
     ap.add_argument("--no-gemm-baseline", action="store_true",
                     help="skip the explicit Khatri-Rao + vendor GEMM comparison")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -314,13 +317,13 @@ def main():
     # solves, normalization, Gram refresh; then the fit, one read-back), and
     # the share of it that the per-mode MTTKRP launches take ----
     als = None
-    if p.als_iters and not args.no_als:
-        iters = 10
+    if (p.als_iters or args.als_iters) and not args.no_als:
+        iters = args.als_iters or 10
         ws_als = torch.empty(api.cp_als_workspace_bytes(dims, R, X.dtype), dtype=torch.uint8,
                              device=dev)
         U0 = [u.clone() for u in U]
         Ua = [u.clone() for u in U0]
-        api.cp_als(X, Ua, iters=2, ws=ws_als, stream=stream)  # warm-up
+        api.cp_als(X, Ua, iters=min(2, iters), ws=ws_als, stream=stream)  # warm-up
         torch.cuda.synchronize()
         Ua = [u.clone() for u in U0]
         torch.cuda.synchronize()

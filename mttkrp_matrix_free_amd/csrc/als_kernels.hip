@@ -86,74 +86,6 @@ __global__ __launch_bounds__(256) void gram_kernel(const T *__restrict__ U, int6
     G[e] = s;
 }
 
-// V = Hadamard_{m != n} G_m and its Cholesky factor L (lower, row-major, in
-// place in Lout).  One workgroup; V lives in LDS when it fits, else in Lout.
-__global__ __launch_bounds__(1024) void als_chol_kernel(const double *__restrict__ Gall,
-                                                        int order, int n, int64_t R,
-                                                        double *__restrict__ Lout,
-                                                        int *__restrict__ flag, int use_lds)
-{
-    extern __shared__ __align__(16) unsigned char smem[];
-    if (*flag) return;
-    double *A = use_lds ? reinterpret_cast<double *>(smem) : Lout;
-    __shared__ int fail;
-    const int tid = threadIdx.x, nt = blockDim.x;
-    const int64_t RR = R * R;
-    // Row pitch of A: R + 1 in LDS (a column read by consecutive threads
-    // then falls on different banks), R in the global fallback.
-    const int64_t P = use_lds ? R + 1 : R;
-    for (int64_t e = tid; e < RR; e += nt) {
-        double v = 1.0;
-        for (int m = 0; m < order; ++m)
-            if (m != n) v *= Gall[(int64_t)m * RR + e];
-        A[(e / R) * P + (e - (e / R) * R)] = v;
-    }
-    if (tid == 0) fail = 0;
-    __syncthreads();
-    // Column by column, right-looking: once column j of L is known, every
-    // entry below the diagonal of the trailing block takes its update
-    //   A_ik -= L_ij L_kj  (i >= k > j)
-    // at once.  Each entry receives its subtractions in the order j = 0, 1,
-    // ... exactly as in the textbook dot products
-    //   L_jj = sqrt(V_jj - sum_{k<j} L_jk^2),  L_ij = (V_ij - sum_{k<j} L_ik L_jk) / L_jj,
-    // so the factor is the same; the work per column is spread over the
-    // workgroup instead of running as one thread's dot product.
-    for (int64_t j = 0; j < R; ++j) {
-        if (tid == 0) {
-            const double d = A[j * P + j];
-            if (!(d > 0.0))
-                fail = 1;
-            else
-                A[j * P + j] = sqrt(d);
-        }
-        __syncthreads();
-        if (fail) break;
-        const double ljj = A[j * P + j];
-        for (int64_t i = j + 1 + tid; i < R; i += nt) A[i * P + j] = A[i * P + j] / ljj;
-        __syncthreads();
-        // trailing block (rows and columns j+1..R-1, lower triangle): thread
-        // (ti, tk) of a 32 x 32 grid takes rows ti, ti+32, ... and columns
-        // tk, tk+32, ... (32-bit indices: R is at most 4096)
-        const int Ri = (int)P, jj = (int)j;
-        const int ti = tid >> 5, tk = tid & 31, ni = nt >> 5;
-        for (int i = jj + 1 + ti; i < (int)R; i += ni) {
-            const double lij = A[i * Ri + jj];
-            for (int k = jj + 1 + tk; k <= i; k += 32)
-                A[i * Ri + k] = __builtin_fma(-lij, A[k * Ri + jj], A[i * Ri + k]);
-        }
-        __syncthreads();
-    }
-    if (fail) {
-        if (tid == 0) *flag = 1;
-        return;
-    }
-    // zero the strict upper triangle and copy out
-    for (int64_t e = tid; e < RR; e += nt) {
-        const int64_t i = e / R, c = e - (e / R) * R;
-        Lout[e] = c > i ? 0.0 : A[i * P + c];
-    }
-}
-
 // Lane read of a double (the lane index is wave-uniform).
 __device__ __forceinline__ double lane_read(double v, int l)
 {
@@ -241,9 +173,11 @@ __device__ __forceinline__ void hadamard_to_lds(const double *__restrict__ Gall,
 // every lane reads its entries with broadcast reads, all issued before the
 // first is used.  The next column's pivot, square root and divisions come
 // from the first updated register before the rest of the update, so their
-// latency overlaps it.  Every entry of L receives the operations of
-// als_chol_kernel in the same order (the factors are equal); entries above
-// the diagonal take throwaway updates and are written as zeros.  L_ij goes
+// latency overlaps it.  Every entry of L receives the operations of the
+// textbook column-by-column factorization,
+//   L_jj = sqrt(V_jj - sum_{k<j} L_jk^2),  L_ij = (V_ij - sum_{k<j} L_ik L_jk) / L_jj,
+// with the subtractions applied one at a time in the order k = 0, 1, ...;
+// entries above the diagonal take throwaway updates and are written as zeros.  L_ij goes
 // to out1[i * s1r + j * s1c] and out2[i * s2r + j * s2c]; rows past R - 1
 // write to spare.  Returns (in every lane) whether a pivot was not positive.
 template <int RM>
@@ -347,37 +281,6 @@ __global__ __launch_bounds__(256) void als_solve_wave_kernel(const double *__res
         if (lane < j) b -= L[(int64_t)j * R + lane] * xj;
     }
     if (lane < R) Unew[row * R + lane] = b;
-}
-
-// Row solves for any R: one workgroup per row, the row vector in LDS.
-__global__ __launch_bounds__(256) void als_solve_block_kernel(const double *__restrict__ M,
-                                                              const double *__restrict__ L,
-                                                              int64_t I, int64_t R,
-                                                              double *__restrict__ Unew,
-                                                              const int *__restrict__ flag)
-{
-    extern __shared__ __align__(16) unsigned char smem[];
-    if (*flag) return;
-    double *x = reinterpret_cast<double *>(smem);
-    const int64_t row = blockIdx.x;
-    const int tid = threadIdx.x;
-    for (int64_t i = tid; i < R; i += 256) x[i] = M[row * R + i];
-    __syncthreads();
-    for (int64_t j = 0; j < R; ++j) {
-        const double xj = x[j] / L[j * R + j];
-        __syncthreads();
-        if (tid == 0) x[j] = xj;
-        for (int64_t i = j + 1 + tid; i < R; i += 256) x[i] -= L[i * R + j] * xj;
-        __syncthreads();
-    }
-    for (int64_t j = R - 1; j >= 0; --j) {
-        const double xj = x[j] / L[j * R + j];
-        __syncthreads();
-        if (tid == 0) x[j] = xj;
-        for (int64_t i = tid; i < j; i += 256) x[i] -= L[j * R + i] * xj;
-        __syncthreads();
-    }
-    for (int64_t i = tid; i < R; i += 256) Unew[row * R + i] = x[i];
 }
 
 // lambda_r = ||U_new(:, r)||_2 and U_n = U_new / lambda_r; one thread per column.
@@ -689,7 +592,8 @@ __global__ __launch_bounds__(kRedThreads) void als_fit_kernel(
     const double *__restrict__ M, const T *__restrict__ Ulast, int64_t Ilast,
     const double *__restrict__ lam64, const double *__restrict__ Gall, int order, int64_t R,
     double *__restrict__ scal, int *__restrict__ flag, double tol, int have_prev,
-    double *__restrict__ out_fit, int *__restrict__ out_flag)
+    double *__restrict__ out_fit, int *__restrict__ out_flag, const double *__restrict__ mparts,
+    int nmparts)
 {
     __shared__ double sh[kRedThreads / 64];
     const int f0 = *flag;
@@ -709,7 +613,9 @@ __global__ __launch_bounds__(kRedThreads) void als_fit_kernel(
     const int64_t RR = R * R;
     double nrm2 = 0.0;
     constexpr int Q = 8;
-    for (int64_t e0 = threadIdx.x; e0 < RR; e0 += (int64_t)kRedThreads * Q) {
+    // (large R: the sum comes in partials from als_model_norm_kernel)
+    for (int i = threadIdx.x; i < nmparts; i += kRedThreads) nrm2 += mparts[i];
+    for (int64_t e0 = threadIdx.x; nmparts == 0 && e0 < RR; e0 += (int64_t)kRedThreads * Q) {
         double v[Q];
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
@@ -750,6 +656,216 @@ __global__ __launch_bounds__(kRedThreads) void als_fit_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Blocked R x R work for ranks past what one workgroup holds (R > 64): the
+// Cholesky factor and the two row substitutions in 64-wide column blocks, the
+// diagonal blocks by one wave (as above), the panels by rows in parallel, and
+// the trailing updates as tiled products.  Within a block every entry gets
+// the textbook operations; across blocks the updates are summed per block
+// before they are applied, so the factor differs from the one-entry-at-a-time
+// order by rounding only.
+// ---------------------------------------------------------------------------
+
+// V = Hadamard_{m != n} G_m (R x R, fp64), one thread per entry, modes in order.
+__global__ __launch_bounds__(256) void als_hadamard_kernel(const double *__restrict__ Gall,
+                                                           int order, int n, int64_t R,
+                                                           double *__restrict__ A,
+                                                           const int *__restrict__ flag)
+{
+    if (*flag) return;
+    const int64_t RR = R * R;
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= RR) return;
+    double v = 1.0;
+    for (int m = 0; m < order; ++m)
+        if (m != n) v *= Gall[(int64_t)m * RR + e];
+    A[e] = v;
+}
+
+// Factor the diagonal block at (k0, k0), nb = min(64, R - k0) wide, of A
+// (R x R, row-major) in place: its lower triangle becomes L_kk, its strict
+// upper triangle zeros.  A non-positive pivot sets the flag to 1.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
+als_chol_diag_kernel(double *__restrict__ A, int64_t R, int64_t k0, int *__restrict__ flag)
+{
+    constexpr int RM = 64, P = RM + 1;
+    struct Smem {
+        double col[256];
+        double B[RM * P + 1];
+        int fail;
+    };
+    __shared__ Smem sm;
+    if (*flag) return;
+    const int tid = threadIdx.x;
+    const int nb = (int)(R - k0 < 64 ? R - k0 : 64);
+    double *Ad = A + k0 * R + k0;
+    for (int e = tid; e < nb * nb; e += 256) {
+        const int r = e / nb, c = e - (e / nb) * nb;
+        sm.B[r * P + c] = Ad[(int64_t)r * R + c];
+    }
+    sm.col[tid] = 0.0;
+    __syncthreads();
+    if (tid < 64) {
+        const bool bad = chol_wave_factor<RM>(sm.B, nb, sm.col, sm.B, P, 1, sm.B, P, 1,
+                                              sm.B + RM * P);
+        if (tid == 0) sm.fail = bad;
+    }
+    __syncthreads();
+    if (sm.fail) {
+        if (tid == 0) *flag = 1;
+        return;
+    }
+    for (int e = tid; e < nb * nb; e += 256) {
+        const int r = e / nb, c = e - (e / nb) * nb;
+        Ad[(int64_t)r * R + c] = sm.B[r * P + c];
+    }
+}
+
+// Row-block substitution with the diagonal block L_kk (nb = min(64, R - k0)
+// wide, at (k0, k0) of L, R x R row-major): every row x of the nb columns of
+// B starting at col0 (rows rows, leading dimension ldb) becomes the solution
+// of  x L_kk^T = b  (S = +1: a forward substitution) or  x L_kk = b  (S = -1:
+// a back substitution), in place.  32 rows per workgroup (two waves), each
+// row on a quad of lanes (as in the one-workgroup update above); the
+// products use the reciprocals of L_kk's diagonal.
+constexpr int kTrsmRows = 32;
+template <int S>
+__global__ __launch_bounds__(2 * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
+als_trsm_rows_kernel(const double *__restrict__ L, int64_t R, int64_t k0,
+                     double *__restrict__ B, int64_t ldb, int64_t col0, int64_t rows,
+                     const int *__restrict__ flag)
+{
+    constexpr int RM = 64, NT = 2 * 64;
+    // L_kk^T rows (forward) or L_kk rows (back) with 64 zeros on the side the
+    // pass reads past, the reciprocals, the workgroup's rows and a spare entry
+    __shared__ double Lb[64 + RM * RM];
+    __shared__ double rd[64];
+    __shared__ double xs[kTrsmRows * RM + 1];
+    if (*flag) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nb = (int)(R - k0 < 64 ? R - k0 : 64);
+    double *E = S > 0 ? Lb : Lb + 64;
+    const double *Lkk = L + k0 * R + k0;
+    if (tid < 64) {
+        if (S > 0)
+            Lb[nb * nb + tid] = 0.0;
+        else
+            Lb[tid] = 0.0;
+    }
+    for (int e = tid; e < nb * nb; e += NT) {
+        const int r = e / nb, c = e - (e / nb) * nb;
+        const double v = Lkk[(int64_t)r * R + c];
+        if (S > 0)
+            E[c * nb + r] = v;  // L_kk^T
+        else
+            E[e] = v;
+    }
+    const int64_t r0 = (int64_t)blockIdx.x * kTrsmRows;
+    for (int e = tid; e < kTrsmRows * nb; e += NT) {
+        const int r = e / nb, c = e - (e / nb) * nb;
+        xs[e] = r0 + r < rows ? B[(r0 + r) * ldb + col0 + c] : 0.0;
+    }
+    __syncthreads();
+    if (tid < nb) rd[tid] = 1.0 / Lkk[(int64_t)tid * R + tid];
+    __syncthreads();
+    {
+        const int q = lane & 3;
+        const int rloc = 16 * wave + (lane >> 2);
+        const bool ok = r0 + rloc < rows;
+        double *xrow = xs + rloc * nb;
+        const bool st = ok && q == 0;
+        double *xout = st ? xrow : xs + kTrsmRows * RM;
+        subst_pass4<S, RM / 4>(xrow, xout, st ? 1 : 0, E, rd, nb, ok, q);
+    }
+    __syncthreads();
+    for (int e = tid; e < kTrsmRows * nb; e += NT) {
+        const int r = e / nb, c = e - (e / nb) * nb;
+        if (r0 + r < rows) B[(r0 + r) * ldb + col0 + c] = xs[e];
+    }
+}
+
+// C (m x n, leading dimension ldc) = beta C + alpha A B with A(i, t) at
+// A[i sai + t sat] and B(t, j) at B[t sbt + j sbj] (element type TA for both;
+// beta = 0 writes alpha A B without reading C).  A thread owns a 4 x 4 block
+// of a 64 x 64 tile and sums over t in increasing order.  lower: tiles above
+// the diagonal are skipped.
+template <typename TA>
+__global__ __launch_bounds__(256) void als_gemm_kernel(double *__restrict__ C, int64_t ldc,
+                                                       const TA *__restrict__ A, int64_t sai,
+                                                       int64_t sat, const TA *__restrict__ B,
+                                                       int64_t sbt, int64_t sbj, int64_t m,
+                                                       int64_t n, int64_t K, double alpha,
+                                                       double beta, int lower,
+                                                       const int *__restrict__ flag)
+{
+    constexpr int KT = 16;
+    __shared__ double As[KT][64 + 1];
+    __shared__ double Bs[KT][64 + 1];
+    if (*flag) return;
+    const int64_t ti = blockIdx.y, tj = blockIdx.x;
+    if (lower && tj > ti) return;
+    const int tid = threadIdx.x;
+    const int ty = tid >> 4, tx = tid & 15;  // rows 4 ty .. 4 ty + 3, columns 4 tx .. 4 tx + 3
+    const int64_t i0 = ti * 64, j0 = tj * 64;
+    double acc[4][4] = {};
+    for (int64_t t0 = 0; t0 < K; t0 += KT) {
+        for (int e = tid; e < KT * 64; e += 256) {
+            const int t = e >> 6, r = e & 63;
+            const int64_t tt = t0 + t;
+            As[t][r] = (tt < K && i0 + r < m) ? (double)A[(i0 + r) * sai + tt * sat] : 0.0;
+            Bs[t][r] = (tt < K && j0 + r < n) ? (double)B[tt * sbt + (j0 + r) * sbj] : 0.0;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+            double a[4], b[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                a[u] = As[t][4 * ty + u];
+                b[u] = Bs[t][4 * tx + u];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[u][v] = __builtin_fma(a[u], b[v], acc[u][v]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int64_t i = i0 + 4 * ty + u, j = j0 + 4 * tx + v;
+            if (i < m && j < n) {
+                double *c = C + i * ldc + j;
+                *c = beta == 0.0 ? alpha * acc[u][v] : __builtin_fma(alpha, acc[u][v], beta * *c);
+            }
+        }
+}
+
+// ||model||^2 partials for large R: workgroup w sums the entries
+// e = w * 256 + tid + k * 256 * gridDim in increasing k per thread, then
+// over the workgroup in a fixed order; als_fit_kernel adds the partials in
+// workgroup order.
+__global__ __launch_bounds__(kRedThreads) void als_model_norm_kernel(
+    const double *__restrict__ lam64, const double *__restrict__ Gall, int order, int64_t R,
+    double *__restrict__ parts, const int *__restrict__ flag)
+{
+    __shared__ double sh[kRedThreads / 64];
+    if (*flag) return;
+    const int64_t RR = R * R;
+    double s = 0.0;
+    for (int64_t e = (int64_t)blockIdx.x * kRedThreads + threadIdx.x; e < RR;
+         e += (int64_t)gridDim.x * kRedThreads) {
+        const int64_t a = e / R, b = e - (e / R) * R;
+        double v = lam64[a] * lam64[b];
+        for (int m = 0; m < order; ++m) v *= Gall[(int64_t)m * RR + e];
+        s += v;
+    }
+    s = block_sum(s, sh);
+    if (threadIdx.x == 0) parts[blockIdx.x] = s;
+}
+
+// ---------------------------------------------------------------------------
 // Host launchers (used by the C-ABI driver)
 // ---------------------------------------------------------------------------
 
@@ -767,6 +883,13 @@ hipError_t launch_sumsq(const T *X, int64_t N, double *partial, int nparts, doub
 template <typename T>
 hipError_t launch_gram(const T *U, int64_t I, int64_t R, double *G, const int *flag, hipStream_t s)
 {
+    if (R > 64) {
+        // G = U^T U as a tiled product (the same per-entry order over i)
+        const unsigned nt = (unsigned)((R + 63) / 64);
+        hipLaunchKernelGGL(als_gemm_kernel<T>, dim3(nt, nt), dim3(256), 0, s, G, R, U, (int64_t)1,
+                           R, U, R, (int64_t)1, R, R, I, 1.0, 0.0, 0, flag);
+        return hipGetLastError();
+    }
     const int64_t n = R * R;
     hipLaunchKernelGGL(gram_kernel<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, U, I, R,
                        G, flag);
@@ -776,30 +899,20 @@ hipError_t launch_gram(const T *U, int64_t I, int64_t R, double *G, const int *f
 hipError_t launch_chol(const double *Gall, int order, int n, int64_t R, double *L, int *flag,
                        hipStream_t s)
 {
-    if (R <= 64) {
-        auto k = R <= 16 ? als_chol_wave_kernel<16>
-                 : R <= 32 ? als_chol_wave_kernel<32>
-                           : als_chol_wave_kernel<64>;
-        hipLaunchKernelGGL(k, dim3(1), dim3(256), 0, s, Gall, order, n, (int)R, L, flag);
-        return hipGetLastError();
-    }
-    const size_t bytes = (size_t)R * (R + 1) * sizeof(double);
-    const int use_lds = bytes <= 64 * 1024;
-    hipLaunchKernelGGL(als_chol_kernel, dim3(1), dim3(1024), use_lds ? bytes : 0, s, Gall, order,
-                       n, R, L, flag, use_lds);
+    if (R > 64) return hipErrorInvalidValue;  // larger ranks: launch_chol_blocked
+    auto k = R <= 16 ? als_chol_wave_kernel<16>
+             : R <= 32 ? als_chol_wave_kernel<32>
+                       : als_chol_wave_kernel<64>;
+    hipLaunchKernelGGL(k, dim3(1), dim3(256), 0, s, Gall, order, n, (int)R, L, flag);
     return hipGetLastError();
 }
 
 hipError_t launch_solve(const double *M, const double *L, int64_t I, int64_t R, double *Unew,
                         const int *flag, hipStream_t s)
 {
-    if (R <= 64) {
-        hipLaunchKernelGGL(als_solve_wave_kernel, dim3((unsigned)((I + 3) / 4)), dim3(256), 0, s, M,
-                           L, I, R, Unew, flag);
-    } else {
-        hipLaunchKernelGGL(als_solve_block_kernel, dim3((unsigned)I), dim3(256),
-                           (size_t)R * sizeof(double), s, M, L, I, R, Unew, flag);
-    }
+    if (R > 64) return hipErrorInvalidValue;  // larger ranks: launch_solve_blocked
+    hipLaunchKernelGGL(als_solve_wave_kernel, dim3((unsigned)((I + 3) / 4)), dim3(256), 0, s, M, L,
+                       I, R, Unew, flag);
     return hipGetLastError();
 }
 
@@ -854,10 +967,77 @@ hipError_t launch_fill(T *p, int64_t n, T v, hipStream_t s)
 template <typename T>
 hipError_t launch_fit(const double *M, const T *Ulast, int64_t Ilast, const double *lam64,
                       const double *Gall, int order, int64_t R, double *scal, int *flag,
-                      double tol, int have_prev, double *out_fit, int *out_flag, hipStream_t s)
+                      double tol, int have_prev, double *out_fit, int *out_flag, double *parts,
+                      int max_parts, hipStream_t s)
 {
+    int np = 0;
+    if (R * R > 65536) {
+        np = (int)std::min<int64_t>(max_parts, (R * R + 2047) / 2048);
+        hipLaunchKernelGGL(als_model_norm_kernel, dim3(np), dim3(kRedThreads), 0, s, lam64, Gall,
+                           order, R, parts, flag);
+    }
     hipLaunchKernelGGL(als_fit_kernel<T>, dim3(1), dim3(kRedThreads), 0, s, M, Ulast, Ilast, lam64,
-                       Gall, order, R, scal, flag, tol, have_prev, out_fit, out_flag);
+                       Gall, order, R, scal, flag, tol, have_prev, out_fit, out_flag, parts, np);
+    return hipGetLastError();
+}
+
+// The blocked factorization of V = Hadamard_{m != n} G_m into A (R x R).
+hipError_t launch_chol_blocked(const double *Gall, int order, int n, int64_t R, double *A,
+                               int *flag, hipStream_t s)
+{
+    const int64_t RR = R * R;
+    hipLaunchKernelGGL(als_hadamard_kernel, dim3((unsigned)((RR + 255) / 256)), dim3(256), 0, s,
+                       Gall, order, n, R, A, flag);
+    for (int64_t k0 = 0; k0 < R; k0 += 64) {
+        const int64_t nb = std::min<int64_t>(64, R - k0), rest = R - k0 - nb;
+        hipLaunchKernelGGL(als_chol_diag_kernel, dim3(1), dim3(256), 0, s, A, R, k0, flag);
+        if (rest == 0) break;
+        // panel: rows below the block solve x L_kk^T = a
+        hipLaunchKernelGGL(als_trsm_rows_kernel<1>,
+                           dim3((unsigned)((rest + kTrsmRows - 1) / kTrsmRows)), dim3(128), 0, s,
+                           (const double *)A, R, k0, A + (k0 + nb) * R, R, k0, rest, flag);
+        // trailing block (lower tiles): A22 -= L21 L21^T
+        const double *L21 = A + (k0 + nb) * R + k0;
+        const unsigned nt = (unsigned)((rest + 63) / 64);
+        hipLaunchKernelGGL(als_gemm_kernel<double>, dim3(nt, nt), dim3(256), 0, s,
+                           A + (k0 + nb) * R + k0 + nb, R, L21, R, (int64_t)1, L21, (int64_t)1, R,
+                           rest, rest, nb, -1.0, 1.0, 1, (const int *)flag);
+    }
+    return hipGetLastError();
+}
+
+// U_new = M V^{-1} with the blocked factor L (R x R): rows of M copied to
+// Unew, then forward (Y L^T = M) and back (U L = Y) substitution by column
+// blocks, each block's result taken off the remaining columns by a product.
+hipError_t launch_solve_blocked(const double *M, const double *L, int64_t I, int64_t R,
+                                double *Unew, const int *flag, hipStream_t s)
+{
+    hipError_t e = hipMemcpyAsync(Unew, M, (size_t)(I * R) * sizeof(double),
+                                  hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return e;
+    const unsigned gr = (unsigned)((I + kTrsmRows - 1) / kTrsmRows), gi = (unsigned)((I + 63) / 64);
+    for (int64_t k0 = 0; k0 < R; k0 += 64) {
+        const int64_t nb = std::min<int64_t>(64, R - k0), rest = R - k0 - nb;
+        hipLaunchKernelGGL(als_trsm_rows_kernel<1>, dim3(gr), dim3(128), 0, s, L, R, k0, Unew, R,
+                           k0, I, flag);
+        if (rest == 0) break;
+        // Y(:, later) -= Y(:, block) L(later, block)^T
+        hipLaunchKernelGGL(als_gemm_kernel<double>, dim3((unsigned)((rest + 63) / 64), gi),
+                           dim3(256), 0, s, Unew + k0 + nb, R, (const double *)(Unew + k0), R,
+                           (int64_t)1, L + (k0 + nb) * R + k0, (int64_t)1, R, I, rest, nb, -1.0,
+                           1.0, 0, flag);
+    }
+    const int64_t last = ((R - 1) / 64) * 64;
+    for (int64_t k0 = last; k0 >= 0; k0 -= 64) {
+        hipLaunchKernelGGL(als_trsm_rows_kernel<-1>, dim3(gr), dim3(128), 0, s, L, R, k0, Unew, R,
+                           k0, I, flag);
+        if (k0 == 0) break;
+        const int64_t nb = std::min<int64_t>(64, R - k0);
+        // U(:, earlier) -= U(:, block) L(block, earlier)
+        hipLaunchKernelGGL(als_gemm_kernel<double>, dim3((unsigned)((k0 + 63) / 64), gi),
+                           dim3(256), 0, s, Unew, R, (const double *)(Unew + k0), R, (int64_t)1,
+                           L + k0 * R, R, (int64_t)1, I, k0, nb, -1.0, 1.0, 0, flag);
+    }
     return hipGetLastError();
 }
 
@@ -872,7 +1052,7 @@ template hipError_t launch_normalize<float>(const double *, int64_t, int64_t, fl
 template hipError_t launch_fill<double>(double *, int64_t, double, hipStream_t);
 template hipError_t launch_fill<float>(float *, int64_t, float, hipStream_t);
 template hipError_t launch_fill<int>(int *, int64_t, int, hipStream_t);
-template hipError_t launch_fit<double>(const double *, const double *, int64_t, const double *, const double *, int, int64_t, double *, int *, double, int, double *, int *, hipStream_t);
-template hipError_t launch_fit<float>(const double *, const float *, int64_t, const double *, const double *, int, int64_t, double *, int *, double, int, double *, int *, hipStream_t);
+template hipError_t launch_fit<double>(const double *, const double *, int64_t, const double *, const double *, int, int64_t, double *, int *, double, int, double *, int *, double *, int, hipStream_t);
+template hipError_t launch_fit<float>(const double *, const float *, int64_t, const double *, const double *, int, int64_t, double *, int *, double, int, double *, int *, double *, int, hipStream_t);
 
 }  // namespace mttkrp

@@ -30,6 +30,10 @@ hipError_t launch_sumsq(const T *X, int64_t N, double *partial, int nparts, doub
                         hipStream_t s);
 template <typename T>
 hipError_t launch_gram(const T *U, int64_t I, int64_t R, double *G, const int *flag, hipStream_t s);
+hipError_t launch_chol_blocked(const double *Gall, int order, int n, int64_t R, double *A,
+                               int *flag, hipStream_t s);
+hipError_t launch_solve_blocked(const double *M, const double *L, int64_t I, int64_t R,
+                                double *Unew, const int *flag, hipStream_t s);
 hipError_t launch_chol(const double *Gall, int order, int n, int64_t R, double *L, int *flag,
                        hipStream_t s);
 hipError_t launch_solve(const double *M, const double *L, int64_t I, int64_t R, double *Unew,
@@ -47,7 +51,8 @@ hipError_t launch_update_small(const double *Gall, int order, int n, const doubl
 template <typename T>
 hipError_t launch_fit(const double *M, const T *Ulast, int64_t Ilast, const double *lam64,
                       const double *Gall, int order, int64_t R, double *scal, int *flag,
-                      double tol, int have_prev, double *out_fit, int *out_flag, hipStream_t s);
+                      double tol, int have_prev, double *out_fit, int *out_flag, double *parts,
+                      int max_parts, hipStream_t s);
 
 namespace {
 
@@ -483,8 +488,16 @@ int cp_als_entry(const T *X, const int64_t *dims, int order, int64_t rank, T *co
             // (the factor is not hidden beside the MTTKRP on a second stream:
             // sharing the chip with the MTTKRP slowed the one-workgroup
             // factorization about threefold, more than the overlap gained)
-            if (!ok(launch_chol(G, order, n, R, Lc, flag, s))) return MTTKRP_EHIP;
-            if (!ok(launch_solve(M, Lc, dims[n], R, Unew, flag, s))) return MTTKRP_EHIP;
+            if (R <= 64) {
+                if (!ok(launch_chol(G, order, n, R, Lc, flag, s))) return MTTKRP_EHIP;
+                if (!ok(launch_solve(M, Lc, dims[n], R, Unew, flag, s))) return MTTKRP_EHIP;
+            } else {
+                // 64-wide column blocks: diagonal blocks by one wave, panels by
+                // rows in parallel, trailing updates as tiled products
+                if (!ok(launch_chol_blocked(G, order, n, R, Lc, flag, s))) return MTTKRP_EHIP;
+                if (!ok(launch_solve_blocked(M, Lc, dims[n], R, Unew, flag, s)))
+                    return MTTKRP_EHIP;
+            }
             if (!ok(launch_normalize<T>(Unew, dims[n], R, factors[n], lam64, lambda, flag, s)))
                 return MTTKRP_EHIP;
             if (!ok(launch_gram<T>(factors[n], dims[n], R, G + (size_t)n * R * R, flag, s)))
@@ -492,7 +505,8 @@ int cp_als_entry(const T *X, const int64_t *dims, int order, int64_t rank, T *co
         }
         Slot *slot = pin.p + (it & 1);
         if (!ok(launch_fit<T>(M, factors[order - 1], dims[order - 1], lam64, G, order, R, scal,
-                              flag, tol, it > 0, &slot->fit, &slot->flag, s)))
+                              flag, tol, it > 0, &slot->fit, &slot->flag, parts, kSumsqParts,
+                              s)))
             return MTTKRP_EHIP;
         if (!ok(hipEventRecord(pin.done[it & 1], s))) return MTTKRP_EHIP;
         if (it > 0) {

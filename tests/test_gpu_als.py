@@ -46,6 +46,9 @@ def rel(a, b):
     ((80, 12, 10), 3, 64, 2),  # mode 0: two 64-row passes of the one-workgroup update
     ((200, 12, 10), 3, 64, 2),  # mode 0 too tall for the one-workgroup update, modes 1-2 not
     ((70, 9, 8), 3, 40, 2), ((33, 21, 17), 3, 20, 2),  # frames that start 48 and 32 wide
+    # blocked factorization and solves (R > 64): 3 blocks, a 4-way case with a
+    # ragged last block, and R = 300 (the model norm summed by workgroups)
+    ((30, 28, 26), 3, 150, 2), ((12, 11, 10, 9), 2, 100, 2), ((40, 38, 36), 3, 300, 2),
 ])
 def test_als_small_vs_oracle(dims, true_rank, R, iters):
     p = inputs.random_cp_problem(dims, true_rank, R, sigma=0.05, seed=31)
@@ -94,6 +97,22 @@ def test_als_not_spd_leaves_factors():
     X = dev(p.X)
     U = [dev(u) for u in Z]
     lam, fit, done, st = api.cp_als(X, U, 3)
+    assert st == _lib.ENOTSPD and done == 0
+    assert all(np.isnan(f) for f in fit)
+    for m in range(3):
+        assert np.array_equal(U[m].cpu().numpy(), Z[m])
+
+
+def test_als_not_spd_blocked_leaves_factors():
+    # R > 64 (the blocked factorization): a zero column makes a pivot of the
+    # second block exactly zero, if no earlier one fails
+    p = inputs.random_cp_problem((10, 9, 8), 2, 80, sigma=0.0, seed=35)
+    Z = [u.copy() for u in p.factors]
+    for u in Z:
+        u[:, 70] = 0.0
+    X = dev(p.X)
+    U = [dev(u) for u in Z]
+    lam, fit, done, st = api.cp_als(X, U, 2)
     assert st == _lib.ENOTSPD and done == 0
     assert all(np.isnan(f) for f in fit)
     for m in range(3):
