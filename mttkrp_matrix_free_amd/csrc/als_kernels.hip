@@ -593,7 +593,7 @@ __global__ __launch_bounds__(kRedThreads) void als_fit_kernel(
     const double *__restrict__ lam64, const double *__restrict__ Gall, int order, int64_t R,
     double *__restrict__ scal, int *__restrict__ flag, double tol, int have_prev,
     double *__restrict__ out_fit, int *__restrict__ out_flag, const double *__restrict__ mparts,
-    int nmparts)
+    int nmparts, const double *__restrict__ colsum)
 {
     __shared__ double sh[kRedThreads / 64];
     const int f0 = *flag;
@@ -604,7 +604,10 @@ __global__ __launch_bounds__(kRedThreads) void als_fit_kernel(
     double inner = 0.0;
     for (int64_t r = threadIdx.x; r < R; r += kRedThreads) {
         double s = 0.0;
-        for (int64_t i = 0; i < Ilast; ++i) s += M[i * R + r] * (double)Ulast[i * R + r];
+        if (colsum)
+            s = colsum[r];  // (large R: the same sums, formed by als_colsum_kernel)
+        else
+            for (int64_t i = 0; i < Ilast; ++i) s += M[i * R + r] * (double)Ulast[i * R + r];
         inner += lam64[r] * s;
     }
     inner = block_sum(inner, sh);
@@ -683,103 +686,68 @@ __global__ __launch_bounds__(256) void als_hadamard_kernel(const double *__restr
 
 // Factor the diagonal block at (k0, k0), nb = min(64, R - k0) wide, of A
 // (R x R, row-major) in place: its lower triangle becomes L_kk, its strict
-// upper triangle zeros.  A non-positive pivot sets the flag to 1.
+// upper triangle zeros.  Then the inverse's transpose X = L_kk^{-T} (rows of
+// X solve x L_kk^T = e_r: forward substitutions of the identity's rows, on
+// lane quads as in the one-workgroup update) goes to W rows k0 .. k0 + nb - 1
+// (pitch 64), so that the panel and row solves with L_kk become products.
+// A non-positive pivot sets the flag to 1.  Dynamic LDS: kCholDiagLds bytes.
+constexpr int kCholDiagDoubles = 256 + (64 * 65 + 1) + (64 * 64 + 64) + 64 + (64 * 64 + 1) + 1;
+constexpr size_t kCholDiagLds = kCholDiagDoubles * sizeof(double);
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
-als_chol_diag_kernel(double *__restrict__ A, int64_t R, int64_t k0, int *__restrict__ flag)
+als_chol_diag_kernel(double *__restrict__ A, int64_t R, int64_t k0, double *__restrict__ W,
+                     int *__restrict__ flag)
 {
     constexpr int RM = 64, P = RM + 1;
-    struct Smem {
-        double col[256];
-        double B[RM * P + 1];
-        int fail;
-    };
-    __shared__ Smem sm;
+    extern __shared__ __align__(16) unsigned char smem[];
+    double *col = reinterpret_cast<double *>(smem);  // 256
+    double *Bk = col + 256;                             // 64 x 65 (+1 spare)
+    double *E = Bk + RM * P + 1;                        // L_kk^T rows, 64 zeros after
+    double *rd = E + RM * RM + 64;                      // 1 / L_jj
+    double *xs = rd + 64;                               // 64 identity rows, then X (+1 spare)
+    int &fail = *reinterpret_cast<int *>(xs + RM * RM + 1);
     if (*flag) return;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nb = (int)(R - k0 < 64 ? R - k0 : 64);
     double *Ad = A + k0 * R + k0;
     for (int e = tid; e < nb * nb; e += 256) {
         const int r = e / nb, c = e - (e / nb) * nb;
-        sm.B[r * P + c] = Ad[(int64_t)r * R + c];
+        Bk[r * P + c] = Ad[(int64_t)r * R + c];
     }
-    sm.col[tid] = 0.0;
+    col[tid] = 0.0;
     __syncthreads();
     if (tid < 64) {
-        const bool bad = chol_wave_factor<RM>(sm.B, nb, sm.col, sm.B, P, 1, sm.B, P, 1,
-                                              sm.B + RM * P);
-        if (tid == 0) sm.fail = bad;
+        const bool bad =
+            chol_wave_factor<RM>(Bk, nb, col, Bk, P, 1, Bk, P, 1, Bk + RM * P);
+        if (tid == 0) fail = bad;
     }
     __syncthreads();
-    if (sm.fail) {
+    if (fail) {
         if (tid == 0) *flag = 1;
         return;
     }
     for (int e = tid; e < nb * nb; e += 256) {
         const int r = e / nb, c = e - (e / nb) * nb;
-        Ad[(int64_t)r * R + c] = sm.B[r * P + c];
+        const double v = Bk[r * P + c];
+        Ad[(int64_t)r * R + c] = v;
+        E[c * nb + r] = v;
+        xs[e] = r == c ? 1.0 : 0.0;
     }
-}
-
-// Row-block substitution with the diagonal block L_kk (nb = min(64, R - k0)
-// wide, at (k0, k0) of L, R x R row-major): every row x of the nb columns of
-// B starting at col0 (rows rows, leading dimension ldb) becomes the solution
-// of  x L_kk^T = b  (S = +1: a forward substitution) or  x L_kk = b  (S = -1:
-// a back substitution), in place.  32 rows per workgroup (two waves), each
-// row on a quad of lanes (as in the one-workgroup update above); the
-// products use the reciprocals of L_kk's diagonal.
-constexpr int kTrsmRows = 32;
-template <int S>
-__global__ __launch_bounds__(2 * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
-als_trsm_rows_kernel(const double *__restrict__ L, int64_t R, int64_t k0,
-                     double *__restrict__ B, int64_t ldb, int64_t col0, int64_t rows,
-                     const int *__restrict__ flag)
-{
-    constexpr int RM = 64, NT = 2 * 64;
-    // L_kk^T rows (forward) or L_kk rows (back) with 64 zeros on the side the
-    // pass reads past, the reciprocals, the workgroup's rows and a spare entry
-    __shared__ double Lb[64 + RM * RM];
-    __shared__ double rd[64];
-    __shared__ double xs[kTrsmRows * RM + 1];
-    if (*flag) return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nb = (int)(R - k0 < 64 ? R - k0 : 64);
-    double *E = S > 0 ? Lb : Lb + 64;
-    const double *Lkk = L + k0 * R + k0;
-    if (tid < 64) {
-        if (S > 0)
-            Lb[nb * nb + tid] = 0.0;
-        else
-            Lb[tid] = 0.0;
-    }
-    for (int e = tid; e < nb * nb; e += NT) {
-        const int r = e / nb, c = e - (e / nb) * nb;
-        const double v = Lkk[(int64_t)r * R + c];
-        if (S > 0)
-            E[c * nb + r] = v;  // L_kk^T
-        else
-            E[e] = v;
-    }
-    const int64_t r0 = (int64_t)blockIdx.x * kTrsmRows;
-    for (int e = tid; e < kTrsmRows * nb; e += NT) {
-        const int r = e / nb, c = e - (e / nb) * nb;
-        xs[e] = r0 + r < rows ? B[(r0 + r) * ldb + col0 + c] : 0.0;
-    }
-    __syncthreads();
-    if (tid < nb) rd[tid] = 1.0 / Lkk[(int64_t)tid * R + tid];
+    if (tid < 64) E[nb * nb + tid] = 0.0;
+    if (tid < nb) rd[tid] = 1.0 / Bk[tid * P + tid];
     __syncthreads();
     {
         const int q = lane & 3;
-        const int rloc = 16 * wave + (lane >> 2);
-        const bool ok = r0 + rloc < rows;
-        double *xrow = xs + rloc * nb;
+        const int r = 16 * wave + (lane >> 2);
+        const bool ok = r < nb;
+        double *xrow = xs + (ok ? r : 0) * nb;
         const bool st = ok && q == 0;
-        double *xout = st ? xrow : xs + kTrsmRows * RM;
-        subst_pass4<S, RM / 4>(xrow, xout, st ? 1 : 0, E, rd, nb, ok, q);
+        double *xout = st ? xrow : xs + RM * RM;
+        subst_pass4<1, RM / 4>(xrow, xout, st ? 1 : 0, E, rd, nb, ok, q);
     }
     __syncthreads();
-    for (int e = tid; e < kTrsmRows * nb; e += NT) {
+    for (int e = tid; e < nb * nb; e += 256) {
         const int r = e / nb, c = e - (e / nb) * nb;
-        if (r0 + r < rows) B[(r0 + r) * ldb + col0 + c] = xs[e];
+        W[(k0 + r) * 64 + c] = xs[e];
     }
 }
 
@@ -840,6 +808,22 @@ __global__ __launch_bounds__(256) void als_gemm_kernel(double *__restrict__ C, i
                 *c = beta == 0.0 ? alpha * acc[u][v] : __builtin_fma(alpha, acc[u][v], beta * *c);
             }
         }
+}
+
+// sum_i M(i, r) U(i, r) for every column r (rows in order), one thread per column.
+template <typename T>
+__global__ __launch_bounds__(256) void als_colsum_kernel(const double *__restrict__ M,
+                                                         const T *__restrict__ U, int64_t I,
+                                                         int64_t R, double *__restrict__ out,
+                                                         const int *__restrict__ flag)
+{
+    if (*flag) return;
+    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (r >= R) return;
+    double s = 0.0;
+#pragma unroll 8
+    for (int64_t i = 0; i < I; ++i) s += M[i * R + r] * (double)U[i * R + r];
+    out[r] = s;
 }
 
 // ||model||^2 partials for large R: workgroup w sums the entries
@@ -968,8 +952,14 @@ template <typename T>
 hipError_t launch_fit(const double *M, const T *Ulast, int64_t Ilast, const double *lam64,
                       const double *Gall, int order, int64_t R, double *scal, int *flag,
                       double tol, int have_prev, double *out_fit, int *out_flag, double *parts,
-                      int max_parts, hipStream_t s)
+                      int max_parts, double *colsum_buf, hipStream_t s)
 {
+    const double *colsum = nullptr;
+    if (R > 256) {
+        hipLaunchKernelGGL(als_colsum_kernel<T>, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, s,
+                           M, Ulast, Ilast, R, colsum_buf, flag);
+        colsum = colsum_buf;
+    }
     int np = 0;
     if (R * R > 65536) {
         np = (int)std::min<int64_t>(max_parts, (R * R + 2047) / 2048);
@@ -977,49 +967,60 @@ hipError_t launch_fit(const double *M, const T *Ulast, int64_t Ilast, const doub
                            order, R, parts, flag);
     }
     hipLaunchKernelGGL(als_fit_kernel<T>, dim3(1), dim3(kRedThreads), 0, s, M, Ulast, Ilast, lam64,
-                       Gall, order, R, scal, flag, tol, have_prev, out_fit, out_flag, parts, np);
+                       Gall, order, R, scal, flag, tol, have_prev, out_fit, out_flag, parts, np,
+                       colsum);
     return hipGetLastError();
 }
 
-// The blocked factorization of V = Hadamard_{m != n} G_m into A (R x R).
+// The blocked factorization of V = Hadamard_{m != n} G_m into A (R x R);
+// W (R x 64) receives the diagonal blocks' L_kk^{-T}.
 hipError_t launch_chol_blocked(const double *Gall, int order, int n, int64_t R, double *A,
-                               int *flag, hipStream_t s)
+                               double *W, int *flag, hipStream_t s)
 {
+    const hipError_t a = allow_large_lds(reinterpret_cast<const void *>(als_chol_diag_kernel));
+    if (a != hipSuccess) return a;
     const int64_t RR = R * R;
     hipLaunchKernelGGL(als_hadamard_kernel, dim3((unsigned)((RR + 255) / 256)), dim3(256), 0, s,
                        Gall, order, n, R, A, flag);
     for (int64_t k0 = 0; k0 < R; k0 += 64) {
         const int64_t nb = std::min<int64_t>(64, R - k0), rest = R - k0 - nb;
-        hipLaunchKernelGGL(als_chol_diag_kernel, dim3(1), dim3(256), 0, s, A, R, k0, flag);
+        hipLaunchKernelGGL(als_chol_diag_kernel, dim3(1), dim3(256), kCholDiagLds, s, A, R, k0, W,
+                           flag);
         if (rest == 0) break;
-        // panel: rows below the block solve x L_kk^T = a
-        hipLaunchKernelGGL(als_trsm_rows_kernel<1>,
-                           dim3((unsigned)((rest + kTrsmRows - 1) / kTrsmRows)), dim3(128), 0, s,
-                           (const double *)A, R, k0, A + (k0 + nb) * R, R, k0, rest, flag);
-        // trailing block (lower tiles): A22 -= L21 L21^T
-        const double *L21 = A + (k0 + nb) * R + k0;
         const unsigned nt = (unsigned)((rest + 63) / 64);
+        // panel: L21 = A21 L_kk^{-T} (in place: a workgroup reads its rows'
+        // whole block before it writes)
+        double *P21 = A + (k0 + nb) * R + k0;
+        hipLaunchKernelGGL(als_gemm_kernel<double>, dim3(1, nt), dim3(256), 0, s, P21, R,
+                           (const double *)P21, R, (int64_t)1, (const double *)(W + k0 * 64),
+                           (int64_t)64, (int64_t)1, rest, nb, nb, 1.0, 0.0, 0, (const int *)flag);
+        // trailing block (lower tiles): A22 -= L21 L21^T
         hipLaunchKernelGGL(als_gemm_kernel<double>, dim3(nt, nt), dim3(256), 0, s,
-                           A + (k0 + nb) * R + k0 + nb, R, L21, R, (int64_t)1, L21, (int64_t)1, R,
-                           rest, rest, nb, -1.0, 1.0, 1, (const int *)flag);
+                           A + (k0 + nb) * R + k0 + nb, R, (const double *)P21, R, (int64_t)1,
+                           (const double *)P21, (int64_t)1, R, rest, rest, nb, -1.0, 1.0, 1,
+                           (const int *)flag);
     }
     return hipGetLastError();
 }
 
-// U_new = M V^{-1} with the blocked factor L (R x R): rows of M copied to
-// Unew, then forward (Y L^T = M) and back (U L = Y) substitution by column
-// blocks, each block's result taken off the remaining columns by a product.
-hipError_t launch_solve_blocked(const double *M, const double *L, int64_t I, int64_t R,
-                                double *Unew, const int *flag, hipStream_t s)
+// U_new = M V^{-1} with the blocked factor L (R x R) and the diagonal blocks'
+// L_kk^{-T} in W: rows of M copied to Unew, then forward (Y L^T = M) and back
+// (U L = Y) substitution by column blocks: a block's unknowns are its
+// right-hand side times L_kk^{-T} (forward) or L_kk^{-1} (back), and are taken
+// off the remaining columns by a product.
+hipError_t launch_solve_blocked(const double *M, const double *L, const double *W, int64_t I,
+                                int64_t R, double *Unew, const int *flag, hipStream_t s)
 {
     hipError_t e = hipMemcpyAsync(Unew, M, (size_t)(I * R) * sizeof(double),
                                   hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return e;
-    const unsigned gr = (unsigned)((I + kTrsmRows - 1) / kTrsmRows), gi = (unsigned)((I + 63) / 64);
+    const unsigned gi = (unsigned)((I + 63) / 64);
     for (int64_t k0 = 0; k0 < R; k0 += 64) {
         const int64_t nb = std::min<int64_t>(64, R - k0), rest = R - k0 - nb;
-        hipLaunchKernelGGL(als_trsm_rows_kernel<1>, dim3(gr), dim3(128), 0, s, L, R, k0, Unew, R,
-                           k0, I, flag);
+        // Y(:, block) = B(:, block) L_kk^{-T}
+        hipLaunchKernelGGL(als_gemm_kernel<double>, dim3(1, gi), dim3(256), 0, s, Unew + k0, R,
+                           (const double *)(Unew + k0), R, (int64_t)1, W + k0 * 64, (int64_t)64,
+                           (int64_t)1, I, nb, nb, 1.0, 0.0, 0, flag);
         if (rest == 0) break;
         // Y(:, later) -= Y(:, block) L(later, block)^T
         hipLaunchKernelGGL(als_gemm_kernel<double>, dim3((unsigned)((rest + 63) / 64), gi),
@@ -1029,10 +1030,12 @@ hipError_t launch_solve_blocked(const double *M, const double *L, int64_t I, int
     }
     const int64_t last = ((R - 1) / 64) * 64;
     for (int64_t k0 = last; k0 >= 0; k0 -= 64) {
-        hipLaunchKernelGGL(als_trsm_rows_kernel<-1>, dim3(gr), dim3(128), 0, s, L, R, k0, Unew, R,
-                           k0, I, flag);
-        if (k0 == 0) break;
         const int64_t nb = std::min<int64_t>(64, R - k0);
+        // U(:, block) = Y(:, block) L_kk^{-1}  (L_kk^{-1} = X^T, X in W)
+        hipLaunchKernelGGL(als_gemm_kernel<double>, dim3(1, gi), dim3(256), 0, s, Unew + k0, R,
+                           (const double *)(Unew + k0), R, (int64_t)1, W + k0 * 64, (int64_t)1,
+                           (int64_t)64, I, nb, nb, 1.0, 0.0, 0, flag);
+        if (k0 == 0) break;
         // U(:, earlier) -= U(:, block) L(block, earlier)
         hipLaunchKernelGGL(als_gemm_kernel<double>, dim3((unsigned)((k0 + 63) / 64), gi),
                            dim3(256), 0, s, Unew, R, (const double *)(Unew + k0), R, (int64_t)1,
@@ -1052,7 +1055,7 @@ template hipError_t launch_normalize<float>(const double *, int64_t, int64_t, fl
 template hipError_t launch_fill<double>(double *, int64_t, double, hipStream_t);
 template hipError_t launch_fill<float>(float *, int64_t, float, hipStream_t);
 template hipError_t launch_fill<int>(int *, int64_t, int, hipStream_t);
-template hipError_t launch_fit<double>(const double *, const double *, int64_t, const double *, const double *, int, int64_t, double *, int *, double, int, double *, int *, double *, int, hipStream_t);
-template hipError_t launch_fit<float>(const double *, const float *, int64_t, const double *, const double *, int, int64_t, double *, int *, double, int, double *, int *, double *, int, hipStream_t);
+template hipError_t launch_fit<double>(const double *, const double *, int64_t, const double *, const double *, int, int64_t, double *, int *, double, int, double *, int *, double *, int, double *, hipStream_t);
+template hipError_t launch_fit<float>(const double *, const float *, int64_t, const double *, const double *, int, int64_t, double *, int *, double, int, double *, int *, double *, int, double *, hipStream_t);
 
 }  // namespace mttkrp

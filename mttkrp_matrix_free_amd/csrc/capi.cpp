@@ -31,9 +31,9 @@ hipError_t launch_sumsq(const T *X, int64_t N, double *partial, int nparts, doub
 template <typename T>
 hipError_t launch_gram(const T *U, int64_t I, int64_t R, double *G, const int *flag, hipStream_t s);
 hipError_t launch_chol_blocked(const double *Gall, int order, int n, int64_t R, double *A,
-                               int *flag, hipStream_t s);
-hipError_t launch_solve_blocked(const double *M, const double *L, int64_t I, int64_t R,
-                                double *Unew, const int *flag, hipStream_t s);
+                               double *W, int *flag, hipStream_t s);
+hipError_t launch_solve_blocked(const double *M, const double *L, const double *W, int64_t I,
+                                int64_t R, double *Unew, const int *flag, hipStream_t s);
 hipError_t launch_chol(const double *Gall, int order, int n, int64_t R, double *L, int *flag,
                        hipStream_t s);
 hipError_t launch_solve(const double *M, const double *L, int64_t I, int64_t R, double *Unew,
@@ -52,7 +52,7 @@ template <typename T>
 hipError_t launch_fit(const double *M, const T *Ulast, int64_t Ilast, const double *lam64,
                       const double *Gall, int order, int64_t R, double *scal, int *flag,
                       double tol, int have_prev, double *out_fit, int *out_flag, double *parts,
-                      int max_parts, hipStream_t s);
+                      int max_parts, double *colsum_buf, hipStream_t s);
 
 namespace {
 
@@ -344,7 +344,7 @@ int mttkrp_all_entry(const T *X, const int64_t *dims, int order, const T *const 
 //   [mttkrp partials][M fp64 maxI x R][Unew fp64 maxI x R][G fp64 d x R x R]
 //   [L fp64 R x R][lambda fp64 R][sumsq partials][scalars: ||X||^2, fit][flag]
 struct AlsLayout {
-    size_t mt, M, Unew, G, L, lam, parts, scal, flag, total;
+    size_t mt, M, Unew, G, L, W, lam, parts, scal, flag, total;
 };
 
 int als_layout(const int64_t *dims, int order, int64_t rank, int elem, AlsLayout &L)
@@ -366,6 +366,8 @@ int als_layout(const int64_t *dims, int order, int64_t rank, int elem, AlsLayout
     off += round256(8 * (size_t)order * R * R);
     L.L = off;
     off += round256(8 * R * R);
+    L.W = off;  // inverses of the blocked factor's diagonal blocks (R > 64)
+    off += rank > 64 ? round256(8 * R * 64) : 0;
     L.lam = off;
     off += round256(8 * R);
     L.parts = off;
@@ -405,6 +407,7 @@ int cp_als_entry(const T *X, const int64_t *dims, int order, int64_t rank, T *co
     double *Unew = reinterpret_cast<double *>(w + L.Unew);
     double *G = reinterpret_cast<double *>(w + L.G);
     double *Lc = reinterpret_cast<double *>(w + L.L);
+    double *Winv = reinterpret_cast<double *>(w + L.W);
     double *lam64 = reinterpret_cast<double *>(w + L.lam);
     double *parts = reinterpret_cast<double *>(w + L.parts);
     double *scal = reinterpret_cast<double *>(w + L.scal);
@@ -494,8 +497,9 @@ int cp_als_entry(const T *X, const int64_t *dims, int order, int64_t rank, T *co
             } else {
                 // 64-wide column blocks: diagonal blocks by one wave, panels by
                 // rows in parallel, trailing updates as tiled products
-                if (!ok(launch_chol_blocked(G, order, n, R, Lc, flag, s))) return MTTKRP_EHIP;
-                if (!ok(launch_solve_blocked(M, Lc, dims[n], R, Unew, flag, s)))
+                if (!ok(launch_chol_blocked(G, order, n, R, Lc, Winv, flag, s)))
+                    return MTTKRP_EHIP;
+                if (!ok(launch_solve_blocked(M, Lc, Winv, dims[n], R, Unew, flag, s)))
                     return MTTKRP_EHIP;
             }
             if (!ok(launch_normalize<T>(Unew, dims[n], R, factors[n], lam64, lambda, flag, s)))
@@ -506,7 +510,7 @@ int cp_als_entry(const T *X, const int64_t *dims, int order, int64_t rank, T *co
         Slot *slot = pin.p + (it & 1);
         if (!ok(launch_fit<T>(M, factors[order - 1], dims[order - 1], lam64, G, order, R, scal,
                               flag, tol, it > 0, &slot->fit, &slot->flag, parts, kSumsqParts,
-                              s)))
+                              Unew, s)))
             return MTTKRP_EHIP;
         if (!ok(hipEventRecord(pin.done[it & 1], s))) return MTTKRP_EHIP;
         if (it > 0) {
