@@ -753,10 +753,12 @@ als_chol_diag_kernel(double *__restrict__ A, int64_t R, int64_t k0, double *__re
 
 // C (m x n, leading dimension ldc) = beta C + alpha A B with A(i, t) at
 // A[i sai + t sat] and B(t, j) at B[t sbt + j sbj] (element type TA for both;
-// beta = 0 writes alpha A B without reading C).  A thread owns a 4 x 4 block
-// of a 64 x 64 tile and sums over t in increasing order.  lower: tiles above
-// the diagonal are skipped.
-template <typename TA>
+// beta = 0 writes alpha A B without reading C).  A workgroup owns a TR x TC
+// tile, a thread a (TR / 16) x (TC / 16) block of it, summed over t in
+// increasing order.  lower: tiles above the diagonal are skipped.  With
+// n <= TC a workgroup reads all of its rows' A before it writes, so C may be
+// A's own columns.
+template <typename TA, int TR, int TC>
 __global__ __launch_bounds__(256) void als_gemm_kernel(double *__restrict__ C, int64_t ldc,
                                                        const TA *__restrict__ A, int64_t sai,
                                                        int64_t sat, const TA *__restrict__ B,
@@ -765,49 +767,72 @@ __global__ __launch_bounds__(256) void als_gemm_kernel(double *__restrict__ C, i
                                                        double beta, int lower,
                                                        const int *__restrict__ flag)
 {
-    constexpr int KT = 16;
-    __shared__ double As[KT][64 + 1];
-    __shared__ double Bs[KT][64 + 1];
+    constexpr int KT = 16, PR = TR / 16, PC = TC / 16;
+    __shared__ double As[KT][TR + 1];
+    __shared__ double Bs[KT][TC + 1];
     if (*flag) return;
     const int64_t ti = blockIdx.y, tj = blockIdx.x;
-    if (lower && tj > ti) return;
+    if (lower && tj * TC > ti * TR + TR - 1) return;
     const int tid = threadIdx.x;
-    const int ty = tid >> 4, tx = tid & 15;  // rows 4 ty .. 4 ty + 3, columns 4 tx .. 4 tx + 3
-    const int64_t i0 = ti * 64, j0 = tj * 64;
-    double acc[4][4] = {};
+    const int ty = tid >> 4, tx = tid & 15;  // rows PR ty .., columns PC tx ..
+    const int64_t i0 = ti * TR, j0 = tj * TC;
+    double acc[PR][PC] = {};
     for (int64_t t0 = 0; t0 < K; t0 += KT) {
-        for (int e = tid; e < KT * 64; e += 256) {
-            const int t = e >> 6, r = e & 63;
+        for (int e = tid; e < KT * TR; e += 256) {
+            const int t = e / TR, r = e % TR;
             const int64_t tt = t0 + t;
             As[t][r] = (tt < K && i0 + r < m) ? (double)A[(i0 + r) * sai + tt * sat] : 0.0;
+        }
+        for (int e = tid; e < KT * TC; e += 256) {
+            const int t = e / TC, r = e % TC;
+            const int64_t tt = t0 + t;
             Bs[t][r] = (tt < K && j0 + r < n) ? (double)B[tt * sbt + (j0 + r) * sbj] : 0.0;
         }
         __syncthreads();
 #pragma unroll
         for (int t = 0; t < KT; ++t) {
-            double a[4], b[4];
+            double a[PR], b[PC];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                a[u] = As[t][4 * ty + u];
-                b[u] = Bs[t][4 * tx + u];
-            }
+            for (int u = 0; u < PR; ++u) a[u] = As[t][PR * ty + u];
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int v = 0; v < PC; ++v) b[v] = Bs[t][PC * tx + v];
 #pragma unroll
-                for (int v = 0; v < 4; ++v) acc[u][v] = __builtin_fma(a[u], b[v], acc[u][v]);
+            for (int u = 0; u < PR; ++u)
+#pragma unroll
+                for (int v = 0; v < PC; ++v) acc[u][v] = __builtin_fma(a[u], b[v], acc[u][v]);
         }
         __syncthreads();
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < PR; ++u)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int64_t i = i0 + 4 * ty + u, j = j0 + 4 * tx + v;
+        for (int v = 0; v < PC; ++v) {
+            const int64_t i = i0 + PR * ty + u, j = j0 + PC * tx + v;
             if (i < m && j < n) {
                 double *c = C + i * ldc + j;
                 *c = beta == 0.0 ? alpha * acc[u][v] : __builtin_fma(alpha, acc[u][v], beta * *c);
             }
         }
+}
+
+// Launches the product above: 16 x 64 tiles when C is A's own columns (n <=
+// 64), 64 x 64 tiles when they fill the chip's compute units, else 32 x 32.
+template <typename TA>
+void launch_gemm(double *C, int64_t ldc, const TA *A, int64_t sai, int64_t sat, const TA *B,
+                 int64_t sbt, int64_t sbj, int64_t m, int64_t n, int64_t K, double alpha,
+                 double beta, int lower, bool inplace, const int *flag, hipStream_t s)
+{
+    auto go = [&](auto kern, int tr, int tc) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)((n + tc - 1) / tc), (unsigned)((m + tr - 1) / tr)),
+                           dim3(256), 0, s, C, ldc, A, sai, sat, B, sbt, sbj, m, n, K, alpha, beta,
+                           lower, flag);
+    };
+    if (inplace)
+        go(als_gemm_kernel<TA, 16, 64>, 16, 64);
+    else if (((m + 63) / 64) * ((n + 63) / 64) >= 256)
+        go(als_gemm_kernel<TA, 64, 64>, 64, 64);
+    else
+        go(als_gemm_kernel<TA, 32, 32>, 32, 32);
 }
 
 // sum_i M(i, r) U(i, r) for every column r (rows in order), one thread per column.
@@ -869,9 +894,8 @@ hipError_t launch_gram(const T *U, int64_t I, int64_t R, double *G, const int *f
 {
     if (R > 64) {
         // G = U^T U as a tiled product (the same per-entry order over i)
-        const unsigned nt = (unsigned)((R + 63) / 64);
-        hipLaunchKernelGGL(als_gemm_kernel<T>, dim3(nt, nt), dim3(256), 0, s, G, R, U, (int64_t)1,
-                           R, U, R, (int64_t)1, R, R, I, 1.0, 0.0, 0, flag);
+        launch_gemm<T>(G, R, U, (int64_t)1, R, U, R, (int64_t)1, R, R, I, 1.0, 0.0, 0, false, flag,
+                       s);
         return hipGetLastError();
     }
     const int64_t n = R * R;
@@ -987,18 +1011,13 @@ hipError_t launch_chol_blocked(const double *Gall, int order, int n, int64_t R, 
         hipLaunchKernelGGL(als_chol_diag_kernel, dim3(1), dim3(256), kCholDiagLds, s, A, R, k0, W,
                            flag);
         if (rest == 0) break;
-        const unsigned nt = (unsigned)((rest + 63) / 64);
-        // panel: L21 = A21 L_kk^{-T} (in place: a workgroup reads its rows'
-        // whole block before it writes)
+        // panel: L21 = A21 L_kk^{-T}, in place
         double *P21 = A + (k0 + nb) * R + k0;
-        hipLaunchKernelGGL(als_gemm_kernel<double>, dim3(1, nt), dim3(256), 0, s, P21, R,
-                           (const double *)P21, R, (int64_t)1, (const double *)(W + k0 * 64),
-                           (int64_t)64, (int64_t)1, rest, nb, nb, 1.0, 0.0, 0, (const int *)flag);
+        launch_gemm<double>(P21, R, P21, R, (int64_t)1, W + k0 * 64, (int64_t)64, (int64_t)1,
+                            rest, nb, nb, 1.0, 0.0, 0, true, flag, s);
         // trailing block (lower tiles): A22 -= L21 L21^T
-        hipLaunchKernelGGL(als_gemm_kernel<double>, dim3(nt, nt), dim3(256), 0, s,
-                           A + (k0 + nb) * R + k0 + nb, R, (const double *)P21, R, (int64_t)1,
-                           (const double *)P21, (int64_t)1, R, rest, rest, nb, -1.0, 1.0, 1,
-                           (const int *)flag);
+        launch_gemm<double>(A + (k0 + nb) * R + k0 + nb, R, P21, R, (int64_t)1, P21, (int64_t)1, R,
+                            rest, rest, nb, -1.0, 1.0, 1, false, flag, s);
     }
     return hipGetLastError();
 }
@@ -1014,32 +1033,26 @@ hipError_t launch_solve_blocked(const double *M, const double *L, const double *
     hipError_t e = hipMemcpyAsync(Unew, M, (size_t)(I * R) * sizeof(double),
                                   hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return e;
-    const unsigned gi = (unsigned)((I + 63) / 64);
     for (int64_t k0 = 0; k0 < R; k0 += 64) {
         const int64_t nb = std::min<int64_t>(64, R - k0), rest = R - k0 - nb;
-        // Y(:, block) = B(:, block) L_kk^{-T}
-        hipLaunchKernelGGL(als_gemm_kernel<double>, dim3(1, gi), dim3(256), 0, s, Unew + k0, R,
-                           (const double *)(Unew + k0), R, (int64_t)1, W + k0 * 64, (int64_t)64,
-                           (int64_t)1, I, nb, nb, 1.0, 0.0, 0, flag);
+        // Y(:, block) = B(:, block) L_kk^{-T}, in place
+        launch_gemm<double>(Unew + k0, R, Unew + k0, R, (int64_t)1, W + k0 * 64, (int64_t)64,
+                            (int64_t)1, I, nb, nb, 1.0, 0.0, 0, true, flag, s);
         if (rest == 0) break;
         // Y(:, later) -= Y(:, block) L(later, block)^T
-        hipLaunchKernelGGL(als_gemm_kernel<double>, dim3((unsigned)((rest + 63) / 64), gi),
-                           dim3(256), 0, s, Unew + k0 + nb, R, (const double *)(Unew + k0), R,
-                           (int64_t)1, L + (k0 + nb) * R + k0, (int64_t)1, R, I, rest, nb, -1.0,
-                           1.0, 0, flag);
+        launch_gemm<double>(Unew + k0 + nb, R, Unew + k0, R, (int64_t)1, L + (k0 + nb) * R + k0,
+                            (int64_t)1, R, I, rest, nb, -1.0, 1.0, 0, false, flag, s);
     }
     const int64_t last = ((R - 1) / 64) * 64;
     for (int64_t k0 = last; k0 >= 0; k0 -= 64) {
         const int64_t nb = std::min<int64_t>(64, R - k0);
-        // U(:, block) = Y(:, block) L_kk^{-1}  (L_kk^{-1} = X^T, X in W)
-        hipLaunchKernelGGL(als_gemm_kernel<double>, dim3(1, gi), dim3(256), 0, s, Unew + k0, R,
-                           (const double *)(Unew + k0), R, (int64_t)1, W + k0 * 64, (int64_t)1,
-                           (int64_t)64, I, nb, nb, 1.0, 0.0, 0, flag);
+        // U(:, block) = Y(:, block) L_kk^{-1} (L_kk^{-1} = X^T, X in W), in place
+        launch_gemm<double>(Unew + k0, R, Unew + k0, R, (int64_t)1, W + k0 * 64, (int64_t)1,
+                            (int64_t)64, I, nb, nb, 1.0, 0.0, 0, true, flag, s);
         if (k0 == 0) break;
         // U(:, earlier) -= U(:, block) L(block, earlier)
-        hipLaunchKernelGGL(als_gemm_kernel<double>, dim3((unsigned)((k0 + 63) / 64), gi),
-                           dim3(256), 0, s, Unew, R, (const double *)(Unew + k0), R, (int64_t)1,
-                           L + k0 * R, R, (int64_t)1, I, k0, nb, -1.0, 1.0, 0, flag);
+        launch_gemm<double>(Unew, R, Unew + k0, R, (int64_t)1, L + k0 * R, R, (int64_t)1, I, k0, nb,
+                            -1.0, 1.0, 0, false, flag, s);
     }
     return hipGetLastError();
 }
