@@ -35,19 +35,20 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 
 def kernel_sources_digest() -> str:
-    """sha256 of the MTTKRP kernel sources, their planner and launchers, and
-    the C header, with comments and blank space removed: traffic counters
-    taken on other code no longer describe the kernels that run, while an edit
-    of a comment leaves them valid.  The CP-ALS kernels (als_kernels.hip) do
-    not take part in the MTTKRP launches the counters describe."""
+    """sha256 of the MTTKRP kernel sources, their planner and launchers, with
+    comments and blank space removed: traffic counters taken on other code no
+    longer describe the kernels that run, while an edit of a comment leaves
+    them valid.  The CP-ALS kernels (als_kernels.hip) and the ablation
+    baselines (ablation_kernels.hip) do not take part in the MTTKRP launches
+    the counters describe."""
     import glob
     import hashlib
     import re
     h = hashlib.sha256()
     files = sorted(glob.glob(os.path.join(ROOT, "mttkrp_matrix_free_amd", "csrc", "*")))
-    files.append(os.path.join(ROOT, "include", "mttkrp.h"))
+    skip = ("als_kernels.hip", "ablation_kernels.hip")
     for f in files:
-        if os.path.isfile(f) and os.path.basename(f) != "als_kernels.hip":
+        if os.path.isfile(f) and os.path.basename(f) not in skip:
             with open(f, "r", encoding="utf-8") as fh:
                 text = fh.read()
             text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -131,6 +132,8 @@ def main():
                          "5-way workload only)")
     ap.add_argument("--no-gemm-baseline", action="store_true",
                     help="skip the explicit Khatri-Rao + vendor GEMM comparison")
+    ap.add_argument("--no-ablation", action="store_true",
+                    help="skip the untiled ELEM / SLICE baselines")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
@@ -391,6 +394,34 @@ def main():
                 "rel_diff_vs_library": diff}
         log(f"[bench] explicit-KR GEMM baseline {gemm}")
 
+    # ---- the untiled matrix-free baselines (one thread per element with
+    # atomics; one workgroup per slice), where they finish in seconds ----
+    ablation = None
+    if not args.no_ablation:
+        if N * R > (1 << 31):
+            ablation = {"skipped": f"N * R = {N * R} products per mode is past the 2^31 bound"}
+        else:
+            ablation = {}
+            for kind in ("elem", "slice"):
+                ms_k, diff = [], 0.0
+                for n in range(d):
+                    Mk = api.mttkrp_ablation(X, U, n, kind, stream=stream)  # warm-up
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    api.mttkrp_ablation(X, U, n, kind, out=Mk, stream=stream)
+                    b.record(stream)
+                    torch.cuda.synchronize()
+                    ms_k.append(a.elapsed_time(b))
+                    api.mttkrp(X, U, n, out=outs[n], ws=ws, stream=stream)
+                    torch.cuda.synchronize()
+                    ref = outs[n].double()
+                    diff = max(diff, float((Mk.double() - ref).norm() / ref.norm().clamp_min(1e-300)))
+                ablation[kind] = {"ms_per_mode": [round(v, 4) for v in ms_k],
+                                  "gflops_all_mode": round(d * flops_mode / (sum(ms_k) / 1e3) / 1e9, 2),
+                                  "rel_diff_vs_library": diff}
+        log(f"[bench] ablation baselines {ablation}")
+
     cfg = {"workload": p.name, "dims": list(dims), "rank": R, "modes": list(range(d)),
            "step": "all-mode MTTKRP sweep", "cache": "warm (back-to-back sweeps)"}
     line = {
@@ -413,6 +444,7 @@ def main():
         "cpu_baseline": cpu,
         "cp_als": als,
         "gemm_baseline": gemm,
+        "ablation": ablation,
     }
     print(json.dumps(line), flush=True)
 

@@ -130,6 +130,23 @@ int cp_als_f32(const float *X, const int64_t *dims, int order, int64_t rank,
                float *const *factors, float *lambda, int iters, double tol, double *fit_hist,
                int *iters_done, void *ws, size_t ws_bytes, void *stream);
 
+/* ---- ablation baselines (comparison only, not the product path) ----
+ * The untiled matrix-free strategies the GenTen page improves on (its
+ * MTTKRP-ELEM and MTTKRP-SLICE).  Same arguments and result as mttkrp_*, no
+ * workspace.  ELEM: one thread per tensor element, one atomic addition per
+ * output entry it touches (out is zeroed first; the order of the additions,
+ * hence the rounding, is not fixed).  SLICE: one workgroup per output row,
+ * partial sums added in a fixed order.  Both compute in the element type. */
+int mttkrp_elem_f64(const double *X, const int64_t *dims, int order, const double *const *factors,
+                    int64_t rank, int mode, double *out, void *stream);
+int mttkrp_elem_f32(const float *X, const int64_t *dims, int order, const float *const *factors,
+                    int64_t rank, int mode, float *out, void *stream);
+int mttkrp_slice_f64(const double *X, const int64_t *dims, int order,
+                     const double *const *factors, int64_t rank, int mode, double *out,
+                     void *stream);
+int mttkrp_slice_f32(const float *X, const int64_t *dims, int order, const float *const *factors,
+                     int64_t rank, int mode, float *out, void *stream);
+
 /* ---- plan introspection (no device work) ----
  * The decomposition mttkrp_* would launch for this problem: which modes are
  * contracted on the matrix cores, which index the tile rows, the tile shape and

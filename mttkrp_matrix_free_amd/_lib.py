@@ -26,6 +26,7 @@ EXPORTS = (
     "mttkrp_workspace_bytes", "mttkrp_all_workspace_bytes", "cp_als_workspace_bytes",
     "mttkrp_f64", "mttkrp_f32", "mttkrp_all_f64", "mttkrp_all_f32",
     "cp_als_f64", "cp_als_f32", "mttkrp_plan",
+    "mttkrp_elem_f64", "mttkrp_elem_f32", "mttkrp_slice_f64", "mttkrp_slice_f32",
 )
 
 
@@ -101,6 +102,9 @@ def lib():
             getattr(L, f).restype = I
         for f in ("cp_als_f64", "cp_als_f32"):
             getattr(L, f).argtypes = [P, P, I, i64, P, P, I, ctypes.c_double, P, P, P, sz, P]
+            getattr(L, f).restype = I
+        for f in ("mttkrp_elem_f64", "mttkrp_elem_f32", "mttkrp_slice_f64", "mttkrp_slice_f32"):
+            getattr(L, f).argtypes = [P, P, I, P, i64, I, P, P]
             getattr(L, f).restype = I
         L.mttkrp_plan.argtypes = [P, I, i64, I, I, ctypes.POINTER(PlanInfo)]
         L.mttkrp_plan.restype = I

@@ -130,6 +130,27 @@ def mttkrp(X: torch.Tensor, factors: Sequence[Optional[torch.Tensor]], mode: int
     return out
 
 
+def mttkrp_ablation(X: torch.Tensor, factors: Sequence[Optional[torch.Tensor]], mode: int,
+                    kind: str, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The untiled matrix-free baselines (kind "elem" or "slice"): the same
+    result as mttkrp(), for comparison only."""
+    if kind not in ("elem", "slice"):
+        raise ValueError("kind must be 'elem' or 'slice'")
+    _check_tensor(X)
+    R = _check_factors(X, factors, skip=mode)
+    if not 0 <= mode < X.dim():
+        raise ValueError("mode out of range")
+    sfx, eb = _DT[X.dtype]
+    if out is None:
+        out = torch.empty((X.shape[mode], R), dtype=X.dtype, device=X.device)
+    fn = getattr(_lib.lib(), f"mttkrp_{kind}_{sfx}")
+    st = fn(X.data_ptr(), _dims(X.shape), X.dim(), _ptrs(factors), R, int(mode), out.data_ptr(),
+            _stream_handle(stream))
+    if st:
+        raise MttkrpError(st, f"mttkrp_{kind}_{sfx}")
+    return out
+
+
 def mttkrp_all(X: torch.Tensor, factors: Sequence[torch.Tensor],
                outs: Optional[List[torch.Tensor]] = None, ws: Optional[torch.Tensor] = None,
                stream=None) -> List[torch.Tensor]:
