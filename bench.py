@@ -279,6 +279,13 @@ def main():
     tr = measured_traffic(p.name)
     roof["traffic"] = (round(float(np.mean(tr["bytes_per_mode"])), 0) if tr else None)
     roof["traffic_unit"] = "bytes/launch (FETCH_SIZE+WRITE_SIZE, copy-calibrated)"
+    # the plain cache model's bounds per mode: T_inf moves every byte once,
+    # T_0 re-reads the d - 1 factor rows for every tensor element (no reuse)
+    t_inf = [max(flops_mode / peak_f, bytes_mode[n] / (HBM_PEAK_GBS * 1e9)) * 1e3 for n in range(d)]
+    t_0 = [max(flops_mode / peak_f, s * (N + (d - 1) * N * R) / (HBM_PEAK_GBS * 1e9)) * 1e3
+           for n in range(d)]
+    roof["model_ms_per_mode"] = {"t_inf": [round(v, 5) for v in t_inf],
+                                 "t_0": [round(v, 5) for v in t_0]}
     roof["per_launch_ms"] = round(sweep_avg / d, 5)
     roof["sweep_ms"] = round(sweep_avg, 5)
     roof["algorithmic_bytes_per_launch"] = bytes_mode

@@ -251,10 +251,12 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
     // SIMD keep the matrix cores busier even though X is then read once per
     // 64 rank columns (measured on the 4-way fp32 rank-512 tensor: -19%).
     const int64_t ncb = ceil_div(rank, 16);  // 16-wide rank blocks
+    // (fp64 form-0 tiles stay at four blocks too: on the 512^3 rank-2000
+    // tensor, modes 0 and 1 took 8.2 ms with four blocks against 9.3 ms with
+    // eight, whose registers leave one wave per SIMD.)
     const bool wide_ok =
         p.form == 1 ? elem_bytes == 4
-                    : (elem_bytes == 8 ||
-                       tile_min_waves(elem_bytes, 2, 8, false, plan_slots(0, k.nouter)) == 2);
+                    : tile_min_waves(elem_bytes, 2, 8, false, plan_slots(0, k.nouter)) == 2;
     if (ncb >= 8 && p.layout == 0 && wide_ok)
         p.nb = 8;
     else
