@@ -818,21 +818,29 @@ __global__ __launch_bounds__(256) void als_gemm_kernel(double *__restrict__ C, i
 // Launches the product above: 16 x 64 tiles when C is A's own columns (n <=
 // 64), 64 x 64 tiles when they fill the chip's compute units, else 32 x 32.
 template <typename TA>
-void launch_gemm(double *C, int64_t ldc, const TA *A, int64_t sai, int64_t sat, const TA *B,
-                 int64_t sbt, int64_t sbj, int64_t m, int64_t n, int64_t K, double alpha,
-                 double beta, int lower, bool inplace, const int *flag, hipStream_t s)
+hipError_t launch_gemm(double *C, int64_t ldc, const TA *A, int64_t sai, int64_t sat, const TA *B,
+                       int64_t sbt, int64_t sbj, int64_t m, int64_t n, int64_t K, double alpha,
+                       double beta, int lower, bool inplace, const int *flag, hipStream_t s)
 {
+    hipError_t e = hipSuccess;
     auto go = [&](auto kern, int tr, int tc) {
-        hipLaunchKernelGGL(kern, dim3((unsigned)((n + tc - 1) / tc), (unsigned)((m + tr - 1) / tr)),
-                           dim3(256), 0, s, C, ldc, A, sai, sat, B, sbt, sbj, m, n, K, alpha, beta,
-                           lower, flag);
+        const int64_t gx = (n + tc - 1) / tc, gy = (m + tr - 1) / tr;
+        if (gx > INT32_MAX || gy > 65535) {  // grid limits
+            e = hipErrorInvalidValue;
+            return;
+        }
+        hipLaunchKernelGGL(kern, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s, C, ldc, A, sai,
+                           sat, B, sbt, sbj, m, n, K, alpha, beta, lower, flag);
+        e = hipGetLastError();
     };
+    if (inplace && n > 64) return hipErrorInvalidValue;
     if (inplace)
         go(als_gemm_kernel<TA, 16, 64>, 16, 64);
     else if (((m + 63) / 64) * ((n + 63) / 64) >= 256)
         go(als_gemm_kernel<TA, 64, 64>, 64, 64);
     else
         go(als_gemm_kernel<TA, 32, 32>, 32, 32);
+    return e;
 }
 
 // sum_i M(i, r) U(i, r) for every column r (rows in order), one thread per column.
@@ -894,9 +902,8 @@ hipError_t launch_gram(const T *U, int64_t I, int64_t R, double *G, const int *f
 {
     if (R > 64) {
         // G = U^T U as a tiled product (the same per-entry order over i)
-        launch_gemm<T>(G, R, U, (int64_t)1, R, U, R, (int64_t)1, R, R, I, 1.0, 0.0, 0, false, flag,
-                       s);
-        return hipGetLastError();
+        return launch_gemm<T>(G, R, U, (int64_t)1, R, U, R, (int64_t)1, R, R, I, 1.0, 0.0, 0, false,
+                              flag, s);
     }
     const int64_t n = R * R;
     hipLaunchKernelGGL(gram_kernel<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, U, I, R,
@@ -1013,11 +1020,13 @@ hipError_t launch_chol_blocked(const double *Gall, int order, int n, int64_t R, 
         if (rest == 0) break;
         // panel: L21 = A21 L_kk^{-T}, in place
         double *P21 = A + (k0 + nb) * R + k0;
-        launch_gemm<double>(P21, R, P21, R, (int64_t)1, W + k0 * 64, (int64_t)64, (int64_t)1,
-                            rest, nb, nb, 1.0, 0.0, 0, true, flag, s);
+        hipError_t e = launch_gemm<double>(P21, R, P21, R, (int64_t)1, W + k0 * 64, (int64_t)64,
+                                           (int64_t)1, rest, nb, nb, 1.0, 0.0, 0, true, flag, s);
+        if (e != hipSuccess) return e;
         // trailing block (lower tiles): A22 -= L21 L21^T
-        launch_gemm<double>(A + (k0 + nb) * R + k0 + nb, R, P21, R, (int64_t)1, P21, (int64_t)1, R,
-                            rest, rest, nb, -1.0, 1.0, 1, false, flag, s);
+        e = launch_gemm<double>(A + (k0 + nb) * R + k0 + nb, R, P21, R, (int64_t)1, P21, (int64_t)1,
+                                R, rest, rest, nb, -1.0, 1.0, 1, false, flag, s);
+        if (e != hipSuccess) return e;
     }
     return hipGetLastError();
 }
@@ -1036,23 +1045,27 @@ hipError_t launch_solve_blocked(const double *M, const double *L, const double *
     for (int64_t k0 = 0; k0 < R; k0 += 64) {
         const int64_t nb = std::min<int64_t>(64, R - k0), rest = R - k0 - nb;
         // Y(:, block) = B(:, block) L_kk^{-T}, in place
-        launch_gemm<double>(Unew + k0, R, Unew + k0, R, (int64_t)1, W + k0 * 64, (int64_t)64,
-                            (int64_t)1, I, nb, nb, 1.0, 0.0, 0, true, flag, s);
+        e = launch_gemm<double>(Unew + k0, R, Unew + k0, R, (int64_t)1, W + k0 * 64, (int64_t)64,
+                                (int64_t)1, I, nb, nb, 1.0, 0.0, 0, true, flag, s);
+        if (e != hipSuccess) return e;
         if (rest == 0) break;
         // Y(:, later) -= Y(:, block) L(later, block)^T
-        launch_gemm<double>(Unew + k0 + nb, R, Unew + k0, R, (int64_t)1, L + (k0 + nb) * R + k0,
-                            (int64_t)1, R, I, rest, nb, -1.0, 1.0, 0, false, flag, s);
+        e = launch_gemm<double>(Unew + k0 + nb, R, Unew + k0, R, (int64_t)1, L + (k0 + nb) * R + k0,
+                                (int64_t)1, R, I, rest, nb, -1.0, 1.0, 0, false, flag, s);
+        if (e != hipSuccess) return e;
     }
     const int64_t last = ((R - 1) / 64) * 64;
     for (int64_t k0 = last; k0 >= 0; k0 -= 64) {
         const int64_t nb = std::min<int64_t>(64, R - k0);
         // U(:, block) = Y(:, block) L_kk^{-1} (L_kk^{-1} = X^T, X in W), in place
-        launch_gemm<double>(Unew + k0, R, Unew + k0, R, (int64_t)1, W + k0 * 64, (int64_t)1,
-                            (int64_t)64, I, nb, nb, 1.0, 0.0, 0, true, flag, s);
+        e = launch_gemm<double>(Unew + k0, R, Unew + k0, R, (int64_t)1, W + k0 * 64, (int64_t)1,
+                                (int64_t)64, I, nb, nb, 1.0, 0.0, 0, true, flag, s);
+        if (e != hipSuccess) return e;
         if (k0 == 0) break;
         // U(:, earlier) -= U(:, block) L(block, earlier)
-        launch_gemm<double>(Unew, R, Unew + k0, R, (int64_t)1, L + k0 * R, R, (int64_t)1, I, k0, nb,
-                            -1.0, 1.0, 0, false, flag, s);
+        e = launch_gemm<double>(Unew, R, Unew + k0, R, (int64_t)1, L + k0 * R, R, (int64_t)1, I, k0,
+                                nb, -1.0, 1.0, 0, false, flag, s);
+        if (e != hipSuccess) return e;
     }
     return hipGetLastError();
 }
