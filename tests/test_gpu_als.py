@@ -103,6 +103,26 @@ def test_als_not_spd_leaves_factors():
         assert np.array_equal(U[m].cpu().numpy(), Z[m])
 
 
+def test_als_rank2000_normal_equations():
+    # the blocked path at the rank of the 512^3 workload (32 diagonal blocks):
+    # after a sweep the last mode's factor satisfies its normal equations,
+    # (U_n diag(lambda)) V = M_n with V the Hadamard product of the other
+    # Grams and M_n the MTTKRP with the other final factors
+    p = inputs.random_cp_problem((60, 56, 52), 4, 2000, sigma=0.1, seed=36)
+    X = dev(p.X)
+    U = [dev(u) for u in p.factors]
+    lam, fit, done, st = api.cp_als(X, U, 1)
+    assert st == 0 and done == 1 and np.isfinite(fit[0])
+    n = 2
+    M = api.mttkrp(X, U, n).double()
+    V = (U[0].t() @ U[0]) * (U[1].t() @ U[1])
+    res = (M - (U[n] * lam) @ V).norm() / M.norm()
+    assert float(res) <= 1e-10, float(res)
+    # the factor columns are unit-norm where lambda > 0
+    nrm = U[n].norm(dim=0)
+    assert torch.allclose(nrm[lam > 0], torch.ones_like(nrm[lam > 0]), atol=1e-12)
+
+
 def test_als_not_spd_blocked_leaves_factors():
     # R > 64 (the blocked factorization): a zero column makes a pivot of the
     # second block exactly zero, if no earlier one fails
