@@ -118,12 +118,14 @@ def log(*a):
 
 
 def main():
+    from mttkrp_matrix_free_amd import inputs  # workload generators (numpy only)
+
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c2",
-                    choices=["c1", "c2", "c3", "c4r8", "c4r64", "c4r512", "c5"])
+    ap.add_argument("--workload", default="3way_256cube_f64_R32_cp32",
+                    choices=sorted(inputs.WORKLOADS))
     ap.add_argument("--cold-reps", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-als", action="store_true", help="skip the CP-ALS timing (5-way workload)")
@@ -149,7 +151,7 @@ def main():
     import numpy as np
     import torch
 
-    from mttkrp_matrix_free_amd import api, inputs
+    from mttkrp_matrix_free_amd import api
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

@@ -119,14 +119,16 @@ def fiveway_als() -> Problem:
                    cp_factors=A, noise_sigma=sigma, als_iters=10)
 
 
+# The workloads, keyed by the name each Problem carries (what it is, with
+# its sizes).
 WORKLOADS = {
-    "c1": small_uniform_3way,
-    "c2": lowrank_cube_256,
-    "c3": highrank_cube_512,
-    "c4r8": lambda: fourway_f32(8),
-    "c4r64": lambda: fourway_f32(64),
-    "c4r512": lambda: fourway_f32(512),
-    "c5": fiveway_als,
+    "3way_64x48x32_f64_R16": small_uniform_3way,
+    "3way_256cube_f64_R32_cp32": lowrank_cube_256,
+    "3way_512cube_f64_R2000": highrank_cube_512,
+    "4way_128x128x128x64_f32_R8": lambda: fourway_f32(8),
+    "4way_128x128x128x64_f32_R64": lambda: fourway_f32(64),
+    "4way_128x128x128x64_f32_R512": lambda: fourway_f32(512),
+    "5way_50x50x50x20x10_f64_R64_als": fiveway_als,
 }
 
 
