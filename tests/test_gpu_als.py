@@ -49,6 +49,7 @@ def rel(a, b):
     # blocked factorization and solves (R > 64): 3 blocks, a 4-way case with a
     # ragged last block, and R = 300 (the model norm summed by workgroups)
     ((30, 28, 26), 3, 150, 2), ((12, 11, 10, 9), 2, 100, 2), ((40, 38, 36), 3, 300, 2),
+    ((20, 18, 16), 3, 65, 2), ((24, 22, 20), 3, 128, 2),  # a 1-wide last block; whole blocks
 ])
 def test_als_small_vs_oracle(dims, true_rank, R, iters):
     p = inputs.random_cp_problem(dims, true_rank, R, sigma=0.05, seed=31)
@@ -155,6 +156,19 @@ def test_als_tolerance_stops_early():
     assert torch.equal(lam2, lam)
     for a, b in zip(U, U2):
         assert torch.equal(a, b)
+
+
+def test_als_float32_blocked():
+    # fp32 factors with R > 64: the blocked R x R path and the tiled Gram of
+    # fp32 factors
+    p = inputs.random_cp_problem((22, 20, 18), 3, 80, sigma=0.05, seed=37)
+    F0, lam0, fit0, st0 = oracle.cp_als(p.X, p.factors, 2, nthreads=NT)
+    X = dev(p.X.astype(np.float32))
+    U = [dev(u.astype(np.float32)) for u in p.factors]
+    lam, fit, done, st = api.cp_als(X, U, 2)
+    assert st == 0 and done == 2
+    for it in range(2):
+        assert abs(fit[it] - fit0[it]) <= 1e-4, (it, fit[it], fit0[it])
 
 
 def test_als_float32():
