@@ -768,8 +768,11 @@ __global__ __launch_bounds__(256) void als_gemm_kernel(double *__restrict__ C, i
                                                        const int *__restrict__ flag)
 {
     constexpr int KT = 16, PR = TR / 16, PC = TC / 16;
-    __shared__ double As[KT][TR + 1];
-    __shared__ double Bs[KT][TC + 1];
+    // unpadded rows: a thread's PR (PC) entries of a row are 16-byte aligned
+    // and read as wide LDS loads (the stores, consecutive across threads, do
+    // not conflict)
+    __shared__ __align__(16) double As[KT][TR];
+    __shared__ __align__(16) double Bs[KT][TC];
     if (*flag) return;
     const int64_t ti = blockIdx.y, tj = blockIdx.x;
     if (lower && tj * TC > ti * TR + TR - 1) return;
