@@ -295,9 +295,13 @@ __global__ __launch_bounds__(256) void als_normalize_kernel(const double *__rest
     if (*flag) return;
     const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (r >= R) return;
+    // (unrolled: the loads of several rows are in flight at once; the sum
+    // still adds the rows in order)
     double s = 0.0;
+#pragma unroll 8
     for (int64_t i = 0; i < I; ++i) s += Unew[i * R + r] * Unew[i * R + r];
     const double lam = sqrt(s);
+#pragma unroll 8
     for (int64_t i = 0; i < I; ++i) {
         const double v = Unew[i * R + r];
         Uout[i * R + r] = (T)(lam > 0.0 ? v / lam : v);
