@@ -394,7 +394,7 @@ int cp_als_entry(const T *X, const int64_t *dims, int order, int64_t rank, T *co
     if (!aligned16(X) || !aligned16(lambda) || (ws && !aligned16(ws))) return MTTKRP_EALIGN;
     for (int m = 0; m < order; ++m)
         if (!aligned16(factors[m])) return MTTKRP_EALIGN;
-    if (rank > 4096) return MTTKRP_ERANGE;  // single-workgroup Cholesky bound
+    if (rank > 4096) return MTTKRP_ERANGE;  // R x R work (blocked factor, Grams) kept to 4096
     AlsLayout L;
     int st = als_layout(dims, order, rank, (int)sizeof(T), L);
     if (st) return st;
