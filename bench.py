@@ -143,8 +143,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(the MTTKRP shards by slabs of the first mode; see the design notes).",
+        print("bench.py runs on one GPU only: there is no multi-GPU path "
+              "(the MTTKRP would shard by slabs of the first mode, one slab per GPU).",
               file=sys.stderr)
         sys.exit(2)
 
