@@ -88,6 +88,17 @@ def test_fiveway_als_workload_vs_stored_oracle():
         assert abs(fit[it] - g["fit"][it]) <= 1e-9, (it, fit[it], g["fit"][it])
     assert np.all(np.diff(fit) >= -1e-12)
     assert rel(lam.cpu().numpy(), g["lambda"]) <= 1e-6
+    # the final factors, as far as the golden stores them (each factor's first
+    # row and the sum of its entries), at the loose bar for many sweeps
+    for m in range(len(p.dims)):
+        Um = U[m].cpu().numpy()
+        e_row = rel(Um[0], g["factor_row0"][m])
+        # (relative to the sum of the entries' magnitudes: the signed sum may
+        # cancel, while the 1e-6 bar is relative to the factor's size)
+        e_sum = abs(float(Um.sum()) - g["factor_sum"][m]) / float(np.abs(Um).sum())
+        say(f"  factor {m}: row 0 {e_row:.2e}, sum {e_sum:.2e}")
+        assert e_row <= 1e-6, (m, e_row)
+        assert e_sum <= 1e-6, (m, e_sum)
 
 
 def test_als_not_spd_leaves_factors():
@@ -122,6 +133,36 @@ def test_als_rank2000_normal_equations():
     # the factor columns are unit-norm where lambda > 0
     nrm = U[n].norm(dim=0)
     assert torch.allclose(nrm[lam > 0], torch.ones_like(nrm[lam > 0]), atol=1e-12)
+
+
+def test_als_rank2000_vs_stored_oracle():
+    """Rank 2000 (the blocked factorization over 32 diagonal blocks and the
+    blocked solves) against the oracle's run on the same inputs, stored by
+    tests/golden/make_oracle_golden.py (oracle only): the fit of every sweep,
+    lambda, and each final factor's first row and entry sum."""
+    g = json.load(open(os.path.join(GOLDEN, "rank2000_als_oracle.json")))
+    c = g["recipe"]
+    p = inputs.random_cp_problem(tuple(c["dims"]), c["true_rank"], c["rank"], sigma=c["sigma"],
+                                 seed=c["seed"])
+    assert list(p.dims) == g["dims"] and p.rank == g["rank"] == 2000
+    X = dev(p.X)
+    U = [dev(u) for u in p.factors]
+    lam, fit, done, st = api.cp_als(X, U, g["iters"])
+    say("  fit gpu   ", fit)
+    say("  fit oracle", g["fit"])
+    assert st == 0 and done == g["iters"]
+    for it in range(g["iters"]):
+        assert abs(fit[it] - g["fit"][it]) <= 1e-9, (it, fit[it], g["fit"][it])
+    e_lam = rel(lam.cpu().numpy(), g["lambda"])
+    say(f"  lambda {e_lam:.2e}")
+    assert e_lam <= 1e-6
+    for m in range(len(p.dims)):
+        Um = U[m].cpu().numpy()
+        e_row = rel(Um[0], g["factor_row0"][m])
+        e_sum = abs(float(Um.sum()) - g["factor_sum"][m]) / float(np.abs(Um).sum())
+        say(f"  factor {m}: row 0 {e_row:.2e}, sum {e_sum:.2e}")
+        assert e_row <= 1e-6, (m, e_row)
+        assert e_sum <= 1e-6, (m, e_sum)
 
 
 def test_als_not_spd_blocked_leaves_factors():

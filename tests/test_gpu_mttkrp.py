@@ -92,12 +92,64 @@ def test_small_workload_64x48x32():
     assert all(e <= 1e-12 for e in errs.values()), errs
 
 
-def test_lowrank_cube_256_sampled_and_closed_form():
+def tile_rows(dims, R, n, dtype):
+    """Output rows that cover every output tile of the plan the library
+    launches for mode n: every row when each output row is a unit of its own
+    (form 1) or the output is a short trailing mode; otherwise two rows of
+    every row tile (at positions that move from tile to tile, so that
+    different lanes and accumulator elements are checked), plus the first and
+    last rows.  Every rank tile, contraction chunk and split contributes to
+    each of these rows, so all of them are checked too."""
+    tdt = torch.float64 if np.dtype(dtype) == np.float64 else torch.float32
+    pl = api.plan(dims, R, n, tdt)
+    I = dims[n]
+    if pl["form"] == 1 or pl["rows"] != I or I <= 64:
+        return list(range(I)), pl
+    rpt = 16 * pl["mb"]
+    rows = {0, I - 1}
+    for t in range(-(-I // rpt)):
+        lo, hi = t * rpt, min(I, (t + 1) * rpt)
+        span = hi - lo
+        rows.add(lo + (t * 5) % span)
+        rows.add(hi - 1 - (t * 3) % span)
+    return sorted(rows), pl
+
+
+def check_every_tile(p, tol):
+    """Every mode of a large workload against the oracle on the rows of
+    tile_rows(), element by element and by relative Frobenius error."""
+    X = dev(p.X)
+    U = [dev(u) for u in p.factors]
+    worst = {}
+    for n in range(p.X.ndim):
+        rows, pl = tile_rows(p.dims, p.rank, n, p.X.dtype)
+        say(f"  {p.name} mode {n}: {len(rows)} rows (form {pl['form']}, layout {pl['layout']}, "
+            f"{16 * pl['mb']}-row tiles, {pl['rtiles']} rank tiles, {pl['splits']} splits)")
+        M = api.mttkrp(X, U, n)
+        torch.cuda.synchronize()
+        Mg = M.cpu().numpy()[rows].astype(np.float64)
+        del M
+        Mo = oracle.mttkrp(p.X, p.factors, n, rows=rows, nthreads=NT)
+        e = rel_fro(Mg, Mo)
+        # element by element: each entry within the bar relative to its row's size
+        scale = np.linalg.norm(Mo, axis=1, keepdims=True) / np.sqrt(Mo.shape[1])
+        elem = float(np.max(np.abs(Mg - Mo) / np.maximum(scale, 1e-300)))
+        say(f"    rel Frobenius {e:.3e}, worst entry / row rms {elem:.3e}")
+        assert e <= tol, (n, e)
+        assert elem <= 10 * tol, (n, elem)
+        worst[n] = e
+    del X, U
+    return worst
+
+
+def test_lowrank_cube_256_full_and_closed_form():
+    """The 256^3 rank-32 CP tensor with noise, as specified, compared in full
+    with the oracle (every output of every mode); then the noise-free tensor
+    in full against the closed form U_n * Hadamard_{m != n}(U_m^T U_m)."""
     p = inputs.lowrank_cube_256(with_noise=True)
-    errs = run_modes(p, rows=lambda I: [0, 1, 77, 128, 200, I - 1])
-    say("  sampled-row errors", errs)
+    errs = run_modes(p)
+    say("  full errors", errs)
     assert all(e <= 1e-12 for e in errs.values()), errs
-    # noise-free: the full output against the closed form U_n * Hadamard(U_m^T U_m)
     q = inputs.lowrank_cube_256(with_noise=False)
     X = dev(q.X)
     U = [dev(u) for u in q.factors]
@@ -112,34 +164,29 @@ def test_lowrank_cube_256_sampled_and_closed_form():
         assert e <= 1e-12
 
 
-def test_highrank_cube_512_sampled_and_inner_products():
+def test_highrank_cube_512_every_tile_and_inner_products():
+    """512^3 fp64, R = 2000: two rows of every output tile of every mode
+    against the oracle, then <X, [[U]]> through every mode."""
     p = inputs.highrank_cube_512()
+    check_every_tile(p, 1e-12)
     X = dev(p.X)
     U = [dev(u) for u in p.factors]
     inner = []
     for n in range(3):
-        say(f"  512^3 R=2000 mode {n}")
         M = api.mttkrp(X, U, n)
-        torch.cuda.synchronize()
         inner.append(float(torch.sum(M * U[n]).item()))
-        rows = [0, 511] if n != 1 else [3, 300]
-        Mo = oracle.mttkrp(p.X, p.factors, n, rows=rows, nthreads=NT)
-        e = rel_fro(M[rows].cpu().numpy(), Mo)
-        say(f"    sampled rows {rows}: {e:.3e}")
-        assert e <= 1e-12
         del M
-    # <X, [[U]]> computed through every mode agrees
     ref = inner[0]
     for v in inner[1:]:
         assert abs(v - ref) <= 1e-12 * abs(ref) * 10, inner
 
 
 @pytest.mark.parametrize("R", [8, 64, 512])
-def test_fourway_f32_sampled(R):
+def test_fourway_f32_every_tile(R):
+    """128x128x128x64 fp32: every form-1 unit (output row), else two rows of
+    every output tile, of every mode against the oracle."""
     p = inputs.fourway_f32(R)
-    errs = run_modes(p, rows=lambda I: [0, I // 3, I - 1])
-    say("  sampled-row errors", errs)
-    assert all(e <= 1e-5 for e in errs.values()), errs
+    check_every_tile(p, 1e-5)
 
 
 TRAILING = [
