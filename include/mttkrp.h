@@ -147,6 +147,29 @@ int mttkrp_slice_f64(const double *X, const int64_t *dims, int order,
 int mttkrp_slice_f32(const float *X, const int64_t *dims, int order, const float *const *factors,
                      int64_t rank, int mode, float *out, void *stream);
 
+/* ---- measurement probes (not part of the MTTKRP) ----
+ * The achievable rates that the roofline fractions are also reported
+ * against: the HBM read rate and the matrix-core rate of the device the
+ * stream belongs to.  Asynchronous on `stream`; time them with events.
+ *
+ * mttkrp_probe_read: reads bytes (a multiple of 16) of buf once with 16-byte
+ *   loads and writes, per workgroup w < mttkrp_probe_read_grid(), the sum
+ *   modulo 2^32 of x ^ y ^ z ^ w over the 32-bit words of the 16-byte groups
+ *   it read to sink[w] (DEVICE, mttkrp_probe_read_grid() words), so the host
+ *   can check that every byte was read.  buf and sink 16-byte aligned.
+ * mttkrp_probe_mfma: elem_bytes = 8 (fp64) or 4 (fp32); every wave of
+ *   mttkrp_probe_mfma_grid() workgroups of four waves runs iters rounds of
+ *   eight independent 16x16x4 MFMAs (2048 flops each) on register operands,
+ *   i.e. mttkrp_probe_mfma_grid() * 4 * 8 * 2048 * iters flops in all, and
+ *   writes one finite value per wave to sink (DEVICE, 4 *
+ *   mttkrp_probe_mfma_grid() doubles).
+ * Both return MTTKRP_EINVAL / MTTKRP_EALIGN for bad arguments, MTTKRP_EHIP
+ * for a failed launch. */
+int mttkrp_probe_read_grid(void);
+int mttkrp_probe_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+int mttkrp_probe_mfma_grid(void);
+int mttkrp_probe_mfma(int elem_bytes, int64_t iters, double *sink, void *stream);
+
 /* ---- plan introspection (no device work) ----
  * The decomposition mttkrp_* would launch for this problem: which modes are
  * contracted on the matrix cores, which index the tile rows, the tile shape and
@@ -172,8 +195,29 @@ typedef struct {
     size_t ws_bytes;     /* workspace of this mode                                    */
     int64_t kchunks;     /* contraction chunks (each sums into its own partial)       */
     int waves;           /* waves per workgroup of the main kernel                    */
+    int launchable;      /* 1: a kernel exists for this tile (0 only for a forced tile) */
+    /* The plain cache model of this plan on MI355X, in seconds (a reading of
+     * the GenTen page's "performance models for an ideal multi-level cache
+     * machine", TL;DR and abstract, whose formulas are not given): the time
+     * each resource needs for the plan's traffic at its peak rate.  model_s
+     * = max(flop, hbm, l2, lds).  t_inf_s: every byte moved once; t_0_s: the
+     * factor rows re-read for every tensor element (no reuse). */
+    double model_flop_s; /* padded tile flops / matrix-core peak                     */
+    double model_hbm_s;  /* X (once per L2-sharing group of rank tiles), factors,
+                            output and split partials / 8 TB/s                      */
+    double model_l2_s;   /* X per rank tile, staged Khatri-Rao tiles, outer and row
+                            factor reads / (8 XCDs x 2 KB/clock)                    */
+    double model_lds_s;  /* operand reads and staging stores / (256 CUs x 128 B/clock) */
+    double model_s;
+    double t_inf_s, t_0_s;
 } mttkrp_plan_info;
 
+/* Experiments only: the environment variable MTTKRP_FORCE_TILE="mb,nb" or
+ * "mb,nb,waves" (mb in {2,4}, nb in {1,2,4,8}, waves in {4,8}) replaces the
+ * planner's wave tile in every plan of the process (the tile-heuristic
+ * validation sweeps tiles this way).  A malformed value makes every call that
+ * plans return MTTKRP_EINVAL, and so does a forced tile no kernel instantiates
+ * (mttkrp_plan then reports launchable = 0 and returns MTTKRP_OK). */
 int mttkrp_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_bytes,
                 mttkrp_plan_info *info);
 

@@ -27,6 +27,7 @@ EXPORTS = (
     "mttkrp_f64", "mttkrp_f32", "mttkrp_all_f64", "mttkrp_all_f32",
     "cp_als_f64", "cp_als_f32", "mttkrp_plan",
     "mttkrp_elem_f64", "mttkrp_elem_f32", "mttkrp_slice_f64", "mttkrp_slice_f32",
+    "mttkrp_probe_read_grid", "mttkrp_probe_read", "mttkrp_probe_mfma_grid", "mttkrp_probe_mfma",
 )
 
 
@@ -51,13 +52,22 @@ class PlanInfo(ctypes.Structure):
         ("ws_bytes", ctypes.c_size_t),
         ("kchunks", ctypes.c_int64),
         ("waves", ctypes.c_int),
+        ("launchable", ctypes.c_int),
+        ("model_flop_s", ctypes.c_double),
+        ("model_hbm_s", ctypes.c_double),
+        ("model_l2_s", ctypes.c_double),
+        ("model_lds_s", ctypes.c_double),
+        ("model_s", ctypes.c_double),
+        ("t_inf_s", ctypes.c_double),
+        ("t_0_s", ctypes.c_double),
     ]
 
     def as_dict(self):
         d = {}
         for name, _ in self._fields_:
             v = getattr(self, name)
-            d[name] = list(v) if isinstance(v, ctypes.Array) else int(v)
+            d[name] = list(v) if isinstance(v, ctypes.Array) else (
+                float(v) if isinstance(v, float) else int(v))
         return d
 
 
@@ -106,6 +116,14 @@ def lib():
         for f in ("mttkrp_elem_f64", "mttkrp_elem_f32", "mttkrp_slice_f64", "mttkrp_slice_f32"):
             getattr(L, f).argtypes = [P, P, I, P, i64, I, P, P]
             getattr(L, f).restype = I
+        L.mttkrp_probe_read_grid.restype = I
+        L.mttkrp_probe_read_grid.argtypes = []
+        L.mttkrp_probe_mfma_grid.restype = I
+        L.mttkrp_probe_mfma_grid.argtypes = []
+        L.mttkrp_probe_read.argtypes = [P, sz, P, P]
+        L.mttkrp_probe_read.restype = I
+        L.mttkrp_probe_mfma.argtypes = [I, i64, P, P]
+        L.mttkrp_probe_mfma.restype = I
         L.mttkrp_plan.argtypes = [P, I, i64, I, I, ctypes.POINTER(PlanInfo)]
         L.mttkrp_plan.restype = I
         _lib = L

@@ -17,6 +17,7 @@
 
 #include "../../include/mttkrp.h"
 #include "plan.hpp"
+#include "tile_select.hpp"
 
 namespace mttkrp {
 
@@ -126,6 +127,7 @@ int bound_plan(const T *X, const int64_t *dims, int order, const T *const *facto
 {
     int st = make_plan(dims, order, rank, mode, (int)sizeof(T), pl);
     if (st) return st;
+    if (!plan_launchable(pl)) return MTTKRP_EINVAL;  // a forced tile without a kernel
     if (pl.ws_bytes > ws_bytes) return MTTKRP_EWORKSPACE;
     if (pl.ws_bytes > 0 && !ws) return MTTKRP_EINVAL;
     pl.kp.X = X;
@@ -180,7 +182,8 @@ bool fusable(const Plan &a, const Plan &b)
            x.nkch == y.nkch && x.IkB == y.IkB && x.bpitch == y.bpitch && x.R == y.R &&
            x.grid_real == y.grid_real && x.grid_per_xcd == y.grid_per_xcd &&
            x.nrtiles == y.nrtiles && x.nsplit == y.nsplit && x.nsplit_it == y.nsplit_it &&
-           a.grid == b.grid;
+           a.grid == b.grid &&
+           (a.elem_bytes == 8 ? select_multi_f64(a) : select_multi_f32(a)) != nullptr;
 }
 
 // A plain split plan: partials summed by split_reduce_kernel, or by the tile
@@ -686,6 +689,15 @@ int mttkrp_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem
     info->ws_bytes = pl.ws_bytes;
     info->kchunks = pl.kp.nkch;
     info->waves = pl.waves;
+    info->launchable = plan_launchable(pl) ? 1 : 0;
+    const PlanModel pm = plan_model(pl, dims, order, mode);
+    info->model_flop_s = pm.flop_s;
+    info->model_hbm_s = pm.hbm_s;
+    info->model_l2_s = pm.l2_s;
+    info->model_lds_s = pm.lds_s;
+    info->model_s = pm.t_s;
+    info->t_inf_s = pm.t_inf_s;
+    info->t_0_s = pm.t_0_s;
     return MTTKRP_OK;
 }
 

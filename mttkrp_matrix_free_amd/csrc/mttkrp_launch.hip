@@ -141,6 +141,12 @@ TileKernel select_kernel<float>(const Plan &pl)
     return pl.form ? select_tile_f32_form1(pl) : select_tile_f32_form0(pl);
 }
 
+bool plan_launchable(const Plan &pl)
+{
+    return pl.elem_bytes == 8 ? select_kernel<double>(pl) != nullptr
+                              : select_kernel<float>(pl) != nullptr;
+}
+
 // with_reduce = false leaves a split plan's partials for a later launch to
 // sum (the all-mode sweep hands them to the next mode's tile kernel).
 template <typename T>

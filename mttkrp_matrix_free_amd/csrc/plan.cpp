@@ -13,6 +13,10 @@
 
 #include <algorithm>
 #include <climits>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
 
 #include "../../include/mttkrp.h"
 
@@ -29,6 +33,27 @@ bool mul_ok(int64_t a, int64_t b, int64_t &out)
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// MTTKRP_FORCE_TILE="mb,nb" or "mb,nb,waves" (experiments only).  Returns 0
+// when unset, 1 with the values when well formed, -1 otherwise.
+int forced_tile(int &mb, int &nb, int &waves)
+{
+    const char *v = std::getenv("MTTKRP_FORCE_TILE");
+    if (!v || !*v) return 0;
+    int a = 0, b = 0, w = 0;
+    char tail = 0;
+    const int got = std::sscanf(v, "%d,%d,%d%c", &a, &b, &w, &tail);
+    if (got == 2 || got == 3) {
+        if ((a == 2 || a == 4) && (b == 1 || b == 2 || b == 4 || b == 8) &&
+            (got == 2 || w == 4 || w == 8)) {
+            mb = a;
+            nb = b;
+            waves = got == 3 ? w : 0;
+            return 1;
+        }
+    }
+    return -1;
+}
 
 }  // namespace
 
@@ -285,6 +310,16 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
         p.mb = (k.In >= 64 && p.nb <= 2) ? 4 : 2;
     }
 
+    // Experiments: a forced wave tile (and workgroup size) replaces the
+    // choice above; everything below follows from it.
+    int f_mb = 0, f_nb = 0, f_waves = 0;
+    const int forced = forced_tile(f_mb, f_nb, f_waves);
+    if (forced < 0) return MTTKRP_EINVAL;
+    if (forced > 0) {
+        p.mb = f_mb;
+        p.nb = f_nb;
+    }
+
     // Workgroup size: form 1 and the row-contiguous layout run eight waves per
     // workgroup (when a wave's registers allow two waves per SIMD), one
     // workgroup per compute unit, so one staged Khatri-Rao tile serves the
@@ -297,6 +332,7 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
                tile_min_waves(elem_bytes, p.mb, p.nb, p.form == 1, plan_slots(p.form, k.nouter)) == 2)
                   ? 8
                   : 4;
+    if (forced > 0 && f_waves) p.waves = f_waves;
     const size_t lds_budget = p.waves == 8 ? kLdsBudgetWide : kLdsBudget;
 
     // Contraction chunks: the Khatri-Rao tile of one chunk (Kc x 16nb) must
@@ -501,6 +537,68 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
     for (int j = 0; j < 3; ++j) p.outer_modes[j] = k.o_mode[j];
     plan = p;
     return MTTKRP_OK;
+}
+
+PlanModel plan_model(const Plan &p, const int64_t *dims, int order, int mode)
+{
+    // Rates (MI355X, published): matrix cores 78.6 / 157.3 TFLOP/s, HBM
+    // 8 TB/s; L2 8 XCDs x 2048 B/clock and LDS 256 CUs x 128 B/clock at
+    // 2.4 GHz.
+    const double s = p.elem_bytes;
+    const double P = p.elem_bytes == 8 ? 78.6e12 : 157.3e12;
+    const double BW = 8.0e12, BW_L2 = 8 * 2048 * 2.4e9, BW_LDS = 256 * 128 * 2.4e9;
+    const KParams &k = p.kp;
+    double N = 1.0, sumI = 0.0;
+    for (int m = 0; m < order; ++m) {
+        N *= (double)dims[m];
+        sumI += (double)dims[m];
+    }
+    const double R = (double)k.R;
+    const double In = (double)dims[mode];
+    PlanModel pm{};
+    // plan-free bounds
+    const double F = 2.0 * R * N;
+    pm.t_inf_s = std::max(F / P, s * (N + R * sumI) / BW);
+    pm.t_0_s = std::max(F / P, s * (N + (order - 1) * N * R) / BW);
+    // the plan's padded work: rows in whole 16 * mb tiles, the contraction in
+    // 16-element steps per chunk, the rank in whole rank tiles
+    const int64_t rpt = 16 * p.mb;
+    const double rows = (p.form == 1 ? (double)k.nunits * (double)k.nrowtiles
+                                     : (double)k.nunits) *
+                        (double)rpt * (double)k.nbatch;
+    const int64_t klast = k.K - (k.nkch - 1) * k.Kc;
+    const double Kpad = (double)((k.nkch - 1) * k.Kc + (klast + 15) / 16 * 16);
+    const double Rpad = (double)(k.nrtiles * 16 * p.nb);
+    pm.flop_s = 2.0 * rows * Kpad * Rpad / P;
+    // wave steps (16 contraction elements of one wave tile) over the launch
+    const double wave_steps = rows / (double)rpt * (Kpad / 16.0) * (double)k.nrtiles;
+    // HBM: X once for every group of rank tiles that run together on one
+    // XCD (the workgroup order keeps a chunk's rank tiles adjacent), the other
+    // factors and the output once, partials written and read once
+    const double resident_xcd = (double)(kNumCU / kNumXCD) * (p.waves == 8 ? 1 : 2);
+    const double rho_x = std::ceil((double)k.nrtiles / resident_xcd);
+    const double rows_k = (double)k.In;  // the kernel's output rows (the block for trailing rows)
+    const double part = k.to_partial ? 2.0 * (double)k.nsplit * rows_k * R * 8.0 : 0.0;
+    pm.hbm_s = (N * s * rho_x + R * (sumI - In) * s + In * R * s + part) / BW;
+    // L2: X once per rank tile; the staged Khatri-Rao tile of every
+    // workgroup (two factor rows per element for a two-factor tile); the
+    // outer factor values every step carries; the row factors of every
+    // form-1 item end
+    const double b_stage = (double)k.grid_real * (double)k.Kc * 16.0 * p.nb * s *
+                           (k.k_mode1 >= 0 ? 2.0 : 1.0);
+    const double outer = (double)plan_slots(p.form, k.nouter) * wave_steps * 64.0 * p.nb * s;
+    const double itemend = p.form == 1 ? (double)k.nunits * (double)k.nitems * (double)k.nrtiles *
+                                             (double)rpt * 16.0 * p.nb * s *
+                                             (k.r_mode1 >= 0 ? 2.0 : 1.0)
+                                       : 0.0;
+    pm.l2_s = (N * s * (double)k.nrtiles + b_stage + outer + itemend) / BW_L2;
+    // LDS: every wave step reads 4 x 16 nb operand values of B per lane; the
+    // staging writes each B tile once per workgroup
+    const double lds = wave_steps * 4.0 * 64.0 * p.nb * s +
+                       (double)k.grid_real * (double)k.Kc * 16.0 * p.nb * s;
+    pm.lds_s = lds / BW_LDS;
+    pm.t_s = std::max(std::max(pm.flop_s, pm.hbm_s), std::max(pm.l2_s, pm.lds_s));
+    return pm;
 }
 
 size_t als_extra_bytes(const int64_t *dims, int order, int64_t rank)

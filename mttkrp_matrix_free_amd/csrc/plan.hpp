@@ -198,7 +198,33 @@ struct KPack {
 
 // Fills `plan` for mode `mode`.  Returns 0 or a MTTKRP_* status.  Pure host
 // code: no HIP call.  Pointers in plan.kp are left null.
+// For experiments, the environment variable MTTKRP_FORCE_TILE="mb,nb" or
+// "mb,nb,waves" replaces the planner's wave tile (and workgroup size); the
+// contraction chunks, splits and grid then follow from it as usual.  A value
+// that is malformed or outside mb in {2,4}, nb in {1,2,4,8}, waves in {4,8}
+// makes every plan fail with MTTKRP_EINVAL.  (A forced tile that no kernel
+// instantiates is reported by plan_launchable.)
 int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_bytes, Plan &plan);
+
+// The plain cache model of one plan (seconds on MI355X): the time each
+// resource needs for the plan's traffic at its peak rate, T(p) the largest.
+// Matrix cores: the padded tile flops at 78.6 (fp64) / 157.3 (fp32)
+// TFLOP/s.  HBM: X once per group of rank tiles that share an L2, the other
+// factors and the output once, split partials written and read, at 8 TB/s.
+// L2: X once per rank tile, the staged Khatri-Rao tiles, the per-step outer
+// factor values and the item-end row factors, at 8 XCDs x 2 KB/clock.  LDS:
+// the matrix-core operand reads of B and the staging stores, at 256 CUs x
+// 128 B/clock.  T_inf and T_0 are the plan-free bounds (every byte moved
+// once; the factor rows re-read for every tensor element).
+struct PlanModel {
+    double flop_s, hbm_s, l2_s, lds_s, t_s;  // t_s = max of the four
+    double t_inf_s, t_0_s;
+};
+PlanModel plan_model(const Plan &p, const int64_t *dims, int order, int mode);
+
+// Whether a kernel instantiation exists for the plan's tile (always true for
+// the planner's own choices; a forced tile may have none).
+bool plan_launchable(const Plan &p);
 
 // Workspace of the CP-ALS driver beyond the MTTKRP workspace (bytes).
 size_t als_extra_bytes(const int64_t *dims, int order, int64_t rank);

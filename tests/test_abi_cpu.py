@@ -213,3 +213,66 @@ def test_workspace_far_below_khatri_rao_at_rank_2000(L):
         assert L.mttkrp_workspace_bytes(dims_arr((512, 512, 512)), 3, 2000, n, 8, ctypes.byref(ws)) == 0
         assert ws.value <= 0.02 * 512 * 512 * 2000 * 8
         assert ws.value <= 16 * 512 * 2000 * 8
+
+
+MODEL_CASES = [((256, 256, 256), 32, 8), ((512, 512, 512), 2000, 8), ((128, 128, 128, 64), 8, 4),
+               ((128, 128, 128, 64), 512, 4), ((50, 50, 50, 20, 10), 64, 8), ((33, 17, 19), 17, 8)]
+
+
+@pytest.mark.parametrize("dims,R,eb", MODEL_CASES)
+def test_plan_cache_model(L, dims, R, eb):
+    """The plan's cache model: T(p) is the largest of its four resource times,
+    never below the plan-free bound T_inf (every byte once, unpadded flops)
+    and never above T_0 for these sizes; the matrix-core term covers at least
+    the algorithmic flops."""
+    d = len(dims)
+    N = 1
+    for v in dims:
+        N *= v
+    P = 78.6e12 if eb == 8 else 157.3e12
+    for n in range(d):
+        info = _lib.PlanInfo()
+        assert L.mttkrp_plan(dims_arr(dims), d, R, n, eb, ctypes.byref(info)) == 0
+        assert info.launchable == 1
+        terms = [info.model_flop_s, info.model_hbm_s, info.model_l2_s, info.model_lds_s]
+        assert all(t > 0 for t in terms)
+        assert info.model_s == max(terms)
+        assert info.model_flop_s >= 2.0 * R * N / P * (1 - 1e-12)
+        assert info.model_s >= info.t_inf_s * (1 - 1e-12)
+        assert info.t_0_s >= info.t_inf_s
+
+
+def test_force_tile_override(L, monkeypatch):
+    """MTTKRP_FORCE_TILE (experiments only) replaces the wave tile; a bad value
+    makes planning fail with EINVAL; a forced tile without a kernel is
+    reported (launchable = 0) and the entry point refuses it before any HIP
+    call."""
+    dims = dims_arr((512, 512, 512))
+    info = _lib.PlanInfo()
+    assert L.mttkrp_plan(dims, 3, 2000, 0, 8, ctypes.byref(info)) == 0
+    base = (info.mb, info.nb, info.waves, info.splits)
+    monkeypatch.setenv("MTTKRP_FORCE_TILE", "4,2")
+    assert L.mttkrp_plan(dims, 3, 2000, 0, 8, ctypes.byref(info)) == 0
+    assert (info.mb, info.nb) == (4, 2) and info.launchable == 1
+    monkeypatch.setenv("MTTKRP_FORCE_TILE", "2,8,8")
+    assert L.mttkrp_plan(dims, 3, 2000, 0, 8, ctypes.byref(info)) == 0
+    assert (info.mb, info.nb, info.waves) == (2, 8, 8) and info.launchable == 0
+    st = L.mttkrp_f64(FAKE, dims, 3, ptrs([FAKE] * 3), 2000, 0, FAKE, FAKE, 1 << 30, None)
+    assert st == _lib.EINVAL
+    for bad in ("3,1", "2", "2,3", "2,4,6", "x", "2,4,8,1"):
+        monkeypatch.setenv("MTTKRP_FORCE_TILE", bad)
+        assert L.mttkrp_plan(dims, 3, 2000, 0, 8, ctypes.byref(info)) == _lib.EINVAL, bad
+    monkeypatch.delenv("MTTKRP_FORCE_TILE")
+    assert L.mttkrp_plan(dims, 3, 2000, 0, 8, ctypes.byref(info)) == 0
+    assert (info.mb, info.nb, info.waves, info.splits) == base
+
+
+def test_probe_validation(L):
+    assert L.mttkrp_probe_read_grid() > 0 and L.mttkrp_probe_mfma_grid() > 0
+    assert L.mttkrp_probe_read(None, 16, FAKE, None) == _lib.EINVAL
+    assert L.mttkrp_probe_read(FAKE, 16, None, None) == _lib.EINVAL
+    assert L.mttkrp_probe_read(FAKE_MIS, 16, FAKE, None) == _lib.EALIGN
+    assert L.mttkrp_probe_read(FAKE, 17, FAKE, None) == _lib.EINVAL
+    assert L.mttkrp_probe_mfma(8, 0, FAKE, None) == _lib.EINVAL
+    assert L.mttkrp_probe_mfma(8, 10, None, None) == _lib.EINVAL
+    assert L.mttkrp_probe_mfma(8, 10, FAKE_MIS, None) == _lib.EALIGN
