@@ -240,6 +240,8 @@ class Workload:
         events around each call): back to back, or after reading `flush` (a
         1 GiB buffer, four times the last-level cache) outside the events."""
         import torch
+        if reps <= 0:
+            return None
         ms = [[] for _ in range(self.d)]
         for _ in range(reps):
             for n in range(self.d):
@@ -342,7 +344,7 @@ def config_entry(w, sweep_ms, warm, cold, peaks):
     """Per-mode and all-mode figures of one workload."""
     import numpy as np
     bound, ai = w.bound()
-    warm_med = [float(np.median(v)) for v in warm]
+    warm_med = [float(np.median(v)) for v in warm] if warm else None
     cold_med = [float(np.median(v)) for v in cold] if cold else None
     e = {
         "workload": w.name, "dims": list(w.dims), "rank": w.R, "dtype": w.dt,
@@ -350,10 +352,11 @@ def config_entry(w, sweep_ms, warm, cold, peaks):
         "tensor_fits_last_level_cache": w.fits_cache(),
         "sweep_ms": round(sweep_ms, 5),
         "gflops_all_mode_sweep": round(w.d * w.flops_mode / (sweep_ms / 1e3) / 1e9, 1),
-        "warm_ms_per_mode": [stats(v) for v in warm],
         "frac_sweep": w.fraction(sweep_ms)[3],
-        "frac_warm": w.fraction(sum(warm_med))[3],
     }
+    if warm_med:
+        e["warm_ms_per_mode"] = [stats(v) for v in warm]
+        e["frac_warm"] = w.fraction(sum(warm_med))[3]
     if cold_med:
         e["cold_ms_per_mode"] = [stats(v) for v in cold]
         e["gflops_all_mode_cold"] = round(w.d * w.flops_mode / (sum(cold_med) / 1e3) / 1e9, 1)
@@ -656,7 +659,7 @@ def main():
     roof = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": frac,
             "basis": ("cold-cache per-mode medians (a 1 GiB read before each mode)" if use_cold
                       else "timed-region sweeps (HIP events on the library's stream)"),
-            "frac_sweep": head["frac_sweep"], "frac_warm_per_mode": head["frac_warm"],
+            "frac_sweep": head["frac_sweep"], "frac_warm_per_mode": head.get("frac_warm"),
             "frac_cold": head.get("frac_cold")}
     if peaks:
         roof["frac_of_achievable"] = head.get("frac_of_achievable")

@@ -167,7 +167,12 @@ double sweep_seconds(const Plan *pl, int order)
 // cost of the cross-stream dependencies (two per call, about 10 us each):
 // measured faster on the 4-way fp32 rank-8 tensor (-8%, ~440 us) and the
 // 5-way tensor (-1.5%), slower on the 256^3 fp64 rank-32 one (+6%, ~90 us).
+// Nor when each mode is long: the two streams' modes then share the chip
+// for their whole length, not only at one mode's tail (512^3 fp64 rank 2000,
+// 8.3 ms per mode: 25.67 ms per sweep on two streams against 25.04 ms for
+// the same modes one after another).
 constexpr double kTwoStreamSweep = 200e-6;
+constexpr double kTwoStreamModeMax = 3e-3;
 
 // Two form-1 plans one multi-mode launch can run in turn: the same tile
 // shape, the same B tile for every workgroup (contraction group, chunking,
@@ -265,7 +270,8 @@ int mttkrp_all_entry(const T *X, const int64_t *dims, int order, const T *const 
     auto in_half = [&](int h) {
         return reinterpret_cast<double *>(static_cast<char *>(ws) + (size_t)h * half);
     };
-    if (sweep_seconds(pl, order) >= kTwoStreamSweep) {
+    const double est = sweep_seconds(pl, order);
+    if (est >= kTwoStreamSweep && est / order < kTwoStreamModeMax) {
         // A long sweep alternates between the caller's stream and a second
         // one, so that one mode's last workgroups, its split reduction and
         // the next mode's first workgroups run side by side.  Each stream has
