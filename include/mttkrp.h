@@ -58,6 +58,7 @@ extern "C" {
 #define MTTKRP_EWORKSPACE (-5) /* ws_bytes smaller than the size the query returns */
 #define MTTKRP_EHIP (-6)       /* a HIP runtime call or kernel launch failed */
 #define MTTKRP_ENOTSPD (-7)    /* CP-ALS: a Cholesky pivot of the R x R system was not positive */
+#define MTTKRP_ESCRATCH (-8)   /* mttkrp_noalloc: the plan needs more than MTTKRP_NOALLOC_SCRATCH_BYTES */
 
 /* Text for a status code (static storage; never NULL). */
 const char *mttkrp_strerror(int status);
@@ -100,6 +101,25 @@ int mttkrp_f64(const double *X, const int64_t *dims, int order, const double *co
                int64_t rank, int mode, double *out, void *ws, size_t ws_bytes, void *stream);
 int mttkrp_f32(const float *X, const int64_t *dims, int order, const float *const *factors,
                int64_t rank, int mode, float *out, void *ws, size_t ws_bytes, void *stream);
+
+/* ---- MTTKRP of one mode without any allocation ----
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * computation, kernels and result, bit for bit, as mttkrp_f64 (elem_bytes =
+ * 8) or mttkrp_f32 (elem_bytes = 4), with X, factors and out as there, but
+ * no workspace argument.  The split partial sums go to a scratch array of
+ * MTTKRP_NOALLOC_SCRATCH_BYTES that the library holds in device memory, one
+ * per GPU, from the first call on that GPU until the process ends.  The call
+ * allocates nothing (no hipMalloc, no hipFree, no allocating library call).
+ * A plan that needs more partial-sum space than the array holds (the size
+ * mttkrp_workspace_bytes reports) is refused with MTTKRP_ESCRATCH before any
+ * HIP call.  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (on different streams, or from different host threads)
+ * race and must be serialised by the caller.  Each call rewrites every
+ * partial it reads, so nothing is carried over from an earlier call. */
+#define MTTKRP_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int mttkrp_noalloc(const void *X, const int64_t *dims, int order, const void *const *factors,
+                   int64_t rank, int mode, void *out, int elem_bytes, void *stream);
 
 /* ---- MTTKRP of every mode (the all-mode sweep of the GenTen page, Fig. 4) ----
  * outs[m] (I_m x R) for m = 0..order-1, in mode order, on one stream.  X is

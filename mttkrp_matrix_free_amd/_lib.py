@@ -19,6 +19,8 @@ EALIGN = -4
 EWORKSPACE = -5
 EHIP = -6
 ENOTSPD = -7
+ESCRATCH = -8
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTS = (
@@ -28,6 +30,7 @@ EXPORTS = (
     "cp_als_f64", "cp_als_f32", "mttkrp_plan",
     "mttkrp_elem_f64", "mttkrp_elem_f32", "mttkrp_slice_f64", "mttkrp_slice_f32",
     "mttkrp_probe_read_grid", "mttkrp_probe_read", "mttkrp_probe_mfma_grid", "mttkrp_probe_mfma",
+    "mttkrp_noalloc",
 )
 
 
@@ -124,6 +127,8 @@ def lib():
         L.mttkrp_probe_read.restype = I
         L.mttkrp_probe_mfma.argtypes = [I, i64, P, P]
         L.mttkrp_probe_mfma.restype = I
+        L.mttkrp_noalloc.argtypes = [P, P, I, P, i64, I, P, I, P]
+        L.mttkrp_noalloc.restype = I
         L.mttkrp_plan.argtypes = [P, I, i64, I, I, ctypes.POINTER(PlanInfo)]
         L.mttkrp_plan.restype = I
         _lib = L

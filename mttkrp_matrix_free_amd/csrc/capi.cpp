@@ -201,6 +201,21 @@ bool plain_split(const Plan &pl)
            pl.kp.nsplit * pl.kp.In * pl.kp.R * 8 < (INT64_C(1) << 31) - 64;
 }
 
+}  // namespace
+
+// Argument checks of a single-mode call, without the workspace (host only).
+int check_mode_call(const void *X, const int64_t *dims, int order, const void *const *factors,
+                    int64_t rank, int mode, const void *out)
+{
+    const int st = check_common(X, dims, order, factors, rank, mode < 0 ? 0 : mode);
+    if (st) return st;
+    if (mode < 0 || mode >= order || !out) return MTTKRP_EINVAL;
+    if (!aligned16(out)) return MTTKRP_EALIGN;
+    return MTTKRP_OK;
+}
+
+namespace {
+
 template <typename T>
 int mttkrp_entry(const T *X, const int64_t *dims, int order, const T *const *factors,
                  int64_t rank, int mode, T *out, void *ws, size_t ws_bytes, void *stream)
@@ -552,6 +567,9 @@ const char *mttkrp_strerror(int status)
     case MTTKRP_EWORKSPACE: return "workspace smaller than the size the query returns";
     case MTTKRP_EHIP: return "HIP runtime call or kernel launch failed";
     case MTTKRP_ENOTSPD: return "CP-ALS: Cholesky pivot of the R x R system not positive";
+    case MTTKRP_ESCRATCH:
+        return "the plan needs more partial-sum space than the no-allocation entry point's "
+               "fixed scratch array holds";
     default: return "unknown status";
     }
 }

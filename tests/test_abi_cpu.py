@@ -50,7 +50,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_strerror_and_version(L):
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         s = _lib.strerror(code)
         assert s and s != "unknown status"
     assert _lib.strerror(-99) == "unknown status"
@@ -276,3 +276,25 @@ def test_probe_validation(L):
     assert L.mttkrp_probe_mfma(8, 0, FAKE, None) == _lib.EINVAL
     assert L.mttkrp_probe_mfma(8, 10, None, None) == _lib.EINVAL
     assert L.mttkrp_probe_mfma(8, 10, FAKE_MIS, None) == _lib.EALIGN
+
+
+def test_noalloc_host_checks(L):
+    """mttkrp_noalloc refuses bad arguments and plans larger than its fixed
+    scratch array on the host, before any HIP call (fake pointers here)."""
+    d = dims_arr((2048, 512, 512))
+    f = ptrs([FAKE] * 3)
+    need = ctypes.c_size_t()
+    assert L.mttkrp_workspace_bytes(d, 3, 2000, 0, 8, ctypes.byref(need)) == 0
+    assert need.value > _lib.NOALLOC_SCRATCH_BYTES
+    assert L.mttkrp_noalloc(FAKE, d, 3, f, 2000, 0, FAKE, 8, None) == _lib.ESCRATCH
+    assert L.mttkrp_noalloc(FAKE, d, 3, f, 2000, 0, FAKE, 2, None) == _lib.EINVAL
+    assert L.mttkrp_noalloc(None, d, 3, f, 2000, 0, FAKE, 8, None) == _lib.EINVAL
+    assert L.mttkrp_noalloc(FAKE, d, 3, f, 2000, 3, FAKE, 8, None) == _lib.EINVAL
+    assert L.mttkrp_noalloc(FAKE, d, 3, f, 2000, 0, FAKE_MIS, 8, None) == _lib.EALIGN
+    assert L.mttkrp_noalloc(FAKE, dims_arr((4, 5)), 2, f, 3, 0, FAKE, 8, None) == _lib.EORDER
+    # every benchmark workload's single-mode call fits the array
+    for dims, R, eb in WORKLOADS[:7]:
+        for n in range(len(dims)):
+            assert L.mttkrp_workspace_bytes(dims_arr(dims), len(dims), R, n, eb,
+                                            ctypes.byref(need)) == 0
+            assert need.value <= _lib.NOALLOC_SCRATCH_BYTES, (dims, R, n)
