@@ -94,9 +94,12 @@ int cp_als_workspace_bytes(const int64_t *dims, int order, int64_t rank, int ele
 
 /* ---- MTTKRP of one mode ----
  * out (I_mode x R) = X_(mode) times the Khatri-Rao product of every other factor.
- * fp64: arithmetic in fp64.  fp32: fp32 products, accumulation of each
- * contraction over at most one tensor fiber in fp32 and every longer sum in
- * fp64; out is rounded to fp32 once. */
+ * fp64: arithmetic in fp64.  fp32: fp32 products; the matrix cores sum in
+ * fp32 over at most one contraction chunk (the part of the contracted mode(s)
+ * whose Khatri-Rao tile fits in LDS: at most 1,840 terms, 288 at the 4-way
+ * benchmark tensors), and every longer sum is in fp64; out is rounded to
+ * fp32 once.  The expected relative error of a chunk's fp32 sum is about
+ * 2^-24 * sqrt(chunk), below 3e-6. */
 int mttkrp_f64(const double *X, const int64_t *dims, int order, const double *const *factors,
                int64_t rank, int mode, double *out, void *ws, size_t ws_bytes, void *stream);
 int mttkrp_f32(const float *X, const int64_t *dims, int order, const float *const *factors,

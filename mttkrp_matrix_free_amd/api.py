@@ -9,6 +9,7 @@ stream, every step of the computation runs in the library's kernels.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 from typing import List, Optional, Sequence
@@ -107,6 +108,16 @@ def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
+def _allocating_on(stream):
+    """Context for the tensors a call allocates itself (workspace, outputs):
+    torch's caching allocator ties a block to the stream that was current
+    when it was allocated and may hand it out again as soon as it is freed,
+    ordered only on that stream.  The kernels run on `stream`, so the block
+    is allocated there: a workspace freed when the call returns is not
+    reused by other work before the queued kernels are done with it."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def mttkrp(X: torch.Tensor, factors: Sequence[Optional[torch.Tensor]], mode: int,
            out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
            stream=None) -> torch.Tensor:
@@ -116,11 +127,12 @@ def mttkrp(X: torch.Tensor, factors: Sequence[Optional[torch.Tensor]], mode: int
     if not 0 <= mode < X.dim():
         raise ValueError("mode out of range")
     sfx, eb = _DT[X.dtype]
-    if out is None:
-        out = torch.empty((X.shape[mode], R), dtype=X.dtype, device=X.device)
     need = workspace_bytes(X.shape, R, mode, X.dtype)
-    if ws is None:
-        ws = _workspace(need, X.device)
+    with _allocating_on(stream):
+        if out is None:
+            out = torch.empty((X.shape[mode], R), dtype=X.dtype, device=X.device)
+        if ws is None:
+            ws = _workspace(need, X.device)
     fn = getattr(_lib.lib(), f"mttkrp_{sfx}")
     st = fn(X.data_ptr(), _dims(X.shape), X.dim(), _ptrs(factors), R, int(mode), out.data_ptr(),
             None if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel(),
@@ -142,7 +154,8 @@ def mttkrp_ablation(X: torch.Tensor, factors: Sequence[Optional[torch.Tensor]], 
         raise ValueError("mode out of range")
     sfx, eb = _DT[X.dtype]
     if out is None:
-        out = torch.empty((X.shape[mode], R), dtype=X.dtype, device=X.device)
+        with _allocating_on(stream):
+            out = torch.empty((X.shape[mode], R), dtype=X.dtype, device=X.device)
     fn = getattr(_lib.lib(), f"mttkrp_{kind}_{sfx}")
     st = fn(X.data_ptr(), _dims(X.shape), X.dim(), _ptrs(factors), R, int(mode), out.data_ptr(),
             _stream_handle(stream))
@@ -160,10 +173,12 @@ def mttkrp_all(X: torch.Tensor, factors: Sequence[torch.Tensor],
     _check_tensor(X)
     R = _check_factors(X, factors)
     sfx, eb = _DT[X.dtype]
-    if outs is None:
-        outs = [torch.empty((X.shape[m], R), dtype=X.dtype, device=X.device) for m in range(X.dim())]
-    if ws is None:
-        ws = _workspace(all_workspace_bytes(X.shape, R, X.dtype), X.device)
+    with _allocating_on(stream):
+        if outs is None:
+            outs = [torch.empty((X.shape[m], R), dtype=X.dtype, device=X.device)
+                    for m in range(X.dim())]
+        if ws is None:
+            ws = _workspace(all_workspace_bytes(X.shape, R, X.dtype), X.device)
     fn = getattr(_lib.lib(), f"mttkrp_all_{sfx}")
     st = fn(X.data_ptr(), _dims(X.shape), X.dim(), _ptrs(factors), R, _ptrs(outs),
             None if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel(),
@@ -186,7 +201,8 @@ def prepare_all(X: torch.Tensor, factors: Sequence[torch.Tensor], outs: List[tor
             raise ValueError(f"output {m} must be a contiguous {X.shape[m]} x {R} tensor")
     need = all_workspace_bytes(X.shape, R, X.dtype)
     if ws is None:
-        ws = _workspace(need, X.device)
+        with _allocating_on(stream):
+            ws = _workspace(need, X.device)
     fn = getattr(_lib.lib(), f"mttkrp_all_{sfx}")
     args = (ctypes.c_void_p(X.data_ptr()), _dims(X.shape), ctypes.c_int(X.dim()), _ptrs(factors),
             ctypes.c_int64(R), _ptrs(outs), ctypes.c_void_p(None if ws is None else ws.data_ptr()),
@@ -212,11 +228,12 @@ def cp_als(X: torch.Tensor, factors: List[torch.Tensor], iters: int, tol: float 
     _check_tensor(X)
     R = _check_factors(X, factors)
     sfx, eb = _DT[X.dtype]
-    lam = torch.empty(R, dtype=X.dtype, device=X.device)
+    with _allocating_on(stream):
+        lam = torch.empty(R, dtype=X.dtype, device=X.device)
+        if ws is None:
+            ws = _workspace(cp_als_workspace_bytes(X.shape, R, X.dtype), X.device)
     fit = (ctypes.c_double * max(1, iters))()
     done = ctypes.c_int(0)
-    if ws is None:
-        ws = _workspace(cp_als_workspace_bytes(X.shape, R, X.dtype), X.device)
     fn = getattr(_lib.lib(), f"cp_als_{sfx}")
     st = fn(X.data_ptr(), _dims(X.shape), X.dim(), R, _ptrs(factors), lam.data_ptr(), int(iters),
             float(tol), fit, ctypes.byref(done), ws.data_ptr(), ws.numel(), _stream_handle(stream))

@@ -301,13 +301,22 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
             else if (tile_min_waves(elem_bytes, 4, 2, false, sl) == 2)
                 p.nb = 2;
         }
+        // Other row-contiguous plans (the output is the unit-stride mode)
+        // take two rank blocks: a 64 x 32 tile feeds its MFMAs from fewer
+        // registers per step than 64 x 64 (tile sweep: 512^3 rank 2000 mode 2
+        // 8.57 -> 8.37 ms, 4-way fp32 rank 64 mode 3 190 -> 176 us).
+        if (!k.tr && p.nb > 2) p.nb = 2;
     } else if (p.nb > 4) {
         p.mb = 2;
     } else if (p.form == 1) {
+        // (256^3 rank 32 keeps 32-row tiles: 64-row ones won 1-2% per mode
+        // alone but lost 2-4% in the all-mode sweep)
         const int64_t tiles64 = k.In * k.nbatch * ceil_div(k.nrows, 64);
         p.mb = (p.nb <= 2 && tiles64 >= 8192) ? 4 : 2;
     } else {
-        p.mb = (k.In >= 64 && p.nb <= 2) ? 4 : 2;
+        // (fp32 single-block tiles are 32 rows: tile sweep, 4-way fp32 rank
+        // 8 modes 1-2, 110 / 115 us against 114 / 117 us for 64 rows)
+        p.mb = (k.In >= 64 && p.nb <= 2 && !(elem_bytes == 4 && p.nb == 1)) ? 4 : 2;
     }
 
     // Experiments: a forced wave tile (and workgroup size) replaces the
