@@ -576,6 +576,276 @@ als_update_small_kernel(const double *__restrict__ Gall, int order, int n,
     }
 }
 
+// The mode update split in two, for R <= RM <= 64 and a mode whose I x R
+// solution fits in LDS (the same sizes as the one-workgroup update above):
+//
+//  - als_side_chol_kernel (on a second stream, beside the mode's MTTKRP,
+//    which it does not need): V = Hadamard of the other Grams, V = L L^T
+//    (the one-wave factorization above), and W = L^{-1}.  It is launched
+//    with eight workgroups, one per XCD, of which the first to be
+//    dispatched does the work: the MTTKRP grid is padded to a multiple of
+//    eight workgroups, and the padding leaves compute units free on one
+//    XCD, where this workgroup then runs without delaying the MTTKRP.
+//  - als_apply_small_kernel (after the MTTKRP, on the caller's stream):
+//    U_new = M V^{-1} = (M W^T) W, the rows' forward and back solves done
+//    as products with W; then the column norms, the normalized factor and
+//    its Gram as in the one-workgroup update.
+//
+// W = L^{-1} column by column (a lane per column c): forward substitution of
+// the unit vector e_c, w_j = b_j / L_jj and b_i -= L_ij w_j for i > j, with
+// the updates of an entry applied in the order j = 0, 1, ....  Lane c keeps
+// the unsolved part of its column in registers, in a frame that moves one
+// entry per step (at step j register k holds entry j + k) and narrows in
+// steps of 16 as the unsolved part shrinks, so the update is a fixed set of
+// fused multiply-adds whose destinations carry the shift (a loop per frame
+// width: the code stays small).  L's column j comes from LDS as broadcast
+// reads of L^T's row j (RM zeros after the last row).
+template <int W, int RM>
+__device__ __forceinline__ void inv_step(double (&b)[RM], int j, int R, int c,
+                                         const double *__restrict__ Lt,
+                                         const double *__restrict__ rd, double *__restrict__ Wout)
+{
+    double lv[W];
+#pragma unroll
+    for (int k = 1; k < W; ++k) lv[k] = Lt[j * R + j + k];
+    const double x = b[0] * rd[j];
+    if (c < R) Wout[j * R + c] = x;
+#pragma unroll
+    for (int k = 1; k < W; ++k) b[k - 1] = __builtin_fma(-lv[k], x, b[k]);
+    b[W - 1] = 0.0;  // entries past the frame are past R - 1
+}
+
+template <int RM>
+__device__ __forceinline__ void tri_inverse_wave(const double *__restrict__ Lt,
+                                                 const double *__restrict__ rd, int R,
+                                                 double *__restrict__ Wout)
+{
+    const int c = threadIdx.x & 63;
+    double b[RM];
+#pragma unroll
+    for (int k = 0; k < RM; ++k) b[k] = (k == c && c < R) ? 1.0 : 0.0;
+    int j = 0;
+    if constexpr (RM >= 64)
+        for (; j < R - 48; ++j) inv_step<64>(b, j, R, c, Lt, rd, Wout);
+    if constexpr (RM >= 48)
+        for (; j < R - 32; ++j) inv_step<48>(b, j, R, c, Lt, rd, Wout);
+    if constexpr (RM >= 32)
+        for (; j < R - 16; ++j) inv_step<32>(b, j, R, c, Lt, rd, Wout);
+    for (; j < R; ++j) inv_step<16>(b, j, R, c, Lt, rd, Wout);
+}
+
+// Dynamic LDS of the side kernel: the column buffers, V (then L, in place,
+// pitch RM + 1, one spare entry), L^T rows with RM zeros after, 1 / L_jj and
+// the failure word.
+template <int RM>
+constexpr size_t side_chol_lds()
+{
+    return (size_t)(256 + (RM * (RM + 1) + 1) + (RM * RM + RM) + RM + 1) * sizeof(double);
+}
+
+template <int RM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
+als_side_chol_kernel(const double *__restrict__ Gall, int order, int n, int R,
+                     double *__restrict__ Wout, int *__restrict__ flag,
+                     unsigned *__restrict__ ticket)
+{
+    constexpr int P = RM + 1;
+    extern __shared__ __align__(16) unsigned char smem[];
+    double *col = reinterpret_cast<double *>(smem);  // 256
+    double *A = col + 256;                           // RM x P (+ 1 spare)
+    double *Lt = A + RM * P + 1;                     // RM x RM, RM zeros after
+    double *rd = Lt + RM * RM + RM;                  // RM
+    int &fail = *reinterpret_cast<int *>(rd + RM);
+    const int tid = threadIdx.x;
+    // Eight workgroups take a ticket each (one vector atomic per workgroup);
+    // the first to run does the work, so it runs on whichever XCD had a
+    // compute unit free.  Every launch takes exactly eight tickets and the
+    // counter starts at zero, so the first ticket of a launch is 0 mod 8.
+    if (tid == 0) fail = (int)(atomicAdd(ticket, 1u) & 7u);
+    __syncthreads();
+    if (fail != 0 || *flag) return;
+    __syncthreads();
+    hadamard_to_lds<RM, 256>(Gall, order, n, R, A, P);
+    col[tid] = 0.0;
+    if (tid < RM) Lt[R * R + tid] = 0.0;
+    __syncthreads();
+    if (tid < 64) {
+        // L overwrites V in place (a row's entries are read into registers
+        // before any is written), and its transpose goes to Lt
+        const bool bad = chol_wave_factor<RM>(A, R, col, A, P, 1, Lt, 1, R, A + RM * P);
+        if (tid == 0) fail = bad;
+    }
+    __syncthreads();
+    if (fail) {
+        if (tid == 0) *flag = 1;
+        return;
+    }
+    if (tid < R) rd[tid] = 1.0 / A[tid * P + tid];
+    __syncthreads();
+    if (tid < 64) tri_inverse_wave<RM>(Lt, rd, R, Wout);
+}
+
+// Dense product of a 4 x 4 block of one of the apply's two products, every
+// sum over k = 0 .. RM - 1 in increasing order: A(i, k) at a[i * sa + k] and
+// B(k, c) at b[k * sbk + c * sbc] (zero past R in both).  W's zero triangle
+// contributes exact zeros, so each sum equals the triangular one with the
+// same order of its nonzero terms.
+template <int RM>
+__device__ __forceinline__ void block4_product(const double *__restrict__ a, int sa,
+                                               const double *__restrict__ b, int sbk, int sbc,
+                                               double (&acc)[4][4])
+{
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[t][u] = 0.0;
+#pragma unroll 8
+    for (int k = 0; k < RM; ++k) {
+        double av[4], bv[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) av[t] = a[t * sa + k];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) bv[u] = b[k * sbk + u * sbc];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc[t][u] = __builtin_fma(av[t], bv[u], acc[t][u]);
+    }
+}
+
+// Dynamic LDS of the apply kernel for I x R (0: not usable): W (RM rows of
+// RM + 1), M then U and Y (each I rounded up to 4 rows of RM), lambda.
+size_t apply_small_lds(int64_t I, int64_t R)
+{
+    if (R > 64 || I > (1 << 20)) return 0;
+    const int64_t rm = R <= 16 ? 16 : R <= 32 ? 32 : 64;
+    const int64_t i4 = (I + 3) / 4 * 4;
+    const size_t b = (size_t)(rm * (rm + 1) + 2 * i4 * rm + 64) * sizeof(double);
+    return b <= 150 * 1024 ? b : 0;
+}
+
+template <typename T, int RM>
+__global__ __launch_bounds__(256) void als_apply_small_kernel(
+    const double *__restrict__ M, int64_t I64, int64_t R64, const double *__restrict__ Win,
+    T *__restrict__ Uout, double *__restrict__ lam64, T *__restrict__ lamT,
+    double *__restrict__ G, const int *__restrict__ flag)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    if (*flag) return;
+    const int I = (int)I64, R = (int)R64;
+    constexpr int PW = RM + 1;  // W's row pitch: lanes reading a column hit distinct banks
+    const int I4 = (I + 3) / 4 * 4;
+    double *W = reinterpret_cast<double *>(smem);  // RM x PW, zero past R
+    double *x = W + RM * PW;                         // M, then U (I4 x RM, zero past I, R)
+    double *y = x + I4 * RM;                         // Y = M W^T
+    double *lam = y + I4 * RM;                       // 64
+    const int tid = threadIdx.x;
+    // W and M into LDS: a thread's loads of a batch are all in flight before
+    // any is stored (one memory round trip per batch, not per element)
+    {
+        constexpr int NW = (RM * PW + 255) / 256;
+        double v[NW];
+#pragma unroll
+        for (int t = 0; t < NW; ++t) {
+            const int e = tid + 256 * t;
+            const int j = e / PW, c = e - (e / PW) * PW;
+            const bool in = e < RM * PW && j < R && c < R;
+            v[t] = Win[in ? j * R + c : 0];
+            v[t] = in ? v[t] : 0.0;
+        }
+#pragma unroll
+        for (int t = 0; t < NW; ++t) {
+            const int e = tid + 256 * t;
+            if (e < RM * PW) W[e] = v[t];
+        }
+    }
+    for (int e0 = 0; e0 < I4 * RM; e0 += 256 * 16) {
+        double v[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const int e = e0 + tid + 256 * t;
+            const int i = e / RM, c = e - (e / RM) * RM;
+            const bool in = i < I && c < R;
+            v[t] = M[in ? i * R + c : 0];
+            v[t] = in ? v[t] : 0.0;
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const int e = e0 + tid + 256 * t;
+            if (e < I4 * RM) x[e] = v[t];
+        }
+    }
+    __syncthreads();
+    constexpr int CB = RM / 4;  // 4-column blocks
+    const int nblk = (I4 / 4) * CB;
+    // forward: Y(i, c) = sum_k M(i, k) W(c, k)
+    for (int blk = tid; blk < nblk; blk += 256) {
+        const int i0 = (blk / CB) * 4, c0 = (blk - (blk / CB) * CB) * 4;
+        double acc[4][4];
+        block4_product<RM>(x + i0 * RM, RM, W + c0 * PW, 1, PW, acc);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) y[(i0 + t) * RM + c0 + u] = acc[t][u];
+    }
+    __syncthreads();
+    // back: U(i, c) = sum_k Y(i, k) W(k, c)
+    for (int blk = tid; blk < nblk; blk += 256) {
+        const int i0 = (blk / CB) * 4, c0 = (blk - (blk / CB) * CB) * 4;
+        double acc[4][4];
+        block4_product<RM>(y + i0 * RM, RM, W + c0, PW, 1, acc);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) x[(i0 + t) * RM + c0 + u] = acc[t][u];
+    }
+    __syncthreads();
+    // column norms (rows in order), then the normalized factor; the LDS copy
+    // keeps the stored (element-type) values for the Gram below
+    if (tid < R) {
+        double sq = 0.0;
+        for (int i = 0; i < I; ++i) sq += x[i * RM + tid] * x[i * RM + tid];
+        const double l = sqrt(sq);
+        lam[tid] = l;
+        lam64[tid] = l;
+        if (lamT) lamT[tid] = (T)l;
+    }
+    __syncthreads();
+    for (int e = tid; e < I * R; e += 256) {
+        const int i = e / R, c = e - (e / R) * R;
+        const double l = lam[c];
+        const T u = (T)(l > 0.0 ? x[i * RM + c] / l : x[i * RM + c]);
+        Uout[e] = u;
+        x[i * RM + c] = (double)u;
+    }
+    __syncthreads();
+    // G = U^T U: a thread takes a 4 x 4 block of entries (each summed over i
+    // in order)
+    const int nb4 = (R + 3) / 4;
+    for (int blk = tid; blk < nb4 * nb4; blk += 256) {
+        const int a0 = (blk / nb4) * 4, c0 = (blk - (blk / nb4) * nb4) * 4;
+        double g[4][4] = {};
+#pragma unroll 4
+        for (int i = 0; i < I; ++i) {
+            double ua[4], uc[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                ua[t] = x[i * RM + a0 + t];
+                uc[t] = x[i * RM + c0 + t];
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) g[t][u] += ua[t] * uc[u];
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (a0 + t < R && c0 + u < R) G[(a0 + t) * R + c0 + u] = g[t][u];
+    }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void fill_kernel(T *__restrict__ p, int64_t n, T v)
 {
@@ -978,6 +1248,40 @@ hipError_t launch_update_small(const double *Gall, int order, int n, const doubl
     return hipGetLastError();
 }
 
+hipError_t launch_side_chol(const double *Gall, int order, int n, int64_t R, double *W, int *flag,
+                            unsigned *ticket, hipStream_t s)
+{
+    if (R > 64) return hipErrorInvalidValue;
+    auto k = R <= 16 ? als_side_chol_kernel<16>
+             : R <= 32 ? als_side_chol_kernel<32>
+                       : als_side_chol_kernel<64>;
+    const size_t lds = R <= 16 ? side_chol_lds<16>() : R <= 32 ? side_chol_lds<32>()
+                                                                : side_chol_lds<64>();
+    if (lds > 64 * 1024) {
+        const hipError_t a = allow_large_lds(reinterpret_cast<const void *>(k));
+        if (a != hipSuccess) return a;
+    }
+    hipLaunchKernelGGL(k, dim3(8), dim3(256), lds, s, Gall, order, n, (int)R, W, flag, ticket);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_apply_small(const double *M, int64_t I, int64_t R, const double *W, T *Uout,
+                              double *lam64, T *lamT, double *G, const int *flag, hipStream_t s)
+{
+    const size_t lds = apply_small_lds(I, R);
+    if (!lds) return hipErrorInvalidValue;
+    auto k = R <= 16 ? als_apply_small_kernel<T, 16>
+             : R <= 32 ? als_apply_small_kernel<T, 32>
+                       : als_apply_small_kernel<T, 64>;
+    if (lds > 64 * 1024) {
+        const hipError_t a = allow_large_lds(reinterpret_cast<const void *>(k));
+        if (a != hipSuccess) return a;
+    }
+    hipLaunchKernelGGL(k, dim3(1), dim3(256), lds, s, M, I, R, W, Uout, lam64, lamT, G, flag);
+    return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_fill(T *p, int64_t n, T v, hipStream_t s)
 {
@@ -1085,6 +1389,8 @@ template hipError_t launch_update_small<double>(const double *, int, int, const 
 template hipError_t launch_update_small<float>(const double *, int, int, const double *, int64_t, int64_t, float *, double *, float *, double *, int *, hipStream_t);
 template hipError_t launch_normalize<double>(const double *, int64_t, int64_t, double *, double *, double *, const int *, hipStream_t);
 template hipError_t launch_normalize<float>(const double *, int64_t, int64_t, float *, double *, float *, const int *, hipStream_t);
+template hipError_t launch_apply_small<double>(const double *, int64_t, int64_t, const double *, double *, double *, double *, double *, const int *, hipStream_t);
+template hipError_t launch_apply_small<float>(const double *, int64_t, int64_t, const double *, float *, double *, float *, double *, const int *, hipStream_t);
 template hipError_t launch_fill<double>(double *, int64_t, double, hipStream_t);
 template hipError_t launch_fill<float>(float *, int64_t, float, hipStream_t);
 template hipError_t launch_fill<int>(int *, int64_t, int, hipStream_t);

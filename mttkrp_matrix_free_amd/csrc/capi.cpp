@@ -45,6 +45,12 @@ hipError_t launch_normalize(const double *Unew, int64_t I, int64_t R, T *Uout, d
 template <typename T>
 hipError_t launch_fill(T *p, int64_t n, T v, hipStream_t s);
 size_t update_small_lds(int64_t I, int64_t R);
+size_t apply_small_lds(int64_t I, int64_t R);
+hipError_t launch_side_chol(const double *Gall, int order, int n, int64_t R, double *W, int *flag,
+                            unsigned *ticket, hipStream_t s);
+template <typename T>
+hipError_t launch_apply_small(const double *M, int64_t I, int64_t R, const double *W, T *Uout,
+                              double *lam64, T *lamT, double *G, const int *flag, hipStream_t s);
 template <typename T>
 hipError_t launch_update_small(const double *Gall, int order, int n, const double *M, int64_t I,
                                int64_t R, T *Uout, double *lam64, T *lamT, double *G, int *flag,
@@ -444,7 +450,9 @@ int cp_als_entry(const T *X, const int64_t *dims, int order, int64_t rank, T *co
     int64_t N = 1;
     for (int m = 0; m < order; ++m) N *= dims[m];
     auto ok = [](hipError_t e) { return e == hipSuccess; };
-    if (!ok(launch_fill<int>(flag, 1, 0, s))) return MTTKRP_EHIP;
+    // the flag word and, 64 bytes on, the side kernel's ticket counter
+    if (!ok(launch_fill<int>(flag, 32, 0, s))) return MTTKRP_EHIP;
+    unsigned *ticket = reinterpret_cast<unsigned *>(flag + 16);
     if (!ok(launch_fill<T>(lambda, R, T(1), s))) return MTTKRP_EHIP;
     if (!ok(launch_sumsq<T>(X, N, parts, kSumsqParts, scal, s))) return MTTKRP_EHIP;
     for (int m = 0; m < order; ++m)
@@ -498,12 +506,54 @@ int cp_als_entry(const T *X, const int64_t *dims, int order, int64_t rank, T *co
         return r;
     };
 
+    // Modes with R <= 64 whose I x R solution fits in LDS split their update:
+    // V, its Cholesky factor and W = L^{-1} (which do not depend on the
+    // MTTKRP) run on a second stream beside the mode's MTTKRP, forked after
+    // the previous update; the rest (U = M W^T W, norms, Gram) follows the
+    // MTTKRP on the caller's stream once the second stream has joined.  W
+    // lives in the L buffer: the next fork comes after this mode's update.
+    auto split_mode = [&](int n) { return R <= 64 && apply_small_lds(dims[n], R) != 0; };
+    struct Side {
+        hipStream_t side = nullptr;
+        hipEvent_t fork = nullptr, join = nullptr;
+        ~Side()
+        {
+            if (fork) (void)hipEventDestroy(fork);
+            if (join) (void)hipEventDestroy(join);
+        }
+    } sd;
+    bool any_split = false;
+    for (int m = 0; m < order; ++m) any_split = any_split || split_mode(m);
+    if (any_split && iters > 0) {
+        if (side_stream(&sd.side) != hipSuccess) return MTTKRP_EHIP;
+        if (!ok(hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming))) return MTTKRP_EHIP;
+        if (!ok(hipEventCreateWithFlags(&sd.join, hipEventDisableTiming))) return MTTKRP_EHIP;
+    }
+
     const T *cf[kMaxOrder];
     for (int m = 0; m < order; ++m) cf[m] = factors[m];
     for (int it = 0; it < iters; ++it) {
         for (int n = 0; n < order; ++n) {
+            const bool split = split_mode(n);
+            if (split) {
+                if (!ok(hipEventRecord(sd.fork, s))) return MTTKRP_EHIP;
+                if (!ok(hipStreamWaitEvent(sd.side, sd.fork, 0))) return MTTKRP_EHIP;
+                if (!ok(launch_side_chol(G, order, n, R, Lc, flag, ticket, sd.side)))
+                    return MTTKRP_EHIP;
+                if (!ok(hipEventRecord(sd.join, sd.side))) return MTTKRP_EHIP;
+            }
             st = mttkrp_one<T>(X, dims, order, cf, R, n, M, 1, w + L.mt, L.M - L.mt, s);
-            if (st) return st;
+            if (st) {
+                if (split) (void)hipStreamWaitEvent(s, sd.join, 0);
+                return st;
+            }
+            if (split) {
+                if (!ok(hipStreamWaitEvent(s, sd.join, 0))) return MTTKRP_EHIP;
+                if (!ok(launch_apply_small<T>(M, dims[n], R, Lc, factors[n], lam64, lambda,
+                                              G + (size_t)n * R * R, flag, s)))
+                    return MTTKRP_EHIP;
+                continue;
+            }
             if (update_small_lds(dims[n], R)) {
                 // Cholesky, solve, normalization and Gram refresh in one
                 // workgroup

@@ -237,8 +237,18 @@ __device__ __forceinline__ void tile_pass(const KParams &p, unsigned char *smem,
     const uint32_t lg = (uint32_t)logical;
     const uint32_t rest = fdiv(lg, p.fd_nrtiles);
     const int64_t rtile = lg - rest * p.fd_nrtiles.d;
-    const uint32_t unit32 = fdiv(rest, p.fd_nsplit);
-    const int64_t split = rest - unit32 * p.fd_nsplit.d;  // output partial written by this workgroup
+    // unit-major (the splits of one unit adjacent) or split-major (the units
+    // of one split adjacent: row tiles that share cache lines then run on one
+    // XCD and walk the same contraction steps together)
+    uint32_t unit32, split32;
+    if (p.split_major) {
+        split32 = fdiv(rest, p.fd_nunits);
+        unit32 = rest - split32 * p.fd_nunits.d;
+    } else {
+        unit32 = fdiv(rest, p.fd_nsplit);
+        split32 = rest - unit32 * p.fd_nsplit.d;
+    }
+    const int64_t split = split32;  // output partial written by this workgroup
     const int64_t unit = unit32;
     const uint32_t kch32 = fdiv((uint32_t)split, p.fd_nsplit_it);
     const int64_t kch = kch32;                                   // contraction chunk

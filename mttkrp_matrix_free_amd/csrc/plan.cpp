@@ -515,6 +515,14 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
             return MTTKRP_ERANGE;
         const int64_t klast = k.K - (k.nkch - 1) * k.Kc;
         k.fd_nrtiles = make_fastdiv(k.nrtiles);
+        k.fd_nunits = make_fastdiv(k.nunits);
+        // Trailing-rows blocks need not be whole cache lines (the 5-way
+        // tensor's 200-row fp64 block is 12.5 lines), so neighbouring row
+        // tiles share lines.  Split-major order keeps every row tile of a
+        // split on one XCD, where the shared lines are fetched once into its
+        // L2 (unit-major order spread them over XCDs: 1.28x the tensor
+        // fetched).
+        k.split_major = k.tr ? 1 : 0;
         k.fd_nsplit = make_fastdiv(k.nsplit);
         k.fd_nsplit_it = make_fastdiv(k.nsplit_it);
         k.fd_nkc_full = make_fastdiv(nkc_full);

@@ -164,7 +164,8 @@ struct KParams {
     void *pend_out;
     int pend_ng;
     // divisors of the index decode (every dividend is below 2^31)
-    FastDiv fd_nrtiles, fd_nsplit, fd_nsplit_it;
+    FastDiv fd_nrtiles, fd_nsplit, fd_nsplit_it, fd_nunits;
+    int split_major;           // 1: workgroup order is (split, unit, rank tile), else (unit, split, rank tile)
     FastDiv fd_nkc_full, fd_nkc_last;  // steps per item: full chunk, last chunk
     FastDiv fd_nrowtiles, fd_odim1, fd_odim2, fd_IrB, fd_IkB;
 };
