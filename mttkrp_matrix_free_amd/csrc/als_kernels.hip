@@ -1025,99 +1025,121 @@ als_chol_diag_kernel(double *__restrict__ A, int64_t R, int64_t k0, double *__re
     }
 }
 
-// C (m x n, leading dimension ldc) = beta C + alpha A B with A(i, t) at
-// A[i sai + t sat] and B(t, j) at B[t sbt + j sbj] (element type TA for both;
-// beta = 0 writes alpha A B without reading C).  A workgroup owns a TR x TC
-// tile, a thread a (TR / 16) x (TC / 16) block of it, summed over t in
-// increasing order.  lower: tiles above the diagonal are skipped.  With
-// n <= TC a workgroup reads all of its rows' A before it writes, so C may be
-// A's own columns.
-template <typename TA, int TR, int TC>
-__global__ __launch_bounds__(256) void als_gemm_kernel(double *__restrict__ C, int64_t ldc,
-                                                       const TA *__restrict__ A, int64_t sai,
-                                                       int64_t sat, const TA *__restrict__ B,
-                                                       int64_t sbt, int64_t sbj, int64_t m,
-                                                       int64_t n, int64_t K, double alpha,
-                                                       double beta, int lower,
-                                                       const int *__restrict__ flag)
+// C (m x n, leading dimension ldc) = beta C + alpha A B on the fp64 matrix
+// cores, with A(i, t) at A[i sai + t sat] and B(t, j) at B[t sbt + j sbj]
+// (element type TA for both, widened to fp64; beta = 0 writes alpha A B
+// without reading C).  A workgroup owns a 64 x 64 tile of C, each of its
+// four waves a 32 x 32 quarter as 2 x 2 blocks of v_mfma_f64_16x16x4f64
+// accumulators; K is staged through LDS in chunks of 64, the next chunk's
+// loads in flight while the matrix cores work on the current one.  lower:
+// tiles above the diagonal are skipped.  C may be A's own columns when n <=
+// 64 (and so K <= 64, one chunk): a workgroup then owns whole rows of C and
+// reads all of its rows of A before it writes (so C and A are not declared
+// restrict).  The sums over t follow the matrix
+// cores' fixed order, so results are deterministic.
+typedef double gdx4 __attribute__((ext_vector_type(4)));
+
+template <typename TA>
+__global__ __launch_bounds__(256) void als_mfma_gemm_kernel(double *C, int64_t ldc, const TA *A,
+                                                            int64_t sai, int64_t sat,
+                                                            const TA *__restrict__ B, int64_t sbt,
+                                                            int64_t sbj, int64_t m, int64_t n,
+                                                            int64_t K, double alpha, double beta,
+                                                            int lower,
+                                                            const int *__restrict__ flag)
 {
-    constexpr int KT = 16, PR = TR / 16, PC = TC / 16;
-    // unpadded rows: a thread's PR (PC) entries of a row are 16-byte aligned
-    // and read as wide LDS loads (the stores, consecutive across threads, do
-    // not conflict)
-    __shared__ __align__(16) double As[KT][TR];
-    __shared__ __align__(16) double Bs[KT][TC];
+    constexpr int TM = 64, TN = 64, KC = 64, PA = TM + 4, NL = TM * KC / 256;
+    extern __shared__ __align__(16) unsigned char smem[];
+    double(*As)[PA] = reinterpret_cast<double(*)[PA]>(smem);                  // KC x PA
+    double(*Bs)[PA] = reinterpret_cast<double(*)[PA]>(smem + KC * PA * sizeof(double));
     if (*flag) return;
     const int64_t ti = blockIdx.y, tj = blockIdx.x;
-    if (lower && tj * TC > ti * TR + TR - 1) return;
-    const int tid = threadIdx.x;
-    const int ty = tid >> 4, tx = tid & 15;  // rows PR ty .., columns PC tx ..
-    const int64_t i0 = ti * TR, j0 = tj * TC;
-    double acc[PR][PC] = {};
-    for (int64_t t0 = 0; t0 < K; t0 += KT) {
-        for (int e = tid; e < KT * TR; e += 256) {
-            const int t = e / TR, r = e % TR;
-            const int64_t tt = t0 + t;
-            As[t][r] = (tt < K && i0 + r < m) ? (double)A[(i0 + r) * sai + tt * sat] : 0.0;
+    if (lower && tj * TN > ti * TM + TM - 1) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = (wave >> 1) * 32, wc = (wave & 1) * 32;  // the wave's quarter
+    const int r16 = lane & 15, q = lane >> 4;
+    const int64_t i0 = ti * TM, j0 = tj * TN;
+    gdx4 acc[2][2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) acc[x][y] = gdx4{0.0, 0.0, 0.0, 0.0};
+    // the unit-stride dimension of each operand runs across consecutive threads
+    const bool a_t = sat == 1, b_c = sbj == 1;
+    double va[NL], vb[NL];
+    // a chunk's operands into registers (zero outside the matrices)
+    auto fetch = [&](int64_t t0) {
+#pragma unroll
+        for (int u = 0; u < NL; ++u) {
+            const int e = tid + 256 * u;
+            const int r = a_t ? e / KC : e % TM, t = a_t ? e % KC : e / TM;
+            const bool ok = i0 + r < m && t0 + t < K;
+            va[u] = ok ? (double)A[(i0 + r) * sai + (t0 + t) * sat] : 0.0;
+            const int c = b_c ? e % TN : e / KC, tb = b_c ? e / TN : e % KC;
+            const bool okb = t0 + tb < K && j0 + c < n;
+            vb[u] = okb ? (double)B[(t0 + tb) * sbt + (j0 + c) * sbj] : 0.0;
         }
-        for (int e = tid; e < KT * TC; e += 256) {
-            const int t = e / TC, r = e % TC;
-            const int64_t tt = t0 + t;
-            Bs[t][r] = (tt < K && j0 + r < n) ? (double)B[tt * sbt + (j0 + r) * sbj] : 0.0;
+    };
+    fetch(0);
+    for (int64_t t0 = 0; t0 < K; t0 += KC) {
+        __syncthreads();  // the previous chunk's operands are read
+#pragma unroll
+        for (int u = 0; u < NL; ++u) {
+            const int e = tid + 256 * u;
+            const int r = a_t ? e / KC : e % TM, t = a_t ? e % KC : e / TM;
+            As[t][r] = va[u];
+            const int c = b_c ? e % TN : e / KC, tb = b_c ? e / TN : e % KC;
+            Bs[tb][c] = vb[u];
         }
         __syncthreads();
+        // the next chunk's loads go out before this chunk's matrix-core work
+        if (t0 + KC < K) fetch(t0 + KC);
 #pragma unroll
-        for (int t = 0; t < KT; ++t) {
-            double a[PR], b[PC];
-#pragma unroll
-            for (int u = 0; u < PR; ++u) a[u] = As[t][PR * ty + u];
-#pragma unroll
-            for (int v = 0; v < PC; ++v) b[v] = Bs[t][PC * tx + v];
-#pragma unroll
-            for (int u = 0; u < PR; ++u)
-#pragma unroll
-                for (int v = 0; v < PC; ++v) acc[u][v] = __builtin_fma(a[u], b[v], acc[u][v]);
+        for (int kk = 0; kk < KC; kk += 4) {
+            const int k = kk + q;
+            const double a0 = As[k][wr + r16], a1 = As[k][wr + 16 + r16];
+            const double b0 = Bs[k][wc + r16], b1 = Bs[k][wc + 16 + r16];
+            acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc[0][0], 0, 0, 0);
+            acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc[0][1], 0, 0, 0);
+            acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc[1][0], 0, 0, 0);
+            acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc[1][1], 0, 0, 0);
         }
-        __syncthreads();
     }
+    // element e of a block holds row 4 e + lane / 16, column lane % 16
 #pragma unroll
-    for (int u = 0; u < PR; ++u)
+    for (int x = 0; x < 2; ++x)
 #pragma unroll
-        for (int v = 0; v < PC; ++v) {
-            const int64_t i = i0 + PR * ty + u, j = j0 + PC * tx + v;
-            if (i < m && j < n) {
-                double *c = C + i * ldc + j;
-                *c = beta == 0.0 ? alpha * acc[u][v] : __builtin_fma(alpha, acc[u][v], beta * *c);
+        for (int y = 0; y < 2; ++y)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t i = i0 + wr + 16 * x + 4 * e + q, j = j0 + wc + 16 * y + r16;
+                if (i < m && j < n) {
+                    double *c = C + i * ldc + j;
+                    const double v = acc[x][y][e];
+                    *c = beta == 0.0 ? alpha * v : __builtin_fma(alpha, v, beta * *c);
+                }
             }
-        }
 }
+constexpr size_t kGemmLds = 2 * 64 * (64 + 4) * sizeof(double);
 
-// Launches the product above: 16 x 64 tiles when C is A's own columns (n <=
-// 64), 64 x 64 tiles when they fill the chip's compute units, else 32 x 32.
+hipError_t allow_large_lds(const void *k);
+
+// Launches the product above on 64 x 64 tiles.  inplace: C is A's own
+// columns (n <= 64).
 template <typename TA>
 hipError_t launch_gemm(double *C, int64_t ldc, const TA *A, int64_t sai, int64_t sat, const TA *B,
                        int64_t sbt, int64_t sbj, int64_t m, int64_t n, int64_t K, double alpha,
                        double beta, int lower, bool inplace, const int *flag, hipStream_t s)
 {
-    hipError_t e = hipSuccess;
-    auto go = [&](auto kern, int tr, int tc) {
-        const int64_t gx = (n + tc - 1) / tc, gy = (m + tr - 1) / tr;
-        if (gx > INT32_MAX || gy > 65535) {  // grid limits
-            e = hipErrorInvalidValue;
-            return;
-        }
-        hipLaunchKernelGGL(kern, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s, C, ldc, A, sai,
-                           sat, B, sbt, sbj, m, n, K, alpha, beta, lower, flag);
-        e = hipGetLastError();
-    };
     if (inplace && n > 64) return hipErrorInvalidValue;
-    if (inplace)
-        go(als_gemm_kernel<TA, 16, 64>, 16, 64);
-    else if (((m + 63) / 64) * ((n + 63) / 64) >= 256)
-        go(als_gemm_kernel<TA, 64, 64>, 64, 64);
-    else
-        go(als_gemm_kernel<TA, 32, 32>, 32, 32);
-    return e;
+    const int64_t gx = (n + 63) / 64, gy = (m + 63) / 64;
+    if (gx > INT32_MAX || gy > 65535) return hipErrorInvalidValue;  // grid limits
+    const hipError_t a = allow_large_lds(reinterpret_cast<const void *>(als_mfma_gemm_kernel<TA>));
+    if (a != hipSuccess) return a;
+    hipLaunchKernelGGL(als_mfma_gemm_kernel<TA>, dim3((unsigned)gx, (unsigned)gy), dim3(256),
+                       kGemmLds, s, C, ldc, A, sai, sat, B, sbt, sbj, m, n, K, alpha, beta, lower,
+                       flag);
+    return hipGetLastError();
 }
 
 // sum_i M(i, r) U(i, r) for every column r (rows in order), one thread per column.
