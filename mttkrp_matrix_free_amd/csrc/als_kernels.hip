@@ -26,6 +26,8 @@
 #include <algorithm>
 #include <type_traits>
 
+#include "als_kernels.hpp"
+
 namespace mttkrp {
 
 constexpr int kRedThreads = 256;
@@ -42,6 +44,158 @@ __device__ __forceinline__ double block_sum(double v, double *sh)
     const int nw = (blockDim.x + 63) >> 6;
     for (int w = 0; w < nw; ++w) t += sh[w];
     return t;
+}
+
+// The failure word as one value for the whole workgroup: thread 0 loads it
+// and the others take its value from LDS, so a write by a kernel running
+// beside this one cannot send the waves down different paths.
+__device__ __forceinline__ int flag_once(const int *flag, int *sh)
+{
+    if (threadIdx.x == 0)
+        *sh = __hip_atomic_load(const_cast<int *>(flag), __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    return *sh;
+}
+
+// Ordering of the split mode update's two streams without events.  A kernel
+// waits (one thread, bounded) until a sequence word written by the kernel it
+// depends on reaches a value, and when done stores its own value to another
+// word.  The host only ever makes a kernel wait for one queued before it, so
+// however the two streams map onto hardware queues the awaited kernel runs
+// first or beside the waiting one.  Past about 10 s of the 100 MHz constant
+// clock the wait gives up: the failure word becomes 3 and the kernel does no
+// work but still stores its word, so no waiter is left behind.
+struct SeqArgs {
+    const unsigned *wait_on;  // word to wait for (null: no wait)
+    unsigned wait_for;        // value it must reach (compared with wrap-around)
+    unsigned *done;           // word to store when finished (null: none)
+    unsigned done_val;
+};
+constexpr long long kSeqWaitTicks = 1000000000LL;
+
+__device__ __noinline__ bool seq_wait_thread(const unsigned *p, unsigned target)
+{
+    if (!p) return true;
+    const long long t0 = wall_clock64();
+    for (;;) {
+        const unsigned v = __hip_atomic_load(const_cast<unsigned *>(p), __ATOMIC_ACQUIRE,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        if ((int)(v - target) >= 0) return true;
+        if (wall_clock64() - t0 > kSeqWaitTicks) return false;
+        __builtin_amdgcn_s_sleep(2);
+    }
+}
+
+// Whole workgroup: wait, then every thread acquires, so what the awaited
+// kernel wrote before its word is visible to each of them.  Returns the
+// failure word read after the wait (one value for the workgroup).
+__device__ __forceinline__ int seq_enter(const SeqArgs &q, int *flag, int *sh)
+{
+    if (threadIdx.x == 0) {
+        int f;
+        if (seq_wait_thread(q.wait_on, q.wait_for)) {
+            f = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            atomicCAS(flag, 0, 3);
+            f = 3;
+        }
+        *sh = f;
+    }
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    return *sh;
+}
+
+// Whole workgroup: every thread releases its writes, then thread 0 stores the
+// word.
+__device__ __forceinline__ void seq_leave(const SeqArgs &q)
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (threadIdx.x == 0 && q.done)
+        __hip_atomic_store(q.done, q.done_val, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The end of a sweep: the fit, the stop decision and the host-visible slot.
+// A sweep whose fit changed by less than tol (tol > 0, a previous sweep's fit
+// in scal[2]) sets the failure word to 2, so every later kernel of the run
+// returns without writing, just as after a failed Cholesky (1).  The slot
+// receives the fit and the word, then the sweep's number (a release at
+// system scope): the host polls that number while the next sweep is
+// already queued, so the device never waits for the host.
+struct FitArgs {
+    const double *Gall;  // the Grams of every mode, this sweep's last included
+    int order;
+    double *scal;        // [0] ||X||^2 in, [1] fit out, [2] the previous fit
+    double tol;
+    int have_prev;
+    double *out_fit;     // host-visible slot
+    int *out_flag;
+    unsigned *out_seq;
+    unsigned seq_val;
+};
+
+// Thread 0, given <X, model> and ||model||^2.
+__device__ __forceinline__ void fit_finish(double inner, double nrm2, int *flag, const FitArgs &fa)
+{
+    const double nx2 = fa.scal[0];
+    double resid = nx2 + nrm2 - 2.0 * inner;
+    if (resid < 0.0) resid = 0.0;
+    const double fit = nx2 > 0.0 ? 1.0 - sqrt(resid) / sqrt(nx2) : __builtin_nan("");
+    const int stop = fa.tol > 0.0 && fa.have_prev && fabs(fit - fa.scal[2]) < fa.tol;
+    fa.scal[1] = fit;
+    fa.scal[2] = fit;
+    if (stop) atomicCAS(flag, 0, 2);
+    *fa.out_fit = fit;
+    *fa.out_flag = stop ? 2 : 0;
+    __hip_atomic_store(fa.out_seq, fa.seq_val, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// Thread 0 of a sweep whose kernels found the failure word set: the word and
+// the sweep's number go to the slot (the fit is not written).
+__device__ __forceinline__ void fit_skip(int f, const FitArgs &fa)
+{
+    *fa.out_flag = f;
+    __hip_atomic_store(fa.out_seq, fa.seq_val, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// ||model||^2 = sum_{a,b} lambda_a lambda_b prod_m G_m(a, b): eight entries
+// per thread and round, every load of a round in flight at once; each thread
+// adds its entries in index order (the workgroup sum follows).
+__device__ __forceinline__ double model_norm_part(const double *__restrict__ lam,
+                                                  const double *__restrict__ Gall, int order,
+                                                  int64_t R)
+{
+    const int64_t RR = R * R;
+    double nrm2 = 0.0;
+    constexpr int Q = 8;
+    for (int64_t e0 = threadIdx.x; e0 < RR; e0 += (int64_t)blockDim.x * Q) {
+        double v[Q];
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            int64_t e = e0 + (int64_t)blockDim.x * q;
+            e = e < RR ? e : RR - 1;
+            const int64_t a = e / R, b = e - (e / R) * R;
+            v[q] = lam[a] * lam[b];
+        }
+        // modes past the order multiply by 1 (exact), so no load waits on a branch
+#pragma unroll
+        for (int m = 0; m < 5; ++m) {
+            const bool use = m < order;
+            const double *Gm = Gall + (use ? (int64_t)m * RR : 0);
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                const int64_t e = e0 + (int64_t)blockDim.x * q;
+                const double g = Gm[e < RR ? e : RR - 1];
+                v[q] *= use ? g : 1.0;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < Q; ++q)
+            if (e0 + (int64_t)blockDim.x * q < RR) nrm2 += v[q];
+    }
+    return nrm2;
 }
 
 // ||X||^2, first pass: one fp64 partial per workgroup (grid-stride, fixed order).
@@ -84,6 +238,42 @@ __global__ __launch_bounds__(256) void gram_kernel(const T *__restrict__ U, int6
     double s = 0.0;
     for (int64_t i = 0; i < I; ++i) s += (double)U[i * R + a] * (double)U[i * R + b];
     G[e] = s;
+}
+
+// The Grams of every mode at the start of a run (R <= 64), in one launch:
+// blockIdx.y is the mode, a thread one entry summed over i in increasing
+// order (as gram_kernel), with eight rows' loads in flight at once.
+struct GramAllArgs {
+    const void *U[5];
+    int64_t I[5];
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void gram_all_kernel(GramAllArgs g, int64_t R,
+                                                       double *__restrict__ G,
+                                                       const int *__restrict__ flag)
+{
+    if (*flag) return;  // (no barrier follows)
+    const int m = blockIdx.y;
+    const T *__restrict__ U = static_cast<const T *>(g.U[m]);
+    const int64_t I = g.I[m];
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= R * R) return;
+    const int64_t a = e / R, b = e - (e / R) * R;
+    double s = 0.0;
+    for (int64_t i0 = 0; i0 < I; i0 += 8) {
+        double ua[8], ub[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int64_t i = i0 + t < I ? i0 + t : I - 1;
+            ua[t] = (double)U[i * R + a];
+            ub[t] = (double)U[i * R + b];
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+            if (i0 + t < I) s += ua[t] * ub[t];
+    }
+    G[(int64_t)m * R * R + e] = s;
 }
 
 // Lane read of a double (the lane index is wave-uniform).
@@ -647,7 +837,7 @@ template <int RM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 als_side_chol_kernel(const double *__restrict__ Gall, int order, int n, int R,
                      double *__restrict__ Wout, int *__restrict__ flag,
-                     unsigned *__restrict__ ticket)
+                     unsigned *__restrict__ ticket, SeqArgs q)
 {
     constexpr int P = RM + 1;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -663,26 +853,30 @@ als_side_chol_kernel(const double *__restrict__ Gall, int order, int n, int R,
     // counter starts at zero, so the first ticket of a launch is 0 mod 8.
     if (tid == 0) fail = (int)(atomicAdd(ticket, 1u) & 7u);
     __syncthreads();
-    if (fail != 0 || *flag) return;
-    __syncthreads();
-    hadamard_to_lds<RM, 256>(Gall, order, n, R, A, P);
-    col[tid] = 0.0;
-    if (tid < RM) Lt[R * R + tid] = 0.0;
-    __syncthreads();
-    if (tid < 64) {
-        // L overwrites V in place (a row's entries are read into registers
-        // before any is written), and its transpose goes to Lt
-        const bool bad = chol_wave_factor<RM>(A, R, col, A, P, 1, Lt, 1, R, A + RM * P);
-        if (tid == 0) fail = bad;
+    if (fail != 0) return;
+    __syncthreads();  // every thread has read the ticket before fail is reused
+    // the previous update's Gram (or the fit before a sweep's first mode)
+    if (seq_enter(q, flag, &fail) == 0) {
+        hadamard_to_lds<RM, 256>(Gall, order, n, R, A, P);
+        col[tid] = 0.0;
+        if (tid < RM) Lt[R * R + tid] = 0.0;
+        __syncthreads();
+        if (tid < 64) {
+            // L overwrites V in place (a row's entries are read into
+            // registers before any is written), and its transpose goes to Lt
+            const bool bad = chol_wave_factor<RM>(A, R, col, A, P, 1, Lt, 1, R, A + RM * P);
+            if (tid == 0) fail = bad;
+        }
+        __syncthreads();
+        if (fail) {
+            if (tid == 0) atomicCAS(flag, 0, 1);
+        } else {
+            if (tid < R) rd[tid] = 1.0 / A[tid * P + tid];
+            __syncthreads();
+            if (tid < 64) tri_inverse_wave<RM>(Lt, rd, R, Wout);
+        }
     }
-    __syncthreads();
-    if (fail) {
-        if (tid == 0) *flag = 1;
-        return;
-    }
-    if (tid < R) rd[tid] = 1.0 / A[tid * P + tid];
-    __syncthreads();
-    if (tid < 64) tri_inverse_wave<RM>(Lt, rd, R, Wout);
+    seq_leave(q);
 }
 
 // Dense product of a 4 x 4 block of one of the apply's two products, every
@@ -725,13 +919,13 @@ size_t apply_small_lds(int64_t I, int64_t R)
 }
 
 template <typename T, int RM>
-__global__ __launch_bounds__(256) void als_apply_small_kernel(
-    const double *__restrict__ M, int64_t I64, int64_t R64, const double *__restrict__ Win,
-    T *__restrict__ Uout, double *__restrict__ lam64, T *__restrict__ lamT,
-    double *__restrict__ G, const int *__restrict__ flag)
+__device__ __forceinline__ void apply_small_body(const double *__restrict__ M, int64_t I64,
+                                                 int64_t R64, const double *__restrict__ Win,
+                                                 T *__restrict__ Uout, double *__restrict__ lam64,
+                                                 T *__restrict__ lamT, double *__restrict__ G,
+                                                 int *__restrict__ flag, const FitArgs &fa)
 {
     extern __shared__ __align__(16) unsigned char smem[];
-    if (*flag) return;
     const int I = (int)I64, R = (int)R64;
     constexpr int PW = RM + 1;  // W's row pitch: lanes reading a column hit distinct banks
     const int I4 = (I + 3) / 4 * 4;
@@ -844,6 +1038,40 @@ __global__ __launch_bounds__(256) void als_apply_small_kernel(
             for (int u = 0; u < 4; ++u)
                 if (a0 + t < R && c0 + u < R) G[(a0 + t) * R + c0 + u] = g[t][u];
     }
+    if (!fa.out_seq) return;
+    // The sweep's last mode: its fit, as als_fit_kernel forms it, from M (the
+    // MTTKRP, still in memory), the stored factor (x), lambda and the Grams
+    // (this one just written by the workgroup).
+    __shared__ double sh[4];
+    __syncthreads();
+    double inner = 0.0;
+    if (tid < R) {
+        double sm = 0.0;
+        for (int i = 0; i < I; ++i) sm += M[(int64_t)i * R + tid] * x[i * RM + tid];
+        inner = lam[tid] * sm;
+    }
+    inner = block_sum(inner, sh);
+    double nrm2 = model_norm_part(lam, fa.Gall, fa.order, R);
+    nrm2 = block_sum(nrm2, sh);
+    if (tid == 0) fit_finish(inner, nrm2, flag, fa);
+}
+
+// The apply waits for its mode's side kernel (W and the failure word), and
+// stores its word when done, for the next mode's side kernel (the Gram).
+// With fa.out_seq set it also ends the sweep (the fit).
+template <typename T, int RM>
+__global__ __launch_bounds__(256) void als_apply_small_kernel(
+    const double *__restrict__ M, int64_t I64, int64_t R64, const double *__restrict__ Win,
+    T *__restrict__ Uout, double *__restrict__ lam64, T *__restrict__ lamT,
+    double *__restrict__ G, int *__restrict__ flag, FitArgs fa, SeqArgs q)
+{
+    __shared__ int sflag;
+    const int f = seq_enter(q, flag, &sflag);
+    if (f == 0)
+        apply_small_body<T, RM>(M, I64, R64, Win, Uout, lam64, lamT, G, flag, fa);
+    else if (fa.out_seq && threadIdx.x == 0)
+        fit_skip(f, fa);
+    seq_leave(q);
 }
 
 template <typename T>
@@ -853,28 +1081,16 @@ __global__ __launch_bounds__(256) void fill_kernel(T *__restrict__ p, int64_t n,
     if (i < n) p[i] = v;
 }
 
-// Fit after the last mode of a sweep; one workgroup.  scal[0] = ||X||^2 in,
-// scal[1] = fit out.
-// The fit after a sweep, and the stop decision: a sweep whose fit changed by
-// less than tol (tol > 0, a previous sweep's fit in scal[2]) sets the flag
-// to 2, so every later kernel of the run returns without writing, just as
-// after a failed Cholesky (flag 1).  The fit and the flag are also stored to
-// the host-visible slot (out_fit, out_flag), so the host learns the outcome
-// without a copy, while the next sweep is already queued.
+// Fit after the last mode of a sweep (when its update is not the split one,
+// which forms the fit itself); one workgroup.
 template <typename T>
-__global__ __launch_bounds__(kRedThreads) void als_fit_kernel(
-    const double *__restrict__ M, const T *__restrict__ Ulast, int64_t Ilast,
-    const double *__restrict__ lam64, const double *__restrict__ Gall, int order, int64_t R,
-    double *__restrict__ scal, int *__restrict__ flag, double tol, int have_prev,
-    double *__restrict__ out_fit, int *__restrict__ out_flag, const double *__restrict__ mparts,
-    int nmparts, const double *__restrict__ colsum)
+__device__ __forceinline__ void fit_body(const double *__restrict__ M, const T *__restrict__ Ulast,
+                                         int64_t Ilast, const double *__restrict__ lam64, int64_t R,
+                                         int *__restrict__ flag, const double *__restrict__ mparts,
+                                         int nmparts, const double *__restrict__ colsum,
+                                         const FitArgs &fa)
 {
     __shared__ double sh[kRedThreads / 64];
-    const int f0 = *flag;
-    if (f0) {
-        if (threadIdx.x == 0) *out_flag = f0;
-        return;
-    }
     double inner = 0.0;
     for (int64_t r = threadIdx.x; r < R; r += kRedThreads) {
         double s = 0.0;
@@ -885,51 +1101,34 @@ __global__ __launch_bounds__(kRedThreads) void als_fit_kernel(
         inner += lam64[r] * s;
     }
     inner = block_sum(inner, sh);
-    // ||model||^2: eight entries per thread and round, every load of a round
-    // in flight at once; each thread still adds its entries in index order
-    const int64_t RR = R * R;
     double nrm2 = 0.0;
-    constexpr int Q = 8;
-    // (large R: the sum comes in partials from als_model_norm_kernel)
-    for (int i = threadIdx.x; i < nmparts; i += kRedThreads) nrm2 += mparts[i];
-    for (int64_t e0 = threadIdx.x; nmparts == 0 && e0 < RR; e0 += (int64_t)kRedThreads * Q) {
-        double v[Q];
-#pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            int64_t e = e0 + (int64_t)kRedThreads * q;
-            e = e < RR ? e : RR - 1;
-            const int64_t a = e / R, b = e - (e / R) * R;
-            v[q] = lam64[a] * lam64[b];
-        }
-        // modes past the order multiply by 1 (exact), so no load waits on a branch
-#pragma unroll
-        for (int m = 0; m < 5; ++m) {
-            const bool use = m < order;
-            const double *Gm = Gall + (use ? (int64_t)m * RR : 0);
-#pragma unroll
-            for (int q = 0; q < Q; ++q) {
-                const int64_t e = e0 + (int64_t)kRedThreads * q;
-                const double g = Gm[e < RR ? e : RR - 1];
-                v[q] *= use ? g : 1.0;
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < Q; ++q)
-            if (e0 + (int64_t)kRedThreads * q < RR) nrm2 += v[q];
+    if (nmparts > 0) {
+        // (large R: the sum comes in partials from als_model_norm_kernel)
+        for (int i = threadIdx.x; i < nmparts; i += kRedThreads) nrm2 += mparts[i];
+    } else {
+        nrm2 = model_norm_part(lam64, fa.Gall, fa.order, R);
     }
     nrm2 = block_sum(nrm2, sh);
-    if (threadIdx.x == 0) {
-        const double nx2 = scal[0];
-        double resid = nx2 + nrm2 - 2.0 * inner;
-        if (resid < 0.0) resid = 0.0;
-        const double fit = nx2 > 0.0 ? 1.0 - sqrt(resid) / sqrt(nx2) : __builtin_nan("");
-        const int stop = tol > 0.0 && have_prev && fabs(fit - scal[2]) < tol;
-        scal[1] = fit;
-        scal[2] = fit;
-        if (stop) *flag = 2;
-        *out_fit = fit;
-        *out_flag = stop ? 2 : 0;
+    if (threadIdx.x == 0) fit_finish(inner, nrm2, flag, fa);
+}
+
+// The fit kernel stores its sequence word when done, for the next sweep's
+// first side kernel (which then sees the stop decision).
+template <typename T>
+__global__ __launch_bounds__(kRedThreads) void als_fit_kernel(
+    const double *__restrict__ M, const T *__restrict__ Ulast, int64_t Ilast,
+    const double *__restrict__ lam64, int64_t R, int *__restrict__ flag,
+    const double *__restrict__ mparts, int nmparts, const double *__restrict__ colsum, FitArgs fa,
+    SeqArgs q)
+{
+    __shared__ int sflag;
+    const int f0 = flag_once(flag, &sflag);
+    if (f0) {
+        if (threadIdx.x == 0) fit_skip(f0, fa);
+    } else {
+        fit_body<T>(M, Ulast, Ilast, lam64, R, flag, mparts, nmparts, colsum, fa);
     }
+    seq_leave(q);
 }
 
 // ---------------------------------------------------------------------------
@@ -1210,6 +1409,27 @@ hipError_t launch_gram(const T *U, int64_t I, int64_t R, double *G, const int *f
     return hipGetLastError();
 }
 
+template <typename T>
+hipError_t launch_gram_all(const T *const *U, const int64_t *dims, int order, int64_t R, double *G,
+                           const int *flag, hipStream_t s)
+{
+    if (R > 64 || order > 5) {
+        for (int m = 0; m < order; ++m) {
+            const hipError_t e = launch_gram<T>(U[m], dims[m], R, G + (size_t)m * R * R, flag, s);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    GramAllArgs g{};
+    for (int m = 0; m < order; ++m) {
+        g.U[m] = U[m];
+        g.I[m] = dims[m];
+    }
+    hipLaunchKernelGGL(gram_all_kernel<T>, dim3((unsigned)((R * R + 255) / 256), (unsigned)order),
+                       dim3(256), 0, s, g, R, G, flag);
+    return hipGetLastError();
+}
+
 hipError_t launch_chol(const double *Gall, int order, int n, int64_t R, double *L, int *flag,
                        hipStream_t s)
 {
@@ -1271,7 +1491,8 @@ hipError_t launch_update_small(const double *Gall, int order, int n, const doubl
 }
 
 hipError_t launch_side_chol(const double *Gall, int order, int n, int64_t R, double *W, int *flag,
-                            unsigned *ticket, hipStream_t s)
+                            unsigned *ticket, const unsigned *wait_on, unsigned wait_for,
+                            unsigned *done, unsigned done_val, hipStream_t s)
 {
     if (R > 64) return hipErrorInvalidValue;
     auto k = R <= 16 ? als_side_chol_kernel<16>
@@ -1283,14 +1504,21 @@ hipError_t launch_side_chol(const double *Gall, int order, int n, int64_t R, dou
         const hipError_t a = allow_large_lds(reinterpret_cast<const void *>(k));
         if (a != hipSuccess) return a;
     }
-    hipLaunchKernelGGL(k, dim3(8), dim3(256), lds, s, Gall, order, n, (int)R, W, flag, ticket);
+    hipLaunchKernelGGL(k, dim3(8), dim3(256), lds, s, Gall, order, n, (int)R, W, flag, ticket,
+                       SeqArgs{wait_on, wait_for, done, done_val});
     return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_apply_small(const double *M, int64_t I, int64_t R, const double *W, T *Uout,
-                              double *lam64, T *lamT, double *G, const int *flag, hipStream_t s)
+                              double *lam64, T *lamT, double *G, int *flag,
+                              const unsigned *wait_on, unsigned wait_for, unsigned *done,
+                              unsigned done_val, const AlsFitOut *fit, hipStream_t s)
 {
+    FitArgs fa{};
+    if (fit)
+        fa = FitArgs{fit->Gall, fit->order, fit->scal,    fit->tol,    fit->have_prev,
+                     fit->out_fit, fit->out_flag, fit->out_seq, fit->seq_val};
     const size_t lds = apply_small_lds(I, R);
     if (!lds) return hipErrorInvalidValue;
     auto k = R <= 16 ? als_apply_small_kernel<T, 16>
@@ -1300,7 +1528,8 @@ hipError_t launch_apply_small(const double *M, int64_t I, int64_t R, const doubl
         const hipError_t a = allow_large_lds(reinterpret_cast<const void *>(k));
         if (a != hipSuccess) return a;
     }
-    hipLaunchKernelGGL(k, dim3(1), dim3(256), lds, s, M, I, R, W, Uout, lam64, lamT, G, flag);
+    hipLaunchKernelGGL(k, dim3(1), dim3(256), lds, s, M, I, R, W, Uout, lam64, lamT, G, flag, fa,
+                       SeqArgs{wait_on, wait_for, done, done_val});
     return hipGetLastError();
 }
 
@@ -1314,10 +1543,13 @@ hipError_t launch_fill(T *p, int64_t n, T v, hipStream_t s)
 
 template <typename T>
 hipError_t launch_fit(const double *M, const T *Ulast, int64_t Ilast, const double *lam64,
-                      const double *Gall, int order, int64_t R, double *scal, int *flag,
-                      double tol, int have_prev, double *out_fit, int *out_flag, double *parts,
-                      int max_parts, double *colsum_buf, hipStream_t s)
+                      int64_t R, int *flag, const AlsFitOut &fit, double *parts, int max_parts,
+                      double *colsum_buf, unsigned *done, unsigned done_val, hipStream_t s)
 {
+    const double *Gall = fit.Gall;
+    const int order = fit.order;
+    const FitArgs fa{fit.Gall,    fit.order,    fit.scal,    fit.tol,    fit.have_prev,
+                     fit.out_fit, fit.out_flag, fit.out_seq, fit.seq_val};
     const double *colsum = nullptr;
     if (R > 256) {
         hipLaunchKernelGGL(als_colsum_kernel<T>, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, s,
@@ -1331,8 +1563,7 @@ hipError_t launch_fit(const double *M, const T *Ulast, int64_t Ilast, const doub
                            order, R, parts, flag);
     }
     hipLaunchKernelGGL(als_fit_kernel<T>, dim3(1), dim3(kRedThreads), 0, s, M, Ulast, Ilast, lam64,
-                       Gall, order, R, scal, flag, tol, have_prev, out_fit, out_flag, parts, np,
-                       colsum);
+                       R, flag, parts, np, colsum, fa, SeqArgs{nullptr, 0u, done, done_val});
     return hipGetLastError();
 }
 
@@ -1407,16 +1638,18 @@ template hipError_t launch_sumsq<double>(const double *, int64_t, double *, int,
 template hipError_t launch_sumsq<float>(const float *, int64_t, double *, int, double *, hipStream_t);
 template hipError_t launch_gram<double>(const double *, int64_t, int64_t, double *, const int *, hipStream_t);
 template hipError_t launch_gram<float>(const float *, int64_t, int64_t, double *, const int *, hipStream_t);
+template hipError_t launch_gram_all<double>(const double *const *, const int64_t *, int, int64_t, double *, const int *, hipStream_t);
+template hipError_t launch_gram_all<float>(const float *const *, const int64_t *, int, int64_t, double *, const int *, hipStream_t);
 template hipError_t launch_update_small<double>(const double *, int, int, const double *, int64_t, int64_t, double *, double *, double *, double *, int *, hipStream_t);
 template hipError_t launch_update_small<float>(const double *, int, int, const double *, int64_t, int64_t, float *, double *, float *, double *, int *, hipStream_t);
 template hipError_t launch_normalize<double>(const double *, int64_t, int64_t, double *, double *, double *, const int *, hipStream_t);
 template hipError_t launch_normalize<float>(const double *, int64_t, int64_t, float *, double *, float *, const int *, hipStream_t);
-template hipError_t launch_apply_small<double>(const double *, int64_t, int64_t, const double *, double *, double *, double *, double *, const int *, hipStream_t);
-template hipError_t launch_apply_small<float>(const double *, int64_t, int64_t, const double *, float *, double *, float *, double *, const int *, hipStream_t);
+template hipError_t launch_apply_small<double>(const double *, int64_t, int64_t, const double *, double *, double *, double *, double *, int *, const unsigned *, unsigned, unsigned *, unsigned, const AlsFitOut *, hipStream_t);
+template hipError_t launch_apply_small<float>(const double *, int64_t, int64_t, const double *, float *, double *, float *, double *, int *, const unsigned *, unsigned, unsigned *, unsigned, const AlsFitOut *, hipStream_t);
 template hipError_t launch_fill<double>(double *, int64_t, double, hipStream_t);
 template hipError_t launch_fill<float>(float *, int64_t, float, hipStream_t);
 template hipError_t launch_fill<int>(int *, int64_t, int, hipStream_t);
-template hipError_t launch_fit<double>(const double *, const double *, int64_t, const double *, const double *, int, int64_t, double *, int *, double, int, double *, int *, double *, int, double *, hipStream_t);
-template hipError_t launch_fit<float>(const double *, const float *, int64_t, const double *, const double *, int, int64_t, double *, int *, double, int, double *, int *, double *, int, double *, hipStream_t);
+template hipError_t launch_fit<double>(const double *, const double *, int64_t, const double *, int64_t, int *, const AlsFitOut &, double *, int, double *, unsigned *, unsigned, hipStream_t);
+template hipError_t launch_fit<float>(const double *, const float *, int64_t, const double *, int64_t, int *, const AlsFitOut &, double *, int, double *, unsigned *, unsigned, hipStream_t);
 
 }  // namespace mttkrp

@@ -16,6 +16,7 @@
 #include <vector>
 
 #include "../../include/mttkrp.h"
+#include "als_kernels.hpp"
 #include "plan.hpp"
 #include "tile_select.hpp"
 
@@ -25,41 +26,6 @@ template <typename T>
 hipError_t launch_mttkrp(const Plan &pl, hipStream_t stream, bool with_reduce);
 template <typename T>
 hipError_t launch_mttkrp_multi(const Plan *const *pls, int np, hipStream_t stream);
-
-template <typename T>
-hipError_t launch_sumsq(const T *X, int64_t N, double *partial, int nparts, double *out,
-                        hipStream_t s);
-template <typename T>
-hipError_t launch_gram(const T *U, int64_t I, int64_t R, double *G, const int *flag, hipStream_t s);
-hipError_t launch_chol_blocked(const double *Gall, int order, int n, int64_t R, double *A,
-                               double *W, int *flag, hipStream_t s);
-hipError_t launch_solve_blocked(const double *M, const double *L, const double *W, int64_t I,
-                                int64_t R, double *Unew, const int *flag, hipStream_t s);
-hipError_t launch_chol(const double *Gall, int order, int n, int64_t R, double *L, int *flag,
-                       hipStream_t s);
-hipError_t launch_solve(const double *M, const double *L, int64_t I, int64_t R, double *Unew,
-                        const int *flag, hipStream_t s);
-template <typename T>
-hipError_t launch_normalize(const double *Unew, int64_t I, int64_t R, T *Uout, double *lam64,
-                            T *lamT, const int *flag, hipStream_t s);
-template <typename T>
-hipError_t launch_fill(T *p, int64_t n, T v, hipStream_t s);
-size_t update_small_lds(int64_t I, int64_t R);
-size_t apply_small_lds(int64_t I, int64_t R);
-hipError_t launch_side_chol(const double *Gall, int order, int n, int64_t R, double *W, int *flag,
-                            unsigned *ticket, hipStream_t s);
-template <typename T>
-hipError_t launch_apply_small(const double *M, int64_t I, int64_t R, const double *W, T *Uout,
-                              double *lam64, T *lamT, double *G, const int *flag, hipStream_t s);
-template <typename T>
-hipError_t launch_update_small(const double *Gall, int order, int n, const double *M, int64_t I,
-                               int64_t R, T *Uout, double *lam64, T *lamT, double *G, int *flag,
-                               hipStream_t s);
-template <typename T>
-hipError_t launch_fit(const double *M, const T *Ulast, int64_t Ilast, const double *lam64,
-                      const double *Gall, int order, int64_t R, double *scal, int *flag,
-                      double tol, int have_prev, double *out_fit, int *out_flag, double *parts,
-                      int max_parts, double *colsum_buf, hipStream_t s);
 
 namespace {
 
@@ -91,6 +57,40 @@ hipError_t side_stream(hipStream_t *out)
     }
     *out = ss[dev];
     return hipSuccess;
+}
+
+// Host-visible slots for the fit and failure word of a CP-ALS run's last two
+// sweeps.  They are allocated (pinned, coherent) on a host thread's first run
+// on a device and kept until the thread ends: a thread runs one call at a
+// time (a call returns only after its kernels are done), so calls never share
+// a slot, and no call pays for the allocation again.
+struct FitSlot {
+    double fit;
+    int flag;
+    unsigned seq;  // the sweep's number plus one, stored last
+};
+
+FitSlot *fit_slots()
+{
+    constexpr int kMaxDev = 64;
+    struct Cache {
+        FitSlot *p[kMaxDev] = {};
+        ~Cache()
+        {
+            for (FitSlot *q : p)
+                if (q) (void)hipHostFree(q);
+        }
+    };
+    thread_local Cache c;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nullptr;
+    if (!c.p[dev]) {
+        void *q = nullptr;
+        if (hipHostMalloc(&q, 2 * sizeof(FitSlot), hipHostMallocCoherent) != hipSuccess)
+            return nullptr;
+        c.p[dev] = static_cast<FitSlot *>(q);
+    }
+    return c.p[dev];
 }
 
 // Checks shared by the MTTKRP entry points.  `factors` may hold NULL at `mode`
@@ -450,78 +450,75 @@ int cp_als_entry(const T *X, const int64_t *dims, int order, int64_t rank, T *co
     int64_t N = 1;
     for (int m = 0; m < order; ++m) N *= dims[m];
     auto ok = [](hipError_t e) { return e == hipSuccess; };
-    // the flag word and, 64 bytes on, the side kernel's ticket counter
+    // the flag block: the failure word, then at 32, 64 and 96 bytes on the
+    // caller's stream's sequence word, the side kernel's ticket counter and
+    // the side stream's sequence word (all zero at the start of a run)
     if (!ok(launch_fill<int>(flag, 32, 0, s))) return MTTKRP_EHIP;
     unsigned *ticket = reinterpret_cast<unsigned *>(flag + 16);
     if (!ok(launch_fill<T>(lambda, R, T(1), s))) return MTTKRP_EHIP;
     if (!ok(launch_sumsq<T>(X, N, parts, kSumsqParts, scal, s))) return MTTKRP_EHIP;
-    for (int m = 0; m < order; ++m)
-        if (!ok(launch_gram<T>(factors[m], dims[m], R, G + (size_t)m * R * R, flag, s)))
-            return MTTKRP_EHIP;
+    if (!ok(launch_gram_all<T>(factors, dims, order, R, G, flag, s))) return MTTKRP_EHIP;
 
     // Each sweep's fit and flag land in host-visible pinned memory (two
-    // slots, written by the fit kernel).  The host reads sweep it - 1's slot
-    // only after sweep it is queued, so the device never waits for the host;
-    // a sweep queued past a stop (convergence or a failed Cholesky) changes
-    // nothing, since its kernels see the flag and return.
-    struct Slot {
-        double fit;
-        int flag;
-        int pad;
-    };
-    struct Pinned {
+    // slots, written at the end of the sweep).  The host polls sweep it - 1's
+    // slot only after sweep it is queued, so the device never waits for the
+    // host; a sweep queued past a stop (convergence or a failed Cholesky)
+    // changes nothing, since its kernels see the flag and return.
+    FitSlot *slots = fit_slots();
+    if (!slots) return MTTKRP_EHIP;
+    for (int j = 0; j < 2; ++j) __atomic_store_n(&slots[j].seq, 0u, __ATOMIC_RELEASE);
+    // On every return the caller's stream is drained: queued kernels may still
+    // write the slots, which the thread's next call reuses.
+    struct Drain {
         hipStream_t s;
-        Slot *p = nullptr;
-        hipEvent_t done[2] = {nullptr, nullptr};
-        ~Pinned()
-        {
-            // queued fit kernels may still write the slots
-            if (p) (void)hipStreamSynchronize(s);
-            for (hipEvent_t e : done)
-                if (e) (void)hipEventDestroy(e);
-            if (p) (void)hipHostFree(p);
-        }
-    } pin{s};
-    if (!ok(hipHostMalloc(reinterpret_cast<void **>(&pin.p), 2 * sizeof(Slot),
-                          hipHostMallocDefault)))
-        return MTTKRP_EHIP;
-    for (hipEvent_t &e : pin.done)
-        if (!ok(hipEventCreateWithFlags(&e, hipEventDisableTiming))) return MTTKRP_EHIP;
-    // Outcome of sweep k: 1 = go on, 0 = stopped after it (converged), or an
-    // error status.
-    auto consume = [&](int k) -> int {
-        if (!ok(hipEventSynchronize(pin.done[k & 1]))) return MTTKRP_EHIP;
-        const Slot &h = pin.p[k & 1];
-        if (h.flag == 1) {
-            *iters_done = k;
-            return MTTKRP_ENOTSPD;
-        }
-        fit_hist[k] = h.fit;
-        *iters_done = k + 1;
-        return h.flag == 2 ? 0 : 1;
-    };
-    auto finish = [&](int r) -> int {
-        // later sweeps may still be queued (their kernels return at once)
-        if (!ok(hipStreamSynchronize(s))) return MTTKRP_EHIP;
-        return r;
-    };
+        ~Drain() { (void)hipStreamSynchronize(s); }
+    } drain{s};
 
     // Modes with R <= 64 whose I x R solution fits in LDS split their update:
     // V, its Cholesky factor and W = L^{-1} (which do not depend on the
-    // MTTKRP) run on a second stream beside the mode's MTTKRP, forked after
-    // the previous update; the rest (U = M W^T W, norms, Gram) follows the
-    // MTTKRP on the caller's stream once the second stream has joined.  W
-    // lives in the L buffer: the next fork comes after this mode's update.
+    // MTTKRP) run on a second stream beside the mode's MTTKRP; the rest (U =
+    // M W^T W, norms, Gram, and after the sweep's last mode the fit) follows
+    // the MTTKRP on the caller's stream.  W lives in the L buffer: the next
+    // side kernel waits for this mode's update.  The streams are ordered by
+    // two sequence words in the flag block, not by events (an event record
+    // and a stream wait each held the caller's stream for several
+    // microseconds per mode):
+    //  - seq_main: the apply kernel of sweep it, mode n stores
+    //    it * (order + 1) + n + 1, and the end of the sweep (the fit kernel, or
+    //    the last mode's apply when it forms the fit) it * (order + 1) +
+    //    order + 1;
+    //  - seq_side: the side kernel of sweep it, mode n stores the same value
+    //    as that mode's apply.
+    // A side kernel waits for seq_main to reach the value before its own (the
+    // previous mode's apply, or the end of the previous sweep, which has then
+    // set the stop flag if it stops); an apply waits for seq_side to reach its
+    // own.  When the previous update on the caller's stream stores no word
+    // (an unsplit mode, or the start of the run), an event orders the side
+    // kernel instead.  Every kernel waits only for one queued before it.
     auto split_mode = [&](int n) { return R <= 64 && apply_small_lds(dims[n], R) != 0; };
+    unsigned *seq_main = reinterpret_cast<unsigned *>(flag + 8);
+    unsigned *seq_side = reinterpret_cast<unsigned *>(flag + 24);
     struct Side {
-        hipStream_t side = nullptr;
+        hipStream_t main = nullptr, side = nullptr;
         hipEvent_t fork = nullptr, join = nullptr;
+        bool live = false;  // side kernels queued since the last join
+        // the caller's stream waits for every side kernel queued so far
+        hipError_t join_now()
+        {
+            if (!live) return hipSuccess;
+            live = false;
+            hipError_t e = hipEventRecord(join, side);
+            if (e == hipSuccess) e = hipStreamWaitEvent(main, join, 0);
+            return e;
+        }
         ~Side()
         {
+            (void)join_now();
             if (fork) (void)hipEventDestroy(fork);
             if (join) (void)hipEventDestroy(join);
         }
     } sd;
+    sd.main = s;
     bool any_split = false;
     for (int m = 0; m < order; ++m) any_split = any_split || split_mode(m);
     if (any_split && iters > 0) {
@@ -530,30 +527,84 @@ int cp_als_entry(const T *X, const int64_t *dims, int order, int64_t rank, T *co
         if (!ok(hipEventCreateWithFlags(&sd.join, hipEventDisableTiming))) return MTTKRP_EHIP;
     }
 
+    // Outcome of sweep k: 1 = go on, 0 = stopped after it (converged), or an
+    // error status.  The slot's sweep number is polled; every so often the
+    // stream is queried, so that a stream that failed or went idle without
+    // the store ends the wait.
+    auto consume = [&](int k) -> int {
+        FitSlot *h = slots + (k & 1);
+        const unsigned want = (unsigned)k + 1u;
+        for (unsigned spin = 1;; ++spin) {
+            if (__atomic_load_n(&h->seq, __ATOMIC_ACQUIRE) == want) break;
+            if ((spin & 255u) == 0u) {
+                const hipError_t q = hipStreamQuery(s);
+                if (q == hipSuccess) {
+                    if (__atomic_load_n(&h->seq, __ATOMIC_ACQUIRE) == want) break;
+                    return MTTKRP_EHIP;
+                }
+                if (q != hipErrorNotReady) return MTTKRP_EHIP;
+            }
+            __builtin_ia32_pause();
+        }
+        const int f = __atomic_load_n(&h->flag, __ATOMIC_RELAXED);
+        if (f == 1 || f == 3) {
+            *iters_done = k;
+            // 3: a wait between the two streams timed out
+            return f == 1 ? MTTKRP_ENOTSPD : MTTKRP_EHIP;
+        }
+        double fit = 0.0;
+        __atomic_load(&h->fit, &fit, __ATOMIC_RELAXED);
+        fit_hist[k] = fit;
+        *iters_done = k + 1;
+        return f == 2 ? 0 : 1;
+    };
+    auto finish = [&](int r) -> int {
+        // later sweeps may still be queued (their kernels return at once)
+        if (!ok(sd.join_now())) return MTTKRP_EHIP;
+        if (!ok(hipStreamSynchronize(s))) return MTTKRP_EHIP;
+        return r;
+    };
+
     const T *cf[kMaxOrder];
     for (int m = 0; m < order; ++m) cf[m] = factors[m];
+    bool main_stored = false;  // the last update queued on s stores seq_main
     for (int it = 0; it < iters; ++it) {
+        const unsigned base = (unsigned)it * (unsigned)(order + 1);
+        const unsigned v_end = base + (unsigned)order + 1u;
+        FitSlot *slot = slots + (it & 1);
+        const AlsFitOut fo{G,          order,       scal,       tol,           it > 0 ? 1 : 0,
+                           &slot->fit, &slot->flag, &slot->seq, (unsigned)it + 1u};
+        bool fit_done = false;
         for (int n = 0; n < order; ++n) {
             const bool split = split_mode(n);
+            const unsigned v = base + (unsigned)n + 1u;
             if (split) {
-                if (!ok(hipEventRecord(sd.fork, s))) return MTTKRP_EHIP;
-                if (!ok(hipStreamWaitEvent(sd.side, sd.fork, 0))) return MTTKRP_EHIP;
-                if (!ok(launch_side_chol(G, order, n, R, Lc, flag, ticket, sd.side)))
+                const unsigned *wait_on = nullptr;
+                if (main_stored) {
+                    wait_on = seq_main;
+                } else {
+                    if (!ok(hipEventRecord(sd.fork, s))) return MTTKRP_EHIP;
+                    if (!ok(hipStreamWaitEvent(sd.side, sd.fork, 0))) return MTTKRP_EHIP;
+                }
+                if (!ok(launch_side_chol(G, order, n, R, Lc, flag, ticket, wait_on, v - 1u,
+                                         seq_side, v, sd.side)))
                     return MTTKRP_EHIP;
-                if (!ok(hipEventRecord(sd.join, sd.side))) return MTTKRP_EHIP;
+                sd.live = true;
             }
             st = mttkrp_one<T>(X, dims, order, cf, R, n, M, 1, w + L.mt, L.M - L.mt, s);
-            if (st) {
-                if (split) (void)hipStreamWaitEvent(s, sd.join, 0);
-                return st;
-            }
+            if (st) return st;
             if (split) {
-                if (!ok(hipStreamWaitEvent(s, sd.join, 0))) return MTTKRP_EHIP;
+                // the sweep's last mode also forms the fit
+                const bool last = n == order - 1;
                 if (!ok(launch_apply_small<T>(M, dims[n], R, Lc, factors[n], lam64, lambda,
-                                              G + (size_t)n * R * R, flag, s)))
+                                              G + (size_t)n * R * R, flag, seq_side, v, seq_main,
+                                              last ? v_end : v, last ? &fo : nullptr, s)))
                     return MTTKRP_EHIP;
+                main_stored = true;
+                fit_done = last;
                 continue;
             }
+            main_stored = false;
             if (update_small_lds(dims[n], R)) {
                 // Cholesky, solve, normalization and Gram refresh in one
                 // workgroup
@@ -562,9 +613,6 @@ int cp_als_entry(const T *X, const int64_t *dims, int order, int64_t rank, T *co
                     return MTTKRP_EHIP;
                 continue;
             }
-            // (the factor is not hidden beside the MTTKRP on a second stream:
-            // sharing the chip with the MTTKRP slowed the one-workgroup
-            // factorization about threefold, more than the overlap gained)
             if (R <= 64) {
                 if (!ok(launch_chol(G, order, n, R, Lc, flag, s))) return MTTKRP_EHIP;
                 if (!ok(launch_solve(M, Lc, dims[n], R, Unew, flag, s))) return MTTKRP_EHIP;
@@ -581,12 +629,12 @@ int cp_als_entry(const T *X, const int64_t *dims, int order, int64_t rank, T *co
             if (!ok(launch_gram<T>(factors[n], dims[n], R, G + (size_t)n * R * R, flag, s)))
                 return MTTKRP_EHIP;
         }
-        Slot *slot = pin.p + (it & 1);
-        if (!ok(launch_fit<T>(M, factors[order - 1], dims[order - 1], lam64, G, order, R, scal,
-                              flag, tol, it > 0, &slot->fit, &slot->flag, parts, kSumsqParts,
-                              Unew, s)))
-            return MTTKRP_EHIP;
-        if (!ok(hipEventRecord(pin.done[it & 1], s))) return MTTKRP_EHIP;
+        if (!fit_done) {
+            if (!ok(launch_fit<T>(M, factors[order - 1], dims[order - 1], lam64, R, flag, fo,
+                                  parts, kSumsqParts, Unew, seq_main, v_end, s)))
+                return MTTKRP_EHIP;
+            main_stored = true;
+        }
         if (it > 0) {
             const int r = consume(it - 1);
             if (r != 1) return finish(r);

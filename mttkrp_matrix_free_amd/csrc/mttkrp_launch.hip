@@ -121,8 +121,17 @@ hipError_t allow_large_lds(const void *k)
     if (cache)
         for (int j = 0; j < ndone[dev]; ++j)
             if (done[dev][j] == k) return hipSuccess;
-    e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e == hipSuccess && cache && ndone[dev] < kMaxKernels) done[dev][ndone[dev]++] = k;
+    // the limit covers static and dynamic LDS together
+    hipFuncAttributes fa;
+    e = hipFuncGetAttributes(&fa, k);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                160 * 1024 - (int)fa.sharedSizeBytes);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();  // leave no sticky error for the caller's next call
+        return e;
+    }
+    if (cache && ndone[dev] < kMaxKernels) done[dev][ndone[dev]++] = k;
     return e;
 }
 
