@@ -770,16 +770,13 @@ als_update_small_kernel(const double *__restrict__ Gall, int order, int n,
 // solution fits in LDS (the same sizes as the one-workgroup update above):
 //
 //  - als_side_chol_kernel (on a second stream, beside the mode's MTTKRP,
-//    which it does not need): V = Hadamard of the other Grams, V = L L^T
-//    (the one-wave factorization above), and W = L^{-1}.  It is launched
-//    with eight workgroups, one per XCD, of which the first to be
-//    dispatched does the work: the MTTKRP grid is padded to a multiple of
-//    eight workgroups, and the padding leaves compute units free on one
-//    XCD, where this workgroup then runs without delaying the MTTKRP.
+//    which it does not need): V = Hadamard of the other Grams, V = L L^T (the
+//    one-wave factorization above), W = L^{-1} and V^{-1} = W^T W.  It is launched with eight workgroups, of which the
+//    first to be dispatched does the work, so it runs wherever a compute
+//    unit is free.
 //  - als_apply_small_kernel (after the MTTKRP, on the caller's stream):
-//    U_new = M V^{-1} = (M W^T) W, the rows' forward and back solves done
-//    as products with W; then the column norms, the normalized factor and
-//    its Gram as in the one-workgroup update.
+//    U_new = M V^{-1}, then the column norms, the normalized factor and its
+//    Gram as in the one-workgroup update.
 //
 // W = L^{-1} column by column (a lane per column c): forward substitution of
 // the unit vector e_c, w_j = b_j / L_jj and b_i -= L_ij w_j for i > j, with
@@ -793,13 +790,14 @@ als_update_small_kernel(const double *__restrict__ Gall, int order, int n,
 template <int W, int RM>
 __device__ __forceinline__ void inv_step(double (&b)[RM], int j, int R, int c,
                                          const double *__restrict__ Lt,
-                                         const double *__restrict__ rd, double *__restrict__ Wout)
+                                         const double *__restrict__ rd, double *__restrict__ Wout,
+                                         int wp)
 {
     double lv[W];
 #pragma unroll
     for (int k = 1; k < W; ++k) lv[k] = Lt[j * R + j + k];
     const double x = b[0] * rd[j];
-    if (c < R) Wout[j * R + c] = x;
+    if (c < R) Wout[j * wp + c] = x;
 #pragma unroll
     for (int k = 1; k < W; ++k) b[k - 1] = __builtin_fma(-lv[k], x, b[k]);
     b[W - 1] = 0.0;  // entries past the frame are past R - 1
@@ -808,7 +806,7 @@ __device__ __forceinline__ void inv_step(double (&b)[RM], int j, int R, int c,
 template <int RM>
 __device__ __forceinline__ void tri_inverse_wave(const double *__restrict__ Lt,
                                                  const double *__restrict__ rd, int R,
-                                                 double *__restrict__ Wout)
+                                                 double *__restrict__ Wout, int wp)
 {
     const int c = threadIdx.x & 63;
     double b[RM];
@@ -816,36 +814,58 @@ __device__ __forceinline__ void tri_inverse_wave(const double *__restrict__ Lt,
     for (int k = 0; k < RM; ++k) b[k] = (k == c && c < R) ? 1.0 : 0.0;
     int j = 0;
     if constexpr (RM >= 64)
-        for (; j < R - 48; ++j) inv_step<64>(b, j, R, c, Lt, rd, Wout);
+        for (; j < R - 48; ++j) inv_step<64>(b, j, R, c, Lt, rd, Wout, wp);
     if constexpr (RM >= 48)
-        for (; j < R - 32; ++j) inv_step<48>(b, j, R, c, Lt, rd, Wout);
+        for (; j < R - 32; ++j) inv_step<48>(b, j, R, c, Lt, rd, Wout, wp);
     if constexpr (RM >= 32)
-        for (; j < R - 16; ++j) inv_step<32>(b, j, R, c, Lt, rd, Wout);
-    for (; j < R; ++j) inv_step<16>(b, j, R, c, Lt, rd, Wout);
+        for (; j < R - 16; ++j) inv_step<32>(b, j, R, c, Lt, rd, Wout, wp);
+    for (; j < R; ++j) inv_step<16>(b, j, R, c, Lt, rd, Wout, wp);
 }
 
-// Dynamic LDS of the side kernel: the column buffers, V (then L, in place,
-// pitch RM + 1, one spare entry), L^T rows with RM zeros after, 1 / L_jj and
-// the failure word.
+// Dense products of 4 x 4 blocks with every sum over an index in increasing
+// order: G(a, c) += sum_i x(i, a) x(i, c) over rows i of x (pitch given),
+// for V^{-1} = W^T W in the side kernel and the Gram in the apply kernel.
+__device__ __forceinline__ void gram4_accumulate(const double *__restrict__ x, int pitch, int rows,
+                                                 int a0, int c0, double (&g)[4][4])
+{
+#pragma unroll 4
+    for (int i = 0; i < rows; ++i) {
+        double ua[4], uc[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            ua[t] = x[i * pitch + a0 + t];
+            uc[t] = x[i * pitch + c0 + t];
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) g[t][u] += ua[t] * uc[u];
+    }
+}
+
+// Dynamic LDS of the side kernel: the column buffers and the failure word,
+// then V (then L, in place, pitch RM + 1, one spare entry), L^T rows with RM
+// zeros after, 1 / L_jj and W (pitch RM + 1).
 template <int RM>
 constexpr size_t side_chol_lds()
 {
-    return (size_t)(256 + (RM * (RM + 1) + 1) + (RM * RM + RM) + RM + 1) * sizeof(double);
+    return (size_t)(256 + 1 + (RM * (RM + 1) + 1) + (RM * RM + RM) + RM + RM * (RM + 1)) *
+           sizeof(double);
 }
-
 template <int RM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 als_side_chol_kernel(const double *__restrict__ Gall, int order, int n, int R,
-                     double *__restrict__ Wout, int *__restrict__ flag,
+                     double *__restrict__ Vinv, int *__restrict__ flag,
                      unsigned *__restrict__ ticket, SeqArgs q)
 {
     constexpr int P = RM + 1;
     extern __shared__ __align__(16) unsigned char smem[];
     double *col = reinterpret_cast<double *>(smem);  // 256
-    double *A = col + 256;                           // RM x P (+ 1 spare)
+    int &fail = *reinterpret_cast<int *>(col + 256);
+    double *A = col + 257;                           // RM x P (+ 1 spare)
     double *Lt = A + RM * P + 1;                     // RM x RM, RM zeros after
     double *rd = Lt + RM * RM + RM;                  // RM
-    int &fail = *reinterpret_cast<int *>(rd + RM);
+    double *Wl = rd + RM;                            // RM x P
     const int tid = threadIdx.x;
     // Eight workgroups take a ticket each (one vector atomic per workgroup);
     // the first to run does the work, so it runs on whichever XCD had a
@@ -855,11 +875,15 @@ als_side_chol_kernel(const double *__restrict__ Gall, int order, int n, int R,
     __syncthreads();
     if (fail != 0) return;
     __syncthreads();  // every thread has read the ticket before fail is reused
-    // the previous update's Gram (or the fit before a sweep's first mode)
+    // the previous mode's update (or the previous sweep's end)
     if (seq_enter(q, flag, &fail) == 0) {
+        constexpr int nb4 = RM / 4;
+        const int a0 = (tid / nb4) * 4, c0 = (tid - (tid / nb4) * nb4) * 4;
+        const bool own = tid < nb4 * nb4;  // a thread per 4 x 4 block
         hadamard_to_lds<RM, 256>(Gall, order, n, R, A, P);
         col[tid] = 0.0;
         if (tid < RM) Lt[R * R + tid] = 0.0;
+        for (int e = tid; e < RM * P; e += 256) Wl[e] = 0.0;
         __syncthreads();
         if (tid < 64) {
             // L overwrites V in place (a row's entries are read into
@@ -873,17 +897,27 @@ als_side_chol_kernel(const double *__restrict__ Gall, int order, int n, int R,
         } else {
             if (tid < R) rd[tid] = 1.0 / A[tid * P + tid];
             __syncthreads();
-            if (tid < 64) tri_inverse_wave<RM>(Lt, rd, R, Wout);
+            if (tid < 64) tri_inverse_wave<RM>(Lt, rd, R, Wl, P);
+            __syncthreads();
+            // V^{-1}(a, c) = sum_k W(k, a) W(k, c), k increasing (W's zero
+            // upper triangle adds exact zeros)
+            if (own) {
+                double g[4][4] = {};
+                gram4_accumulate(Wl, P, RM, a0, c0, g);
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (a0 + t < R && c0 + u < R) Vinv[(a0 + t) * R + c0 + u] = g[t][u];
+            }
         }
     }
     seq_leave(q);
 }
 
-// Dense product of a 4 x 4 block of one of the apply's two products, every
-// sum over k = 0 .. RM - 1 in increasing order: A(i, k) at a[i * sa + k] and
-// B(k, c) at b[k * sbk + c * sbc] (zero past R in both).  W's zero triangle
-// contributes exact zeros, so each sum equals the triangular one with the
-// same order of its nonzero terms.
+// Dense product of a 4 x 4 block of the apply's product, every sum over
+// k = 0 .. RM - 1 in increasing order: A(i, k) at a[i * sa + k] and B(k, c)
+// at b[k * sbk + c * sbc] (zero past R in both, which adds exact zeros).
 template <int RM>
 __device__ __forceinline__ void block4_product(const double *__restrict__ a, int sa,
                                                const double *__restrict__ b, int sbk, int sbc,
@@ -920,22 +954,22 @@ size_t apply_small_lds(int64_t I, int64_t R)
 
 template <typename T, int RM>
 __device__ __forceinline__ void apply_small_body(const double *__restrict__ M, int64_t I64,
-                                                 int64_t R64, const double *__restrict__ Win,
+                                                 int64_t R64, const double *__restrict__ Vinv,
                                                  T *__restrict__ Uout, double *__restrict__ lam64,
                                                  T *__restrict__ lamT, double *__restrict__ G,
                                                  int *__restrict__ flag, const FitArgs &fa)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     const int I = (int)I64, R = (int)R64;
-    constexpr int PW = RM + 1;  // W's row pitch: lanes reading a column hit distinct banks
+    constexpr int PW = RM + 1;  // V^{-1}'s row pitch: lanes reading a column hit distinct banks
     const int I4 = (I + 3) / 4 * 4;
-    double *W = reinterpret_cast<double *>(smem);  // RM x PW, zero past R
-    double *x = W + RM * PW;                         // M, then U (I4 x RM, zero past I, R)
-    double *y = x + I4 * RM;                         // Y = M W^T
+    double *W = reinterpret_cast<double *>(smem);  // V^{-1}: RM x PW, zero past R
+    double *x = W + RM * PW;                         // M (I4 x RM, zero past I, R)
+    double *y = x + I4 * RM;                         // U
     double *lam = y + I4 * RM;                       // 64
     const int tid = threadIdx.x;
-    // W and M into LDS: a thread's loads of a batch are all in flight before
-    // any is stored (one memory round trip per batch, not per element)
+    // V^{-1} and M into LDS: a thread's loads of a batch are all in flight
+    // before any is stored (one memory round trip per batch, not per element)
     {
         constexpr int NW = (RM * PW + 255) / 256;
         double v[NW];
@@ -944,7 +978,7 @@ __device__ __forceinline__ void apply_small_body(const double *__restrict__ M, i
             const int e = tid + 256 * t;
             const int j = e / PW, c = e - (e / PW) * PW;
             const bool in = e < RM * PW && j < R && c < R;
-            v[t] = Win[in ? j * R + c : 0];
+            v[t] = Vinv[in ? j * R + c : 0];
             v[t] = in ? v[t] : 0.0;
         }
 #pragma unroll
@@ -972,33 +1006,22 @@ __device__ __forceinline__ void apply_small_body(const double *__restrict__ M, i
     __syncthreads();
     constexpr int CB = RM / 4;  // 4-column blocks
     const int nblk = (I4 / 4) * CB;
-    // forward: Y(i, c) = sum_k M(i, k) W(c, k)
+    // U(i, c) = sum_k M(i, k) V^{-1}(k, c)
     for (int blk = tid; blk < nblk; blk += 256) {
         const int i0 = (blk / CB) * 4, c0 = (blk - (blk / CB) * CB) * 4;
         double acc[4][4];
-        block4_product<RM>(x + i0 * RM, RM, W + c0 * PW, 1, PW, acc);
+        block4_product<RM>(x + i0 * RM, RM, W + c0, PW, 1, acc);
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int u = 0; u < 4; ++u) y[(i0 + t) * RM + c0 + u] = acc[t][u];
     }
     __syncthreads();
-    // back: U(i, c) = sum_k Y(i, k) W(k, c)
-    for (int blk = tid; blk < nblk; blk += 256) {
-        const int i0 = (blk / CB) * 4, c0 = (blk - (blk / CB) * CB) * 4;
-        double acc[4][4];
-        block4_product<RM>(y + i0 * RM, RM, W + c0, PW, 1, acc);
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int u = 0; u < 4; ++u) x[(i0 + t) * RM + c0 + u] = acc[t][u];
-    }
-    __syncthreads();
     // column norms (rows in order), then the normalized factor; the LDS copy
-    // keeps the stored (element-type) values for the Gram below
+    // keeps the stored (element-type) values for the Gram and the fit
     if (tid < R) {
         double sq = 0.0;
-        for (int i = 0; i < I; ++i) sq += x[i * RM + tid] * x[i * RM + tid];
+        for (int i = 0; i < I; ++i) sq += y[i * RM + tid] * y[i * RM + tid];
         const double l = sqrt(sq);
         lam[tid] = l;
         lam64[tid] = l;
@@ -1008,9 +1031,9 @@ __device__ __forceinline__ void apply_small_body(const double *__restrict__ M, i
     for (int e = tid; e < I * R; e += 256) {
         const int i = e / R, c = e - (e / R) * R;
         const double l = lam[c];
-        const T u = (T)(l > 0.0 ? x[i * RM + c] / l : x[i * RM + c]);
+        const T u = (T)(l > 0.0 ? y[i * RM + c] / l : y[i * RM + c]);
         Uout[e] = u;
-        x[i * RM + c] = (double)u;
+        y[i * RM + c] = (double)u;
     }
     __syncthreads();
     // G = U^T U: a thread takes a 4 x 4 block of entries (each summed over i
@@ -1019,19 +1042,7 @@ __device__ __forceinline__ void apply_small_body(const double *__restrict__ M, i
     for (int blk = tid; blk < nb4 * nb4; blk += 256) {
         const int a0 = (blk / nb4) * 4, c0 = (blk - (blk / nb4) * nb4) * 4;
         double g[4][4] = {};
-#pragma unroll 4
-        for (int i = 0; i < I; ++i) {
-            double ua[4], uc[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                ua[t] = x[i * RM + a0 + t];
-                uc[t] = x[i * RM + c0 + t];
-            }
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int u = 0; u < 4; ++u) g[t][u] += ua[t] * uc[u];
-        }
+        gram4_accumulate(y, RM, I, a0, c0, g);
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -1039,15 +1050,15 @@ __device__ __forceinline__ void apply_small_body(const double *__restrict__ M, i
                 if (a0 + t < R && c0 + u < R) G[(a0 + t) * R + c0 + u] = g[t][u];
     }
     if (!fa.out_seq) return;
-    // The sweep's last mode: its fit, as als_fit_kernel forms it, from M (the
-    // MTTKRP, still in memory), the stored factor (x), lambda and the Grams
-    // (this one just written by the workgroup).
+    // The sweep's last mode: its fit, as als_fit_kernel forms it, from M (x),
+    // the stored factor (y), lambda and the Grams (this one just written by
+    // the workgroup).
     __shared__ double sh[4];
     __syncthreads();
     double inner = 0.0;
     if (tid < R) {
         double sm = 0.0;
-        for (int i = 0; i < I; ++i) sm += M[(int64_t)i * R + tid] * x[i * RM + tid];
+        for (int i = 0; i < I; ++i) sm += x[i * RM + tid] * y[i * RM + tid];
         inner = lam[tid] * sm;
     }
     inner = block_sum(inner, sh);
@@ -1056,19 +1067,19 @@ __device__ __forceinline__ void apply_small_body(const double *__restrict__ M, i
     if (tid == 0) fit_finish(inner, nrm2, flag, fa);
 }
 
-// The apply waits for its mode's side kernel (W and the failure word), and
-// stores its word when done, for the next mode's side kernel (the Gram).
-// With fa.out_seq set it also ends the sweep (the fit).
+// The apply waits for its mode's side kernel (V^{-1} and the failure word),
+// and stores its word when done, for the next mode's side kernel.  With
+// fa.out_seq set it also ends the sweep (the fit).
 template <typename T, int RM>
 __global__ __launch_bounds__(256) void als_apply_small_kernel(
-    const double *__restrict__ M, int64_t I64, int64_t R64, const double *__restrict__ Win,
+    const double *__restrict__ M, int64_t I64, int64_t R64, const double *__restrict__ Vinv,
     T *__restrict__ Uout, double *__restrict__ lam64, T *__restrict__ lamT,
     double *__restrict__ G, int *__restrict__ flag, FitArgs fa, SeqArgs q)
 {
     __shared__ int sflag;
     const int f = seq_enter(q, flag, &sflag);
     if (f == 0)
-        apply_small_body<T, RM>(M, I64, R64, Win, Uout, lam64, lamT, G, flag, fa);
+        apply_small_body<T, RM>(M, I64, R64, Vinv, Uout, lam64, lamT, G, flag, fa);
     else if (fa.out_seq && threadIdx.x == 0)
         fit_skip(f, fa);
     seq_leave(q);
@@ -1490,8 +1501,8 @@ hipError_t launch_update_small(const double *Gall, int order, int n, const doubl
     return hipGetLastError();
 }
 
-hipError_t launch_side_chol(const double *Gall, int order, int n, int64_t R, double *W, int *flag,
-                            unsigned *ticket, const unsigned *wait_on, unsigned wait_for,
+hipError_t launch_side_chol(const double *Gall, int order, int n, int64_t R, double *Vinv,
+                            int *flag, unsigned *ticket, const unsigned *wait_on, unsigned wait_for,
                             unsigned *done, unsigned done_val, hipStream_t s)
 {
     if (R > 64) return hipErrorInvalidValue;
@@ -1504,13 +1515,13 @@ hipError_t launch_side_chol(const double *Gall, int order, int n, int64_t R, dou
         const hipError_t a = allow_large_lds(reinterpret_cast<const void *>(k));
         if (a != hipSuccess) return a;
     }
-    hipLaunchKernelGGL(k, dim3(8), dim3(256), lds, s, Gall, order, n, (int)R, W, flag, ticket,
+    hipLaunchKernelGGL(k, dim3(8), dim3(256), lds, s, Gall, order, n, (int)R, Vinv, flag, ticket,
                        SeqArgs{wait_on, wait_for, done, done_val});
     return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_apply_small(const double *M, int64_t I, int64_t R, const double *W, T *Uout,
+hipError_t launch_apply_small(const double *M, int64_t I, int64_t R, const double *Vinv, T *Uout,
                               double *lam64, T *lamT, double *G, int *flag,
                               const unsigned *wait_on, unsigned wait_for, unsigned *done,
                               unsigned done_val, const AlsFitOut *fit, hipStream_t s)
@@ -1528,8 +1539,8 @@ hipError_t launch_apply_small(const double *M, int64_t I, int64_t R, const doubl
         const hipError_t a = allow_large_lds(reinterpret_cast<const void *>(k));
         if (a != hipSuccess) return a;
     }
-    hipLaunchKernelGGL(k, dim3(1), dim3(256), lds, s, M, I, R, W, Uout, lam64, lamT, G, flag, fa,
-                       SeqArgs{wait_on, wait_for, done, done_val});
+    hipLaunchKernelGGL(k, dim3(1), dim3(256), lds, s, M, I, R, Vinv, Uout, lam64, lamT, G, flag,
+                       fa, SeqArgs{wait_on, wait_for, done, done_val});
     return hipGetLastError();
 }
 

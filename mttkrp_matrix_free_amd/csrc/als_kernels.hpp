@@ -49,15 +49,15 @@ template <typename T>
 hipError_t launch_fill(T *p, int64_t n, T v, hipStream_t s);
 size_t update_small_lds(int64_t I, int64_t R);
 size_t apply_small_lds(int64_t I, int64_t R);
-// The split update's side kernel (V, its Cholesky factor, W = L^{-1} into W)
-// and apply kernel (U = M W^T W, norms, Gram; with fit non-null also the end
-// of the sweep).  Each waits until *wait_on reaches wait_for (none if
+// The split update's side kernel (V, its Cholesky factor and V^{-1} into
+// Vinv) and apply kernel (U = M V^{-1}, norms, Gram; with fit non-null also
+// the end of the sweep).  Each waits until *wait_on reaches wait_for (none if
 // wait_on is null) and stores done_val to *done when finished.
-hipError_t launch_side_chol(const double *Gall, int order, int n, int64_t R, double *W, int *flag,
-                            unsigned *ticket, const unsigned *wait_on, unsigned wait_for,
+hipError_t launch_side_chol(const double *Gall, int order, int n, int64_t R, double *Vinv,
+                            int *flag, unsigned *ticket, const unsigned *wait_on, unsigned wait_for,
                             unsigned *done, unsigned done_val, hipStream_t s);
 template <typename T>
-hipError_t launch_apply_small(const double *M, int64_t I, int64_t R, const double *W, T *Uout,
+hipError_t launch_apply_small(const double *M, int64_t I, int64_t R, const double *Vinv, T *Uout,
                               double *lam64, T *lamT, double *G, int *flag,
                               const unsigned *wait_on, unsigned wait_for, unsigned *done,
                               unsigned done_val, const AlsFitOut *fit, hipStream_t s);

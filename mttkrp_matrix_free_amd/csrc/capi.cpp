@@ -475,11 +475,11 @@ int cp_als_entry(const T *X, const int64_t *dims, int order, int64_t rank, T *co
     } drain{s};
 
     // Modes with R <= 64 whose I x R solution fits in LDS split their update:
-    // V, its Cholesky factor and W = L^{-1} (which do not depend on the
-    // MTTKRP) run on a second stream beside the mode's MTTKRP; the rest (U =
-    // M W^T W, norms, Gram, and after the sweep's last mode the fit) follows
-    // the MTTKRP on the caller's stream.  W lives in the L buffer: the next
-    // side kernel waits for this mode's update.  The streams are ordered by
+    // V, its Cholesky factor and V^{-1} (which do not depend on the MTTKRP)
+    // run on a second stream beside the mode's MTTKRP; the rest (U = M V^{-1},
+    // norms, Gram, and after the sweep's last mode the fit) follows the
+    // MTTKRP on the caller's stream.  V^{-1} lives in the L
+    // buffer: the next side kernel waits for this mode's update.  The streams are ordered by
     // two sequence words in the flag block, not by events (an event record
     // and a stream wait each held the caller's stream for several
     // microseconds per mode):
@@ -594,7 +594,11 @@ int cp_als_entry(const T *X, const int64_t *dims, int order, int64_t rank, T *co
             st = mttkrp_one<T>(X, dims, order, cf, R, n, M, 1, w + L.mt, L.M - L.mt, s);
             if (st) return st;
             if (split) {
-                // the sweep's last mode also forms the fit
+                // the sweep's last mode also forms the fit.  (The Gram stays
+                // here: formed by the next side kernel from the stored
+                // factor, it made that kernel outlast the MTTKRP it hides
+                // under, and the side kernel after it then took a compute
+                // unit that the next MTTKRP's grid needed.)
                 const bool last = n == order - 1;
                 if (!ok(launch_apply_small<T>(M, dims[n], R, Lc, factors[n], lam64, lambda,
                                               G + (size_t)n * R * R, flag, seq_side, v, seq_main,
