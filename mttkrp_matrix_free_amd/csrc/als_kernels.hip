@@ -915,43 +915,26 @@ als_side_chol_kernel(const double *__restrict__ Gall, int order, int n, int R,
     seq_leave(q);
 }
 
-// Dense product of a 4 x 4 block of the apply's product, every sum over
-// k = 0 .. RM - 1 in increasing order: A(i, k) at a[i * sa + k] and B(k, c)
-// at b[k * sbk + c * sbc] (zero past R in both, which adds exact zeros).
-template <int RM>
-__device__ __forceinline__ void block4_product(const double *__restrict__ a, int sa,
-                                               const double *__restrict__ b, int sbk, int sbc,
-                                               double (&acc)[4][4])
-{
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) acc[t][u] = 0.0;
-#pragma unroll 8
-    for (int k = 0; k < RM; ++k) {
-        double av[4], bv[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) av[t] = a[t * sa + k];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) bv[u] = b[k * sbk + u * sbc];
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int u = 0; u < 4; ++u) acc[t][u] = __builtin_fma(av[t], bv[u], acc[t][u]);
-    }
-}
-
-// Dynamic LDS of the apply kernel for I x R (0: not usable): W (RM rows of
-// RM + 1), M then U and Y (each I rounded up to 4 rows of RM), lambda.
+// Dynamic LDS of the apply kernel for I x R (0: not usable): V^{-1} (RM rows
+// of RM + 1), M and U (each I rounded up to 16 rows of RM + 1), lambda and
+// its reciprocals.
 size_t apply_small_lds(int64_t I, int64_t R)
 {
     if (R > 64 || I > (1 << 20)) return 0;
     const int64_t rm = R <= 16 ? 16 : R <= 32 ? 32 : 64;
-    const int64_t i4 = (I + 3) / 4 * 4;
-    const size_t b = (size_t)(rm * (rm + 1) + 2 * i4 * rm + 64) * sizeof(double);
+    const int64_t i16 = (I + 15) / 16 * 16;
+    const size_t b = (size_t)(rm * (rm + 1) + 2 * i16 * (rm + 1) + 128) * sizeof(double);
     return b <= 150 * 1024 ? b : 0;
 }
 
+typedef double adx4 __attribute__((ext_vector_type(4)));
+
+// U = M V^{-1} and the Gram on the fp64 matrix cores (v_mfma_f64_16x16x4f64:
+// lane (r, q) = (lane % 16, lane / 16) supplies A(r, k + q) and B(k + q, r);
+// element e of the result holds row 4 e + q, column r).  The raw Gram
+// U^T U gives the column norms (its diagonal), so no serial pass over the
+// rows is needed; the Gram of the normalized factor is the raw one scaled by
+// 1 / (lambda_a lambda_c).  A zero column keeps its values (scale 1).
 template <typename T, int RM>
 __device__ __forceinline__ void apply_small_body(const double *__restrict__ M, int64_t I64,
                                                  int64_t R64, const double *__restrict__ Vinv,
@@ -961,18 +944,23 @@ __device__ __forceinline__ void apply_small_body(const double *__restrict__ M, i
 {
     extern __shared__ __align__(16) unsigned char smem[];
     const int I = (int)I64, R = (int)R64;
-    constexpr int PW = RM + 1;  // V^{-1}'s row pitch: lanes reading a column hit distinct banks
-    const int I4 = (I + 3) / 4 * 4;
+    // row pitches RM + 1: the sixteen rows a matrix-core operand reads fall on
+    // distinct banks
+    constexpr int PW = RM + 1, XP = RM + 1;
+    constexpr int CT = RM / 16;  // 16-column tiles
+    const int I16 = (I + 15) / 16 * 16;
     double *W = reinterpret_cast<double *>(smem);  // V^{-1}: RM x PW, zero past R
-    double *x = W + RM * PW;                         // M (I4 x RM, zero past I, R)
-    double *y = x + I4 * RM;                         // U
-    double *lam = y + I4 * RM;                       // 64
-    const int tid = threadIdx.x;
+    double *x = W + RM * PW;                         // M: I16 x XP, zero past I and R
+    double *y = x + I16 * XP;                        // U: I16 x XP
+    double *lam = y + I16 * XP;                      // 64, then 64 reciprocals
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r16 = lane & 15, q = lane >> 4;
     // V^{-1} and M into LDS: a thread's loads of a batch are all in flight
-    // before any is stored (one memory round trip per batch, not per element)
+    // before any is stored, and M's first batch goes out with V^{-1}'s (one
+    // memory round trip for both when M fits in it)
     {
         constexpr int NW = (RM * PW + 255) / 256;
-        double v[NW];
+        double v[NW], m[16];
 #pragma unroll
         for (int t = 0; t < NW; ++t) {
             const int e = tid + 256 * t;
@@ -981,73 +969,131 @@ __device__ __forceinline__ void apply_small_body(const double *__restrict__ M, i
             v[t] = Vinv[in ? j * R + c : 0];
             v[t] = in ? v[t] : 0.0;
         }
+        for (int e0 = 0; e0 < I16 * RM; e0 += 256 * 16) {
 #pragma unroll
-        for (int t = 0; t < NW; ++t) {
-            const int e = tid + 256 * t;
-            if (e < RM * PW) W[e] = v[t];
+            for (int t = 0; t < 16; ++t) {
+                const int e = e0 + tid + 256 * t;
+                const int i = e / RM, c = e - (e / RM) * RM;
+                const bool in = i < I && c < R;
+                m[t] = M[in ? i * R + c : 0];
+                m[t] = in ? m[t] : 0.0;
+            }
+            if (e0 == 0) {
+#pragma unroll
+                for (int t = 0; t < NW; ++t) {
+                    const int e = tid + 256 * t;
+                    if (e < RM * PW) W[e] = v[t];
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                const int e = e0 + tid + 256 * t;
+                const int i = e / RM, c = e - (e / RM) * RM;
+                if (e < I16 * RM) x[i * XP + c] = m[t];
+            }
         }
     }
-    for (int e0 = 0; e0 < I4 * RM; e0 += 256 * 16) {
-        double v[16];
+    __syncthreads();
+    // U(i, c) = sum_k M(i, k) V^{-1}(k, c): 16 x 16 tiles, four to a wave at a
+    // time, their matrix-core chains interleaved and each step's operands
+    // read before its products
+    const int ntile = (I16 / 16) * CT;
+    for (int t0 = wave; t0 < ntile; t0 += 16) {
+        adx4 acc[4];
+        int xo[4], wo[4];
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            const int e = e0 + tid + 256 * t;
-            const int i = e / RM, c = e - (e / RM) * RM;
-            const bool in = i < I && c < R;
-            v[t] = M[in ? i * R + c : 0];
-            v[t] = in ? v[t] : 0.0;
+        for (int u = 0; u < 4; ++u) {
+            acc[u] = adx4{0.0, 0.0, 0.0, 0.0};
+            const int t = t0 + 4 * u < ntile ? t0 + 4 * u : t0;  // (spare tiles redo t0)
+            const int rt = t / CT, ct = t - (t / CT) * CT;
+            xo[u] = (rt * 16 + r16) * XP + q;
+            wo[u] = q * PW + ct * 16 + r16;
         }
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            const int e = e0 + tid + 256 * t;
-            if (e < I4 * RM) x[e] = v[t];
-        }
-    }
-    __syncthreads();
-    constexpr int CB = RM / 4;  // 4-column blocks
-    const int nblk = (I4 / 4) * CB;
-    // U(i, c) = sum_k M(i, k) V^{-1}(k, c)
-    for (int blk = tid; blk < nblk; blk += 256) {
-        const int i0 = (blk / CB) * 4, c0 = (blk - (blk / CB) * CB) * 4;
-        double acc[4][4];
-        block4_product<RM>(x + i0 * RM, RM, W + c0, PW, 1, acc);
+        for (int kk = 0; kk < RM; kk += 4) {
+            double av[4], bv[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int u = 0; u < 4; ++u) y[(i0 + t) * RM + c0 + u] = acc[t][u];
-    }
-    __syncthreads();
-    // column norms (rows in order), then the normalized factor; the LDS copy
-    // keeps the stored (element-type) values for the Gram and the fit
-    if (tid < R) {
-        double sq = 0.0;
-        for (int i = 0; i < I; ++i) sq += y[i * RM + tid] * y[i * RM + tid];
-        const double l = sqrt(sq);
-        lam[tid] = l;
-        lam64[tid] = l;
-        if (lamT) lamT[tid] = (T)l;
-    }
-    __syncthreads();
-    for (int e = tid; e < I * R; e += 256) {
-        const int i = e / R, c = e - (e / R) * R;
-        const double l = lam[c];
-        const T u = (T)(l > 0.0 ? y[i * RM + c] / l : y[i * RM + c]);
-        Uout[e] = u;
-        y[i * RM + c] = (double)u;
-    }
-    __syncthreads();
-    // G = U^T U: a thread takes a 4 x 4 block of entries (each summed over i
-    // in order)
-    const int nb4 = (R + 3) / 4;
-    for (int blk = tid; blk < nb4 * nb4; blk += 256) {
-        const int a0 = (blk / nb4) * 4, c0 = (blk - (blk / nb4) * nb4) * 4;
-        double g[4][4] = {};
-        gram4_accumulate(y, RM, I, a0, c0, g);
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
+            for (int u = 0; u < 4; ++u) {
+                av[u] = x[xo[u] + kk];
+                bv[u] = W[wo[u] + kk * PW];
+            }
 #pragma unroll
             for (int u = 0; u < 4; ++u)
-                if (a0 + t < R && c0 + u < R) G[(a0 + t) * R + c0 + u] = g[t][u];
+                acc[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[u], bv[u], acc[u], 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int t = t0 + 4 * u;
+            if (t < ntile) {
+                const int rt = t / CT, ct = t - (t / CT) * CT;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    y[(rt * 16 + 4 * e + q) * XP + ct * 16 + r16] = acc[u][e];
+            }
+        }
+    }
+    __syncthreads();
+    // the raw Gram U^T U (rows past I are zero): CT x CT tiles, a wave's
+    // tiles interleaved the same way
+    constexpr int NG = CT * CT, GPW = (NG + 3) / 4;
+    adx4 g[GPW];
+    int ga[GPW], gc[GPW];
+#pragma unroll
+    for (int j = 0; j < GPW; ++j) {
+        g[j] = adx4{0.0, 0.0, 0.0, 0.0};
+        const int t = wave + 4 * j < NG ? wave + 4 * j : 0;
+        ga[j] = (t / CT) * 16 + r16;
+        gc[j] = (t - (t / CT) * CT) * 16 + r16;
+    }
+#pragma unroll 4
+    for (int kk = 0; kk < I16; kk += 4) {
+        double av[GPW], bv[GPW];
+#pragma unroll
+        for (int j = 0; j < GPW; ++j) {
+            av[j] = y[(kk + q) * XP + ga[j]];
+            bv[j] = y[(kk + q) * XP + gc[j]];
+        }
+#pragma unroll
+        for (int j = 0; j < GPW; ++j)
+            g[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[j], bv[j], g[j], 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < GPW; ++j) {
+        const int t = wave + 4 * j;
+        if (t < NG && t / CT == t - (t / CT) * CT)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (4 * e + q == r16) lam[(t / CT) * 16 + r16] = sqrt(g[j][e]);
+    }
+    __syncthreads();
+    // 1 / lambda per column (1 for a zero column, which keeps its values)
+    double *rlam = lam + 64;
+    if (tid < RM) rlam[tid] = lam[tid] > 0.0 ? 1.0 / lam[tid] : 1.0;
+    __syncthreads();
+    if (tid < R) {
+        lam64[tid] = lam[tid];
+        if (lamT) lamT[tid] = (T)lam[tid];
+    }
+    // the normalized factor; the LDS copy keeps the stored (element-type)
+    // values for the fit
+    for (int e = tid; e < I * R; e += 256) {
+        const int i = e / R, c = e - (e / R) * R;
+        const T u = (T)(y[i * XP + c] * rlam[c]);
+        Uout[e] = u;
+        y[i * XP + c] = (double)u;
+    }
+#pragma unroll
+    for (int j = 0; j < GPW; ++j) {
+        const int t = wave + 4 * j;
+        if (t < NG) {
+            const int at = t / CT, ct = t - (t / CT) * CT;
+            const int c = ct * 16 + r16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int a = at * 16 + 4 * e + q;
+                if (a < R && c < R) G[a * R + c] = g[j][e] * rlam[a] * rlam[c];
+            }
+        }
     }
     if (!fa.out_seq) return;
     // The sweep's last mode: its fit, as als_fit_kernel forms it, from M (x),
@@ -1058,7 +1104,7 @@ __device__ __forceinline__ void apply_small_body(const double *__restrict__ M, i
     double inner = 0.0;
     if (tid < R) {
         double sm = 0.0;
-        for (int i = 0; i < I; ++i) sm += x[i * RM + tid] * y[i * RM + tid];
+        for (int i = 0; i < I; ++i) sm += x[i * XP + tid] * y[i * XP + tid];
         inner = lam[tid] * sm;
     }
     inner = block_sum(inner, sh);
