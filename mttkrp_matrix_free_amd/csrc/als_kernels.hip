@@ -125,6 +125,7 @@ __device__ __forceinline__ void seq_leave(const SeqArgs &q)
 // system scope): the host polls that number while the next sweep is
 // already queued, so the device never waits for the host.
 struct FitArgs {
+    const double *V;     // (split update) the Hadamard product of the other Grams
     const double *Gall;  // the Grams of every mode, this sweep's last included
     int order;
     double *scal;        // [0] ||X||^2 in, [1] fit out, [2] the previous fit
@@ -855,8 +856,8 @@ constexpr size_t side_chol_lds()
 template <int RM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 als_side_chol_kernel(const double *__restrict__ Gall, int order, int n, int R,
-                     double *__restrict__ Vinv, int *__restrict__ flag,
-                     unsigned *__restrict__ ticket, SeqArgs q)
+                     double *__restrict__ Vinv, double *__restrict__ Vout,
+                     int *__restrict__ flag, unsigned *__restrict__ ticket, SeqArgs q)
 {
     constexpr int P = RM + 1;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -885,6 +886,8 @@ als_side_chol_kernel(const double *__restrict__ Gall, int order, int n, int R,
         if (tid < RM) Lt[R * R + tid] = 0.0;
         for (int e = tid; e < RM * P; e += 256) Wl[e] = 0.0;
         __syncthreads();
+        if (Vout)  // V itself, for the fit (before L overwrites it)
+            for (int e = tid; e < R * R; e += 256) Vout[e] = A[(e / R) * P + e - (e / R) * R];
         if (tid < 64) {
             // L overwrites V in place (a row's entries are read into
             // registers before any is written), and its transpose goes to Lt
@@ -1045,17 +1048,19 @@ __device__ __forceinline__ void apply_small_body(const double *__restrict__ M, i
         ga[j] = (t / CT) * 16 + r16;
         gc[j] = (t - (t / CT) * CT) * 16 + r16;
     }
-#pragma unroll 4
-    for (int kk = 0; kk < I16; kk += 4) {
-        double av[GPW], bv[GPW];
+    for (int k0 = 0; k0 < I16; k0 += 16) {
 #pragma unroll
-        for (int j = 0; j < GPW; ++j) {
-            av[j] = y[(kk + q) * XP + ga[j]];
-            bv[j] = y[(kk + q) * XP + gc[j]];
+        for (int kk = k0; kk < k0 + 16; kk += 4) {
+            double av[GPW], bv[GPW];
+#pragma unroll
+            for (int j = 0; j < GPW; ++j) {
+                av[j] = y[(kk + q) * XP + ga[j]];
+                bv[j] = y[(kk + q) * XP + gc[j]];
+            }
+#pragma unroll
+            for (int j = 0; j < GPW; ++j)
+                g[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[j], bv[j], g[j], 0, 0, 0);
         }
-#pragma unroll
-        for (int j = 0; j < GPW; ++j)
-            g[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[j], bv[j], g[j], 0, 0, 0);
     }
 #pragma unroll
     for (int j = 0; j < GPW; ++j) {
@@ -1096,9 +1101,10 @@ __device__ __forceinline__ void apply_small_body(const double *__restrict__ M, i
         }
     }
     if (!fa.out_seq) return;
-    // The sweep's last mode: its fit, as als_fit_kernel forms it, from M (x),
-    // the stored factor (y), lambda and the Grams (this one just written by
-    // the workgroup).
+    // The sweep's last mode: its fit, from M (x), the stored factor (y) and
+    // lambda, and ||model||^2 = sum_{a,c} lambda_a lambda_c V(a, c) G(a, c),
+    // with V = the Hadamard product of the other modes' Grams (stored by this
+    // mode's side kernel) and G this mode's Gram (still in the accumulators).
     __shared__ double sh[4];
     __syncthreads();
     double inner = 0.0;
@@ -1108,7 +1114,35 @@ __device__ __forceinline__ void apply_small_body(const double *__restrict__ M, i
         inner = lam[tid] * sm;
     }
     inner = block_sum(inner, sh);
-    double nrm2 = model_norm_part(lam, fa.Gall, fa.order, R);
+    double nrm2 = 0.0;
+    {
+        double vv[GPW][4];
+#pragma unroll
+        for (int j = 0; j < GPW; ++j) {
+            const int t = wave + 4 * j < NG ? wave + 4 * j : 0;
+            const int at = t / CT, ct = t - (t / CT) * CT;
+            const int c = ct * 16 + r16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int a = at * 16 + 4 * e + q;
+                vv[j][e] = fa.V[a < R && c < R ? a * R + c : 0];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < GPW; ++j) {
+            const int t = wave + 4 * j;
+            if (t < NG) {
+                const int at = t / CT, ct = t - (t / CT) * CT;
+                const int c = ct * 16 + r16;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int a = at * 16 + 4 * e + q;
+                    if (a < R && c < R)
+                        nrm2 += lam[a] * lam[c] * vv[j][e] * (g[j][e] * rlam[a] * rlam[c]);
+                }
+            }
+        }
+    }
     nrm2 = block_sum(nrm2, sh);
     if (tid == 0) fit_finish(inner, nrm2, flag, fa);
 }
@@ -1548,8 +1582,8 @@ hipError_t launch_update_small(const double *Gall, int order, int n, const doubl
 }
 
 hipError_t launch_side_chol(const double *Gall, int order, int n, int64_t R, double *Vinv,
-                            int *flag, unsigned *ticket, const unsigned *wait_on, unsigned wait_for,
-                            unsigned *done, unsigned done_val, hipStream_t s)
+                            double *Vout, int *flag, unsigned *ticket, const unsigned *wait_on,
+                            unsigned wait_for, unsigned *done, unsigned done_val, hipStream_t s)
 {
     if (R > 64) return hipErrorInvalidValue;
     auto k = R <= 16 ? als_side_chol_kernel<16>
@@ -1561,8 +1595,8 @@ hipError_t launch_side_chol(const double *Gall, int order, int n, int64_t R, dou
         const hipError_t a = allow_large_lds(reinterpret_cast<const void *>(k));
         if (a != hipSuccess) return a;
     }
-    hipLaunchKernelGGL(k, dim3(8), dim3(256), lds, s, Gall, order, n, (int)R, Vinv, flag, ticket,
-                       SeqArgs{wait_on, wait_for, done, done_val});
+    hipLaunchKernelGGL(k, dim3(8), dim3(256), lds, s, Gall, order, n, (int)R, Vinv, Vout, flag,
+                       ticket, SeqArgs{wait_on, wait_for, done, done_val});
     return hipGetLastError();
 }
 
@@ -1574,8 +1608,8 @@ hipError_t launch_apply_small(const double *M, int64_t I, int64_t R, const doubl
 {
     FitArgs fa{};
     if (fit)
-        fa = FitArgs{fit->Gall, fit->order, fit->scal,    fit->tol,    fit->have_prev,
-                     fit->out_fit, fit->out_flag, fit->out_seq, fit->seq_val};
+        fa = FitArgs{fit->V,       fit->Gall,     fit->order,   fit->scal,   fit->tol,
+                     fit->have_prev, fit->out_fit, fit->out_flag, fit->out_seq, fit->seq_val};
     const size_t lds = apply_small_lds(I, R);
     if (!lds) return hipErrorInvalidValue;
     auto k = R <= 16 ? als_apply_small_kernel<T, 16>
@@ -1605,8 +1639,8 @@ hipError_t launch_fit(const double *M, const T *Ulast, int64_t Ilast, const doub
 {
     const double *Gall = fit.Gall;
     const int order = fit.order;
-    const FitArgs fa{fit.Gall,    fit.order,    fit.scal,    fit.tol,    fit.have_prev,
-                     fit.out_fit, fit.out_flag, fit.out_seq, fit.seq_val};
+    const FitArgs fa{fit.V,         fit.Gall,     fit.order,    fit.scal,   fit.tol,
+                     fit.have_prev, fit.out_fit, fit.out_flag, fit.out_seq, fit.seq_val};
     const double *colsum = nullptr;
     if (R > 256) {
         hipLaunchKernelGGL(als_colsum_kernel<T>, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, s,

@@ -14,6 +14,7 @@ namespace mttkrp {
 // host-visible slot (fit, failure word, then the sweep's number, stored last
 // with a system-scope release so that the host can poll it).
 struct AlsFitOut {
+    const double *V;     // (split update) the Hadamard product of the other Grams, R x R
     const double *Gall;  // the Grams of every mode, R x R each
     int order;
     double *scal;        // [0] ||X||^2 in, [1] fit out, [2] the previous fit
@@ -50,12 +51,12 @@ hipError_t launch_fill(T *p, int64_t n, T v, hipStream_t s);
 size_t update_small_lds(int64_t I, int64_t R);
 size_t apply_small_lds(int64_t I, int64_t R);
 // The split update's side kernel (V, its Cholesky factor and V^{-1} into
-// Vinv) and apply kernel (U = M V^{-1}, norms, Gram; with fit non-null also
+// Vinv; with Vout non-null V itself too, for the fit) and apply kernel (U = M V^{-1}, norms, Gram; with fit non-null also
 // the end of the sweep).  Each waits until *wait_on reaches wait_for (none if
 // wait_on is null) and stores done_val to *done when finished.
 hipError_t launch_side_chol(const double *Gall, int order, int n, int64_t R, double *Vinv,
-                            int *flag, unsigned *ticket, const unsigned *wait_on, unsigned wait_for,
-                            unsigned *done, unsigned done_val, hipStream_t s);
+                            double *Vout, int *flag, unsigned *ticket, const unsigned *wait_on,
+                            unsigned wait_for, unsigned *done, unsigned done_val, hipStream_t s);
 template <typename T>
 hipError_t launch_apply_small(const double *M, int64_t I, int64_t R, const double *Vinv, T *Uout,
                               double *lam64, T *lamT, double *G, int *flag,

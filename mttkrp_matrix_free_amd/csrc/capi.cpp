@@ -396,8 +396,10 @@ int als_layout(const int64_t *dims, int order, int64_t rank, int elem, AlsLayout
     off += round256(8 * (size_t)order * R * R);
     L.L = off;
     off += round256(8 * R * R);
-    L.W = off;  // inverses of the blocked factor's diagonal blocks (R > 64)
-    off += rank > 64 ? round256(8 * R * 64) : 0;
+    // inverses of the blocked factor's diagonal blocks (R > 64, R x 64), or
+    // the last mode's V for the fit (R <= 64, R x R)
+    L.W = off;
+    off += round256(8 * R * 64);
     L.lam = off;
     off += round256(8 * R);
     L.parts = off;
@@ -572,7 +574,7 @@ int cp_als_entry(const T *X, const int64_t *dims, int order, int64_t rank, T *co
         const unsigned base = (unsigned)it * (unsigned)(order + 1);
         const unsigned v_end = base + (unsigned)order + 1u;
         FitSlot *slot = slots + (it & 1);
-        const AlsFitOut fo{G,          order,       scal,       tol,           it > 0 ? 1 : 0,
+        const AlsFitOut fo{Winv,       G,           order,      scal,      tol, it > 0 ? 1 : 0,
                            &slot->fit, &slot->flag, &slot->seq, (unsigned)it + 1u};
         bool fit_done = false;
         for (int n = 0; n < order; ++n) {
@@ -586,8 +588,9 @@ int cp_als_entry(const T *X, const int64_t *dims, int order, int64_t rank, T *co
                     if (!ok(hipEventRecord(sd.fork, s))) return MTTKRP_EHIP;
                     if (!ok(hipStreamWaitEvent(sd.side, sd.fork, 0))) return MTTKRP_EHIP;
                 }
-                if (!ok(launch_side_chol(G, order, n, R, Lc, flag, ticket, wait_on, v - 1u,
-                                         seq_side, v, sd.side)))
+                // the last mode's side kernel also keeps V for the fit
+                if (!ok(launch_side_chol(G, order, n, R, Lc, n == order - 1 ? Winv : nullptr,
+                                         flag, ticket, wait_on, v - 1u, seq_side, v, sd.side)))
                     return MTTKRP_EHIP;
                 sd.live = true;
             }
