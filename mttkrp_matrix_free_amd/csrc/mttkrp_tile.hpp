@@ -643,7 +643,7 @@ __device__ __forceinline__ void tile_pass(const KParams &p, unsigned char *smem,
 
     // ---- main loop: steps over (item, k-chunk); the loads of the next PD
     // steps are in flight while a step runs on the matrix cores ----
-    constexpr int PD = tile_prefetch(sizeof(T), MB, NB, FORM1, S);
+    constexpr int PD = tile_prefetch(sizeof(T), MB, NB, FORM1, S, RC, W);
     T abuf[PD + 1][NA];
     T wbuf[PD + 1][SS][NB];
     LoadCursor lc;
@@ -995,7 +995,7 @@ __device__ __forceinline__ void tile_pass(const KParams &p, unsigned char *smem,
 }
 
 template <typename T, int MB, int NB, bool RC, bool VEC, bool FORM1, int W, int S>
-__global__ __launch_bounds__(64 * W, (tile_min_waves(sizeof(T), MB, NB, FORM1, S))) void
+__global__ __launch_bounds__(64 * W, (tile_occupancy(sizeof(T), MB, NB, FORM1, S, RC, W))) void
 mttkrp_tile_kernel(KParams p)
 {
     extern __shared__ __align__(16) unsigned char smem[];

@@ -341,8 +341,18 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
                tile_min_waves(elem_bytes, p.mb, p.nb, p.form == 1, plan_slots(p.form, k.nouter)) == 2)
                   ? 8
                   : 4;
+    // Rank-tiled fp64 row-contiguous plans with the 64 x 32 tile: four-wave
+    // workgroups, three per compute unit (tile_three_waves), once the rank
+    // makes them matrix-core bound
+    if (elem_bytes == 8 && p.form == 0 && p.layout == 1 && p.mb == 4 && p.nb == 2 &&
+        plan_slots(p.form, k.nouter) == 1 && rank >= 256)
+        p.waves = 4;
     if (forced > 0 && f_waves) p.waves = f_waves;
-    const size_t lds_budget = p.waves == 8 ? kLdsBudgetWide : kLdsBudget;
+    const int occ = tile_occupancy(elem_bytes, p.mb, p.nb, p.form == 1,
+                                   plan_slots(p.form, k.nouter), p.layout == 1, p.waves);
+    const size_t lds_budget = p.waves == 8 ? kLdsBudgetWide
+                              : occ == 3   ? kLdsBudgetThree
+                                           : kLdsBudget;
 
     // Contraction chunks: the Khatri-Rao tile of one chunk (Kc x 16nb) must
     // fit in the workgroup's LDS; longer contractions are split into chunks
@@ -382,12 +392,12 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
     // workgroup share its steps evenly, so a chunk may hold any number of
     // items.
     const size_t b_tile = (size_t)k.Kc * k.bpitch * elem_bytes;
-    // Workgroups resident at once: by waves (two or one per SIMD, from the
-    // register model) and by LDS.  A grid that needs a second, partial round
+    // Workgroups resident at once: by waves (one to three per SIMD, the
+    // instantiation's occupancy) and by LDS.  A grid that needs a second, partial round
     // leaves most of the chip idle in it, so the split is rounded down to
     // whole rounds.
     const int slots = plan_slots(p.form, k.nouter);
-    const int per_cu_waves = 4 * tile_min_waves(elem_bytes, p.mb, p.nb, p.form == 1, slots);
+    const int per_cu_waves = 4 * occ;
     // Cross-wave reduction space: one row of column sums per wave (form 1);
     // for form 0 every wave's tile of fp64 sums when that fits the LDS budget
     // (one round, the store spread over the workgroup), else W/2 tiles (a
@@ -400,6 +410,7 @@ int make_plan(const int64_t *dims, int order, int64_t rank, int mode, int elem_b
     const int64_t per_cu = std::max<int64_t>(
         1, std::min<int64_t>(per_cu_waves / p.waves, (int64_t)(160 * 1024 / lds_est)));
     const int64_t resident = per_cu * kNumCU;
+    p.per_cu = (int)per_cu;
     (void)b_tile;
     // The split that best fills whole rounds of resident workgroups (the
     // smallest one among equals), up to two rounds' worth.  Form 0 cuts the
@@ -592,7 +603,7 @@ PlanModel plan_model(const Plan &p, const int64_t *dims, int order, int mode)
     // HBM: X once for every group of rank tiles that run together on one
     // XCD (the workgroup order keeps a chunk's rank tiles adjacent), the other
     // factors and the output once, partials written and read once
-    const double resident_xcd = (double)(kNumCU / kNumXCD) * (p.waves == 8 ? 1 : 2);
+    const double resident_xcd = (double)(kNumCU / kNumXCD) * (double)p.per_cu;
     const double rho_x = std::ceil((double)k.nrtiles / resident_xcd);
     const double rows_k = (double)k.In;  // the kernel's output rows (the block for trailing rows)
     const double part = k.to_partial ? 2.0 * (double)k.nsplit * rows_k * R * 8.0 : 0.0;

@@ -36,6 +36,7 @@ constexpr int kMaxOrder = 5;
 constexpr int kNumCU = 256;            // MI355X compute units
 constexpr int kNumXCD = 8;             // accelerator complex dies (L2 domains)
 constexpr size_t kLdsBudget = 80 * 1024;       // dynamic LDS of a 4-wave workgroup (2 per CU)
+constexpr size_t kLdsBudgetThree = 52 * 1024;  // the same at three workgroups per CU
 constexpr size_t kLdsBudgetWide = 144 * 1024;  // dynamic LDS of an 8-wave workgroup (1 per CU)
 
 // Outer-factor slots a tile kernel carries per step: none for form 1 (its
@@ -65,12 +66,33 @@ __host__ __device__ constexpr int tile_min_waves(int elem, int mb, int nb, bool 
 {
     return tile_regs(elem, mb, nb, form1, slots, 2) <= 256 ? 2 : 1;
 }
+// Waves per SIMD of a kernel instantiation (its launch bound).  Besides the
+// register model's one or two: three for the fp64 form-0 tiles of the
+// rank-tiled, matrix-core-bound plans -- 32 x 64 tiles of row-major outputs
+// and 64 x 32 tiles of row-contiguous outputs, one outer slot, four-wave
+// workgroups -- whose kernels fit 168 registers without spills once they
+// keep one step of tensor loads in flight (512^3 rank 2000: the matrix cores
+// busy 85% of a launch at two waves per SIMD; 8.30 -> 8.05 ms per mode).
+__host__ __device__ constexpr bool tile_three_waves(int elem, int mb, int nb, bool form1, int slots,
+                                                    bool rc, int w)
+{
+    return elem == 8 && !form1 && slots == 1 && w == 4 &&
+           ((mb == 2 && nb == 4 && !rc) || (mb == 4 && nb == 2 && rc));
+}
+__host__ __device__ constexpr int tile_occupancy(int elem, int mb, int nb, bool form1, int slots,
+                                                bool rc, int w)
+{
+    return tile_three_waves(elem, mb, nb, form1, slots, rc, w)
+               ? 3
+               : tile_min_waves(elem, mb, nb, form1, slots);
+}
 // Steps of tensor loads kept in flight: two when a third buffer fits the
-// budget of that occupancy, else one.
-__host__ __device__ constexpr int tile_prefetch(int elem, int mb, int nb, bool form1, int slots)
+// budget of the instantiation's occupancy, else one.
+__host__ __device__ constexpr int tile_prefetch(int elem, int mb, int nb, bool form1, int slots,
+                                                bool rc, int w)
 {
     return tile_regs(elem, mb, nb, form1, slots, 3) <=
-                   512 / tile_min_waves(elem, mb, nb, form1, slots)
+                   512 / tile_occupancy(elem, mb, nb, form1, slots, rc, w)
                ? 2
                : 1;
 }
@@ -176,6 +198,7 @@ struct Plan {
     int layout = 0;   // 0: contraction index contiguous; 1: rows contiguous
     int mb = 4, nb = 2;
     int waves = 4;    // waves per workgroup (4 or 8)
+    int per_cu = 1;   // workgroups resident per compute unit (registers and LDS)
     bool b_in_lds = true;
     bool vec = true;
     int k_modes[2] = {-1, -1};
