@@ -46,6 +46,10 @@ def rel(a, b):
     ((80, 12, 10), 3, 64, 2),  # mode 0: two 64-row passes of the one-workgroup update
     ((200, 12, 10), 3, 64, 2),  # mode 0 too tall for the one-workgroup update, modes 1-2 not
     ((70, 9, 8), 3, 40, 2), ((33, 21, 17), 3, 20, 2),  # frames that start 48 and 32 wide
+    # an unsplit last mode (the fit kernel ends the sweep and orders the next
+    # sweep's first side kernel) and an unsplit middle mode (an event orders
+    # the side kernel after it)
+    ((12, 10, 200), 3, 64, 3), ((12, 200, 10), 3, 64, 3),
     # blocked factorization and solves (R > 64): 3 blocks, a 4-way case with a
     # ragged last block, and R = 300 (the model norm summed by workgroups)
     ((30, 28, 26), 3, 150, 2), ((12, 11, 10, 9), 2, 100, 2), ((40, 38, 36), 3, 300, 2),
@@ -222,3 +226,48 @@ def test_als_float32():
     # fp32 inputs differ from the fp64 ones by rounding: compare the fit loosely
     for it in range(4):
         assert abs(fit[it] - fit0[it]) <= 1e-4, (it, fit[it], fit0[it])
+
+
+def test_als_two_host_threads_at_once():
+    """Two host threads run split-update CP-ALS calls at the same time, each on
+    its own stream.  They share the library's second stream on the device; each
+    kernel waits only for work queued before it, so both calls finish, with
+    the results (bit for bit) of the same calls run one at a time."""
+    import threading
+    probs = [inputs.random_cp_problem(d, 3, 32, sigma=0.05, seed=sd)
+             for d, sd in (((40, 36, 30), 41), ((30, 28, 26, 6), 42))]
+    ref = []
+    for p in probs:
+        U = [dev(u) for u in p.factors]
+        lam, fit, done, st = api.cp_als(dev(p.X), U, 6)
+        assert st == 0 and done == 6
+        ref.append((lam.cpu().numpy(), np.array(fit), [u.cpu().numpy() for u in U]))
+    out = [None, None]
+    errs = []
+
+    def run(i):
+        try:
+            s = torch.cuda.Stream()
+            p = probs[i]
+            with torch.cuda.stream(s):
+                X = dev(p.X)
+                U = [dev(u) for u in p.factors]
+                lam, fit, done, st = api.cp_als(X, U, 6, stream=s)
+                s.synchronize()
+                out[i] = (st, done, lam.cpu().numpy(), np.array(fit), [u.cpu().numpy() for u in U])
+        except Exception as e:  # reported below
+            errs.append(repr(e))
+
+    threads = [threading.Thread(target=run, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not errs, errs
+    for i in range(2):
+        st, done, lam, fit, U = out[i]
+        assert st == 0 and done == 6
+        assert np.array_equal(lam, ref[i][0])
+        assert np.array_equal(fit, ref[i][1])
+        for a, b in zip(U, ref[i][2]):
+            assert np.array_equal(a, b)
