@@ -1224,12 +1224,14 @@ __global__ __launch_bounds__(kRedThreads) void als_fit_kernel(
 
 // ---------------------------------------------------------------------------
 // Blocked R x R work for ranks past what one workgroup holds (R > 64): the
-// Cholesky factor and the two row substitutions in 64-wide column blocks, the
-// diagonal blocks by one wave (as above), the panels by rows in parallel, and
-// the trailing updates as tiled products.  Within a block every entry gets
+// Cholesky factorization in 64-wide column blocks, the diagonal blocks by
+// one wave (as above), carried out on V with the rows of M and of the
+// identity appended, so that the forward substitution and the factor's
+// inverse come out of the same block steps; the back substitution is then
+// one product with that inverse.  Within a diagonal block every entry gets
 // the textbook operations; across blocks the updates are summed per block
-// before they are applied, so the factor differs from the one-entry-at-a-time
-// order by rounding only.
+// (through the block's inverse) before they are applied, so the result
+// differs from the one-entry-at-a-time order by rounding only.
 // ---------------------------------------------------------------------------
 
 // V = Hadamard_{m != n} G_m (R x R, fp64), one thread per entry, modes in order.
@@ -1253,13 +1255,15 @@ __global__ __launch_bounds__(256) void als_hadamard_kernel(const double *__restr
 // upper triangle zeros.  Then the inverse's transpose X = L_kk^{-T} (rows of
 // X solve x L_kk^T = e_r: forward substitutions of the identity's rows, on
 // lane quads as in the one-workgroup update) goes to W rows k0 .. k0 + nb - 1
-// (pitch 64), so that the panel and row solves with L_kk become products.
-// A non-positive pivot sets the flag to 1.  Dynamic LDS: kCholDiagLds bytes.
+// (pitch 64), and Z = X X^T = (L_kk L_kk^T)^{-1}, the inverse of the block
+// as it entered, to Z (64 x 64, pitch 64, zero outside nb x nb), so that the
+// block step below needs products only.  A non-positive pivot sets the flag
+// to 1.  Dynamic LDS: kCholDiagLds bytes.
 constexpr int kCholDiagDoubles = 256 + (64 * 65 + 1) + (64 * 64 + 64) + 64 + (64 * 64 + 1) + 1;
 constexpr size_t kCholDiagLds = kCholDiagDoubles * sizeof(double);
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 als_chol_diag_kernel(double *__restrict__ A, int64_t R, int64_t k0, double *__restrict__ W,
-                     int *__restrict__ flag)
+                     double *__restrict__ Z, int *__restrict__ flag)
 {
     constexpr int RM = 64, P = RM + 1;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -1313,6 +1317,200 @@ als_chol_diag_kernel(double *__restrict__ A, int64_t R, int64_t k0, double *__re
         const int r = e / nb, c = e - (e / nb) * nb;
         W[(k0 + r) * 64 + c] = xs[e];
     }
+    // Z = X X^T on the matrix cores: wave w forms the 32 x 32 quarter at
+    // (wr, wc) as 2 x 2 blocks of 16 x 16 (lane (r16, q) supplies A(r16, t + q)
+    // and B(t + q, r16); element e of a block holds row 4 e + q).
+    {
+        const int r16 = lane & 15, q = lane >> 4;
+        const int wr = (wave >> 1) * 32, wc = (wave & 1) * 32;
+        adx4 acc[2][2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int y = 0; y < 2; ++y) acc[x][y] = adx4{0.0, 0.0, 0.0, 0.0};
+        for (int t0 = 0; t0 < nb; t0 += 4) {
+            const int t = t0 + q;
+            double a[2], b[2];
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                const int r = wr + 16 * x + r16;
+                a[x] = (r < nb && t < nb) ? xs[r * nb + t] : 0.0;
+                const int c = wc + 16 * x + r16;
+                b[x] = (c < nb && t < nb) ? xs[c * nb + t] : 0.0;
+            }
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int y = 0; y < 2; ++y)
+                    acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[x], b[y], acc[x][y], 0, 0, 0);
+        }
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int y = 0; y < 2; ++y)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    Z[(wr + 16 * x + 4 * e + q) * 64 + wc + 16 * y + r16] = acc[x][y][e];
+    }
+}
+
+// One block step k of the factorization V = L L^T carried out on the
+// augmented rows [V; M; I] (V's own factor is never stored: its column blocks
+// enter in product form through Z_k and W_k from the diagonal kernel).
+//   trailing, every active row block i and column block j > k:
+//       C(i, j) -= C(i, k) Z_k C_V(j, k)^T    (V rows: tiles j <= i only)
+//   panel, the M rows and the identity rows:
+//       Y(i, k) = C(i, k) W_k
+// The identity rows' block b is active from step b on (column blocks before
+// b of L^{-T} are zero).  After the last step Y_M = M L^{-T} (the forward
+// substitution) and Y_I = L^{-T}, so U = M V^{-1} = Y_M Y_I^T.  Each task is
+// a 64 x 64 tile, two 64 x 64 x 64 products on the matrix cores (the panel
+// one), operands staged in LDS as in the tiled product below; column block k
+// is only read during step k, so the tasks of a step are independent.
+struct AugStep {
+    double *CV, *CM, *CI;  // working rows: V (R x R), M (I x R), identity (R x R)
+    double *YM, *YI;       // outputs: M L^{-T} (I x R), L^{-T} (R x R)
+    const double *W;       // W_k at rows k0 .. (pitch 64)
+    const double *Z;       // Z_k (64 x 64)
+    int64_t R, I;
+    int k, nblk, mblk;
+    const int *flag;
+};
+constexpr int kAugPitch = 68;
+constexpr size_t kAugLds = 2 * 64 * kAugPitch * sizeof(double);
+
+__global__ __launch_bounds__(256) void als_aug_step_kernel(AugStep a)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    double(*As)[kAugPitch] = reinterpret_cast<double(*)[kAugPitch]>(smem);  // As[t][r] = A(r, t)
+    double(*Bs)[kAugPitch] =
+        reinterpret_cast<double(*)[kAugPitch]>(smem + 64 * kAugPitch * sizeof(double));
+    if (*a.flag) return;
+    const int k = a.k;
+    const int x = blockIdx.x, y = blockIdx.y;
+    const int j = k + x;
+    const int nA = a.nblk - 1 - k;
+    int sec;
+    int64_t rb;
+    if (y < nA) {
+        sec = 0;
+        rb = k + 1 + y;
+        if (x == 0 || j > rb) return;  // V rows: trailing lower tiles only
+    } else if (y < nA + k + 1) {
+        sec = 1;
+        rb = y - nA;
+    } else {
+        sec = 2;
+        rb = y - nA - (k + 1);
+    }
+    const int64_t R = a.R;
+    double *C = sec == 0 ? a.CV : sec == 1 ? a.CI : a.CM;
+    const int64_t r0 = rb * 64, k0 = (int64_t)k * 64, j0 = (int64_t)j * 64;
+    const int nr = (int)min<int64_t>(64, (sec == 2 ? a.I : R) - r0);
+    const int kn = (int)min<int64_t>(64, R - k0);
+    const int jn = (int)min<int64_t>(64, R - j0);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = (wave >> 1) * 32, wc = (wave & 1) * 32;
+    const int r16 = lane & 15, q = lane >> 4;
+    const int tl = tid & 63, th = tid >> 6;  // load mapping: 64 along the row, 4 rows per pass
+    // A operand: C(r0 + r, k0 + t); B operand: W_k (panel) or Z_k (trailing),
+    // both read along their rows by consecutive threads
+    {
+        double va[16], vb[16];
+        const double *Bsrc = x == 0 ? a.W + k0 * 64 : a.Z;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int r = th + 4 * u;
+            va[u] = (r < nr && tl < kn) ? C[(r0 + r) * R + k0 + tl] : 0.0;
+            vb[u] = (r < kn && tl < kn) ? Bsrc[r * 64 + tl] : 0.0;
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int r = th + 4 * u;
+            As[tl][r] = va[u];
+            Bs[r][tl] = vb[u];
+        }
+    }
+    __syncthreads();
+    adx4 acc[2][2];
+    auto product = [&]() {
+#pragma unroll
+        for (int xx = 0; xx < 2; ++xx)
+#pragma unroll
+            for (int yy = 0; yy < 2; ++yy) acc[xx][yy] = adx4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int kk = 0; kk < 64; kk += 4) {
+            const int kq = kk + q;
+            const double a0 = As[kq][wr + r16], a1 = As[kq][wr + 16 + r16];
+            const double b0 = Bs[kq][wc + r16], b1 = Bs[kq][wc + 16 + r16];
+            acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc[0][0], 0, 0, 0);
+            acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc[0][1], 0, 0, 0);
+            acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc[1][0], 0, 0, 0);
+            acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc[1][1], 0, 0, 0);
+        }
+    };
+    if (x == 0) {
+        // panel: Y(r0 + r, k0 + c) = (C(i, k) W_k)(r, c)
+        product();
+        double *Y = sec == 1 ? a.YI : a.YM;
+#pragma unroll
+        for (int xx = 0; xx < 2; ++xx)
+#pragma unroll
+            for (int yy = 0; yy < 2; ++yy)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = wr + 16 * xx + 4 * e + q, c = wc + 16 * yy + r16;
+                    if (r < nr && c < kn) Y[(r0 + r) * R + k0 + c] = acc[xx][yy][e];
+                }
+        return;
+    }
+    // trailing: T = C(i, k) Z_k, then C(i, j) -= T C_V(j, k)^T.  The second
+    // operand's loads go out before the first product.
+    double vb[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        const int c = th + 4 * u;
+        vb[u] = (c < jn && tl < kn) ? a.CV[(j0 + c) * R + k0 + tl] : 0.0;
+    }
+    product();
+    __syncthreads();  // every wave is done with the first operands
+#pragma unroll
+    for (int xx = 0; xx < 2; ++xx)
+#pragma unroll
+        for (int yy = 0; yy < 2; ++yy)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                As[wc + 16 * yy + r16][wr + 16 * xx + 4 * e + q] = acc[xx][yy][e];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) Bs[tl][th + 4 * u] = vb[u];
+    __syncthreads();
+    product();
+#pragma unroll
+    for (int xx = 0; xx < 2; ++xx)
+#pragma unroll
+        for (int yy = 0; yy < 2; ++yy)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = wr + 16 * xx + 4 * e + q, c = wc + 16 * yy + r16;
+                if (r < nr && c < jn) {
+                    double *p = C + (r0 + r) * R + j0 + c;
+                    *p -= acc[xx][yy][e];
+                }
+            }
+}
+
+// C = [V rows untouched; identity rows] and Y_I = 0 (entries of L^{-T}
+// below its diagonal blocks are never written by the steps).
+__global__ __launch_bounds__(256) void als_aug_init_kernel(double *__restrict__ CI,
+                                                           double *__restrict__ YI, int64_t R,
+                                                           const int *__restrict__ flag)
+{
+    if (*flag) return;
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= R * R) return;
+    const int64_t r = e / R;
+    CI[e] = (e - r * R) == r ? 1.0 : 0.0;
+    YI[e] = 0.0;
 }
 
 // C (m x n, leading dimension ldc) = beta C + alpha A B on the fp64 matrix
@@ -1322,15 +1520,14 @@ als_chol_diag_kernel(double *__restrict__ A, int64_t R, int64_t k0, double *__re
 // four waves a 32 x 32 quarter as 2 x 2 blocks of v_mfma_f64_16x16x4f64
 // accumulators; K is staged through LDS in chunks of 64, the next chunk's
 // loads in flight while the matrix cores work on the current one.  lower:
-// tiles above the diagonal are skipped.  C may be A's own columns when n <=
-// 64 (and so K <= 64, one chunk): a workgroup then owns whole rows of C and
-// reads all of its rows of A before it writes (so C and A are not declared
-// restrict).  The sums over t follow the matrix
-// cores' fixed order, so results are deterministic.
+// tiles above the diagonal are skipped.  C must not overlap A or B.  The
+// sums over t follow the matrix cores' fixed order, so results are
+// deterministic.
 typedef double gdx4 __attribute__((ext_vector_type(4)));
 
 template <typename TA>
-__global__ __launch_bounds__(256) void als_mfma_gemm_kernel(double *C, int64_t ldc, const TA *A,
+__global__ __launch_bounds__(256) void als_mfma_gemm_kernel(double *__restrict__ C, int64_t ldc,
+                                                            const TA *__restrict__ A,
                                                             int64_t sai, int64_t sat,
                                                             const TA *__restrict__ B, int64_t sbt,
                                                             int64_t sbj, int64_t m, int64_t n,
@@ -1414,14 +1611,12 @@ constexpr size_t kGemmLds = 2 * 64 * (64 + 4) * sizeof(double);
 
 hipError_t allow_large_lds(const void *k);
 
-// Launches the product above on 64 x 64 tiles.  inplace: C is A's own
-// columns (n <= 64).
+// Launches the product above on 64 x 64 tiles.
 template <typename TA>
 hipError_t launch_gemm(double *C, int64_t ldc, const TA *A, int64_t sai, int64_t sat, const TA *B,
                        int64_t sbt, int64_t sbj, int64_t m, int64_t n, int64_t K, double alpha,
-                       double beta, int lower, bool inplace, const int *flag, hipStream_t s)
+                       double beta, int lower, const int *flag, hipStream_t s)
 {
-    if (inplace && n > 64) return hipErrorInvalidValue;
     const int64_t gx = (n + 63) / 64, gy = (m + 63) / 64;
     if (gx > INT32_MAX || gy > 65535) return hipErrorInvalidValue;  // grid limits
     const hipError_t a = allow_large_lds(reinterpret_cast<const void *>(als_mfma_gemm_kernel<TA>));
@@ -1491,7 +1686,7 @@ hipError_t launch_gram(const T *U, int64_t I, int64_t R, double *G, const int *f
 {
     if (R > 64) {
         // G = U^T U as a tiled product (the same per-entry order over i)
-        return launch_gemm<T>(G, R, U, (int64_t)1, R, U, R, (int64_t)1, R, R, I, 1.0, 0.0, 0, false,
+        return launch_gemm<T>(G, R, U, (int64_t)1, R, U, R, (int64_t)1, R, R, I, 1.0, 0.0, 0,
                               flag, s);
     }
     const int64_t n = R * R;
@@ -1524,7 +1719,7 @@ hipError_t launch_gram_all(const T *const *U, const int64_t *dims, int order, in
 hipError_t launch_chol(const double *Gall, int order, int n, int64_t R, double *L, int *flag,
                        hipStream_t s)
 {
-    if (R > 64) return hipErrorInvalidValue;  // larger ranks: launch_chol_blocked
+    if (R > 64) return hipErrorInvalidValue;  // larger ranks: launch_update_blocked
     auto k = R <= 16 ? als_chol_wave_kernel<16>
              : R <= 32 ? als_chol_wave_kernel<32>
                        : als_chol_wave_kernel<64>;
@@ -1535,7 +1730,7 @@ hipError_t launch_chol(const double *Gall, int order, int n, int64_t R, double *
 hipError_t launch_solve(const double *M, const double *L, int64_t I, int64_t R, double *Unew,
                         const int *flag, hipStream_t s)
 {
-    if (R > 64) return hipErrorInvalidValue;  // larger ranks: launch_solve_blocked
+    if (R > 64) return hipErrorInvalidValue;  // larger ranks: launch_update_blocked
     hipLaunchKernelGGL(als_solve_wave_kernel, dim3((unsigned)((I + 3) / 4)), dim3(256), 0, s, M, L,
                        I, R, Unew, flag);
     return hipGetLastError();
@@ -1658,70 +1853,42 @@ hipError_t launch_fit(const double *M, const T *Ulast, int64_t Ilast, const doub
     return hipGetLastError();
 }
 
-// The blocked factorization of V = Hadamard_{m != n} G_m into A (R x R);
-// W (R x 64) receives the diagonal blocks' L_kk^{-T}.
-hipError_t launch_chol_blocked(const double *Gall, int order, int n, int64_t R, double *A,
-                               double *W, int *flag, hipStream_t s)
+// U_new = M V^{-1} for ranks past the one-workgroup update (R > 64), by
+// 64-wide column blocks: V = Hadamard_{m != n} G_m into CV, M into CM, the
+// identity into CI, then per block k the diagonal kernel (L_kk, W_k, Z_k) and
+// one step launch (panels and trailing updates of every row block), and at
+// the end U = Y_M Y_I^T into CM (which the caller passes as U_new).
+hipError_t launch_update_blocked(const double *Gall, int order, int n, int64_t R, const double *M,
+                                 int64_t I, double *CV, double *CI, double *CM, double *YI,
+                                 double *YM, double *W, double *Z, int *flag, hipStream_t s)
 {
-    const hipError_t a = allow_large_lds(reinterpret_cast<const void *>(als_chol_diag_kernel));
-    if (a != hipSuccess) return a;
+    const int nblk = (int)((R + 63) / 64);
+    const int64_t mblk = (I + 63) / 64;
+    if (mblk + 2 * (int64_t)nblk > 65535) return hipErrorInvalidValue;  // grid limit
+    hipError_t e = allow_large_lds(reinterpret_cast<const void *>(als_chol_diag_kernel));
+    if (e != hipSuccess) return e;
+    e = allow_large_lds(reinterpret_cast<const void *>(als_aug_step_kernel));
+    if (e != hipSuccess) return e;
     const int64_t RR = R * R;
     hipLaunchKernelGGL(als_hadamard_kernel, dim3((unsigned)((RR + 255) / 256)), dim3(256), 0, s,
-                       Gall, order, n, R, A, flag);
-    for (int64_t k0 = 0; k0 < R; k0 += 64) {
-        const int64_t nb = std::min<int64_t>(64, R - k0), rest = R - k0 - nb;
-        hipLaunchKernelGGL(als_chol_diag_kernel, dim3(1), dim3(256), kCholDiagLds, s, A, R, k0, W,
-                           flag);
-        if (rest == 0) break;
-        // panel: L21 = A21 L_kk^{-T}, in place
-        double *P21 = A + (k0 + nb) * R + k0;
-        hipError_t e = launch_gemm<double>(P21, R, P21, R, (int64_t)1, W + k0 * 64, (int64_t)64,
-                                           (int64_t)1, rest, nb, nb, 1.0, 0.0, 0, true, flag, s);
-        if (e != hipSuccess) return e;
-        // trailing block (lower tiles): A22 -= L21 L21^T
-        e = launch_gemm<double>(A + (k0 + nb) * R + k0 + nb, R, P21, R, (int64_t)1, P21, (int64_t)1,
-                                R, rest, rest, nb, -1.0, 1.0, 1, false, flag, s);
-        if (e != hipSuccess) return e;
-    }
-    return hipGetLastError();
-}
-
-// U_new = M V^{-1} with the blocked factor L (R x R) and the diagonal blocks'
-// L_kk^{-T} in W: rows of M copied to Unew, then forward (Y L^T = M) and back
-// (U L = Y) substitution by column blocks: a block's unknowns are its
-// right-hand side times L_kk^{-T} (forward) or L_kk^{-1} (back), and are taken
-// off the remaining columns by a product.
-hipError_t launch_solve_blocked(const double *M, const double *L, const double *W, int64_t I,
-                                int64_t R, double *Unew, const int *flag, hipStream_t s)
-{
-    hipError_t e = hipMemcpyAsync(Unew, M, (size_t)(I * R) * sizeof(double),
-                                  hipMemcpyDeviceToDevice, s);
+                       Gall, order, n, R, CV, flag);
+    hipLaunchKernelGGL(als_aug_init_kernel, dim3((unsigned)((RR + 255) / 256)), dim3(256), 0, s,
+                       CI, YI, R, flag);
+    e = hipMemcpyAsync(CM, M, (size_t)(I * R) * sizeof(double), hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return e;
-    for (int64_t k0 = 0; k0 < R; k0 += 64) {
-        const int64_t nb = std::min<int64_t>(64, R - k0), rest = R - k0 - nb;
-        // Y(:, block) = B(:, block) L_kk^{-T}, in place
-        e = launch_gemm<double>(Unew + k0, R, Unew + k0, R, (int64_t)1, W + k0 * 64, (int64_t)64,
-                                (int64_t)1, I, nb, nb, 1.0, 0.0, 0, true, flag, s);
-        if (e != hipSuccess) return e;
-        if (rest == 0) break;
-        // Y(:, later) -= Y(:, block) L(later, block)^T
-        e = launch_gemm<double>(Unew + k0 + nb, R, Unew + k0, R, (int64_t)1, L + (k0 + nb) * R + k0,
-                                (int64_t)1, R, I, rest, nb, -1.0, 1.0, 0, false, flag, s);
-        if (e != hipSuccess) return e;
+    AugStep a{CV, CM, CI, YM, YI, W, Z, R, I, 0, nblk, (int)mblk, flag};
+    for (int k = 0; k < nblk; ++k) {
+        hipLaunchKernelGGL(als_chol_diag_kernel, dim3(1), dim3(256), kCholDiagLds, s, CV, R,
+                           (int64_t)k * 64, W, Z, flag);
+        a.k = k;
+        const unsigned gy = (unsigned)((nblk - 1 - k) + (k + 1) + mblk);
+        hipLaunchKernelGGL(als_aug_step_kernel, dim3((unsigned)(nblk - k), gy), dim3(256), kAugLds,
+                           s, a);
     }
-    const int64_t last = ((R - 1) / 64) * 64;
-    for (int64_t k0 = last; k0 >= 0; k0 -= 64) {
-        const int64_t nb = std::min<int64_t>(64, R - k0);
-        // U(:, block) = Y(:, block) L_kk^{-1} (L_kk^{-1} = X^T, X in W), in place
-        e = launch_gemm<double>(Unew + k0, R, Unew + k0, R, (int64_t)1, W + k0 * 64, (int64_t)1,
-                                (int64_t)64, I, nb, nb, 1.0, 0.0, 0, true, flag, s);
-        if (e != hipSuccess) return e;
-        if (k0 == 0) break;
-        // U(:, earlier) -= U(:, block) L(block, earlier)
-        e = launch_gemm<double>(Unew, R, Unew + k0, R, (int64_t)1, L + k0 * R, R, (int64_t)1, I, k0,
-                                nb, -1.0, 1.0, 0, false, flag, s);
-        if (e != hipSuccess) return e;
-    }
+    // U = Y_M Y_I^T: A(i, t) = Y_M[i R + t], B(t, j) = Y_I[j R + t]
+    e = launch_gemm<double>(CM, R, YM, R, (int64_t)1, YI, (int64_t)1, R, I, R, R, 1.0, 0.0, 0, flag,
+                            s);
+    if (e != hipSuccess) return e;
     return hipGetLastError();
 }
 

@@ -374,7 +374,7 @@ int mttkrp_all_entry(const T *X, const int64_t *dims, int order, const T *const 
 //   [mttkrp partials][M fp64 maxI x R][Unew fp64 maxI x R][G fp64 d x R x R]
 //   [L fp64 R x R][lambda fp64 R][sumsq partials][scalars: ||X||^2, fit][flag]
 struct AlsLayout {
-    size_t mt, M, Unew, G, L, W, lam, parts, scal, flag, total;
+    size_t mt, M, Unew, G, L, W, Z, CI, YI, YM, lam, parts, scal, flag, total;
 };
 
 int als_layout(const int64_t *dims, int order, int64_t rank, int elem, AlsLayout &L)
@@ -400,6 +400,16 @@ int als_layout(const int64_t *dims, int order, int64_t rank, int elem, AlsLayout
     // the last mode's V for the fit (R <= 64, R x R)
     L.W = off;
     off += round256(8 * R * 64);
+    // the blocked update (R > 64): Z_k, the identity rows, L^{-T}, M L^{-T}
+    const bool blocked = rank > 64;
+    L.Z = off;
+    off += blocked ? round256(8 * 64 * 64) : 0;
+    L.CI = off;
+    off += blocked ? round256(8 * R * R) : 0;
+    L.YI = off;
+    off += blocked ? round256(8 * R * R) : 0;
+    L.YM = off;
+    off += blocked ? round256(8 * (size_t)maxI * R) : 0;
     L.lam = off;
     off += round256(8 * R);
     L.parts = off;
@@ -440,6 +450,10 @@ int cp_als_entry(const T *X, const int64_t *dims, int order, int64_t rank, T *co
     double *G = reinterpret_cast<double *>(w + L.G);
     double *Lc = reinterpret_cast<double *>(w + L.L);
     double *Winv = reinterpret_cast<double *>(w + L.W);
+    double *Zk = reinterpret_cast<double *>(w + L.Z);
+    double *CI = reinterpret_cast<double *>(w + L.CI);
+    double *YI = reinterpret_cast<double *>(w + L.YI);
+    double *YM = reinterpret_cast<double *>(w + L.YM);
     double *lam64 = reinterpret_cast<double *>(w + L.lam);
     double *parts = reinterpret_cast<double *>(w + L.parts);
     double *scal = reinterpret_cast<double *>(w + L.scal);
@@ -624,11 +638,11 @@ int cp_als_entry(const T *X, const int64_t *dims, int order, int64_t rank, T *co
                 if (!ok(launch_chol(G, order, n, R, Lc, flag, s))) return MTTKRP_EHIP;
                 if (!ok(launch_solve(M, Lc, dims[n], R, Unew, flag, s))) return MTTKRP_EHIP;
             } else {
-                // 64-wide column blocks: diagonal blocks by one wave, panels by
-                // rows in parallel, trailing updates as tiled products
-                if (!ok(launch_chol_blocked(G, order, n, R, Lc, Winv, flag, s)))
-                    return MTTKRP_EHIP;
-                if (!ok(launch_solve_blocked(M, Lc, Winv, dims[n], R, Unew, flag, s)))
+                // 64-wide column blocks: per block the diagonal factor and
+                // inverse by one wave, then one launch of tiled products for
+                // the panels and trailing updates of V, M and the identity
+                if (!ok(launch_update_blocked(G, order, n, R, M, dims[n], Lc, CI, Unew, YI, YM,
+                                              Winv, Zk, flag, s)))
                     return MTTKRP_EHIP;
             }
             if (!ok(launch_normalize<T>(Unew, dims[n], R, factors[n], lam64, lambda, flag, s)))
