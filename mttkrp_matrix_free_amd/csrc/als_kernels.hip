@@ -1225,7 +1225,7 @@ __global__ __launch_bounds__(kRedThreads) void als_fit_kernel(
 // ---------------------------------------------------------------------------
 // Blocked R x R work for ranks past what one workgroup holds (R > 64): the
 // Cholesky factorization in 64-wide column blocks, the diagonal blocks by
-// one wave (as above), carried out on V with the rows of M and of the
+// one workgroup, carried out on V with the rows of M and of the
 // identity appended, so that the forward substitution and the factor's
 // inverse come out of the same block steps; the back substitution is then
 // one product with that inverse.  Within a diagonal block every entry gets
@@ -1250,78 +1250,95 @@ __global__ __launch_bounds__(256) void als_hadamard_kernel(const double *__restr
     A[e] = v;
 }
 
-// Factor the diagonal block at (k0, k0), nb = min(64, R - k0) wide, of A
-// (R x R, row-major) in place: its lower triangle becomes L_kk, its strict
-// upper triangle zeros.  Then the inverse's transpose X = L_kk^{-T} (rows of
-// X solve x L_kk^T = e_r: forward substitutions of the identity's rows, on
-// lane quads as in the one-workgroup update) goes to W rows k0 .. k0 + nb - 1
-// (pitch 64), and Z = X X^T = (L_kk L_kk^T)^{-1}, the inverse of the block
-// as it entered, to Z (64 x 64, pitch 64, zero outside nb x nb), so that the
-// block step below needs products only.  A non-positive pivot sets the flag
-// to 1.  Dynamic LDS: kCholDiagLds bytes.
-constexpr int kCholDiagDoubles = 256 + (64 * 65 + 1) + (64 * 64 + 64) + 64 + (64 * 64 + 1) + 1;
-constexpr size_t kCholDiagLds = kCholDiagDoubles * sizeof(double);
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
-als_chol_diag_kernel(double *__restrict__ A, int64_t R, int64_t k0, double *__restrict__ W,
-                     double *__restrict__ Z, int *__restrict__ flag)
+// The diagonal block B = A(k0 .. k0 + nb - 1, same columns) of A (R x R,
+// row-major: the current Schur complement), nb = min(64, R - k0): its
+// Cholesky factor's inverse transpose X = L_kk^{-T} to W rows k0 .. k0 + nb
+// - 1 (pitch 64) and Z = X X^T = B^{-1} to Z (64 x 64, pitch 64, zero
+// outside nb x nb), so that the block step below needs products only.  X is
+// found as the rows of the identity appended below B and carried through
+// B's right-looking factorization (their forward substitution), so one chain
+// of 64 pivots gives both: pivot p with d = B(p, p) and l(j) = B(j, p) /
+// sqrt(d) takes B(i, j) -= l(i) l(j) and, for an identity row, sets its
+// entry p to C(i, p) / sqrt(d) and takes C(i, j) -= C(i, p) l(j) / sqrt(d)
+// (j > p).  Rows and columns past nb are the identity's (pivots 1).  Waves 0
+// and 1 hold columns 0-31 and 32-63 of B's rows, waves 2 and 3 those of the
+// identity rows (lane i: row i); pivot p's column of each goes to every wave
+// through LDS (two buffers, one barrier per pivot).  A pivot that is not
+// positive sets the flag to 1.
+__global__ __launch_bounds__(256) void als_chol_diag_kernel(const double *__restrict__ A,
+                                                            int64_t R, int64_t k0,
+                                                            double *__restrict__ W,
+                                                            double *__restrict__ Z,
+                                                            int *__restrict__ flag)
 {
-    constexpr int RM = 64, P = RM + 1;
-    extern __shared__ __align__(16) unsigned char smem[];
-    double *col = reinterpret_cast<double *>(smem);  // 256
-    double *Bk = col + 256;                             // 64 x 65 (+1 spare)
-    double *E = Bk + RM * P + 1;                        // L_kk^T rows, 64 zeros after
-    double *rd = E + RM * RM + 64;                      // 1 / L_jj
-    double *xs = rd + 64;                               // 64 identity rows, then X (+1 spare)
-    int &fail = *reinterpret_cast<int *>(xs + RM * RM + 1);
+    __shared__ double colB[2][64];  // B(:, p), zero above the pivot
+    __shared__ double colI[2][64];  // C(:, p) of the identity rows
+    __shared__ double Xs[64 * 65];
     if (*flag) return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nb = (int)(R - k0 < 64 ? R - k0 : 64);
-    double *Ad = A + k0 * R + k0;
-    for (int e = tid; e < nb * nb; e += 256) {
-        const int r = e / nb, c = e - (e / nb) * nb;
-        Bk[r * P + c] = Ad[(int64_t)r * R + c];
+    const int i = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int part = wave >> 1, half = wave & 1;
+    const int nb = (int)min<int64_t>(64, R - k0);
+    const bool rin = i < nb;
+    // every lane loads (a clamped, in-range address) and keeps the value
+    // only for B's rows inside the block: no load sits under a branch
+    double a[32];
+    const double *Ar = A + (k0 + (rin ? i : 0)) * R + k0;
+    const bool keep = part == 0 && rin;
+#pragma unroll
+    for (int jj = 0; jj < 32; ++jj) {
+        const int j = 32 * half + jj;
+        const double g = Ar[j < nb ? j : 0];
+        a[jj] = (keep && j < nb) ? g : (i == j ? 1.0 : 0.0);
     }
-    col[tid] = 0.0;
-    __syncthreads();
-    if (tid < 64) {
-        const bool bad =
-            chol_wave_factor<RM>(Bk, nb, col, Bk, P, 1, Bk, P, 1, Bk + RM * P);
-        if (tid == 0) fail = bad;
+    // the values are formed here (the selects are not carried into the loop)
+#pragma unroll
+    for (int jj = 0; jj < 32; ++jj) asm volatile("" : "+v"(a[jj]));
+    bool bad = false;
+#pragma unroll
+    for (int p = 0; p < 64; ++p) {
+        const int b = p & 1;
+        if (half == (p >> 5)) {
+            const double v = a[p & 31];
+            if (part == 0)
+                colB[b][i] = i >= p ? v : 0.0;
+            else
+                colI[b][i] = v;
+        }
+        __syncthreads();
+        const double d = colB[b][p];
+        bad = bad || !(d > 0.0);
+        const double rd = 1.0 / d;
+        const double own = part == 0 ? colB[b][i] : colI[b][i];
+        const double t = own * rd;
+        // columns before p read zeros (finished); entry p of an identity row
+        // is set below
+#pragma unroll
+        for (int jj = 0; jj < 32; ++jj) a[jj] = __builtin_fma(-t, colB[b][32 * half + jj], a[jj]);
+        if (part == 1 && half == (p >> 5)) a[p & 31] = own / sqrt(d);
+        // each pivot's updates are done here, not deferred to where the
+        // values are next read (which would keep every pivot's operands live)
+#pragma unroll
+        for (int jj = 0; jj < 32; ++jj) asm volatile("" : "+v"(a[jj]));
     }
-    __syncthreads();
-    if (fail) {
-        if (tid == 0) *flag = 1;
+    if (bad) {
+        if (threadIdx.x == 0) *flag = 1;
         return;
     }
-    for (int e = tid; e < nb * nb; e += 256) {
-        const int r = e / nb, c = e - (e / nb) * nb;
-        const double v = Bk[r * P + c];
-        Ad[(int64_t)r * R + c] = v;
-        E[c * nb + r] = v;
-        xs[e] = r == c ? 1.0 : 0.0;
-    }
-    if (tid < 64) E[nb * nb + tid] = 0.0;
-    if (tid < nb) rd[tid] = 1.0 / Bk[tid * P + tid];
-    __syncthreads();
-    {
-        const int q = lane & 3;
-        const int r = 16 * wave + (lane >> 2);
-        const bool ok = r < nb;
-        double *xrow = xs + (ok ? r : 0) * nb;
-        const bool st = ok && q == 0;
-        double *xout = st ? xrow : xs + RM * RM;
-        subst_pass4<1, RM / 4>(xrow, xout, st ? 1 : 0, E, rd, nb, ok, q);
+    if (part == 1) {
+#pragma unroll
+        for (int jj = 0; jj < 32; ++jj) {
+            const int j = 32 * half + jj;
+            Xs[i * 65 + j] = a[jj];
+            if (rin && j < nb) W[(k0 + i) * 64 + j] = a[jj];
+        }
     }
     __syncthreads();
-    for (int e = tid; e < nb * nb; e += 256) {
-        const int r = e / nb, c = e - (e / nb) * nb;
-        W[(k0 + r) * 64 + c] = xs[e];
-    }
     // Z = X X^T on the matrix cores: wave w forms the 32 x 32 quarter at
     // (wr, wc) as 2 x 2 blocks of 16 x 16 (lane (r16, q) supplies A(r16, t + q)
     // and B(t + q, r16); element e of a block holds row 4 e + q).
     {
-        const int r16 = lane & 15, q = lane >> 4;
+        const int r16 = i & 15, q = i >> 4;
         const int wr = (wave >> 1) * 32, wc = (wave & 1) * 32;
         adx4 acc[2][2];
 #pragma unroll
@@ -1330,19 +1347,19 @@ als_chol_diag_kernel(double *__restrict__ A, int64_t R, int64_t k0, double *__re
             for (int y = 0; y < 2; ++y) acc[x][y] = adx4{0.0, 0.0, 0.0, 0.0};
         for (int t0 = 0; t0 < nb; t0 += 4) {
             const int t = t0 + q;
-            double a[2], b[2];
+            double av[2], bv[2];
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
                 const int r = wr + 16 * x + r16;
-                a[x] = (r < nb && t < nb) ? xs[r * nb + t] : 0.0;
+                av[x] = (r < nb && t < nb) ? Xs[r * 65 + t] : 0.0;
                 const int c = wc + 16 * x + r16;
-                b[x] = (c < nb && t < nb) ? xs[c * nb + t] : 0.0;
+                bv[x] = (c < nb && t < nb) ? Xs[c * 65 + t] : 0.0;
             }
 #pragma unroll
             for (int x = 0; x < 2; ++x)
 #pragma unroll
                 for (int y = 0; y < 2; ++y)
-                    acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[x], b[y], acc[x][y], 0, 0, 0);
+                    acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[x], bv[y], acc[x][y], 0, 0, 0);
         }
 #pragma unroll
         for (int x = 0; x < 2; ++x)
@@ -1855,7 +1872,7 @@ hipError_t launch_fit(const double *M, const T *Ulast, int64_t Ilast, const doub
 
 // U_new = M V^{-1} for ranks past the one-workgroup update (R > 64), by
 // 64-wide column blocks: V = Hadamard_{m != n} G_m into CV, M into CM, the
-// identity into CI, then per block k the diagonal kernel (L_kk, W_k, Z_k) and
+// identity into CI, then per block k the diagonal kernel (W_k, Z_k) and
 // one step launch (panels and trailing updates of every row block), and at
 // the end U = Y_M Y_I^T into CM (which the caller passes as U_new).
 hipError_t launch_update_blocked(const double *Gall, int order, int n, int64_t R, const double *M,
@@ -1865,9 +1882,7 @@ hipError_t launch_update_blocked(const double *Gall, int order, int n, int64_t R
     const int nblk = (int)((R + 63) / 64);
     const int64_t mblk = (I + 63) / 64;
     if (mblk + 2 * (int64_t)nblk > 65535) return hipErrorInvalidValue;  // grid limit
-    hipError_t e = allow_large_lds(reinterpret_cast<const void *>(als_chol_diag_kernel));
-    if (e != hipSuccess) return e;
-    e = allow_large_lds(reinterpret_cast<const void *>(als_aug_step_kernel));
+    hipError_t e = allow_large_lds(reinterpret_cast<const void *>(als_aug_step_kernel));
     if (e != hipSuccess) return e;
     const int64_t RR = R * R;
     hipLaunchKernelGGL(als_hadamard_kernel, dim3((unsigned)((RR + 255) / 256)), dim3(256), 0, s,
@@ -1878,8 +1893,8 @@ hipError_t launch_update_blocked(const double *Gall, int order, int n, int64_t R
     if (e != hipSuccess) return e;
     AugStep a{CV, CM, CI, YM, YI, W, Z, R, I, 0, nblk, (int)mblk, flag};
     for (int k = 0; k < nblk; ++k) {
-        hipLaunchKernelGGL(als_chol_diag_kernel, dim3(1), dim3(256), kCholDiagLds, s, CV, R,
-                           (int64_t)k * 64, W, Z, flag);
+        hipLaunchKernelGGL(als_chol_diag_kernel, dim3(1), dim3(256), 0, s, CV, R, (int64_t)k * 64,
+                           W, Z, flag);
         a.k = k;
         const unsigned gy = (unsigned)((nblk - 1 - k) + (k + 1) + mblk);
         hipLaunchKernelGGL(als_aug_step_kernel, dim3((unsigned)(nblk - k), gy), dim3(256), kAugLds,
