@@ -25,6 +25,7 @@
 
 #include <algorithm>
 #include <type_traits>
+#include <utility>
 
 #include "als_kernels.hpp"
 
@@ -1250,6 +1251,59 @@ __global__ __launch_bounds__(256) void als_hadamard_kernel(const double *__restr
     A[e] = v;
 }
 
+// Pivot p = 32 ph + PP of the diagonal kernel below (PP a compile-time
+// constant, so that the register holding column p, the LDS buffer and the
+// next pivot's column are fixed at compile time).
+template <int PP>
+__device__ __forceinline__ void chol_aug_pivot(double (&a)[32], bool &bad, int ph, int i, int half,
+                                               int part, double (*colB)[64], double (*colI)[64])
+{
+    constexpr int b = PP & 1, pn = (PP + 1) & 31;
+    const int p = 32 * ph + PP;
+    __syncthreads();
+    const double d = colB[b][p];
+    double bp[32];
+#pragma unroll
+    for (int jj = 0; jj < 32; ++jj) bp[jj] = colB[b][32 * half + jj];
+    const double own = part == 0 ? colB[b][i] : colI[b][i];
+    bad = bad || !(d > 0.0);
+    // 1 / sqrt(d) from the hardware estimate and two Newton steps
+    // (y <- y + y (1 - d y^2) / 2), then 1 / d as its square
+    double y = __builtin_amdgcn_rsq(d);
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const double e = __builtin_fma(-d * y, y, 1.0);
+        y = __builtin_fma(0.5 * y, e, y);
+    }
+    const double t = own * (y * y);
+    // the next pivot's column first, so that its owner's LDS write is on its
+    // way while the other columns are updated
+    a[pn] = __builtin_fma(-t, bp[pn], a[pn]);
+    if (p + 1 < 64 && half == ((p + 1) >> 5)) {
+        if (part == 0)
+            colB[b ^ 1][i] = i >= p + 1 ? a[pn] : 0.0;
+        else
+            colI[b ^ 1][i] = a[pn];
+    }
+    // columns before p read zeros (finished); entry p of an identity row is
+    // set below
+#pragma unroll
+    for (int jj = 0; jj < 32; ++jj)
+        if (jj != pn) a[jj] = __builtin_fma(-t, bp[jj], a[jj]);
+    if (part == 1 && half == ph) a[PP] = own * y;
+    // the pivot's updates are done here, not deferred to where the values are
+    // next read (which would keep every pivot's operands live)
+#pragma unroll
+    for (int jj = 0; jj < 32; ++jj) asm volatile("" : "+v"(a[jj]));
+}
+template <int... PP>
+__device__ __forceinline__ void chol_aug_pivots(std::integer_sequence<int, PP...>, double (&a)[32],
+                                                bool &bad, int ph, int i, int half, int part,
+                                                double (*colB)[64], double (*colI)[64])
+{
+    (chol_aug_pivot<PP>(a, bad, ph, i, half, part, colB, colI), ...);
+}
+
 // The diagonal block B = A(k0 .. k0 + nb - 1, same columns) of A (R x R,
 // row-major: the current Schur complement), nb = min(64, R - k0): its
 // Cholesky factor's inverse transpose X = L_kk^{-T} to W rows k0 .. k0 + nb
@@ -1263,7 +1317,9 @@ __global__ __launch_bounds__(256) void als_hadamard_kernel(const double *__restr
 // (j > p).  Rows and columns past nb are the identity's (pivots 1).  Waves 0
 // and 1 hold columns 0-31 and 32-63 of B's rows, waves 2 and 3 those of the
 // identity rows (lane i: row i); pivot p's column of each goes to every wave
-// through LDS (two buffers, one barrier per pivot).  A pivot that is not
+// through LDS (two buffers, one barrier per pivot), and 1 / sqrt(d) comes
+// from the hardware estimate refined by Newton steps, 1 / d as its square
+// (the chain of pivots is the kernel's critical path).  A pivot that is not
 // positive sets the flag to 1.
 __global__ __launch_bounds__(256) void als_chol_diag_kernel(const double *__restrict__ A,
                                                             int64_t R, int64_t k0,
@@ -1294,33 +1350,16 @@ __global__ __launch_bounds__(256) void als_chol_diag_kernel(const double *__rest
     // the values are formed here (the selects are not carried into the loop)
 #pragma unroll
     for (int jj = 0; jj < 32; ++jj) asm volatile("" : "+v"(a[jj]));
-    bool bad = false;
-#pragma unroll
-    for (int p = 0; p < 64; ++p) {
-        const int b = p & 1;
-        if (half == (p >> 5)) {
-            const double v = a[p & 31];
-            if (part == 0)
-                colB[b][i] = i >= p ? v : 0.0;
-            else
-                colI[b][i] = v;
-        }
-        __syncthreads();
-        const double d = colB[b][p];
-        bad = bad || !(d > 0.0);
-        const double rd = 1.0 / d;
-        const double own = part == 0 ? colB[b][i] : colI[b][i];
-        const double t = own * rd;
-        // columns before p read zeros (finished); entry p of an identity row
-        // is set below
-#pragma unroll
-        for (int jj = 0; jj < 32; ++jj) a[jj] = __builtin_fma(-t, colB[b][32 * half + jj], a[jj]);
-        if (part == 1 && half == (p >> 5)) a[p & 31] = own / sqrt(d);
-        // each pivot's updates are done here, not deferred to where the
-        // values are next read (which would keep every pivot's operands live)
-#pragma unroll
-        for (int jj = 0; jj < 32; ++jj) asm volatile("" : "+v"(a[jj]));
+    // pivot 0's column
+    if (half == 0) {
+        if (part == 0)
+            colB[0][i] = a[0];
+        else
+            colI[0][i] = a[0];
     }
+    bool bad = false;
+    for (int ph = 0; ph < 2; ++ph)
+        chol_aug_pivots(std::make_integer_sequence<int, 32>(), a, bad, ph, i, half, part, colB, colI);
     if (bad) {
         if (threadIdx.x == 0) *flag = 1;
         return;
