@@ -1321,25 +1321,22 @@ __device__ __forceinline__ void chol_aug_pivots(std::integer_sequence<int, PP...
 // from the hardware estimate refined by Newton steps, 1 / d as its square
 // (the chain of pivots is the kernel's critical path).  A pivot that is not
 // positive sets the flag to 1.
-__global__ __launch_bounds__(256) void als_chol_diag_kernel(const double *__restrict__ A,
-                                                            int64_t R, int64_t k0,
-                                                            double *__restrict__ W,
-                                                            double *__restrict__ Z,
-                                                            int *__restrict__ flag)
+// (The work of the kernel for the block at Ab, row stride lda -- global
+// memory, or LDS when the block step below runs it -- with LDS buffers colB,
+// colI (2 x 64 each) and Xs (64 x 65).)
+__device__ __forceinline__ void chol_diag_block(const double *Ab, int64_t lda, int nb, int64_t k0,
+                                                double *__restrict__ W, double *__restrict__ Z,
+                                                int *__restrict__ flag, double (*colB)[64],
+                                                double (*colI)[64], double *Xs)
 {
-    __shared__ double colB[2][64];  // B(:, p), zero above the pivot
-    __shared__ double colI[2][64];  // C(:, p) of the identity rows
-    __shared__ double Xs[64 * 65];
-    if (*flag) return;
     const int i = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int part = wave >> 1, half = wave & 1;
-    const int nb = (int)min<int64_t>(64, R - k0);
     const bool rin = i < nb;
     // every lane loads (a clamped, in-range address) and keeps the value
     // only for B's rows inside the block: no load sits under a branch
     double a[32];
-    const double *Ar = A + (k0 + (rin ? i : 0)) * R + k0;
+    const double *Ar = Ab + (rin ? i : 0) * lda;
     const bool keep = part == 0 && rin;
 #pragma unroll
     for (int jj = 0; jj < 32; ++jj) {
@@ -1410,6 +1407,20 @@ __global__ __launch_bounds__(256) void als_chol_diag_kernel(const double *__rest
     }
 }
 
+__global__ __launch_bounds__(256) void als_chol_diag_kernel(const double *__restrict__ A,
+                                                            int64_t R, int64_t k0,
+                                                            double *__restrict__ W,
+                                                            double *__restrict__ Z,
+                                                            int *__restrict__ flag)
+{
+    __shared__ double colB[2][64];  // B(:, p), zero above the pivot
+    __shared__ double colI[2][64];  // C(:, p) of the identity rows
+    __shared__ double Xs[64 * 65];
+    if (*flag) return;
+    chol_diag_block(A + k0 * R + k0, R, (int)min<int64_t>(64, R - k0), k0, W, Z, flag, colB, colI,
+                    Xs);
+}
+
 // One block step k of the factorization V = L L^T carried out on the
 // augmented rows [V; M; I] (V's own factor is never stored: its column blocks
 // enter in product form through Z_k and W_k from the diagonal kernel).
@@ -1422,18 +1433,24 @@ __global__ __launch_bounds__(256) void als_chol_diag_kernel(const double *__rest
 // substitution) and Y_I = L^{-T}, so U = M V^{-1} = Y_M Y_I^T.  Each task is
 // a 64 x 64 tile, two 64 x 64 x 64 products on the matrix cores (the panel
 // one), operands staged in LDS as in the tiled product below; column block k
-// is only read during step k, so the tasks of a step are independent.
+// is only read during step k, so the tasks of a step are independent.  The
+// task of the next diagonal block, tile (k + 1, k + 1), then runs that
+// block's diagonal kernel on the tile it has just formed (W_{k+1} and
+// Z_{k+1}, into the other Z buffer) while the step's other tasks go on, so
+// the chain of diagonal blocks overlaps the trailing updates.
 struct AugStep {
     double *CV, *CM, *CI;  // working rows: V (R x R), M (I x R), identity (R x R)
     double *YM, *YI;       // outputs: M L^{-T} (I x R), L^{-T} (R x R)
-    const double *W;       // W_k at rows k0 .. (pitch 64)
-    const double *Z;       // Z_k (64 x 64)
+    double *W;             // W_k at rows k0 .. (pitch 64)
+    double *Z;             // Z_k at Z + (k & 1) 4096 (64 x 64 each)
     int64_t R, I;
     int k, nblk, mblk;
-    const int *flag;
+    int *flag;
 };
 constexpr int kAugPitch = 68;
 constexpr size_t kAugLds = 2 * 64 * kAugPitch * sizeof(double);
+static_assert(kAugLds >= (2 * 64 * 65 + 4 * 64) * sizeof(double),
+              "the step's LDS also holds the diagonal kernel's buffers");
 
 __global__ __launch_bounds__(256) void als_aug_step_kernel(AugStep a)
 {
@@ -1473,7 +1490,7 @@ __global__ __launch_bounds__(256) void als_aug_step_kernel(AugStep a)
     // both read along their rows by consecutive threads
     {
         double va[16], vb[16];
-        const double *Bsrc = x == 0 ? a.W + k0 * 64 : a.Z;
+        const double *Bsrc = x == 0 ? a.W + k0 * 64 : a.Z + (k & 1) * 4096;
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
             const int r = th + 4 * u;
@@ -1541,6 +1558,11 @@ __global__ __launch_bounds__(256) void als_aug_step_kernel(AugStep a)
     for (int u = 0; u < 16; ++u) Bs[tl][th + 4 * u] = vb[u];
     __syncthreads();
     product();
+    // the next diagonal block's tile: its new values also go to LDS (after
+    // every wave is done with the operands there) for the diagonal kernel
+    const bool next_diag = sec == 0 && x == 1 && rb == k + 1;
+    double *Ts = reinterpret_cast<double *>(smem);  // 64 x 65
+    if (next_diag) __syncthreads();
 #pragma unroll
     for (int xx = 0; xx < 2; ++xx)
 #pragma unroll
@@ -1550,9 +1572,18 @@ __global__ __launch_bounds__(256) void als_aug_step_kernel(AugStep a)
                 const int r = wr + 16 * xx + 4 * e + q, c = wc + 16 * yy + r16;
                 if (r < nr && c < jn) {
                     double *p = C + (r0 + r) * R + j0 + c;
-                    *p -= acc[xx][yy][e];
+                    const double v = *p - acc[xx][yy][e];
+                    *p = v;
+                    if (next_diag) Ts[r * 65 + c] = v;
                 }
             }
+    if (next_diag) {
+        __syncthreads();
+        double *Xs = Ts + 64 * 65;
+        double(*colB)[64] = reinterpret_cast<double(*)[64]>(Xs + 64 * 65);
+        double(*colI)[64] = colB + 2;
+        chol_diag_block(Ts, 65, jn, j0, a.W, a.Z + ((k + 1) & 1) * 4096, a.flag, colB, colI, Xs);
+    }
 }
 
 // C = [V rows untouched; identity rows] and Y_I = 0 (entries of L^{-T}
@@ -1911,9 +1942,10 @@ hipError_t launch_fit(const double *M, const T *Ulast, int64_t Ilast, const doub
 
 // U_new = M V^{-1} for ranks past the one-workgroup update (R > 64), by
 // 64-wide column blocks: V = Hadamard_{m != n} G_m into CV, M into CM, the
-// identity into CI, then per block k the diagonal kernel (W_k, Z_k) and
-// one step launch (panels and trailing updates of every row block), and at
-// the end U = Y_M Y_I^T into CM (which the caller passes as U_new).
+// identity into CI, then the first diagonal block (W_0, Z_0) and per block
+// k one step launch (panels and trailing updates of every row block, and
+// block k + 1's diagonal kernel), and at the end U = Y_M Y_I^T into CM
+// (which the caller passes as U_new).
 hipError_t launch_update_blocked(const double *Gall, int order, int n, int64_t R, const double *M,
                                  int64_t I, double *CV, double *CI, double *CM, double *YI,
                                  double *YM, double *W, double *Z, int *flag, hipStream_t s)
@@ -1931,9 +1963,10 @@ hipError_t launch_update_blocked(const double *Gall, int order, int n, int64_t R
     e = hipMemcpyAsync(CM, M, (size_t)(I * R) * sizeof(double), hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return e;
     AugStep a{CV, CM, CI, YM, YI, W, Z, R, I, 0, nblk, (int)mblk, flag};
+    // the first diagonal block; each step forms the next one's
+    hipLaunchKernelGGL(als_chol_diag_kernel, dim3(1), dim3(256), 0, s, CV, R, (int64_t)0, W, Z,
+                       flag);
     for (int k = 0; k < nblk; ++k) {
-        hipLaunchKernelGGL(als_chol_diag_kernel, dim3(1), dim3(256), 0, s, CV, R, (int64_t)k * 64,
-                           W, Z, flag);
         a.k = k;
         const unsigned gy = (unsigned)((nblk - 1 - k) + (k + 1) + mblk);
         hipLaunchKernelGGL(als_aug_step_kernel, dim3((unsigned)(nblk - k), gy), dim3(256), kAugLds,

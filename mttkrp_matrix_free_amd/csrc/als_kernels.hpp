@@ -36,7 +36,7 @@ template <typename T>
 hipError_t launch_gram_all(const T *const *U, const int64_t *dims, int order, int64_t R, double *G,
                            const int *flag, hipStream_t s);
 // R > 64: U_new = M V^{-1} into CM by 64-wide column blocks (CV, CI, YI: R x R;
-// CM, YM: I x R; W: R x 64; Z: 64 x 64 -- all workspace).
+// CM, YM: I x R; W: R x 64; Z: 2 x 64 x 64 -- all workspace).
 hipError_t launch_update_blocked(const double *Gall, int order, int n, int64_t R, const double *M,
                                  int64_t I, double *CV, double *CI, double *CM, double *YI,
                                  double *YM, double *W, double *Z, int *flag, hipStream_t s);

@@ -403,7 +403,7 @@ int als_layout(const int64_t *dims, int order, int64_t rank, int elem, AlsLayout
     // the blocked update (R > 64): Z_k, the identity rows, L^{-T}, M L^{-T}
     const bool blocked = rank > 64;
     L.Z = off;
-    off += blocked ? round256(8 * 64 * 64) : 0;
+    off += blocked ? round256(8 * 2 * 64 * 64) : 0;
     L.CI = off;
     off += blocked ? round256(8 * R * R) : 0;
     L.YI = off;
