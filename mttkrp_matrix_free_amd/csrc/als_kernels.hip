@@ -475,7 +475,11 @@ __global__ __launch_bounds__(256) void als_solve_wave_kernel(const double *__res
     if (lane < R) Unew[row * R + lane] = b;
 }
 
-// lambda_r = ||U_new(:, r)||_2 and U_n = U_new / lambda_r; one thread per column.
+// lambda_r = ||U_new(:, r)||_2 and U_n = U_new / lambda_r.  A workgroup
+// takes 16 columns; thread (c, g) sums the squares of rows g, g + 16, ... of
+// column c in order, and the 16 group sums of a column are added in group
+// order (a fixed order, so results do not depend on scheduling); then every
+// thread scales its rows.
 template <typename T>
 __global__ __launch_bounds__(256) void als_normalize_kernel(const double *__restrict__ Unew,
                                                             int64_t I, int64_t R,
@@ -484,22 +488,37 @@ __global__ __launch_bounds__(256) void als_normalize_kernel(const double *__rest
                                                             T *__restrict__ lamT,
                                                             const int *__restrict__ flag)
 {
+    __shared__ double part[16][17];
+    __shared__ double lam_s[16];
     if (*flag) return;
-    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (r >= R) return;
-    // (unrolled: the loads of several rows are in flight at once; the sum
-    // still adds the rows in order)
+    const int c = threadIdx.x & 15, g = threadIdx.x >> 4;
+    const int64_t r = (int64_t)blockIdx.x * 16 + c;
+    const bool ok = r < R;
     double s = 0.0;
-#pragma unroll 8
-    for (int64_t i = 0; i < I; ++i) s += Unew[i * R + r] * Unew[i * R + r];
-    const double lam = sqrt(s);
-#pragma unroll 8
-    for (int64_t i = 0; i < I; ++i) {
+    if (ok) {
+#pragma unroll 4
+        for (int64_t i = g; i < I; i += 16) s += Unew[i * R + r] * Unew[i * R + r];
+    }
+    part[g][c] = s;
+    __syncthreads();
+    if (g == 0) {
+        double t = part[0][c];
+        for (int h = 1; h < 16; ++h) t += part[h][c];
+        const double lam = sqrt(t);
+        lam_s[c] = lam;
+        if (ok) {
+            lam64[r] = lam;
+            if (lamT) lamT[r] = (T)lam;
+        }
+    }
+    __syncthreads();
+    if (!ok) return;
+    const double lam = lam_s[c];
+#pragma unroll 4
+    for (int64_t i = g; i < I; i += 16) {
         const double v = Unew[i * R + r];
         Uout[i * R + r] = (T)(lam > 0.0 ? v / lam : v);
     }
-    lam64[r] = lam;
-    if (lamT) lamT[r] = (T)lam;
 }
 
 // Quad-local lane moves (DPP quad permutations): the value of lane 0 of this
@@ -1606,10 +1625,13 @@ __global__ __launch_bounds__(256) void als_aug_init_kernel(double *__restrict__ 
 // without reading C).  A workgroup owns a 64 x 64 tile of C, each of its
 // four waves a 32 x 32 quarter as 2 x 2 blocks of v_mfma_f64_16x16x4f64
 // accumulators; K is staged through LDS in chunks of 64, the next chunk's
-// loads in flight while the matrix cores work on the current one.  lower:
-// tiles above the diagonal are skipped.  C must not overlap A or B.  The
-// sums over t follow the matrix cores' fixed order, so results are
-// deterministic.
+// loads in flight while the matrix cores work on the current one.  shape:
+// kGemmFull; kGemmSym (C symmetric, m = n: the tiles on and below the
+// diagonal are formed, each one below also stored transposed above); or
+// kGemmUpperB (B(t, j) = 0 for t below j's 64-column tile: the sum for that
+// tile starts there).  C must not overlap A or B.  The sums over t follow
+// the matrix cores' fixed order, so results are deterministic.
+constexpr int kGemmFull = 0, kGemmSym = 1, kGemmUpperB = 2;
 typedef double gdx4 __attribute__((ext_vector_type(4)));
 
 template <typename TA>
@@ -1619,7 +1641,7 @@ __global__ __launch_bounds__(256) void als_mfma_gemm_kernel(double *__restrict__
                                                             const TA *__restrict__ B, int64_t sbt,
                                                             int64_t sbj, int64_t m, int64_t n,
                                                             int64_t K, double alpha, double beta,
-                                                            int lower,
+                                                            int shape,
                                                             const int *__restrict__ flag)
 {
     constexpr int TM = 64, TN = 64, KC = 64, PA = TM + 4, NL = TM * KC / 256;
@@ -1628,7 +1650,7 @@ __global__ __launch_bounds__(256) void als_mfma_gemm_kernel(double *__restrict__
     double(*Bs)[PA] = reinterpret_cast<double(*)[PA]>(smem + KC * PA * sizeof(double));
     if (*flag) return;
     const int64_t ti = blockIdx.y, tj = blockIdx.x;
-    if (lower && tj * TN > ti * TM + TM - 1) return;
+    if (shape == kGemmSym && tj > ti) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = (wave >> 1) * 32, wc = (wave & 1) * 32;  // the wave's quarter
     const int r16 = lane & 15, q = lane >> 4;
@@ -1654,8 +1676,9 @@ __global__ __launch_bounds__(256) void als_mfma_gemm_kernel(double *__restrict__
             vb[u] = okb ? (double)B[(t0 + tb) * sbt + (j0 + c) * sbj] : 0.0;
         }
     };
-    fetch(0);
-    for (int64_t t0 = 0; t0 < K; t0 += KC) {
+    const int64_t kbeg = shape == kGemmUpperB ? (j0 < K ? j0 : K) : 0;
+    fetch(kbeg);
+    for (int64_t t0 = kbeg; t0 < K; t0 += KC) {
         __syncthreads();  // the previous chunk's operands are read
 #pragma unroll
         for (int u = 0; u < NL; ++u) {
@@ -1691,6 +1714,10 @@ __global__ __launch_bounds__(256) void als_mfma_gemm_kernel(double *__restrict__
                     double *c = C + i * ldc + j;
                     const double v = acc[x][y][e];
                     *c = beta == 0.0 ? alpha * v : __builtin_fma(alpha, v, beta * *c);
+                    if (shape == kGemmSym && ti != tj) {
+                        double *ct = C + j * ldc + i;
+                        *ct = beta == 0.0 ? alpha * v : __builtin_fma(alpha, v, beta * *ct);
+                    }
                 }
             }
 }
@@ -1702,14 +1729,14 @@ hipError_t allow_large_lds(const void *k);
 template <typename TA>
 hipError_t launch_gemm(double *C, int64_t ldc, const TA *A, int64_t sai, int64_t sat, const TA *B,
                        int64_t sbt, int64_t sbj, int64_t m, int64_t n, int64_t K, double alpha,
-                       double beta, int lower, const int *flag, hipStream_t s)
+                       double beta, int shape, const int *flag, hipStream_t s)
 {
     const int64_t gx = (n + 63) / 64, gy = (m + 63) / 64;
     if (gx > INT32_MAX || gy > 65535) return hipErrorInvalidValue;  // grid limits
     const hipError_t a = allow_large_lds(reinterpret_cast<const void *>(als_mfma_gemm_kernel<TA>));
     if (a != hipSuccess) return a;
     hipLaunchKernelGGL(als_mfma_gemm_kernel<TA>, dim3((unsigned)gx, (unsigned)gy), dim3(256),
-                       kGemmLds, s, C, ldc, A, sai, sat, B, sbt, sbj, m, n, K, alpha, beta, lower,
+                       kGemmLds, s, C, ldc, A, sai, sat, B, sbt, sbj, m, n, K, alpha, beta, shape,
                        flag);
     return hipGetLastError();
 }
@@ -1773,7 +1800,7 @@ hipError_t launch_gram(const T *U, int64_t I, int64_t R, double *G, const int *f
 {
     if (R > 64) {
         // G = U^T U as a tiled product (the same per-entry order over i)
-        return launch_gemm<T>(G, R, U, (int64_t)1, R, U, R, (int64_t)1, R, R, I, 1.0, 0.0, 0,
+        return launch_gemm<T>(G, R, U, (int64_t)1, R, U, R, (int64_t)1, R, R, I, 1.0, 0.0, kGemmSym,
                               flag, s);
     }
     const int64_t n = R * R;
@@ -1827,7 +1854,7 @@ template <typename T>
 hipError_t launch_normalize(const double *Unew, int64_t I, int64_t R, T *Uout, double *lam64,
                             T *lamT, const int *flag, hipStream_t s)
 {
-    hipLaunchKernelGGL(als_normalize_kernel<T>, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, s,
+    hipLaunchKernelGGL(als_normalize_kernel<T>, dim3((unsigned)((R + 15) / 16)), dim3(256), 0, s,
                        Unew, I, R, Uout, lam64, lamT, flag);
     return hipGetLastError();
 }
@@ -1973,8 +2000,9 @@ hipError_t launch_update_blocked(const double *Gall, int order, int n, int64_t R
                            s, a);
     }
     // U = Y_M Y_I^T: A(i, t) = Y_M[i R + t], B(t, j) = Y_I[j R + t]
-    e = launch_gemm<double>(CM, R, YM, R, (int64_t)1, YI, (int64_t)1, R, I, R, R, 1.0, 0.0, 0, flag,
-                            s);
+    // (L^{-T} is upper triangular: B(t, j) = Y_I(j, t) = 0 for t < j)
+    e = launch_gemm<double>(CM, R, YM, R, (int64_t)1, YI, (int64_t)1, R, I, R, R, 1.0, 0.0,
+                            kGemmUpperB, flag, s);
     if (e != hipSuccess) return e;
     return hipGetLastError();
 }
