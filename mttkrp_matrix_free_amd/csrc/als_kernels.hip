@@ -1634,8 +1634,10 @@ __global__ __launch_bounds__(256) void als_aug_init_kernel(double *__restrict__ 
 constexpr int kGemmFull = 0, kGemmSym = 1, kGemmUpperB = 2;
 typedef double gdx4 __attribute__((ext_vector_type(4)));
 
+// (Two workgroups per compute unit, as the LDS allows: the registers are
+// held to two waves per SIMD.)
 template <typename TA>
-__global__ __launch_bounds__(256) void als_mfma_gemm_kernel(double *__restrict__ C, int64_t ldc,
+__global__ __launch_bounds__(256, 2) void als_mfma_gemm_kernel(double *__restrict__ C, int64_t ldc,
                                                             const TA *__restrict__ A,
                                                             int64_t sai, int64_t sat,
                                                             const TA *__restrict__ B, int64_t sbt,
@@ -1660,20 +1662,32 @@ __global__ __launch_bounds__(256) void als_mfma_gemm_kernel(double *__restrict__
     for (int x = 0; x < 2; ++x)
 #pragma unroll
         for (int y = 0; y < 2; ++y) acc[x][y] = gdx4{0.0, 0.0, 0.0, 0.0};
-    // the unit-stride dimension of each operand runs across consecutive threads
+    // The unit-stride dimension of each operand runs across consecutive
+    // threads: thread tid takes, for u = 0 .. NL - 1, the element at lane
+    // index tid % 64 along that dimension and tid / 64 + 4 u along the other.
+    // Its byte offset inside the chunk's tile is a fixed 32-bit part (per
+    // thread) plus u times a uniform step, so the loads need no per-thread
+    // 64-bit addresses.
     const bool a_t = sat == 1, b_c = sbj == 1;
+    const int lo = tid & 63, hi = tid >> 6;
+    const uint32_t voffA = (uint32_t)(((a_t ? hi : lo) * sai + (a_t ? lo : hi) * sat) * (int64_t)sizeof(TA));
+    const uint32_t voffB = (uint32_t)(((b_c ? hi : lo) * sbt + (b_c ? lo : hi) * sbj) * (int64_t)sizeof(TA));
+    const int64_t stepA = 4 * (a_t ? sai : sat), stepB = 4 * (b_c ? sbt : sbj);
     double va[NL], vb[NL];
     // a chunk's operands into registers (zero outside the matrices)
     auto fetch = [&](int64_t t0) {
+        const TA *Ab = A + i0 * sai + t0 * sat;
+        const TA *Bb = B + t0 * sbt + j0 * sbj;
 #pragma unroll
         for (int u = 0; u < NL; ++u) {
-            const int e = tid + 256 * u;
-            const int r = a_t ? e / KC : e % TM, t = a_t ? e % KC : e / TM;
+            const int r = a_t ? hi + 4 * u : lo, t = a_t ? lo : hi + 4 * u;
             const bool ok = i0 + r < m && t0 + t < K;
-            va[u] = ok ? (double)A[(i0 + r) * sai + (t0 + t) * sat] : 0.0;
-            const int c = b_c ? e % TN : e / KC, tb = b_c ? e / TN : e % KC;
+            const char *pa = reinterpret_cast<const char *>(Ab + u * stepA) + voffA;
+            va[u] = ok ? (double)*reinterpret_cast<const TA *>(pa) : 0.0;
+            const int c = b_c ? lo : hi + 4 * u, tb = b_c ? hi + 4 * u : lo;
             const bool okb = t0 + tb < K && j0 + c < n;
-            vb[u] = okb ? (double)B[(t0 + tb) * sbt + (j0 + c) * sbj] : 0.0;
+            const char *pb = reinterpret_cast<const char *>(Bb + u * stepB) + voffB;
+            vb[u] = okb ? (double)*reinterpret_cast<const TA *>(pb) : 0.0;
         }
     };
     const int64_t kbeg = shape == kGemmUpperB ? (j0 < K ? j0 : K) : 0;
@@ -1682,16 +1696,15 @@ __global__ __launch_bounds__(256) void als_mfma_gemm_kernel(double *__restrict__
         __syncthreads();  // the previous chunk's operands are read
 #pragma unroll
         for (int u = 0; u < NL; ++u) {
-            const int e = tid + 256 * u;
-            const int r = a_t ? e / KC : e % TM, t = a_t ? e % KC : e / TM;
+            const int r = a_t ? hi + 4 * u : lo, t = a_t ? lo : hi + 4 * u;
             As[t][r] = va[u];
-            const int c = b_c ? e % TN : e / KC, tb = b_c ? e / TN : e % KC;
+            const int c = b_c ? lo : hi + 4 * u, tb = b_c ? hi + 4 * u : lo;
             Bs[tb][c] = vb[u];
         }
         __syncthreads();
         // the next chunk's loads go out before this chunk's matrix-core work
         if (t0 + KC < K) fetch(t0 + KC);
-#pragma unroll
+#pragma unroll 4
         for (int kk = 0; kk < KC; kk += 4) {
             const int k = kk + q;
             const double a0 = As[k][wr + r16], a1 = As[k][wr + 16 + r16];
@@ -1714,12 +1727,31 @@ __global__ __launch_bounds__(256) void als_mfma_gemm_kernel(double *__restrict__
                     double *c = C + i * ldc + j;
                     const double v = acc[x][y][e];
                     *c = beta == 0.0 ? alpha * v : __builtin_fma(alpha, v, beta * *c);
-                    if (shape == kGemmSym && ti != tj) {
-                        double *ct = C + j * ldc + i;
-                        *ct = beta == 0.0 ? alpha * v : __builtin_fma(alpha, v, beta * *ct);
-                    }
                 }
             }
+    if (shape == kGemmSym && ti != tj) {
+        // the transposed tile above the diagonal, through LDS so that
+        // consecutive threads store consecutive entries of a row
+        double(*Ts)[PA] = As;  // Ts[j - j0][i - i0]
+        __syncthreads();       // every wave is done with the operands
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int y = 0; y < 2; ++y)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    Ts[wc + 16 * y + r16][wr + 16 * x + 4 * e + q] = acc[x][y][e];
+        __syncthreads();
+        for (int u = 0; u < TN * TM / 256; ++u) {
+            const int jr = hi + 4 * u, ic = lo;  // row j0 + jr of C, column i0 + ic
+            const int64_t j = j0 + jr, i = i0 + ic;
+            if (j < n && i < m) {
+                double *c = C + j * ldc + i;
+                const double v = Ts[jr][ic];
+                *c = beta == 0.0 ? alpha * v : __builtin_fma(alpha, v, beta * *c);
+            }
+        }
+    }
 }
 constexpr size_t kGemmLds = 2 * 64 * (64 + 4) * sizeof(double);
 
