@@ -1477,7 +1477,7 @@ __global__ __launch_bounds__(256) void als_aug_step_kernel(AugStep a)
     double(*As)[kAugPitch] = reinterpret_cast<double(*)[kAugPitch]>(smem);  // As[t][r] = A(r, t)
     double(*Bs)[kAugPitch] =
         reinterpret_cast<double(*)[kAugPitch]>(smem + 64 * kAugPitch * sizeof(double));
-    if (*a.flag) return;
+    __shared__ int sflag;
     const int k = a.k;
     const int x = blockIdx.x, y = blockIdx.y;
     const int j = k + x;
@@ -1506,7 +1506,9 @@ __global__ __launch_bounds__(256) void als_aug_step_kernel(AugStep a)
     const int r16 = lane & 15, q = lane >> 4;
     const int tl = tid & 63, th = tid >> 6;  // load mapping: 64 along the row, 4 rows per pass
     // A operand: C(r0 + r, k0 + t); B operand: W_k (panel) or Z_k (trailing),
-    // both read along their rows by consecutive threads
+    // both read along their rows by consecutive threads.  (The failure word
+    // is read once for the workgroup while these loads are in flight; they
+    // stay inside the matrices either way, and nothing is stored past it.)
     {
         double va[16], vb[16];
         const double *Bsrc = x == 0 ? a.W + k0 * 64 : a.Z + (k & 1) * 4096;
@@ -1516,6 +1518,7 @@ __global__ __launch_bounds__(256) void als_aug_step_kernel(AugStep a)
             va[u] = (r < nr && tl < kn) ? C[(r0 + r) * R + k0 + tl] : 0.0;
             vb[u] = (r < kn && tl < kn) ? Bsrc[r * 64 + tl] : 0.0;
         }
+        if (flag_once(a.flag, &sflag)) return;
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
             const int r = th + 4 * u;
@@ -1575,6 +1578,17 @@ __global__ __launch_bounds__(256) void als_aug_step_kernel(AugStep a)
                 As[wc + 16 * yy + r16][wr + 16 * xx + 4 * e + q] = acc[xx][yy][e];
 #pragma unroll
     for (int u = 0; u < 16; ++u) Bs[tl][th + 4 * u] = vb[u];
+    // this thread's entries of C(i, j) go out before the second product
+    double cv[16];
+#pragma unroll
+    for (int xx = 0; xx < 2; ++xx)
+#pragma unroll
+        for (int yy = 0; yy < 2; ++yy)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = wr + 16 * xx + 4 * e + q, c = wc + 16 * yy + r16;
+                cv[(xx * 2 + yy) * 4 + e] = (r < nr && c < jn) ? C[(r0 + r) * R + j0 + c] : 0.0;
+            }
     __syncthreads();
     product();
     // the next diagonal block's tile: its new values also go to LDS (after
@@ -1590,9 +1604,8 @@ __global__ __launch_bounds__(256) void als_aug_step_kernel(AugStep a)
             for (int e = 0; e < 4; ++e) {
                 const int r = wr + 16 * xx + 4 * e + q, c = wc + 16 * yy + r16;
                 if (r < nr && c < jn) {
-                    double *p = C + (r0 + r) * R + j0 + c;
-                    const double v = *p - acc[xx][yy][e];
-                    *p = v;
+                    const double v = cv[(xx * 2 + yy) * 4 + e] - acc[xx][yy][e];
+                    C[(r0 + r) * R + j0 + c] = v;
                     if (next_diag) Ts[r * 65 + c] = v;
                 }
             }
