@@ -1270,21 +1270,25 @@ __global__ __launch_bounds__(256) void als_hadamard_kernel(const double *__restr
     A[e] = v;
 }
 
-// Pivot p = 32 ph + PP of the diagonal kernel below (PP a compile-time
-// constant, so that the register holding column p, the LDS buffer and the
-// next pivot's column are fixed at compile time).
+// Pivot p = 16 pq + PP of the diagonal kernel below (PP a compile-time
+// constant, so that the registers of column p, the LDS buffer and the next
+// pivot's column are fixed at compile time; pq, the wave holding column p, is
+// uniform).  Lane i holds row i of B (b) and of the identity rows (c) in the
+// wave's 16 columns.
 template <int PP>
-__device__ __forceinline__ void chol_aug_pivot(double (&a)[32], bool &bad, int ph, int i, int half,
-                                               int part, double (*colB)[64], double (*colI)[64])
+__device__ __forceinline__ void chol_aug_pivot(double (&b)[16], double (&c)[16], bool &bad, int pq,
+                                               int i, int wave, double (*colB)[64],
+                                               double (*colI)[64])
 {
-    constexpr int b = PP & 1, pn = (PP + 1) & 31;
-    const int p = 32 * ph + PP;
+    constexpr int buf = PP & 1, pn = (PP + 1) & 15;
+    const int p = 16 * pq + PP;
+    const int owner_next = pq + (PP == 15 ? 1 : 0);
     __syncthreads();
-    const double d = colB[b][p];
-    double bp[32];
+    const double d = colB[buf][p];
+    double lp[16];  // B(j, p) = B(p, j) for this wave's columns (zero before p)
 #pragma unroll
-    for (int jj = 0; jj < 32; ++jj) bp[jj] = colB[b][32 * half + jj];
-    const double own = part == 0 ? colB[b][i] : colI[b][i];
+    for (int jj = 0; jj < 16; ++jj) lp[jj] = colB[buf][16 * wave + jj];
+    const double ownb = colB[buf][i], ownc = colI[buf][i];
     bad = bad || !(d > 0.0);
     // 1 / sqrt(d) from the hardware estimate and two Newton steps
     // (y <- y + y (1 - d y^2) / 2), then 1 / d as its square
@@ -1294,55 +1298,59 @@ __device__ __forceinline__ void chol_aug_pivot(double (&a)[32], bool &bad, int p
         const double e = __builtin_fma(-d * y, y, 1.0);
         y = __builtin_fma(0.5 * y, e, y);
     }
-    const double t = own * (y * y);
-    // the next pivot's column first, so that its owner's LDS write is on its
-    // way while the other columns are updated
-    a[pn] = __builtin_fma(-t, bp[pn], a[pn]);
-    if (p + 1 < 64 && half == ((p + 1) >> 5)) {
-        if (part == 0)
-            colB[b ^ 1][i] = i >= p + 1 ? a[pn] : 0.0;
-        else
-            colI[b ^ 1][i] = a[pn];
+    const double rd = y * y;
+    const double tb = ownb * rd, tc = ownc * rd;
+    // the next pivot's column first, so that its owner's LDS writes are on
+    // their way while the other columns are updated
+    b[pn] = __builtin_fma(-tb, lp[pn], b[pn]);
+    c[pn] = __builtin_fma(-tc, lp[pn], c[pn]);
+    if (p + 1 < 64 && wave == owner_next) {
+        colB[buf ^ 1][i] = i >= p + 1 ? b[pn] : 0.0;
+        colI[buf ^ 1][i] = c[pn];
     }
     // columns before p read zeros (finished); entry p of an identity row is
-    // set below
+    // set below (B's entry p is not needed again)
 #pragma unroll
-    for (int jj = 0; jj < 32; ++jj)
-        if (jj != pn) a[jj] = __builtin_fma(-t, bp[jj], a[jj]);
-    if (part == 1 && half == ph) a[PP] = own * y;
+    for (int jj = 0; jj < 16; ++jj)
+        if (jj != pn) {
+            b[jj] = __builtin_fma(-tb, lp[jj], b[jj]);
+            c[jj] = __builtin_fma(-tc, lp[jj], c[jj]);
+        }
+    if (wave == pq) c[PP] = ownc * y;
     // the pivot's updates are done here, not deferred to where the values are
     // next read (which would keep every pivot's operands live)
 #pragma unroll
-    for (int jj = 0; jj < 32; ++jj) asm volatile("" : "+v"(a[jj]));
+    for (int jj = 0; jj < 16; ++jj) {
+        asm volatile("" : "+v"(b[jj]));
+        asm volatile("" : "+v"(c[jj]));
+    }
 }
 template <int... PP>
-__device__ __forceinline__ void chol_aug_pivots(std::integer_sequence<int, PP...>, double (&a)[32],
-                                                bool &bad, int ph, int i, int half, int part,
-                                                double (*colB)[64], double (*colI)[64])
+__device__ __forceinline__ void chol_aug_pivots(std::integer_sequence<int, PP...>, double (&b)[16],
+                                                double (&c)[16], bool &bad, int pq, int i,
+                                                int wave, double (*colB)[64], double (*colI)[64])
 {
-    (chol_aug_pivot<PP>(a, bad, ph, i, half, part, colB, colI), ...);
+    (chol_aug_pivot<PP>(b, c, bad, pq, i, wave, colB, colI), ...);
 }
 
 // The diagonal block B = A(k0 .. k0 + nb - 1, same columns) of A (R x R,
-// row-major: the current Schur complement), nb = min(64, R - k0): its
-// Cholesky factor's inverse transpose X = L_kk^{-T} to W rows k0 .. k0 + nb
-// - 1 (pitch 64) and Z = X X^T = B^{-1} to Z (64 x 64, pitch 64, zero
-// outside nb x nb), so that the block step below needs products only.  X is
+// row-major: the current Schur complement), nb = min(64, R - k0), at Ab with
+// row stride lda (global memory, or LDS when the block step below runs it;
+// 64 x 64 entries are read, so a block narrower than 64 comes padded with the
+// identity's rows and columns, whose pivots are 1): its Cholesky factor's
+// inverse transpose X = L_kk^{-T} to W rows k0 .. k0 + nb - 1 (pitch 64;
+// zero in columns past nb) and Z = X X^T = B^{-1} to Z (64 x 64, pitch 64,
+// zero outside nb x nb), so that the block step needs products only.  X is
 // found as the rows of the identity appended below B and carried through
 // B's right-looking factorization (their forward substitution), so one chain
-// of 64 pivots gives both: pivot p with d = B(p, p) and l(j) = B(j, p) /
-// sqrt(d) takes B(i, j) -= l(i) l(j) and, for an identity row, sets its
-// entry p to C(i, p) / sqrt(d) and takes C(i, j) -= C(i, p) l(j) / sqrt(d)
-// (j > p).  Rows and columns past nb are the identity's (pivots 1).  Waves 0
-// and 1 hold columns 0-31 and 32-63 of B's rows, waves 2 and 3 those of the
-// identity rows (lane i: row i); pivot p's column of each goes to every wave
-// through LDS (two buffers, one barrier per pivot), and 1 / sqrt(d) comes
-// from the hardware estimate refined by Newton steps, 1 / d as its square
-// (the chain of pivots is the kernel's critical path).  A pivot that is not
-// positive sets the flag to 1.
-// (The work of the kernel for the block at Ab, row stride lda -- global
-// memory, or LDS when the block step below runs it -- with LDS buffers colB,
-// colI (2 x 64 each) and Xs (64 x 65).)
+// of 64 pivots gives both: pivot p with d = B(p, p) takes B(i, j) -=
+// B(i, p) B(p, j) / d and C(i, j) -= C(i, p) B(p, j) / d for j > p, and sets
+// C(i, p) to C(i, p) / sqrt(d).  Wave w holds columns 16 w .. 16 w + 15 of
+// both B's row and the identity row of its lane; pivot p's column of each
+// goes to every wave through LDS (two buffers, one barrier per pivot), so a
+// lane reads 16 of B's entries per pivot.  A pivot that is not positive sets
+// the flag to 1.  LDS: colB, colI (2 x 64 each), Xs (64 x 65, which may be
+// the block's own LDS copy).
 __device__ __forceinline__ void chol_diag_block(const double *Ab, int64_t lda, int nb, int64_t k0,
                                                 double *__restrict__ W, double *__restrict__ Z,
                                                 int *__restrict__ flag, double (*colB)[64],
@@ -1350,42 +1358,40 @@ __device__ __forceinline__ void chol_diag_block(const double *Ab, int64_t lda, i
 {
     const int i = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int part = wave >> 1, half = wave & 1;
-    const bool rin = i < nb;
-    // every lane loads (a clamped, in-range address) and keeps the value
-    // only for B's rows inside the block: no load sits under a branch
-    double a[32];
-    const double *Ar = Ab + (rin ? i : 0) * lda;
-    const bool keep = part == 0 && rin;
+    double b[16], c[16];
+    {
+        const double *Ar = Ab + i * lda + 16 * wave;
 #pragma unroll
-    for (int jj = 0; jj < 32; ++jj) {
-        const int j = 32 * half + jj;
-        const double g = Ar[j < nb ? j : 0];
-        a[jj] = (keep && j < nb) ? g : (i == j ? 1.0 : 0.0);
+        for (int jj = 0; jj < 16; ++jj) {
+            b[jj] = Ar[jj];
+            c[jj] = i == 16 * wave + jj ? 1.0 : 0.0;
+        }
     }
-    // the values are formed here (the selects are not carried into the loop)
 #pragma unroll
-    for (int jj = 0; jj < 32; ++jj) asm volatile("" : "+v"(a[jj]));
+    for (int jj = 0; jj < 16; ++jj) {
+        asm volatile("" : "+v"(b[jj]));
+        asm volatile("" : "+v"(c[jj]));
+    }
     // pivot 0's column
-    if (half == 0) {
-        if (part == 0)
-            colB[0][i] = a[0];
-        else
-            colI[0][i] = a[0];
+    if (wave == 0) {
+        colB[0][i] = b[0];
+        colI[0][i] = c[0];
     }
     bool bad = false;
-    for (int ph = 0; ph < 2; ++ph)
-        chol_aug_pivots(std::make_integer_sequence<int, 32>(), a, bad, ph, i, half, part, colB, colI);
+    for (int pq = 0; pq < 4; ++pq)
+        chol_aug_pivots(std::make_integer_sequence<int, 16>(), b, c, bad, pq, i, wave, colB, colI);
+    __syncthreads();  // (every wave is past its last read of Xs's memory)
     if (bad) {
         if (threadIdx.x == 0) *flag = 1;
         return;
     }
-    if (part == 1) {
+    {
+        const bool rin = i < nb;
 #pragma unroll
-        for (int jj = 0; jj < 32; ++jj) {
-            const int j = 32 * half + jj;
-            Xs[i * 65 + j] = a[jj];
-            if (rin && j < nb) W[(k0 + i) * 64 + j] = a[jj];
+        for (int jj = 0; jj < 16; ++jj) Xs[i * 65 + 16 * wave + jj] = c[jj];
+        if (rin) {
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) W[(k0 + i) * 64 + 16 * wave + jj] = c[jj];
         }
     }
     __syncthreads();
@@ -1407,8 +1413,8 @@ __device__ __forceinline__ void chol_diag_block(const double *Ab, int64_t lda, i
             for (int x = 0; x < 2; ++x) {
                 const int r = wr + 16 * x + r16;
                 av[x] = (r < nb && t < nb) ? Xs[r * 65 + t] : 0.0;
-                const int c = wc + 16 * x + r16;
-                bv[x] = (c < nb && t < nb) ? Xs[c * 65 + t] : 0.0;
+                const int cc = wc + 16 * x + r16;
+                bv[x] = (cc < nb && t < nb) ? Xs[cc * 65 + t] : 0.0;
             }
 #pragma unroll
             for (int x = 0; x < 2; ++x)
@@ -1436,8 +1442,8 @@ __global__ __launch_bounds__(256) void als_chol_diag_kernel(const double *__rest
     __shared__ double colI[2][64];  // C(:, p) of the identity rows
     __shared__ double Xs[64 * 65];
     if (*flag) return;
-    chol_diag_block(A + k0 * R + k0, R, (int)min<int64_t>(64, R - k0), k0, W, Z, flag, colB, colI,
-                    Xs);
+    // (a whole 64-wide block: the caller launches it for R - k0 >= 64 only)
+    chol_diag_block(A + k0 * R + k0, R, 64, k0, W, Z, flag, colB, colI, Xs);
 }
 
 // One block step k of the factorization V = L L^T carried out on the
@@ -1607,14 +1613,16 @@ __global__ __launch_bounds__(256) void als_aug_step_kernel(AugStep a)
                     const double v = cv[(xx * 2 + yy) * 4 + e] - acc[xx][yy][e];
                     C[(r0 + r) * R + j0 + c] = v;
                     if (next_diag) Ts[r * 65 + c] = v;
+                } else if (next_diag) {
+                    Ts[r * 65 + c] = r == c ? 1.0 : 0.0;  // a narrow last block's padding
                 }
             }
     if (next_diag) {
         __syncthreads();
-        double *Xs = Ts + 64 * 65;
-        double(*colB)[64] = reinterpret_cast<double(*)[64]>(Xs + 64 * 65);
+        double(*colB)[64] = reinterpret_cast<double(*)[64]>(Ts + 64 * 65);
         double(*colI)[64] = colB + 2;
-        chol_diag_block(Ts, 65, jn, j0, a.W, a.Z + ((k + 1) & 1) * 4096, a.flag, colB, colI, Xs);
+        // (the block is read into registers before Xs, at Ts, is written)
+        chol_diag_block(Ts, 65, jn, j0, a.W, a.Z + ((k + 1) & 1) * 4096, a.flag, colB, colI, Ts);
     }
 }
 
@@ -2035,7 +2043,9 @@ hipError_t launch_update_blocked(const double *Gall, int order, int n, int64_t R
     e = hipMemcpyAsync(CM, M, (size_t)(I * R) * sizeof(double), hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return e;
     AugStep a{CV, CM, CI, YM, YI, W, Z, R, I, 0, nblk, (int)mblk, flag};
-    // the first diagonal block; each step forms the next one's
+    // the first diagonal block (a whole one: R > 64); each step forms the
+    // next one's
+    if (R <= 64) return hipErrorInvalidValue;
     hipLaunchKernelGGL(als_chol_diag_kernel, dim3(1), dim3(256), 0, s, CV, R, (int64_t)0, W, Z,
                        flag);
     for (int k = 0; k < nblk; ++k) {
