@@ -1650,8 +1650,12 @@ __global__ __launch_bounds__(256) void als_aug_init_kernel(double *__restrict__ 
 // kGemmFull; kGemmSym (C symmetric, m = n: the tiles on and below the
 // diagonal are formed, each one below also stored transposed above); or
 // kGemmUpperB (B(t, j) = 0 for t below j's 64-column tile: the sum for that
-// tile starts there).  C must not overlap A or B.  The sums over t follow
-// the matrix cores' fixed order, so results are deterministic.
+// tile starts there).  kseg > 0 (kGemmFull or kGemmUpperB, beta = 0): the
+// sum of a tile is cut into segments of kseg chunks, workgroup z taking
+// segment z and storing its partial sum to part + z m n (m x n, pitch n);
+// als_gemm_segments_kernel then adds a tile's segments in order.  C must not
+// overlap A or B.  The sums over t follow the matrix cores' fixed order, so
+// results are deterministic.
 constexpr int kGemmFull = 0, kGemmSym = 1, kGemmUpperB = 2;
 typedef double gdx4 __attribute__((ext_vector_type(4)));
 
@@ -1664,7 +1668,8 @@ __global__ __launch_bounds__(256, 2) void als_mfma_gemm_kernel(double *__restric
                                                             const TA *__restrict__ B, int64_t sbt,
                                                             int64_t sbj, int64_t m, int64_t n,
                                                             int64_t K, double alpha, double beta,
-                                                            int shape,
+                                                            int shape, int kseg,
+                                                            double *__restrict__ part,
                                                             const int *__restrict__ flag)
 {
     constexpr int TM = 64, TN = 64, KC = 64, PA = TM + 4, NL = TM * KC / 256;
@@ -1711,9 +1716,12 @@ __global__ __launch_bounds__(256, 2) void als_mfma_gemm_kernel(double *__restric
             vb[u] = okb ? (double)*reinterpret_cast<const TA *>(pb) : 0.0;
         }
     };
-    const int64_t kbeg = shape == kGemmUpperB ? (j0 < K ? j0 : K) : 0;
+    const int64_t kfirst = shape == kGemmUpperB ? (j0 < K ? j0 : K) : 0;
+    const int64_t kbeg = kseg > 0 ? kfirst + (int64_t)blockIdx.z * kseg * KC : kfirst;
+    if (blockIdx.z > 0 && kbeg >= K) return;  // past this tile's sum
+    const int64_t kend = kseg > 0 ? min(K, kbeg + (int64_t)kseg * KC) : K;
     fetch(kbeg);
-    for (int64_t t0 = kbeg; t0 < K; t0 += KC) {
+    for (int64_t t0 = kbeg; t0 < kend; t0 += KC) {
         __syncthreads();  // the previous chunk's operands are read
 #pragma unroll
         for (int u = 0; u < NL; ++u) {
@@ -1724,7 +1732,7 @@ __global__ __launch_bounds__(256, 2) void als_mfma_gemm_kernel(double *__restric
         }
         __syncthreads();
         // the next chunk's loads go out before this chunk's matrix-core work
-        if (t0 + KC < K) fetch(t0 + KC);
+        if (t0 + KC < kend) fetch(t0 + KC);
 #pragma unroll 4
         for (int kk = 0; kk < KC; kk += 4) {
             const int k = kk + q;
@@ -1745,9 +1753,13 @@ __global__ __launch_bounds__(256, 2) void als_mfma_gemm_kernel(double *__restric
             for (int e = 0; e < 4; ++e) {
                 const int64_t i = i0 + wr + 16 * x + 4 * e + q, j = j0 + wc + 16 * y + r16;
                 if (i < m && j < n) {
-                    double *c = C + i * ldc + j;
                     const double v = acc[x][y][e];
-                    *c = beta == 0.0 ? alpha * v : __builtin_fma(alpha, v, beta * *c);
+                    if (kseg > 0) {
+                        part[(int64_t)blockIdx.z * m * n + i * n + j] = v;
+                    } else {
+                        double *c = C + i * ldc + j;
+                        *c = beta == 0.0 ? alpha * v : __builtin_fma(alpha, v, beta * *c);
+                    }
                 }
             }
     if (shape == kGemmSym && ti != tj) {
@@ -1778,36 +1790,89 @@ constexpr size_t kGemmLds = 2 * 64 * (64 + 4) * sizeof(double);
 
 hipError_t allow_large_lds(const void *k);
 
-// Launches the product above on 64 x 64 tiles.
+// C(i, j) = alpha sum_{z < segments of j's tile} part[z m n + i n + j], the
+// segments added in order.
+__global__ __launch_bounds__(256) void als_gemm_segments_kernel(double *__restrict__ C, int64_t ldc,
+                                                                const double *__restrict__ part,
+                                                                int64_t m, int64_t n, int64_t K,
+                                                                int shape, int kseg, double alpha,
+                                                                const int *__restrict__ flag)
+{
+    if (*flag) return;
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= m * n) return;
+    const int64_t i = e / n, j = e - (e / n) * n;
+    const int64_t j0 = j / 64 * 64;
+    const int64_t kfirst = shape == kGemmUpperB ? (j0 < K ? j0 : K) : 0;
+    const int64_t seg = (int64_t)kseg * 64;
+    const int64_t nz = kfirst < K ? (K - kfirst + seg - 1) / seg : 1;
+    double v = 0.0;
+    for (int64_t z = 0; z < nz; ++z) v += part[z * m * n + e];
+    C[i * ldc + j] = alpha * v;
+}
+
+// Launches the product above on 64 x 64 tiles.  part, part_elems: room for
+// segment partial sums (nullptr / 0: none).  With
+// room for at least two m x n partials, a long sum (kGemmFull or kGemmUpperB
+// with beta = 0) is cut into segments so that the launch has enough
+// workgroups of balanced length.
 template <typename TA>
 hipError_t launch_gemm(double *C, int64_t ldc, const TA *A, int64_t sai, int64_t sat, const TA *B,
                        int64_t sbt, int64_t sbj, int64_t m, int64_t n, int64_t K, double alpha,
-                       double beta, int shape, const int *flag, hipStream_t s)
+                       double beta, int shape, const int *flag, hipStream_t s,
+                       double *part = nullptr, int64_t part_elems = 0)
 {
     const int64_t gx = (n + 63) / 64, gy = (m + 63) / 64;
     if (gx > INT32_MAX || gy > 65535) return hipErrorInvalidValue;  // grid limits
     const hipError_t a = allow_large_lds(reinterpret_cast<const void *>(als_mfma_gemm_kernel<TA>));
     if (a != hipSuccess) return a;
-    hipLaunchKernelGGL(als_mfma_gemm_kernel<TA>, dim3((unsigned)gx, (unsigned)gy), dim3(256),
-                       kGemmLds, s, C, ldc, A, sai, sat, B, sbt, sbj, m, n, K, alpha, beta, shape,
-                       flag);
+    // up to four segments when fewer than 512 tiles would each run a long sum
+    // (as many as the partial space holds)
+    int kseg = 0;
+    int64_t nseg = 1;
+    const int64_t nchunk = (K + 63) / 64;
+    if (part && shape != kGemmSym && beta == 0.0 && gx * gy < 512 && nchunk > 8 && m * n > 0) {
+        const int64_t ns = std::min<int64_t>({(int64_t)4, part_elems / (m * n), nchunk / 4});
+        if (ns >= 2) {
+            kseg = (int)((nchunk + ns - 1) / ns);
+            nseg = (nchunk + kseg - 1) / kseg;
+        }
+    }
+    hipLaunchKernelGGL(als_mfma_gemm_kernel<TA>, dim3((unsigned)gx, (unsigned)gy, (unsigned)nseg),
+                       dim3(256), kGemmLds, s, C, ldc, A, sai, sat, B, sbt, sbj, m, n, K, alpha, beta,
+                       shape, kseg, part, flag);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || kseg == 0) return e;
+    hipLaunchKernelGGL(als_gemm_segments_kernel, dim3((unsigned)((m * n + 255) / 256)), dim3(256), 0,
+                       s, C, ldc, part, m, n, K, shape, kseg, alpha, flag);
     return hipGetLastError();
 }
 
-// sum_i M(i, r) U(i, r) for every column r (rows in order), one thread per column.
+// sum_i M(i, r) U(i, r) for every column r.  A workgroup takes 16 columns;
+// thread (c, g) sums rows g, g + 16, ... of column c in order, and the 16
+// group sums are added in group order (a fixed order).
 template <typename T>
 __global__ __launch_bounds__(256) void als_colsum_kernel(const double *__restrict__ M,
                                                          const T *__restrict__ U, int64_t I,
                                                          int64_t R, double *__restrict__ out,
                                                          const int *__restrict__ flag)
 {
+    __shared__ double part[16][17];
     if (*flag) return;
-    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (r >= R) return;
+    const int c = threadIdx.x & 15, g = threadIdx.x >> 4;
+    const int64_t r = (int64_t)blockIdx.x * 16 + c;
     double s = 0.0;
-#pragma unroll 8
-    for (int64_t i = 0; i < I; ++i) s += M[i * R + r] * (double)U[i * R + r];
-    out[r] = s;
+    if (r < R) {
+#pragma unroll 4
+        for (int64_t i = g; i < I; i += 16) s += M[i * R + r] * (double)U[i * R + r];
+    }
+    part[g][c] = s;
+    __syncthreads();
+    if (g == 0 && r < R) {
+        double t = part[0][c];
+        for (int h = 1; h < 16; ++h) t += part[h][c];
+        out[r] = t;
+    }
 }
 
 // ||model||^2 partials for large R: workgroup w sums the entries
@@ -2005,7 +2070,7 @@ hipError_t launch_fit(const double *M, const T *Ulast, int64_t Ilast, const doub
                      fit.have_prev, fit.out_fit, fit.out_flag, fit.out_seq, fit.seq_val};
     const double *colsum = nullptr;
     if (R > 256) {
-        hipLaunchKernelGGL(als_colsum_kernel<T>, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, s,
+        hipLaunchKernelGGL(als_colsum_kernel<T>, dim3((unsigned)((R + 15) / 16)), dim3(256), 0, s,
                            M, Ulast, Ilast, R, colsum_buf, flag);
         colsum = colsum_buf;
     }
@@ -2056,8 +2121,10 @@ hipError_t launch_update_blocked(const double *Gall, int order, int n, int64_t R
     }
     // U = Y_M Y_I^T: A(i, t) = Y_M[i R + t], B(t, j) = Y_I[j R + t]
     // (L^{-T} is upper triangular: B(t, j) = Y_I(j, t) = 0 for t < j)
+    // (the identity rows' working copy is free after the last step: it holds
+    // the segment partial sums)
     e = launch_gemm<double>(CM, R, YM, R, (int64_t)1, YI, (int64_t)1, R, I, R, R, 1.0, 0.0,
-                            kGemmUpperB, flag, s);
+                            kGemmUpperB, flag, s, CI, R * R);
     if (e != hipSuccess) return e;
     return hipGetLastError();
 }
