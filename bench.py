@@ -376,7 +376,10 @@ def config_entry(w, sweep_ms, warm, cold, peaks):
 def als_leg(w, iters):
     """CP-ALS: time per sweep of the whole driver (per mode: MTTKRP, Hadamard
     of Grams, Cholesky, row solves, normalization, Gram refresh; then the fit,
-    one read-back), and the share of it the MTTKRP launches take."""
+    one read-back), and the share of it the MTTKRP launches take.  A call also
+    has a fixed set-up (||X||^2, the starting Grams, the host's set-up), so the
+    steady per-sweep time is reported as well: the difference between an
+    `iters`-sweep call and a one-sweep call, over iters - 1."""
     import torch
 
     from mttkrp_matrix_free_amd import api
@@ -385,12 +388,19 @@ def als_leg(w, iters):
     U0 = [u.clone() for u in w.U]
     Ua = [u.clone() for u in U0]
     api.cp_als(w.X, Ua, iters=min(2, iters), ws=ws_als, stream=w.stream)  # warm-up
-    Ua = [u.clone() for u in U0]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    _, hist, done, st = api.cp_als(w.X, Ua, iters=iters, ws=ws_als, stream=w.stream)
-    torch.cuda.synchronize()
-    t_als = (time.perf_counter() - t0) / max(1, done)
+
+    def timed_call(n):
+        Ub = [u.clone() for u in U0]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        out = api.cp_als(w.X, Ub, iters=n, ws=ws_als, stream=w.stream)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, out, Ub
+
+    t_one = timed_call(1)[0] if iters > 1 else None
+    t_call, (_, hist, done, st), Ua = timed_call(iters)
+    t_als = t_call / max(1, done)
+    t_steady = (t_call - t_one) / (done - 1) if (t_one is not None and done > 1) else None
     # the same iterations' MTTKRP launches alone, mode after mode on one
     # stream as the driver issues them
     ev_c = torch.cuda.Event(enable_timing=True)
@@ -403,10 +413,15 @@ def als_leg(w, iters):
     torch.cuda.synchronize()
     t_mt = ev_c.elapsed_time(ev_d) / 1e3 / iters
     del ws_als
-    return {"ms_per_iter": round(t_als * 1e3, 4), "iters": int(done), "status": int(st),
-            "final_fit": round(float(hist[done - 1]), 6) if done else None,
-            "mttkrp_ms_per_iter": round(t_mt * 1e3, 4),
-            "mttkrp_share": round(t_mt / t_als, 3)}
+    out = {"ms_per_iter": round(t_als * 1e3, 4), "iters": int(done), "status": int(st),
+           "final_fit": round(float(hist[done - 1]), 6) if done else None,
+           "mttkrp_ms_per_iter": round(t_mt * 1e3, 4),
+           "mttkrp_share": round(t_mt / t_als, 3)}
+    if t_steady is not None and t_steady > 0:
+        out["ms_per_sweep_steady"] = round(t_steady * 1e3, 4)
+        out["mttkrp_share_steady"] = round(t_mt / t_steady, 3)
+        out["call_setup_ms"] = round((t_one - t_steady) * 1e3, 4)
+    return out
 
 
 def cpu_baseline(w, budget_s):
