@@ -1454,7 +1454,9 @@ __global__ __launch_bounds__(256) void als_chol_diag_kernel(const double *__rest
 //   panel, the M rows and the identity rows:
 //       Y(i, k) = C(i, k) W_k
 // The identity rows' block b is active from step b on (column blocks before
-// b of L^{-T} are zero).  After the last step Y_M = M L^{-T} (the forward
+// b of L^{-T} are zero); until then its entries are the identity's, so at
+// step b they are formed rather than read (CI needs no set-up).  After the
+// last step Y_M = M L^{-T} (the forward
 // substitution) and Y_I = L^{-T}, so U = M V^{-1} = Y_M Y_I^T.  Each task is
 // a 64 x 64 tile, two 64 x 64 x 64 products on the matrix cores (the panel
 // one), operands staged in LDS as in the tiled product below; column block k
@@ -1518,10 +1520,13 @@ __global__ __launch_bounds__(256) void als_aug_step_kernel(AugStep a)
     {
         double va[16], vb[16];
         const double *Bsrc = x == 0 ? a.W + k0 * 64 : a.Z + (k & 1) * 4096;
+        // (an identity row block at its own step is still the identity)
+        const bool eye = sec == 1 && rb == k;
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
             const int r = th + 4 * u;
-            va[u] = (r < nr && tl < kn) ? C[(r0 + r) * R + k0 + tl] : 0.0;
+            va[u] = (r < nr && tl < kn) ? (eye ? (r == tl ? 1.0 : 0.0) : C[(r0 + r) * R + k0 + tl])
+                                        : 0.0;
             vb[u] = (r < kn && tl < kn) ? Bsrc[r * 64 + tl] : 0.0;
         }
         if (flag_once(a.flag, &sflag)) return;
@@ -1584,7 +1589,10 @@ __global__ __launch_bounds__(256) void als_aug_step_kernel(AugStep a)
                 As[wc + 16 * yy + r16][wr + 16 * xx + 4 * e + q] = acc[xx][yy][e];
 #pragma unroll
     for (int u = 0; u < 16; ++u) Bs[tl][th + 4 * u] = vb[u];
-    // this thread's entries of C(i, j) go out before the second product
+    // this thread's entries of C(i, j) go out before the second product (an
+    // identity row block's entries right of its own block are still zero at
+    // its own step)
+    const bool zero_old = sec == 1 && rb == k;
     double cv[16];
 #pragma unroll
     for (int xx = 0; xx < 2; ++xx)
@@ -1593,7 +1601,8 @@ __global__ __launch_bounds__(256) void als_aug_step_kernel(AugStep a)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = wr + 16 * xx + 4 * e + q, c = wc + 16 * yy + r16;
-                cv[(xx * 2 + yy) * 4 + e] = (r < nr && c < jn) ? C[(r0 + r) * R + j0 + c] : 0.0;
+                cv[(xx * 2 + yy) * 4 + e] =
+                    (r < nr && c < jn && !zero_old) ? C[(r0 + r) * R + j0 + c] : 0.0;
             }
     __syncthreads();
     product();
@@ -1624,20 +1633,6 @@ __global__ __launch_bounds__(256) void als_aug_step_kernel(AugStep a)
         // (the block is read into registers before Xs, at Ts, is written)
         chol_diag_block(Ts, 65, jn, j0, a.W, a.Z + ((k + 1) & 1) * 4096, a.flag, colB, colI, Ts);
     }
-}
-
-// C = [V rows untouched; identity rows] and Y_I = 0 (entries of L^{-T}
-// below its diagonal blocks are never written by the steps).
-__global__ __launch_bounds__(256) void als_aug_init_kernel(double *__restrict__ CI,
-                                                           double *__restrict__ YI, int64_t R,
-                                                           const int *__restrict__ flag)
-{
-    if (*flag) return;
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (e >= R * R) return;
-    const int64_t r = e / R;
-    CI[e] = (e - r * R) == r ? 1.0 : 0.0;
-    YI[e] = 0.0;
 }
 
 // C (m x n, leading dimension ldc) = beta C + alpha A B on the fp64 matrix
@@ -2086,8 +2081,8 @@ hipError_t launch_fit(const double *M, const T *Ulast, int64_t Ilast, const doub
 }
 
 // U_new = M V^{-1} for ranks past the one-workgroup update (R > 64), by
-// 64-wide column blocks: V = Hadamard_{m != n} G_m into CV, M into CM, the
-// identity into CI, then the first diagonal block (W_0, Z_0) and per block
+// 64-wide column blocks: V = Hadamard_{m != n} G_m into CV, M into CM, then
+// the first diagonal block (W_0, Z_0) and per block
 // k one step launch (panels and trailing updates of every row block, and
 // block k + 1's diagonal kernel), and at the end U = Y_M Y_I^T into CM
 // (which the caller passes as U_new).
@@ -2103,8 +2098,6 @@ hipError_t launch_update_blocked(const double *Gall, int order, int n, int64_t R
     const int64_t RR = R * R;
     hipLaunchKernelGGL(als_hadamard_kernel, dim3((unsigned)((RR + 255) / 256)), dim3(256), 0, s,
                        Gall, order, n, R, CV, flag);
-    hipLaunchKernelGGL(als_aug_init_kernel, dim3((unsigned)((RR + 255) / 256)), dim3(256), 0, s,
-                       CI, YI, R, flag);
     e = hipMemcpyAsync(CM, M, (size_t)(I * R) * sizeof(double), hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return e;
     AugStep a{CV, CM, CI, YM, YI, W, Z, R, I, 0, nblk, (int)mblk, flag};
