@@ -638,9 +638,10 @@ int cp_als_entry(const T *X, const int64_t *dims, int order, int64_t rank, T *co
                 if (!ok(launch_chol(G, order, n, R, Lc, flag, s))) return MTTKRP_EHIP;
                 if (!ok(launch_solve(M, Lc, dims[n], R, Unew, flag, s))) return MTTKRP_EHIP;
             } else {
-                // 64-wide column blocks: per block the diagonal factor and
-                // inverse by one wave, then one launch of tiled products for
-                // the panels and trailing updates of V, M and the identity
+                // 64-wide column blocks: per block the diagonal block's
+                // factor and inverse by one workgroup, then one launch of
+                // tiled products for the panels and trailing updates of V, M
+                // and the identity
                 if (!ok(launch_update_blocked(G, order, n, R, M, dims[n], Lc, CI, Unew, YI, YM,
                                               Winv, Zk, flag, s)))
                     return MTTKRP_EHIP;
