@@ -55,16 +55,16 @@ def kernel_sources_digest() -> str:
     """sha256 of the MTTKRP kernel sources, their planner and launchers, with
     comments and blank space removed: traffic counters taken on other code no
     longer describe the kernels that run, while an edit of a comment leaves
-    them valid.  The CP-ALS kernels, the ablation baselines, the measurement
-    probes and the C ABI file do not take part in the MTTKRP launches the
-    counters describe."""
+    them valid.  The CP-ALS kernels and their header, the ablation baselines,
+    the measurement probes and the C ABI file do not take part in the MTTKRP
+    launches the counters describe."""
     import glob
     import hashlib
     import re
     h = hashlib.sha256()
     files = sorted(glob.glob(os.path.join(ROOT, "mttkrp_matrix_free_amd", "csrc", "*")))
-    skip = ("als_kernels.hip", "ablation_kernels.hip", "peak_probe.hip", "capi.cpp",
-            "noalloc.hip")
+    skip = ("als_kernels.hip", "als_kernels.hpp", "ablation_kernels.hip", "peak_probe.hip",
+            "capi.cpp", "noalloc.hip")
     for f in files:
         if os.path.isfile(f) and os.path.basename(f) not in skip:
             with open(f, "r", encoding="utf-8") as fh:
