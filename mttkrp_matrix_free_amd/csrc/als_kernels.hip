@@ -1654,10 +1654,11 @@ __global__ __launch_bounds__(256) void als_aug_step_kernel(AugStep a)
 constexpr int kGemmFull = 0, kGemmSym = 1, kGemmUpperB = 2;
 typedef double gdx4 __attribute__((ext_vector_type(4)));
 
-// (Two workgroups per compute unit, as the LDS allows: the registers are
-// held to two waves per SIMD.)
+// (Chunks of 32: the operands take 35 KB of LDS and the registers are held
+// to three waves per SIMD, so three workgroups share a compute unit.)
+constexpr int kGemmKC = 32;
 template <typename TA>
-__global__ __launch_bounds__(256, 2) void als_mfma_gemm_kernel(double *__restrict__ C, int64_t ldc,
+__global__ __launch_bounds__(256, 3) void als_mfma_gemm_kernel(double *__restrict__ C, int64_t ldc,
                                                             const TA *__restrict__ A,
                                                             int64_t sai, int64_t sat,
                                                             const TA *__restrict__ B, int64_t sbt,
@@ -1667,7 +1668,8 @@ __global__ __launch_bounds__(256, 2) void als_mfma_gemm_kernel(double *__restric
                                                             double *__restrict__ part,
                                                             const int *__restrict__ flag)
 {
-    constexpr int TM = 64, TN = 64, KC = 64, PA = TM + 4, NL = TM * KC / 256;
+    constexpr int TM = 64, TN = 64, KC = kGemmKC, PA = TM + 4, NL = TM * KC / 256;
+    static_assert(KC == 32 && NL == 8, "the load mapping below assumes chunks of 32");
     extern __shared__ __align__(16) unsigned char smem[];
     double(*As)[PA] = reinterpret_cast<double(*)[PA]>(smem);                  // KC x PA
     double(*Bs)[PA] = reinterpret_cast<double(*)[PA]>(smem + KC * PA * sizeof(double));
@@ -1684,16 +1686,20 @@ __global__ __launch_bounds__(256, 2) void als_mfma_gemm_kernel(double *__restric
 #pragma unroll
         for (int y = 0; y < 2; ++y) acc[x][y] = gdx4{0.0, 0.0, 0.0, 0.0};
     // The unit-stride dimension of each operand runs across consecutive
-    // threads: thread tid takes, for u = 0 .. NL - 1, the element at lane
-    // index tid % 64 along that dimension and tid / 64 + 4 u along the other.
-    // Its byte offset inside the chunk's tile is a fixed 32-bit part (per
+    // threads: along a 64-long dimension (rows of A, columns of B) thread tid
+    // takes index tid % 64 and tid / 64 + 4 u along the chunk's 32; along the
+    // chunk, index tid % 32 and tid / 32 + 8 u along the other (u = 0 .. NL -
+    // 1).  Its byte offset inside the chunk's tile is a fixed 32-bit part (per
     // thread) plus u times a uniform step, so the loads need no per-thread
     // 64-bit addresses.
     const bool a_t = sat == 1, b_c = sbj == 1;
-    const int lo = tid & 63, hi = tid >> 6;
-    const uint32_t voffA = (uint32_t)(((a_t ? hi : lo) * sai + (a_t ? lo : hi) * sat) * (int64_t)sizeof(TA));
-    const uint32_t voffB = (uint32_t)(((b_c ? hi : lo) * sbt + (b_c ? lo : hi) * sbj) * (int64_t)sizeof(TA));
-    const int64_t stepA = 4 * (a_t ? sai : sat), stepB = 4 * (b_c ? sbt : sbj);
+    const int lo = tid & 63, hi = tid >> 6, lo32 = tid & 31, hi32 = tid >> 5;
+    const int ra = a_t ? hi32 : lo, ta = a_t ? lo32 : hi;   // A's (row, t) at u = 0
+    const int tb0 = b_c ? hi : lo32, cb = b_c ? lo : hi32;  // B's (t, column) at u = 0
+    const int dra = a_t ? 8 : 0, dta = a_t ? 0 : 4, dtb = b_c ? 4 : 0, dcb = b_c ? 0 : 8;
+    const uint32_t voffA = (uint32_t)((ra * sai + ta * sat) * (int64_t)sizeof(TA));
+    const uint32_t voffB = (uint32_t)((tb0 * sbt + cb * sbj) * (int64_t)sizeof(TA));
+    const int64_t stepA = dra * sai + dta * sat, stepB = dtb * sbt + dcb * sbj;
     double va[NL], vb[NL];
     // a chunk's operands into registers (zero outside the matrices)
     auto fetch = [&](int64_t t0) {
@@ -1701,11 +1707,11 @@ __global__ __launch_bounds__(256, 2) void als_mfma_gemm_kernel(double *__restric
         const TA *Bb = B + t0 * sbt + j0 * sbj;
 #pragma unroll
         for (int u = 0; u < NL; ++u) {
-            const int r = a_t ? hi + 4 * u : lo, t = a_t ? lo : hi + 4 * u;
+            const int r = ra + dra * u, t = ta + dta * u;
             const bool ok = i0 + r < m && t0 + t < K;
             const char *pa = reinterpret_cast<const char *>(Ab + u * stepA) + voffA;
             va[u] = ok ? (double)*reinterpret_cast<const TA *>(pa) : 0.0;
-            const int c = b_c ? lo : hi + 4 * u, tb = b_c ? hi + 4 * u : lo;
+            const int c = cb + dcb * u, tb = tb0 + dtb * u;
             const bool okb = t0 + tb < K && j0 + c < n;
             const char *pb = reinterpret_cast<const char *>(Bb + u * stepB) + voffB;
             vb[u] = okb ? (double)*reinterpret_cast<const TA *>(pb) : 0.0;
@@ -1720,10 +1726,8 @@ __global__ __launch_bounds__(256, 2) void als_mfma_gemm_kernel(double *__restric
         __syncthreads();  // the previous chunk's operands are read
 #pragma unroll
         for (int u = 0; u < NL; ++u) {
-            const int r = a_t ? hi + 4 * u : lo, t = a_t ? lo : hi + 4 * u;
-            As[t][r] = va[u];
-            const int c = b_c ? lo : hi + 4 * u, tb = b_c ? hi + 4 * u : lo;
-            Bs[tb][c] = vb[u];
+            As[ta + dta * u][ra + dra * u] = va[u];
+            Bs[tb0 + dtb * u][cb + dcb * u] = vb[u];
         }
         __syncthreads();
         // the next chunk's loads go out before this chunk's matrix-core work
@@ -1759,7 +1763,8 @@ __global__ __launch_bounds__(256, 2) void als_mfma_gemm_kernel(double *__restric
             }
     if (shape == kGemmSym && ti != tj) {
         // the transposed tile above the diagonal, through LDS so that
-        // consecutive threads store consecutive entries of a row
+        // consecutive threads store consecutive entries of a row (As and Bs
+        // together hold the 64 x 64 tile)
         double(*Ts)[PA] = As;  // Ts[j - j0][i - i0]
         __syncthreads();       // every wave is done with the operands
 #pragma unroll
@@ -1781,7 +1786,8 @@ __global__ __launch_bounds__(256, 2) void als_mfma_gemm_kernel(double *__restric
         }
     }
 }
-constexpr size_t kGemmLds = 2 * 64 * (64 + 4) * sizeof(double);
+constexpr size_t kGemmLds = 2 * kGemmKC * (64 + 4) * sizeof(double);
+static_assert(2 * kGemmKC >= 64, "the mirrored tile fits the operands' LDS");
 
 hipError_t allow_large_lds(const void *k);
 
@@ -1799,7 +1805,7 @@ __global__ __launch_bounds__(256) void als_gemm_segments_kernel(double *__restri
     const int64_t i = e / n, j = e - (e / n) * n;
     const int64_t j0 = j / 64 * 64;
     const int64_t kfirst = shape == kGemmUpperB ? (j0 < K ? j0 : K) : 0;
-    const int64_t seg = (int64_t)kseg * 64;
+    const int64_t seg = (int64_t)kseg * kGemmKC;
     const int64_t nz = kfirst < K ? (K - kfirst + seg - 1) / seg : 1;
     double v = 0.0;
     for (int64_t z = 0; z < nz; ++z) v += part[z * m * n + e];
@@ -1821,12 +1827,12 @@ hipError_t launch_gemm(double *C, int64_t ldc, const TA *A, int64_t sai, int64_t
     if (gx > INT32_MAX || gy > 65535) return hipErrorInvalidValue;  // grid limits
     const hipError_t a = allow_large_lds(reinterpret_cast<const void *>(als_mfma_gemm_kernel<TA>));
     if (a != hipSuccess) return a;
-    // up to four segments when fewer than 512 tiles would each run a long sum
+    // up to four segments when fewer than 768 tiles would each run a long sum
     // (as many as the partial space holds)
     int kseg = 0;
     int64_t nseg = 1;
-    const int64_t nchunk = (K + 63) / 64;
-    if (part && shape != kGemmSym && beta == 0.0 && gx * gy < 512 && nchunk > 8 && m * n > 0) {
+    const int64_t nchunk = (K + kGemmKC - 1) / kGemmKC;
+    if (part && shape != kGemmSym && beta == 0.0 && gx * gy < 768 && nchunk > 16 && m * n > 0) {
         const int64_t ns = std::min<int64_t>({(int64_t)4, part_elems / (m * n), nchunk / 4});
         if (ns >= 2) {
             kseg = (int)((nchunk + ns - 1) / ns);
