@@ -2096,6 +2096,8 @@ hipError_t launch_update_blocked(const double *Gall, int order, int n, int64_t R
                                  int64_t I, double *CV, double *CI, double *CM, double *YI,
                                  double *YM, double *W, double *Z, int *flag, hipStream_t s)
 {
+    // (the first diagonal block is a whole one only for R > 64)
+    if (R <= 64) return hipErrorInvalidValue;
     const int nblk = (int)((R + 63) / 64);
     const int64_t mblk = (I + 63) / 64;
     if (mblk + 2 * (int64_t)nblk > 65535) return hipErrorInvalidValue;  // grid limit
@@ -2107,9 +2109,7 @@ hipError_t launch_update_blocked(const double *Gall, int order, int n, int64_t R
     e = hipMemcpyAsync(CM, M, (size_t)(I * R) * sizeof(double), hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return e;
     AugStep a{CV, CM, CI, YM, YI, W, Z, R, I, 0, nblk, (int)mblk, flag};
-    // the first diagonal block (a whole one: R > 64); each step forms the
-    // next one's
-    if (R <= 64) return hipErrorInvalidValue;
+    // the first diagonal block; each step forms the next one's
     hipLaunchKernelGGL(als_chol_diag_kernel, dim3(1), dim3(256), 0, s, CV, R, (int64_t)0, W, Z,
                        flag);
     for (int k = 0; k < nblk; ++k) {
