@@ -54,6 +54,8 @@ def rel(a, b):
     # ragged last block, and R = 300 (the model norm summed by workgroups)
     ((30, 28, 26), 3, 150, 2), ((12, 11, 10, 9), 2, 100, 2), ((40, 38, 36), 3, 300, 2),
     ((20, 18, 16), 3, 65, 2), ((24, 22, 20), 3, 128, 2),  # a 1-wide last block; whole blocks
+    # blocked update with many row blocks of M (a 700-row mode, first and middle)
+    ((700, 20, 18), 3, 100, 2), ((20, 700, 18), 3, 130, 2),
 ])
 def test_als_small_vs_oracle(dims, true_rank, R, iters):
     p = inputs.random_cp_problem(dims, true_rank, R, sigma=0.05, seed=31)
