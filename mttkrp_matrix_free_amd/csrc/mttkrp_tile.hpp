@@ -551,15 +551,10 @@ __device__ __forceinline__ void tile_pass(const KParams &p, unsigned char *smem,
             }
             // Reduce the tile rows against their factor rows and the outer
             // multiplier, one accumulator row g = (mb, e) at a time.  The
-            // factor loads of row g + 1 are issued before row g is used, so
-            // the round trips overlap while only two rows of factor values
-            // are held.  They use 32-bit offsets from the factor's base (its
+            // factor loads use 32-bit offsets from the factor's base (its
             // span is below 2^31 bytes); indices are clamped (rows past the
-            // tile's end are masked afterwards) and a missing second row
-            // factor reads the first and counts as 1, so no load sits under a
-            // branch.
-            // For fp32 the weights and their products with the tile are formed
-            // in fp32; the row sums are fp64.
+            // tile's end are masked afterwards), so no load depends on its
+            // lane's row.
             const bool two = p.Ur1 != nullptr;
             const unsigned IrB = (unsigned)p.IrB;
             const unsigned RS = (unsigned)(R * SZ);
@@ -569,51 +564,106 @@ __device__ __forceinline__ void tile_pass(const KParams &p, unsigned char *smem,
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) cofs_z[nb] = (unsigned)(colc[nb] * SZ);
             constexpr int NG = MB * 4;
-            T za[2][NB], zb[2][NB];
-            auto zload = [&](int g, T *a, T *b) {
-                const int64_t rr = row0 + (g >> 2) * 16 + Mfma<T>::row(q, g & 3);
-                const unsigned rc = rr < p.nrows ? (unsigned)rr : 0u;
-                const unsigned ia = two ? fdiv(rc, p.fd_IrB) : rc;
-                const unsigned ib = two ? rc - ia * IrB : 0u;
-                const unsigned oa = ia * RS, ob = ib * RS;
+            T w[NB];
+            auto outer_weight = [&]() {
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
-                    a[nb] = *reinterpret_cast<const T *>(za_base + (oa + cofs_z[nb]));
-                    b[nb] = *reinterpret_cast<const T *>(zb_base + (ob + cofs_z[nb]));
+                    T v = T(1);
+#pragma unroll
+                    for (int j = 0; j < 3; ++j) v *= j < p.nouter ? wv[j][nb] : T(1);
+                    w[nb] = v;
                 }
             };
-            zload(0, za[0], zb[0]);
-            T w[NB];
-#pragma unroll
-            for (int g = 0; g < NG; ++g) {
-                asm volatile("" ::: "memory");
-                if (g + 1 < NG) zload(g + 1, za[(g + 1) & 1], zb[(g + 1) & 1]);
-                if (g == 0) {
+            if constexpr (sizeof(T) == 8) {
+                // fp64: with at most 16 values of a factor per lane the loads
+                // of all rows go out at once (one round trip); otherwise the
+                // loads of row g + 1 are issued before row g is used, so only
+                // two rows are held.  An absent second factor reads the first
+                // and counts as 1 (no load sits under a branch).
+                constexpr bool ZALL = NG * NB <= 16;
+                constexpr int ZR = ZALL ? NG : 2;
+                T za[ZR][NB], zb[ZR][NB];
+                auto zload = [&](int g, T *a, T *b) {
+                    const int64_t rr = row0 + (g >> 2) * 16 + Mfma<T>::row(q, g & 3);
+                    const unsigned rc = rr < p.nrows ? (unsigned)rr : 0u;
+                    const unsigned ia = two ? fdiv(rc, p.fd_IrB) : rc;
+                    const unsigned ib = two ? rc - ia * IrB : 0u;
+                    const unsigned oa = ia * RS, ob = ib * RS;
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) {
-                        T v = T(1);
-#pragma unroll
-                        for (int j = 0; j < 3; ++j) v *= j < p.nouter ? wv[j][nb] : T(1);
-                        w[nb] = v;
+                        a[nb] = *reinterpret_cast<const T *>(za_base + (oa + cofs_z[nb]));
+                        b[nb] = *reinterpret_cast<const T *>(zb_base + (ob + cofs_z[nb]));
                     }
-                }
-                const int mb = g >> 2, e = g & 3;
-                const bool rok = row0 + mb * 16 + Mfma<T>::row(q, e) < p.nrows;
+                };
+                if (ZALL) {
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    if constexpr (sizeof(T) == 4) {
-                        // fp32: weight and product in fp32, the sum in fp64
-                        // (columns past the rank are never stored: no mask)
-                        T z = za[g & 1][nb] * (two ? zb[g & 1][nb] : T(1)) * w[nb];
-                        z = rok ? z : T(0);
-                        accrow[nb] += (double)(z * acc[mb][nb][e]);
-                    } else {
-                        const double zbv = two ? (double)zb[g & 1][nb] : 1.0;
-                        const double z = (double)za[g & 1][nb] * zbv * (double)w[nb];
+                    for (int g = 0; g < NG; ++g) zload(g, za[g % ZR], zb[g % ZR]);
+                } else {
+                    zload(0, za[0], zb[0]);
+                }
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+                    asm volatile("" ::: "memory");
+                    if (!ZALL && g + 1 < NG) zload(g + 1, za[(g + 1) % ZR], zb[(g + 1) % ZR]);
+                    if (g == 0) outer_weight();
+                    const int mb = g >> 2, e = g & 3;
+                    const bool rok = row0 + mb * 16 + Mfma<T>::row(q, e) < p.nrows;
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        const double zbv = two ? (double)zb[g % ZR][nb] : 1.0;
+                        const double z = (double)za[g % ZR][nb] * zbv * (double)w[nb];
                         const double t = z * (double)acc[mb][nb][e];
                         accrow[nb] += (rok && colok[nb]) ? t : 0.0;
                     }
                 }
+            } else {
+                // fp32: one copy of the row loop with a second row factor
+                // (TWO) and one without (its values are not read).  The
+                // factor values of ZR rows are loaded together: one round trip
+                // per batch of rows, at most 16 values of a factor per lane.
+                // The weights and their products with the tile are formed in
+                // fp32, the row sums in fp64 (columns past the rank are never
+                // stored: no mask).
+                auto rows = [&](auto two_c) {
+                    constexpr bool TWO = decltype(two_c)::value;
+                    constexpr int ZR = NG * NB <= 16 ? NG : 16 / NB;
+                    static_assert(NG % ZR == 0 && ZR >= 1, "whole batches of rows");
+                    T za[ZR][NB], zb[TWO ? ZR : 1][NB];
+                    auto zload = [&](int g, int u) {
+                        const int64_t rr = row0 + (g >> 2) * 16 + Mfma<T>::row(q, g & 3);
+                        const unsigned rc = rr < p.nrows ? (unsigned)rr : 0u;
+                        const unsigned ia = TWO ? fdiv(rc, p.fd_IrB) : rc;
+                        const unsigned oa = ia * RS;
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb) {
+                            za[u][nb] = *reinterpret_cast<const T *>(za_base + (oa + cofs_z[nb]));
+                            if constexpr (TWO)
+                                zb[u][nb] = *reinterpret_cast<const T *>(
+                                    zb_base + ((rc - ia * IrB) * RS + cofs_z[nb]));
+                        }
+                    };
+#pragma unroll
+                    for (int g = 0; g < NG; ++g) {
+                        if (g % ZR == 0) {
+                            asm volatile("" ::: "memory");
+#pragma unroll
+                            for (int u = 0; u < ZR; ++u) zload(g + u, u);
+                        }
+                        if (g == 0) outer_weight();  // (after the first batch's loads)
+                        const int mb = g >> 2, e = g & 3, u = g % ZR;
+                        const bool rok = row0 + mb * 16 + Mfma<T>::row(q, e) < p.nrows;
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb) {
+                            T z = TWO ? za[u][nb] * zb[TWO ? u : 0][nb] * w[nb] : za[u][nb] * w[nb];
+                            z = rok ? z : T(0);
+                            accrow[nb] += (double)(z * acc[mb][nb][e]);
+                        }
+                    }
+                };
+                if (two)
+                    rows(std::integral_constant<bool, true>());
+                else
+                    rows(std::integral_constant<bool, false>());
             }
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
