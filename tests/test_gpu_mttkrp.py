@@ -73,6 +73,10 @@ SWEEP = [
     ((17, 19, 23, 4), 19, np.float64),   # short last mode merged into the contraction
     ((9, 10, 11, 12, 13), 7, np.float32),
     ((24, 20, 50, 48), 72, np.float32),  # fp32 long merged contraction: 9 chunks, ragged last
+    # item reductions against two row factors (merged row modes): fp32 16- and 32-column
+    # tiles, and fp64 with an outer mode (every row's factor loads at once)
+    ((8, 50, 40, 20, 10), 16, np.float32), ((4, 33, 45, 60), 24, np.float32),
+    ((6, 30, 20, 24, 9), 12, np.float64),
 ]
 
 
