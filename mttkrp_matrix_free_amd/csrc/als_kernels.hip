@@ -1254,20 +1254,30 @@ __global__ __launch_bounds__(kRedThreads) void als_fit_kernel(
 // differs from the one-entry-at-a-time order by rounding only.
 // ---------------------------------------------------------------------------
 
-// V = Hadamard_{m != n} G_m (R x R, fp64), one thread per entry, modes in order.
-__global__ __launch_bounds__(256) void als_hadamard_kernel(const double *__restrict__ Gall,
-                                                           int order, int n, int64_t R,
-                                                           double *__restrict__ A,
-                                                           const int *__restrict__ flag)
+// Set-up of the blocked update in one launch: entries e < R^2 form V =
+// Hadamard_{m != n} G_m (modes in order) on and below the diagonal 64 x 64
+// tiles (the tiles above are never read), the rest copy M into its working
+// rows CM.
+__global__ __launch_bounds__(256) void als_aug_setup_kernel(const double *__restrict__ Gall,
+                                                            int order, int n, int64_t R,
+                                                            double *__restrict__ CV,
+                                                            const double *__restrict__ M,
+                                                            double *__restrict__ CM, int64_t IR,
+                                                            const int *__restrict__ flag)
 {
     if (*flag) return;
     const int64_t RR = R * R;
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (e >= RR) return;
-    double v = 1.0;
-    for (int m = 0; m < order; ++m)
-        if (m != n) v *= Gall[(int64_t)m * RR + e];
-    A[e] = v;
+    if (e < RR) {
+        const int64_t i = e / R, c = e - i * R;
+        if ((c >> 6) > (i >> 6)) return;
+        double v = 1.0;
+        for (int m = 0; m < order; ++m)
+            if (m != n) v *= Gall[(int64_t)m * RR + e];
+        CV[e] = v;
+    } else if (e - RR < IR) {
+        CM[e - RR] = M[e - RR];
+    }
 }
 
 // Pivot p = 16 pq + PP of the diagonal kernel below (PP a compile-time
@@ -1571,27 +1581,15 @@ __global__ __launch_bounds__(256) void als_aug_step_kernel(AugStep a)
         return;
     }
     // trailing: T = C(i, k) Z_k, then C(i, j) -= T C_V(j, k)^T.  The second
-    // operand's loads go out before the first product.
+    // operand's loads and this thread's entries of C(i, j) go out before the
+    // first product (an identity row block's entries right of its own block
+    // are still zero at its own step).
     double vb[16];
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
         const int c = th + 4 * u;
         vb[u] = (c < jn && tl < kn) ? a.CV[(j0 + c) * R + k0 + tl] : 0.0;
     }
-    product();
-    __syncthreads();  // every wave is done with the first operands
-#pragma unroll
-    for (int xx = 0; xx < 2; ++xx)
-#pragma unroll
-        for (int yy = 0; yy < 2; ++yy)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                As[wc + 16 * yy + r16][wr + 16 * xx + 4 * e + q] = acc[xx][yy][e];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) Bs[tl][th + 4 * u] = vb[u];
-    // this thread's entries of C(i, j) go out before the second product (an
-    // identity row block's entries right of its own block are still zero at
-    // its own step)
     const bool zero_old = sec == 1 && rb == k;
     double cv[16];
 #pragma unroll
@@ -1604,6 +1602,17 @@ __global__ __launch_bounds__(256) void als_aug_step_kernel(AugStep a)
                 cv[(xx * 2 + yy) * 4 + e] =
                     (r < nr && c < jn && !zero_old) ? C[(r0 + r) * R + j0 + c] : 0.0;
             }
+    product();
+    __syncthreads();  // every wave is done with the first operands
+#pragma unroll
+    for (int xx = 0; xx < 2; ++xx)
+#pragma unroll
+        for (int yy = 0; yy < 2; ++yy)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                As[wc + 16 * yy + r16][wr + 16 * xx + 4 * e + q] = acc[xx][yy][e];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) Bs[tl][th + 4 * u] = vb[u];
     __syncthreads();
     product();
     // the next diagonal block's tile: its new values also go to LDS (after
@@ -2087,7 +2096,8 @@ hipError_t launch_fit(const double *M, const T *Ulast, int64_t Ilast, const doub
 }
 
 // U_new = M V^{-1} for ranks past the one-workgroup update (R > 64), by
-// 64-wide column blocks: V = Hadamard_{m != n} G_m into CV, M into CM, then
+// 64-wide column blocks: V = Hadamard_{m != n} G_m into CV (its tiles on and
+// below the diagonal) and M into CM in one launch, then
 // the first diagonal block (W_0, Z_0) and per block
 // k one step launch (panels and trailing updates of every row block, and
 // block k + 1's diagonal kernel), and at the end U = Y_M Y_I^T into CM
@@ -2103,11 +2113,10 @@ hipError_t launch_update_blocked(const double *Gall, int order, int n, int64_t R
     if (mblk + 2 * (int64_t)nblk > 65535) return hipErrorInvalidValue;  // grid limit
     hipError_t e = allow_large_lds(reinterpret_cast<const void *>(als_aug_step_kernel));
     if (e != hipSuccess) return e;
-    const int64_t RR = R * R;
-    hipLaunchKernelGGL(als_hadamard_kernel, dim3((unsigned)((RR + 255) / 256)), dim3(256), 0, s,
-                       Gall, order, n, R, CV, flag);
-    e = hipMemcpyAsync(CM, M, (size_t)(I * R) * sizeof(double), hipMemcpyDeviceToDevice, s);
-    if (e != hipSuccess) return e;
+    const int64_t RR = R * R, IR = I * R;
+    if ((RR + IR + 255) / 256 > INT32_MAX) return hipErrorInvalidValue;  // grid limit
+    hipLaunchKernelGGL(als_aug_setup_kernel, dim3((unsigned)((RR + IR + 255) / 256)), dim3(256), 0,
+                       s, Gall, order, n, R, CV, M, CM, IR, flag);
     AugStep a{CV, CM, CI, YM, YI, W, Z, R, I, 0, nblk, (int)mblk, flag};
     // the first diagonal block; each step forms the next one's
     hipLaunchKernelGGL(als_chol_diag_kernel, dim3(1), dim3(256), 0, s, CV, R, (int64_t)0, W, Z,
