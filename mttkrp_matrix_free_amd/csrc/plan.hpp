@@ -67,16 +67,18 @@ __host__ __device__ constexpr int tile_min_waves(int elem, int mb, int nb, bool 
     return tile_regs(elem, mb, nb, form1, slots, 2) <= 256 ? 2 : 1;
 }
 // Waves per SIMD of a kernel instantiation (its launch bound).  Besides the
-// register model's one or two: three for the fp64 form-0 tiles of the
-// rank-tiled, matrix-core-bound plans -- 32 x 64 tiles of row-major outputs
-// and 64 x 32 tiles of row-contiguous outputs, one outer slot, four-wave
-// workgroups -- whose kernels fit 168 registers without spills once they
-// keep one step of tensor loads in flight (512^3 rank 2000: the matrix cores
-// busy 85% of a launch at two waves per SIMD; 8.30 -> 8.05 ms per mode).
+// register model's one or two: three for the form-0 tiles of the rank-tiled,
+// matrix-core-bound plans -- 32 x 64 tiles of row-major outputs and 64 x 32
+// tiles of row-contiguous outputs, four-wave workgroups, one outer slot in
+// fp64, one or two in fp32 -- whose kernels fit 168 registers without spills
+// once they keep one step of tensor loads in flight (512^3 rank 2000: the
+// matrix cores busy 85% of a launch at two waves per SIMD; 8.30 -> 8.05 ms
+// per mode; 128 x 128 x 128 x 64 fp32 rank 512: 1.29 -> 1.22 ms, rank 64:
+// 0.18 -> 0.17 ms).
 __host__ __device__ constexpr bool tile_three_waves(int elem, int mb, int nb, bool form1, int slots,
                                                     bool rc, int w)
 {
-    return elem == 8 && !form1 && slots == 1 && w == 4 &&
+    return !form1 && w == 4 && (elem == 8 ? slots == 1 : (slots == 1 || slots == 2)) &&
            ((mb == 2 && nb == 4 && !rc) || (mb == 4 && nb == 2 && rc));
 }
 __host__ __device__ constexpr int tile_occupancy(int elem, int mb, int nb, bool form1, int slots,
