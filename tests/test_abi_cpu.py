@@ -215,6 +215,27 @@ def test_workspace_far_below_khatri_rao_at_rank_2000(L):
         assert ws.value <= 16 * 512 * 2000 * 8
 
 
+def test_three_wave_plans_leave_room_for_three_workgroups(L):
+    """Four-wave form-0 workgroups of the 32 x 64 row-major and 64 x 32
+    row-contiguous tiles run three waves per SIMD (fp64 with one outer slot,
+    fp32 with one or two): their LDS must let three share a compute unit
+    (160 KB).  The matrix-core-bound workloads take such plans."""
+    seen = 0
+    for dims, R, eb in WORKLOADS:
+        d = len(dims)
+        for n in range(d):
+            info = _lib.PlanInfo()
+            assert L.mttkrp_plan(dims_arr(dims), d, R, n, eb, ctypes.byref(info)) == 0
+            slots = max(1, sum(1 for m in info.outer_modes if m >= 0))
+            tile = (info.mb, info.nb, info.layout)
+            three = (info.form == 0 and info.waves == 4 and tile in ((2, 4, 0), (4, 2, 1)) and
+                     (slots == 1 if eb == 8 else slots in (1, 2)))
+            if three:
+                seen += 1
+                assert 3 * info.lds_bytes <= 160 * 1024, (dims, R, n, info.lds_bytes)
+    assert seen >= 10  # the 512^3 rank-2000 modes and the fp32 rank-64 and rank-512 modes
+
+
 MODEL_CASES = [((256, 256, 256), 32, 8), ((512, 512, 512), 2000, 8), ((128, 128, 128, 64), 8, 4),
                ((128, 128, 128, 64), 512, 4), ((50, 50, 50, 20, 10), 64, 8), ((33, 17, 19), 17, 8)]
 
